@@ -1,0 +1,284 @@
+// C ABI of libcp_attn: argument validation, error reporting and kernel dispatch.
+// Every check runs on the host before any launch, so a rejected call touches no
+// device memory.  Nothing here allocates or synchronizes.
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "cp_attn.h"
+#include "launch.h"
+
+namespace cp {
+// defined in attn_rowwise.hip / attn_bwd_mfma.hip
+hipError_t launch_attn_bwd_rowwise_bf16(const AttnProblem& p, const void* q, const void* k,
+                                        const void* v, const void* out, const float* lse,
+                                        const void* dout, float* dq, float* dk, float* dv,
+                                        int accumulate, float* delta, hipStream_t s);
+}  // namespace cp
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cp_status_t fail(cp_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+cp_status_t ok() {
+  g_last_error.clear();
+  return CP_OK;
+}
+
+cp_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + uintptr_t(bbytes) && b0 < a0 + uintptr_t(abytes);
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t dtype_bytes(int32_t dt) { return dt == CP_DTYPE_BF16 ? 2 : 4; }
+
+// Shared validation of cp_attn_fwd / cp_attn_bwd arguments; fills the device problem.
+cp_status_t check_attn(const cp_attn_args_t* a, const void* q, const void* k, const void* v,
+                       cp::AttnProblem* p) {
+  if (!a) return fail(CP_ERR_INVALID, "args is NULL");
+  if (!q || !k || !v) return fail(CP_ERR_INVALID, "q, k and v must be non-NULL");
+  if (a->batch < 1 || a->seqlen_q < 1 || a->seqlen_k < 1 || a->heads_q < 1 || a->heads_kv < 1 ||
+      a->head_dim < 1)
+    return fail(CP_ERR_INVALID,
+                "sizes must be >= 1 (batch=%lld seqlen_q=%lld seqlen_k=%lld heads_q=%lld "
+                "heads_kv=%lld head_dim=%lld)",
+                (long long)a->batch, (long long)a->seqlen_q, (long long)a->seqlen_k,
+                (long long)a->heads_q, (long long)a->heads_kv, (long long)a->head_dim);
+  if (a->heads_q % a->heads_kv)
+    return fail(CP_ERR_INVALID, "heads_q %lld is not a multiple of heads_kv %lld",
+                (long long)a->heads_q, (long long)a->heads_kv);
+  if (a->dtype != CP_DTYPE_BF16 && a->dtype != CP_DTYPE_F32)
+    return fail(CP_ERR_INVALID, "unknown dtype %d", (int)a->dtype);
+  if (a->causal != 0 && a->causal != 1) return fail(CP_ERR_INVALID, "causal must be 0 or 1");
+  if (a->window < 0 || a->window > INT_MAX)
+    return fail(CP_ERR_INVALID, "window %lld must be in [0, 2^31)", (long long)a->window);
+  if ((a->q_seg == nullptr) != (a->k_seg == nullptr))
+    return fail(CP_ERR_INVALID, "q_seg and k_seg must both be given or both be NULL");
+  if (!(a->softmax_scale >= 0.0f) || std::isinf(a->softmax_scale))
+    return fail(CP_ERR_INVALID, "softmax_scale must be finite and >= 0 (0 selects 1/sqrt(D))");
+  if (a->seqlen_q > INT_MAX || a->seqlen_k > INT_MAX || a->batch > 65535 || a->heads_q > 65535)
+    return fail(CP_ERR_UNSUPPORTED, "sizes beyond the launch grid (batch, heads_q <= 65535; seqlen < 2^31)");
+  if (!a->q_pos && (a->q_offset < 0 || a->q_offset + a->seqlen_q > INT_MAX))
+    return fail(CP_ERR_INVALID, "q_offset %lld: positions must lie in [0, 2^31)", (long long)a->q_offset);
+  if (!a->k_pos && (a->k_offset < 0 || a->k_offset + a->seqlen_k > INT_MAX))
+    return fail(CP_ERR_INVALID, "k_offset %lld: positions must lie in [0, 2^31)", (long long)a->k_offset);
+  if (a->dtype == CP_DTYPE_BF16) {
+    if (a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
+      return fail(CP_ERR_UNSUPPORTED, "bf16 attention is built for head_dim 32, 64, 128 (got %lld)",
+                  (long long)a->head_dim);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+      return fail(CP_ERR_INVALID, "bf16 q, k, v must be 16-byte aligned");
+  } else if (a->head_dim > 128) {
+    return fail(CP_ERR_UNSUPPORTED, "float32 attention is built for head_dim <= 128 (got %lld)",
+                (long long)a->head_dim);
+  }
+  p->B = int(a->batch);
+  p->Sq = int(a->seqlen_q);
+  p->Sk = int(a->seqlen_k);
+  p->Hq = int(a->heads_q);
+  p->Hkv = int(a->heads_kv);
+  p->D = int(a->head_dim);
+  p->causal = a->causal;
+  p->q_offset = int(a->q_pos ? 0 : a->q_offset);
+  p->k_offset = int(a->k_pos ? 0 : a->k_offset);
+  p->q_pos = a->q_pos;
+  p->k_pos = a->k_pos;
+  p->q_seg = a->q_seg;
+  p->k_seg = a->k_seg;
+  p->window = int(a->window);
+  p->scale = a->softmax_scale > 0.0f ? a->softmax_scale : 1.0f / std::sqrt(float(a->head_dim));
+  return CP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cp_status_string(cp_status_t st) {
+  switch (st) {
+    case CP_OK: return "CP_OK";
+    case CP_ERR_INVALID: return "CP_ERR_INVALID";
+    case CP_ERR_UNSUPPORTED: return "CP_ERR_UNSUPPORTED";
+    case CP_ERR_ALIAS: return "CP_ERR_ALIAS";
+    case CP_ERR_HIP: return "CP_ERR_HIP";
+  }
+  return "CP_ERR_UNKNOWN";
+}
+
+const char* cp_last_error(void) { return g_last_error.c_str(); }
+
+cp_status_t cp_attn_fwd(const cp_attn_args_t* a, const void* q, const void* k, const void* v,
+                        void* out, float* lse, hipStream_t stream) {
+  cp::AttnProblem p;
+  cp_status_t st = check_attn(a, q, k, v, &p);
+  if (st != CP_OK) return st;
+  if (!out || !lse) return fail(CP_ERR_INVALID, "out and lse must be non-NULL");
+  const int64_t eb = dtype_bytes(a->dtype);
+  const int64_t qbytes = a->batch * a->seqlen_q * a->heads_q * a->head_dim * eb;
+  const int64_t kbytes = a->batch * a->seqlen_k * a->heads_kv * a->head_dim * eb;
+  const int64_t lbytes = a->batch * a->heads_q * a->seqlen_q * 4;
+  for (const void* in : {q, k, v}) {
+    const int64_t ib = (in == q) ? qbytes : kbytes;
+    if (overlaps(out, qbytes, in, ib) || overlaps(lse, lbytes, in, ib))
+      return fail(CP_ERR_ALIAS, "out/lse overlap an input");
+  }
+  if (overlaps(out, qbytes, lse, lbytes)) return fail(CP_ERR_ALIAS, "out overlaps lse");
+  hipError_t e;
+  if (a->dtype == CP_DTYPE_BF16) {
+    if (!aligned(out, 16)) return fail(CP_ERR_INVALID, "bf16 out must be 16-byte aligned");
+    e = cp::launch_attn_fwd_bf16(p, q, k, v, out, lse, stream);
+  } else {
+    e = cp::launch_attn_fwd_f32(p, static_cast<const float*>(q), static_cast<const float*>(k),
+                                static_cast<const float*>(v), static_cast<float*>(out), lse, stream);
+  }
+  return hip_status(e, "cp_attn_fwd launch");
+}
+
+size_t cp_attn_bwd_workspace_size(const cp_attn_args_t* a) {
+  if (!a || a->batch < 1 || a->heads_q < 1 || a->seqlen_q < 1) return 0;
+  const size_t n = size_t(a->batch) * size_t(a->heads_q) * size_t(a->seqlen_q) * sizeof(float);
+  return (n + 255) & ~size_t(255);
+}
+
+cp_status_t cp_attn_bwd(const cp_attn_args_t* a, const void* q, const void* k, const void* v,
+                        const void* out, const float* lse, const void* dout, float* dq, float* dk,
+                        float* dv, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  cp::AttnProblem p;
+  cp_status_t st = check_attn(a, q, k, v, &p);
+  if (st != CP_OK) return st;
+  if (!out || !lse || !dout || !dq || !dk || !dv)
+    return fail(CP_ERR_INVALID, "out, lse, dout, dq, dk, dv must be non-NULL");
+  if (accumulate != 0 && accumulate != 1) return fail(CP_ERR_INVALID, "accumulate must be 0 or 1");
+  const size_t need = cp_attn_bwd_workspace_size(a);
+  if (!workspace || workspace_bytes < need)
+    return fail(CP_ERR_INVALID, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (!aligned(workspace, 16)) return fail(CP_ERR_INVALID, "workspace must be 16-byte aligned");
+  const int64_t eb = dtype_bytes(a->dtype);
+  const int64_t qbytes = a->batch * a->seqlen_q * a->heads_q * a->head_dim * eb;
+  const int64_t kbytes = a->batch * a->seqlen_k * a->heads_kv * a->head_dim * eb;
+  const int64_t lbytes = a->batch * a->heads_q * a->seqlen_q * 4;
+  const int64_t dqb = a->batch * a->seqlen_q * a->heads_q * a->head_dim * 4;
+  const int64_t dkb = a->batch * a->seqlen_k * a->heads_kv * a->head_dim * 4;
+  const void* ins[] = {q, k, v, out, lse, dout, workspace};
+  const int64_t inb[] = {qbytes, kbytes, kbytes, qbytes, lbytes, qbytes, int64_t(need)};
+  const void* outs[] = {dq, dk, dv};
+  const int64_t outb[] = {dqb, dkb, dkb};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 7; ++i)
+      if (overlaps(outs[o], outb[o], ins[i], inb[i]))
+        return fail(CP_ERR_ALIAS, "a gradient buffer overlaps an input or the workspace");
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlaps(outs[o], outb[o], outs[o2], outb[o2]))
+        return fail(CP_ERR_ALIAS, "gradient buffers overlap each other");
+  }
+  float* delta = static_cast<float*>(workspace);
+  hipError_t e;
+  if (a->dtype == CP_DTYPE_BF16) {
+    if (!aligned(out, 16) || !aligned(dout, 16))
+      return fail(CP_ERR_INVALID, "bf16 out and dout must be 16-byte aligned");
+    e = cp::launch_attn_bwd_bf16(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, stream);
+  } else {
+    e = cp::launch_attn_bwd_f32(p, static_cast<const float*>(q), static_cast<const float*>(k),
+                                static_cast<const float*>(v), static_cast<const float*>(out), lse,
+                                static_cast<const float*>(dout), dq, dk, dv, accumulate, delta, stream);
+  }
+  return hip_status(e, "cp_attn_bwd launch");
+}
+
+cp_status_t cp_lse_merge(int64_t batch, int64_t seqlen, int64_t heads, int64_t head_dim,
+                         float* out_acc, float* lse_acc, const void* out_blk, const float* lse_blk,
+                         int32_t blk_dtype, hipStream_t stream) {
+  if (batch < 1 || seqlen < 1 || heads < 1 || head_dim < 1)
+    return fail(CP_ERR_INVALID, "sizes must be >= 1");
+  if (blk_dtype != CP_DTYPE_BF16 && blk_dtype != CP_DTYPE_F32)
+    return fail(CP_ERR_INVALID, "unknown blk_dtype %d", (int)blk_dtype);
+  if (head_dim % 4 || 64 % (head_dim / 4))
+    return fail(CP_ERR_UNSUPPORTED, "merge is built for head_dim in {4,8,16,32,64,128,256} (got %lld)",
+                (long long)head_dim);
+  if (!out_acc || !lse_acc || !out_blk || !lse_blk) return fail(CP_ERR_INVALID, "NULL buffer");
+  if (!aligned(out_acc, 16) || !aligned(out_blk, blk_dtype == CP_DTYPE_BF16 ? 8 : 16))
+    return fail(CP_ERR_INVALID, "out_acc must be 16-byte aligned, out_blk 8 (bf16) / 16 (f32)");
+  const int64_t rows = batch * seqlen * heads;
+  if (overlaps(out_acc, rows * head_dim * 4, out_blk, rows * head_dim * dtype_bytes(blk_dtype)) ||
+      overlaps(lse_acc, rows * 4, lse_blk, rows * 4) || overlaps(out_acc, rows * head_dim * 4, lse_acc, rows * 4))
+    return fail(CP_ERR_ALIAS, "merge buffers overlap");
+  return hip_status(cp::launch_lse_merge(batch, seqlen, heads, head_dim, out_acc, lse_acc, out_blk,
+                                         lse_blk, blk_dtype == CP_DTYPE_BF16, stream),
+                    "cp_lse_merge launch");
+}
+
+static cp_status_t relayout(const void* in, void* out, int64_t P, int64_t batch, int64_t seqlen,
+                            int64_t heads, int64_t head_dim, int64_t eb, bool inverse,
+                            hipStream_t stream) {
+  if (P < 1 || batch < 1 || seqlen < 1 || heads < 1 || head_dim < 1)
+    return fail(CP_ERR_INVALID, "sizes must be >= 1");
+  if (eb != 2 && eb != 4) return fail(CP_ERR_INVALID, "elem_bytes must be 2 or 4 (got %lld)", (long long)eb);
+  if (seqlen % P)
+    return fail(CP_ERR_INVALID, "seqlen %lld is not divisible by the Ulysses degree %lld",
+                (long long)seqlen, (long long)P);
+  if (heads % P)
+    return fail(CP_ERR_INVALID,
+                "heads %lld is not divisible by the Ulysses degree %lld (the degree cannot exceed "
+                "the head count; for k/v, the kv head count)",
+                (long long)heads, (long long)P);
+  if (!in || !out) return fail(CP_ERR_INVALID, "NULL buffer");
+  const int64_t bytes = batch * seqlen * heads * head_dim * eb;
+  if (overlaps(in, bytes, out, bytes)) return fail(CP_ERR_ALIAS, "in and out overlap");
+  if ((seqlen / P) * heads * head_dim * eb >= (int64_t(1) << 31) || P * batch * P >= (int64_t(1) << 31))
+    return fail(CP_ERR_UNSUPPORTED, "relayout span exceeds 2^31 bytes");
+  return hip_status(cp::launch_ulysses(in, out, P, batch, seqlen, heads, head_dim, eb, inverse, stream),
+                    "cp_ulysses_relayout launch");
+}
+
+cp_status_t cp_ulysses_relayout(const void* in, void* out, int64_t P, int64_t batch, int64_t seqlen,
+                                int64_t heads, int64_t head_dim, int64_t elem_bytes,
+                                hipStream_t stream) {
+  return relayout(in, out, P, batch, seqlen, heads, head_dim, elem_bytes, false, stream);
+}
+
+cp_status_t cp_ulysses_relayout_inv(const void* in, void* out, int64_t P, int64_t batch,
+                                    int64_t seqlen, int64_t heads, int64_t head_dim,
+                                    int64_t elem_bytes, hipStream_t stream) {
+  return relayout(in, out, P, batch, seqlen, heads, head_dim, elem_bytes, true, stream);
+}
+
+cp_status_t cp_zigzag_reorder(const void* in, void* out, int64_t batch, int64_t seqlen,
+                              int64_t row_bytes, int64_t P, int32_t strategy, int32_t inverse,
+                              hipStream_t stream) {
+  if (batch < 1 || seqlen < 1 || row_bytes < 1 || P < 1) return fail(CP_ERR_INVALID, "sizes must be >= 1");
+  if (strategy == 1) return fail(CP_ERR_UNSUPPORTED, "reorder strategy 1 (striped) is not built");
+  if (strategy != 0) return fail(CP_ERR_INVALID, "unknown reorder strategy %d", (int)strategy);
+  if (inverse != 0 && inverse != 1) return fail(CP_ERR_INVALID, "inverse must be 0 or 1");
+  if (seqlen % (2 * P))
+    return fail(CP_ERR_INVALID, "seqlen %lld is not divisible into 2P = %lld chunks", (long long)seqlen,
+                (long long)(2 * P));
+  if (!in || !out) return fail(CP_ERR_INVALID, "NULL buffer");
+  const int64_t bytes = batch * seqlen * row_bytes;
+  if (overlaps(in, bytes, out, bytes)) return fail(CP_ERR_ALIAS, "in and out overlap");
+  if (batch * 2 * P >= (int64_t(1) << 31)) return fail(CP_ERR_UNSUPPORTED, "too many chunks");
+  return hip_status(cp::launch_zigzag(in, out, batch, seqlen, row_bytes, P, inverse != 0, stream),
+                    "cp_zigzag_reorder launch");
+}
+
+}  // extern "C"

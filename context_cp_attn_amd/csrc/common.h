@@ -1,0 +1,59 @@
+// Internal helpers shared by the HIP kernels of libcp_attn (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define CP_DEVICE __device__ __forceinline__
+
+namespace cp {
+
+// ---- bf16 <-> f32 -------------------------------------------------------------
+// bf16 is stored as its 16 raw bits.  Widening is exact (shift into the high half).
+CP_DEVICE float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Narrowing rounds to nearest, ties to even, through the compiler's __bf16 cast
+// (one v_cvt_pk_bf16_f32 on gfx950).
+CP_DEVICE uint16_t f32_to_bf16(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+CP_DEVICE uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static CP_DEVICE float load(const float* p) { return *p; }
+  static CP_DEVICE void store(float* p, float x) { *p = x; }
+};
+template <> struct Elem<uint16_t> {
+  static CP_DEVICE float load(const uint16_t* p) { return bf16_to_f32(*p); }
+  static CP_DEVICE void store(uint16_t* p, float x) { *p = f32_to_bf16(x); }
+};
+
+// ---- wave64 reductions ----------------------------------------------------------
+CP_DEVICE float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// ---- visibility of a (query, key) pair -------------------------------------------
+// Positions are int32 global token indices; segments int32 document ids.
+struct MaskSpec {
+  int causal;
+  int window;        // 0 = none
+  int has_seg;
+};
+
+CP_DEVICE bool pair_visible(const MaskSpec& m, int qp, int kp, int qs, int ks) {
+  bool vis = true;
+  if (m.causal) vis = vis && (kp <= qp);
+  if (m.has_seg) vis = vis && (qs == ks);
+  if (m.window) vis = vis && (qp - kp < m.window);
+  return vis;
+}
+
+}  // namespace cp

@@ -1,0 +1,44 @@
+// Kernel launchers behind the C ABI.  Arguments are already validated by api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cp {
+
+// Device-side description of one attention block (see cp_attn_args_t).
+struct AttnProblem {
+  int B, Sq, Sk, Hq, Hkv, D;
+  int causal;
+  int q_offset, k_offset;     // used when the position arrays are NULL
+  const int* q_pos;           // [Sq] or NULL
+  const int* k_pos;           // [Sk] or NULL
+  const int* q_seg;           // [B,Sq] or NULL
+  const int* k_seg;           // [B,Sk] or NULL
+  int window;                 // 0 = none
+  float scale;                // softmax scale (natural-log domain)
+};
+
+// forward
+hipError_t launch_attn_fwd_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
+                                void* out, float* lse, hipStream_t s);
+hipError_t launch_attn_fwd_f32(const AttnProblem& p, const float* q, const float* k, const float* v,
+                               float* out, float* lse, hipStream_t s);
+
+// backward: delta workspace is [B,Hq,Sq] float32
+hipError_t launch_attn_bwd_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
+                                const void* out, const float* lse, const void* dout, float* dq,
+                                float* dk, float* dv, int accumulate, float* delta, hipStream_t s);
+hipError_t launch_attn_bwd_f32(const AttnProblem& p, const float* q, const float* k, const float* v,
+                               const float* out, const float* lse, const float* dout, float* dq,
+                               float* dk, float* dv, int accumulate, float* delta, hipStream_t s);
+
+// data movement
+hipError_t launch_lse_merge(int64_t B, int64_t S, int64_t H, int64_t D, float* acc, float* lse_acc,
+                            const void* blk, const float* lse_blk, int blk_is_bf16, hipStream_t s);
+hipError_t launch_ulysses(const void* in, void* out, int64_t P, int64_t B, int64_t S, int64_t H,
+                          int64_t D, int64_t eb, bool inverse, hipStream_t s);
+hipError_t launch_zigzag(const void* in, void* out, int64_t B, int64_t S, int64_t row_bytes,
+                         int64_t P, bool inverse, hipStream_t s);
+
+}  // namespace cp

@@ -1,0 +1,217 @@
+// Data-movement kernels: the Ulysses sequence<->head relayout of all simulated ranks
+// and the zigzag (dual-chunk-swap) reorder.  Both are permutations of contiguous
+// byte runs, so each is a streaming copy: every thread moves VPT vectors of VB bytes,
+// writes are fully coalesced in output order and reads are coalesced within a run.
+//
+// Ulysses relayout: handbook "Context parallelism: Ring Attention and Ulysses",
+// §"Ulysses" (seq_to_head / head_to_seq).  A run is one rank's head slice of one
+// token: (H/P)*D elements.
+// Zigzag: the same handbook, §"The zigzag partition" (rank r takes chunks r and
+// 2P-1-r); a run is one chunk of S/(2P) token rows.
+#include "common.h"
+#include "launch.h"
+
+namespace cp {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVPT = 4;  // vectors per thread per pass: loads issued before stores
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int VB> struct Vec;
+template <> struct Vec<16> { using T = u32x4; };
+template <> struct Vec<8> { using T = u32x2; };
+template <> struct Vec<4> { using T = uint32_t; };
+template <> struct Vec<2> { using T = uint16_t; };
+template <> struct Vec<1> { using T = uint8_t; };
+
+// in [P][B][Sp][P][R] (source rank s, batch, row i, destination p, vector r)
+// out [P][B][P][Sp][R] (destination p, batch, source s, row i, vector r)
+// One grid slice per (p, b, s) output span of Sp*R vectors.
+template <typename V>
+__global__ __launch_bounds__(kThreads) void ulysses_fwd_kernel(const V* __restrict__ in,
+                                                               V* __restrict__ out, int P, int B,
+                                                               int Sp, int R, int blocks_per_span) {
+  const int span = blockIdx.x / blocks_per_span;
+  const int blk = blockIdx.x - span * blocks_per_span;
+  const int s = span % P;
+  const int pb = span / P;
+  const int b = pb % B;
+  const int p = pb / B;
+  // per-span counts fit in 32 bits (checked by the launcher)
+  const uint32_t n = uint32_t(Sp) * uint32_t(R);
+  const V* src = in + (int64_t(s) * B + b) * Sp * int64_t(P) * R + int64_t(p) * R;
+  V* dst = out + int64_t(span) * n;
+  const uint32_t PR = uint32_t(P) * uint32_t(R);
+  for (uint32_t base = uint32_t(blk) * kThreads * kVPT + threadIdx.x; base < n;
+       base += uint32_t(blocks_per_span) * kThreads * kVPT) {
+    V vals[kVPT];
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const uint32_t idx = base + uint32_t(u) * kThreads;
+      if (idx < n) {
+        const uint32_t i = idx / uint32_t(R);
+        const uint32_t r = idx - i * uint32_t(R);
+        vals[u] = __builtin_nontemporal_load(src + int64_t(i) * PR + r);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const uint32_t idx = base + uint32_t(u) * kThreads;
+      if (idx < n) __builtin_nontemporal_store(vals[u], dst + idx);
+    }
+  }
+}
+
+// in [P][B][P][Sp][R] (p, b, s, i, r) -> out [P][B][Sp][P][R] (s, b, i, p, r).
+// One grid slice per (s, b) output span of Sp*P*R vectors.
+template <typename V>
+__global__ __launch_bounds__(kThreads) void ulysses_inv_kernel(const V* __restrict__ in,
+                                                               V* __restrict__ out, int P, int B,
+                                                               int Sp, int R, int blocks_per_span) {
+  const int span = blockIdx.x / blocks_per_span;
+  const int blk = blockIdx.x - span * blocks_per_span;
+  const int s = span / B;
+  const int b = span - s * B;
+  const uint32_t PR = uint32_t(P) * uint32_t(R);
+  const uint32_t n = uint32_t(Sp) * PR;  // fits in 32 bits (checked by the launcher)
+  V* dst = out + int64_t(span) * n;
+  // element (p, i, r) of the source lives at ((p*B + b)*P + s)*Sp*R + i*R + r
+  const V* src = in + (int64_t(b) * P + s) * Sp * int64_t(R);
+  const int64_t pstride = int64_t(B) * P * Sp * R;
+  for (uint32_t base = uint32_t(blk) * kThreads * kVPT + threadIdx.x; base < n;
+       base += uint32_t(blocks_per_span) * kThreads * kVPT) {
+    V vals[kVPT];
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const uint32_t idx = base + uint32_t(u) * kThreads;
+      if (idx < n) {
+        const uint32_t i = idx / PR;
+        const uint32_t rem = idx - i * PR;
+        const uint32_t p = rem / uint32_t(R);
+        const uint32_t r = rem - p * uint32_t(R);
+        vals[u] = __builtin_nontemporal_load(src + int64_t(p) * pstride + int64_t(i) * R + r);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const uint32_t idx = base + uint32_t(u) * kThreads;
+      if (idx < n) __builtin_nontemporal_store(vals[u], dst + idx);
+    }
+  }
+}
+
+// Chunk copy: the output slot j of batch b receives input chunk order(j) (forward)
+// or the output chunk order(j) receives input slot j (inverse), where order(2r) = r
+// and order(2r+1) = 2P-1-r.
+template <typename V>
+__global__ __launch_bounds__(kThreads) void zigzag_kernel(const V* __restrict__ in,
+                                                          V* __restrict__ out, int P,
+                                                          int64_t chunk_vecs, int inverse,
+                                                          int blocks_per_span) {
+  const int span = blockIdx.x / blocks_per_span;
+  const int blk = blockIdx.x - span * blocks_per_span;
+  const int nch = 2 * P;
+  const int b = span / nch;
+  const int slot = span - b * nch;
+  const int r = slot >> 1;
+  const int chunk = (slot & 1) ? (nch - 1 - r) : r;
+  const int src_c = inverse ? slot : chunk;
+  const int dst_c = inverse ? chunk : slot;
+  const V* src = in + (int64_t(b) * nch + src_c) * chunk_vecs;
+  V* dst = out + (int64_t(b) * nch + dst_c) * chunk_vecs;
+  for (int64_t base = (int64_t(blk) * kThreads * kVPT) + threadIdx.x; base < chunk_vecs;
+       base += int64_t(blocks_per_span) * kThreads * kVPT) {
+    V vals[kVPT];
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const int64_t idx = base + int64_t(u) * kThreads;
+      if (idx < chunk_vecs) vals[u] = __builtin_nontemporal_load(src + idx);
+    }
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const int64_t idx = base + int64_t(u) * kThreads;
+      if (idx < chunk_vecs) __builtin_nontemporal_store(vals[u], dst + idx);
+    }
+  }
+}
+
+int pick_vec_bytes(int64_t run_bytes, const void* a, const void* b) {
+  const uintptr_t al = reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b);
+  for (int vb = 16; vb > 1; vb >>= 1)
+    if (run_bytes % vb == 0 && al % vb == 0) return vb;
+  return 1;
+}
+
+// Blocks per span so that the whole grid holds about 8 resident blocks per CU
+// (256 CUs) while a span never gets more blocks than it has work.
+int blocks_for(int64_t spans, int64_t vecs_per_span) {
+  const int64_t per_block = int64_t(kThreads) * kVPT;
+  int64_t need = (vecs_per_span + per_block - 1) / per_block;
+  int64_t want = (2048 + spans - 1) / spans;
+  if (want < 1) want = 1;
+  int64_t bps = need < want ? need : want;
+  return int(bps < 1 ? 1 : bps);
+}
+
+template <int VB>
+hipError_t ulysses_vb(const void* in, void* out, int P, int B, int Sp, int64_t run_bytes,
+                      bool inverse, hipStream_t s) {
+  using V = typename Vec<VB>::T;
+  const int R = int(run_bytes / VB);
+  if (!inverse) {
+    const int64_t spans = int64_t(P) * B * P;
+    const int bps = blocks_for(spans, int64_t(Sp) * R);
+    hipLaunchKernelGGL(ulysses_fwd_kernel<V>, dim3(unsigned(spans * bps)), dim3(kThreads), 0, s,
+                       static_cast<const V*>(in), static_cast<V*>(out), P, B, Sp, R, bps);
+  } else {
+    const int64_t spans = int64_t(P) * B;
+    const int bps = blocks_for(spans, int64_t(Sp) * P * R);
+    hipLaunchKernelGGL(ulysses_inv_kernel<V>, dim3(unsigned(spans * bps)), dim3(kThreads), 0, s,
+                       static_cast<const V*>(in), static_cast<V*>(out), P, B, Sp, R, bps);
+  }
+  return hipGetLastError();
+}
+
+template <int VB>
+hipError_t zigzag_vb(const void* in, void* out, int B, int P, int64_t chunk_bytes, bool inverse,
+                     hipStream_t s) {
+  using V = typename Vec<VB>::T;
+  const int64_t cv = chunk_bytes / VB;
+  const int64_t spans = int64_t(B) * 2 * P;
+  const int bps = blocks_for(spans, cv);
+  hipLaunchKernelGGL(zigzag_kernel<V>, dim3(unsigned(spans * bps)), dim3(kThreads), 0, s,
+                     static_cast<const V*>(in), static_cast<V*>(out), P, cv, inverse ? 1 : 0, bps);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ulysses(const void* in, void* out, int64_t P, int64_t B, int64_t S, int64_t H,
+                          int64_t D, int64_t eb, bool inverse, hipStream_t s) {
+  const int64_t run = (H / P) * D * eb;
+  const int Sp = int(S / P);
+  switch (pick_vec_bytes(run, in, out)) {
+    case 16: return ulysses_vb<16>(in, out, int(P), int(B), Sp, run, inverse, s);
+    case 8: return ulysses_vb<8>(in, out, int(P), int(B), Sp, run, inverse, s);
+    case 4: return ulysses_vb<4>(in, out, int(P), int(B), Sp, run, inverse, s);
+    case 2: return ulysses_vb<2>(in, out, int(P), int(B), Sp, run, inverse, s);
+    default: return ulysses_vb<1>(in, out, int(P), int(B), Sp, run, inverse, s);
+  }
+}
+
+hipError_t launch_zigzag(const void* in, void* out, int64_t B, int64_t S, int64_t row_bytes,
+                         int64_t P, bool inverse, hipStream_t s) {
+  const int64_t chunk = (S / (2 * P)) * row_bytes;
+  switch (pick_vec_bytes(chunk, in, out)) {
+    case 16: return zigzag_vb<16>(in, out, int(B), int(P), chunk, inverse, s);
+    case 8: return zigzag_vb<8>(in, out, int(B), int(P), chunk, inverse, s);
+    case 4: return zigzag_vb<4>(in, out, int(B), int(P), chunk, inverse, s);
+    case 2: return zigzag_vb<2>(in, out, int(B), int(P), chunk, inverse, s);
+    default: return zigzag_vb<1>(in, out, int(B), int(P), chunk, inverse, s);
+  }
+}
+
+}  // namespace cp

@@ -1,0 +1,127 @@
+"""P context-parallel ranks simulated on one GPU: the ring and Ulysses shares.
+
+Host-side sequencing only; every step is a libcp_attn kernel.
+
+Ring (handbook "Context parallelism: Ring Attention and Ulysses", §"Ring
+Attention"): rank r keeps its queries; at step s it holds the KV block of rank
+src = (r - s) mod P, attends to it at the block's global positions and merges the
+partial (out, lse) into its running result.  On one GPU the block "arriving" from
+the left neighbour is a view of block src.  With the zigzag partition (§"The zigzag
+partition") the inputs are first reordered so that rank r's share is the contiguous
+slice r of the reordered sequence, holding chunks r and 2P-1-r.
+
+Ulysses (§"Ulysses"): the sequence -> head relayout gives each rank the whole
+sequence for H/P heads; attention runs per rank; the inverse relayout returns the
+output to sequence order.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import ops
+
+
+def rank_positions(rank: int, P: int, S: int, layout: str = "zigzag", device="cuda") -> torch.Tensor:
+    """int32 global positions of the tokens rank ``rank`` holds (increasing)."""
+    if S % (2 * P):
+        raise ValueError(f"sequence {S} not divisible into {2 * P} chunks")
+    c = S // (2 * P)
+    if layout == "zigzag":
+        chunks = (rank, 2 * P - 1 - rank)
+    elif layout == "contiguous":
+        chunks = (2 * rank, 2 * rank + 1)
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    pos = torch.cat([torch.arange(ch * c, (ch + 1) * c, dtype=torch.int32) for ch in chunks])
+    return pos.to(device)
+
+
+def _block(t, r, C):
+    return None if t is None else t[:, r * C:(r + 1) * C]
+
+
+class RingShare:
+    """One rank's ring pass over P KV blocks, forward and backward.
+
+    q, k, v, seg are the whole tensors in the partition's order: for ``zigzag`` the
+    output of ``ops.zigzag_reorder``; for ``contiguous`` the sequence order.  Rank
+    r's rows (queries and its own KV block) are slice r of length S/P.
+    """
+
+    def __init__(self, q, k, v, P: int, rank: int, layout="zigzag", seg=None, causal=True,
+                 window=0, scale=0.0):
+        self.q, self.k, self.v, self.seg = q, k, v, seg
+        self.P, self.rank, self.layout = P, rank, layout
+        self.S = q.shape[1]
+        self.C = self.S // P
+        self.mask = dict(causal=causal, window=window, scale=scale)
+        self.pos = [rank_positions(r, P, self.S, layout, q.device) for r in range(P)]
+        self.ws = None
+
+    def _skip(self, src):
+        # A contiguous causal block later than the rank's own sees nothing; the
+        # handbook's loop skips it too.  Zigzag blocks always hold visible pairs.
+        return self.layout == "contiguous" and self.mask["causal"] and src > self.rank
+
+    def _mask(self, src):
+        r, C = self.rank, self.C
+        m = dict(self.mask, q_pos=self.pos[r], k_pos=self.pos[src])
+        if self.seg is not None:
+            m.update(q_seg=_block(self.seg, r, C).contiguous(), k_seg=_block(self.seg, src, C).contiguous())
+        return m
+
+    def forward(self):
+        """(out [B,S/P,Hq,D] float32, lse [B,Hq,S/P]) of this rank after P steps."""
+        r, C, P = self.rank, self.C, self.P
+        ql = _block(self.q, r, C)
+        B, _, Hq, D = ql.shape
+        acc = torch.zeros(B, C, Hq, D, device=ql.device, dtype=torch.float32)
+        lse = torch.full((B, Hq, C), float("-inf"), device=ql.device, dtype=torch.float32)
+        blk_o = torch.empty(B, C, Hq, D, device=ql.device, dtype=ql.dtype)
+        blk_l = torch.empty(B, Hq, C, device=ql.device, dtype=torch.float32)
+        for step in range(P):
+            src = (r - step) % P
+            if self._skip(src):
+                continue
+            ops.attn_fwd(ql, _block(self.k, src, C), _block(self.v, src, C), out=blk_o, lse=blk_l,
+                         **self._mask(src))
+            ops.lse_merge(acc, lse, blk_o, blk_l)
+        return acc, lse
+
+    def backward(self, out, lse, dout, dq, dk, dv):
+        """Accumulate this rank's gradients: dq [B,S/P,..] of its queries, and the
+        partial dk/dv of every block into the whole-sequence dk/dv buffers."""
+        r, C, P = self.rank, self.C, self.P
+        ql = _block(self.q, r, C)
+        for step in range(P):
+            src = (r - step) % P
+            if self._skip(src):
+                continue
+            ops.attn_bwd(ql, _block(self.k, src, C), _block(self.v, src, C), out, lse, dout,
+                         dq=dq, dk=_block(dk, src, C), dv=_block(dv, src, C), accumulate=True,
+                         **self._mask(src))
+        return dq, dk, dv
+
+
+def ring_forward_all(q, k, v, P, layout="zigzag", seg=None, **mask):
+    """Every rank's ring forward; returns per-rank (out fp32, lse)."""
+    return [RingShare(q, k, v, P, r, layout, seg, **mask).forward() for r in range(P)]
+
+
+def ulysses_forward(q_stack, k_stack, v_stack, P, **mask):
+    """q_stack [P][B][S/P][Hq][D], k/v [P][B][S/P][Hkv][D] (rank s holds sequence slice s).
+
+    Returns (out_stack [P][B][S/P][Hq][D], lse [P][B][Hq/P][S], the relayouted q, k, v):
+    rank p attends over the whole sequence with q heads [p*Hq/P, (p+1)*Hq/P).
+    """
+    ql = ops.ulysses_relayout(q_stack, P)
+    kl = ops.ulysses_relayout(k_stack, P)
+    vl = ops.ulysses_relayout(v_stack, P)
+    outs, lses = [], []
+    for p in range(P):
+        o, l = ops.attn_fwd(ql[p], kl[p], vl[p], **mask)
+        outs.append(o)
+        lses.append(l)
+    out_l = torch.stack(outs)
+    return ops.ulysses_relayout_inv(out_l, P), torch.stack(lses), (ql, kl, vl, out_l)

@@ -1,0 +1,174 @@
+"""Thin torch binding of the C ABI: shape checks and argument marshalling only.
+
+Every function launches on torch's current HIP stream and returns without
+synchronizing.  All arithmetic happens in the HIP kernels of libcp_attn.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+_DT = {torch.bfloat16: _lib.CP_DTYPE_BF16, torch.float32: _lib.CP_DTYPE_F32}
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _opt_i32(t, name, n):
+    if t is None:
+        return None
+    _dev(t, name, torch.int32)
+    if t.numel() != n:
+        raise ValueError(f"{name} has {t.numel()} entries, expected {n}")
+    return t
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def make_args(q, k, *, causal=True, q_offset=0, k_offset=0, q_pos=None, k_pos=None, q_seg=None,
+              k_seg=None, window=0, scale=0.0) -> _lib.AttnArgs:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B,Sq,Hq,D] and k/v [B,Sk,Hkv,D]")
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    _opt_i32(q_pos, "q_pos", Sq)
+    _opt_i32(k_pos, "k_pos", Sk)
+    _opt_i32(q_seg, "q_seg", B * Sq)
+    _opt_i32(k_seg, "k_seg", B * Sk)
+    return _lib.AttnArgs(B, Sq, Sk, Hq, Hkv, D, _DT[q.dtype], int(causal), int(q_offset),
+                         int(k_offset), _ptr(q_pos), _ptr(k_pos), _ptr(q_seg), _ptr(k_seg),
+                         int(window), float(scale))
+
+
+def _check_qkv(q, k, v):
+    _dev(q, "q")
+    _dev(k, "k", q.dtype)
+    _dev(v, "v", q.dtype)
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+
+
+def attn_fwd(q, k, v, *, out=None, lse=None, **mask):
+    """(out [B,Sq,Hq,D] q.dtype, lse [B,Hq,Sq] fp32) of one attention block.
+
+    mask keywords: causal, q_offset, k_offset, q_pos, k_pos, q_seg, k_seg, window, scale.
+    """
+    _check_qkv(q, k, v)
+    a = make_args(q, k, **mask)
+    B, Sq, Hq, _ = q.shape
+    out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
+    lse = torch.empty(B, Hq, Sq, device=q.device, dtype=torch.float32) if lse is None else _dev(lse, "lse", torch.float32)
+    if out.shape != q.shape or lse.shape != (B, Hq, Sq):
+        raise ValueError("out/lse shape mismatch")
+    lib = _lib.load()
+    _lib.check(lib.cp_attn_fwd(ctypes.byref(a), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                               out.data_ptr(), lse.data_ptr(), _stream()))
+    return out, lse
+
+
+def bwd_workspace(q, k, **mask) -> torch.Tensor:
+    a = make_args(q, k, **mask)
+    n = _lib.load().cp_attn_bwd_workspace_size(ctypes.byref(a))
+    return torch.empty(max(n, 16), device=q.device, dtype=torch.uint8)
+
+
+def attn_bwd(q, k, v, out, lse, dout, *, dq=None, dk=None, dv=None, accumulate=False, workspace=None,
+             **mask):
+    """(dq, dk, dv) float32 of one attention block given the rows' final (out, lse)."""
+    _check_qkv(q, k, v)
+    _dev(out, "out", q.dtype)
+    _dev(dout, "dout", q.dtype)
+    _dev(lse, "lse", torch.float32)
+    a = make_args(q, k, **mask)
+    f32 = dict(device=q.device, dtype=torch.float32)
+    if accumulate and (dq is None or dk is None or dv is None):
+        raise ValueError("accumulate needs dq, dk and dv")
+    dq = torch.empty(q.shape, **f32) if dq is None else _dev(dq, "dq", torch.float32)
+    dk = torch.empty(k.shape, **f32) if dk is None else _dev(dk, "dk", torch.float32)
+    dv = torch.empty(v.shape, **f32) if dv is None else _dev(dv, "dv", torch.float32)
+    lib = _lib.load()
+    need = lib.cp_attn_bwd_workspace_size(ctypes.byref(a))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    _lib.check(lib.cp_attn_bwd(ctypes.byref(a), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                               out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                               dk.data_ptr(), dv.data_ptr(), int(bool(accumulate)),
+                               workspace.data_ptr(), workspace.numel(), _stream()))
+    return dq, dk, dv
+
+
+def lse_merge(out_acc, lse_acc, out_blk, lse_blk):
+    """In place: (out_acc, lse_acc) <- merge((out_acc, lse_acc), (out_blk, lse_blk))."""
+    _dev(out_acc, "out_acc", torch.float32)
+    _dev(lse_acc, "lse_acc", torch.float32)
+    _dev(out_blk, "out_blk")
+    _dev(lse_blk, "lse_blk", torch.float32)
+    if out_blk.dtype not in _DT or out_acc.shape != out_blk.shape or lse_acc.shape != lse_blk.shape:
+        raise ValueError("merge shape/dtype mismatch")
+    B, S, H, D = out_acc.shape
+    if lse_acc.shape != (B, H, S):
+        raise ValueError("lse must be [B,H,S]")
+    _lib.check(_lib.load().cp_lse_merge(B, S, H, D, out_acc.data_ptr(), lse_acc.data_ptr(),
+                                        out_blk.data_ptr(), lse_blk.data_ptr(), _DT[out_blk.dtype],
+                                        _stream()))
+    return out_acc, lse_acc
+
+
+def ulysses_relayout(x, P, out=None):
+    """[P][B][S/P][H][D] -> [P][B][S][H/P][D] (sequence -> head, all ranks)."""
+    _dev(x, "x")
+    if x.dim() != 5 or x.shape[0] != P:
+        raise ValueError("x must be [P][B][S/P][H][D]")
+    _, B, Sp, H, D = x.shape
+    if H % P:
+        raise _lib.CpError(_lib.CP_ERR_INVALID, f"heads {H} not divisible by the Ulysses degree {P}")
+    out = torch.empty(P, B, Sp * P, H // P, D, device=x.device, dtype=x.dtype) if out is None else _dev(out, "out", x.dtype)
+    _lib.check(_lib.load().cp_ulysses_relayout(x.data_ptr(), out.data_ptr(), P, B, Sp * P, H, D,
+                                               x.element_size(), _stream()))
+    return out
+
+
+def ulysses_relayout_inv(y, P, out=None):
+    """[P][B][S][H/P][D] -> [P][B][S/P][H][D] (head -> sequence, all ranks)."""
+    _dev(y, "y")
+    if y.dim() != 5 or y.shape[0] != P:
+        raise ValueError("y must be [P][B][S][H/P][D]")
+    _, B, S, Hp, D = y.shape
+    if S % P:
+        raise _lib.CpError(_lib.CP_ERR_INVALID, f"seqlen {S} not divisible by the Ulysses degree {P}")
+    out = torch.empty(P, B, S // P, Hp * P, D, device=y.device, dtype=y.dtype) if out is None else _dev(out, "out", y.dtype)
+    _lib.check(_lib.load().cp_ulysses_relayout_inv(y.data_ptr(), out.data_ptr(), P, B, S, Hp * P, D,
+                                                   y.element_size(), _stream()))
+    return out
+
+
+def zigzag_reorder(x, P, inverse=False, strategy=0, out=None):
+    """Zigzag (dual-chunk-swap) reorder of x [B][S][...] along S; inverse undoes it."""
+    _dev(x, "x")
+    if x.dim() < 2:
+        raise ValueError("x must be [B][S][...]")
+    B, S = x.shape[0], x.shape[1]
+    row_bytes = x[0, 0].numel() * x.element_size() if x.numel() else 0
+    out = torch.empty_like(x) if out is None else _dev(out, "out", x.dtype)
+    _lib.check(_lib.load().cp_zigzag_reorder(x.data_ptr(), out.data_ptr(), B, S, row_bytes, P,
+                                             int(strategy), int(bool(inverse)), _stream()))
+    return out

@@ -1,0 +1,157 @@
+/*
+ * cp_attn.h — C ABI of the context-parallel attention hot path on one MI355X (gfx950).
+ *
+ * Every entry point is asynchronous on the caller's HIP stream, allocates no device
+ * memory, never synchronizes, and keeps no global state other than a thread-local
+ * message describing the last failure.  All tensors are caller-owned, contiguous,
+ * row-major device buffers; pointers must stay valid until the stream work ends.
+ * Failures are reported by status code (never by abort); cp_last_error() gives the
+ * detail.  Validation happens on the host before any launch, so an invalid call
+ * touches no device memory.
+ *
+ * Sources of the operations (cited by page title and section):
+ *   [H]  handbook "Context parallelism: Ring Attention and Ulysses"
+ *   [MP] MaxText PR "Add Packing Support for Context Parallelism (Ring Attention)"
+ *   [MU] MaxText PR "Add TPU Ulysses context parallelism"
+ *   [HF] transformers PR "[distributed] Context parallel module, with Ulysses"
+ */
+#ifndef CP_ATTN_H
+#define CP_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { CP_DTYPE_BF16 = 0, CP_DTYPE_F32 = 1 } cp_dtype_t;
+
+typedef enum {
+  CP_OK = 0,
+  CP_ERR_INVALID = 1,      /* a size, shape relation or flag the operation does not admit */
+  CP_ERR_UNSUPPORTED = 2,  /* valid, but no kernel is compiled for it (head_dim, dtype)   */
+  CP_ERR_ALIAS = 3,        /* an output buffer overlaps an input it must not overlap      */
+  CP_ERR_HIP = 4           /* the HIP runtime reported an error at launch                 */
+} cp_status_t;
+
+/*
+ * Problem description of one attention block, following [H] §"Which operations
+ * partition directly": attention(q, k, v, causal, q_offset, k_offset) -> (out, lse),
+ * with q [Sq, H, D], k/v [Sk, H, D], lse [H, Sq]; extended by a batch dimension,
+ * grouped kv heads ([H] §"Ulysses", degree bounded by the kv head count), per-token
+ * positions (needed by a zigzag rank's two chunks, [H] §"The zigzag partition"),
+ * segment ids for packed documents ([MP] §Description, the segment_pos commit) and a
+ * sliding window ([HF] §Tests).
+ *
+ * Key j is visible to query i iff all of:
+ *   causal == 0  or  kpos[j] <= qpos[i]
+ *   q_seg == NULL  or  q_seg[b,i] == k_seg[b,j]
+ *   window == 0  or  qpos[i] - kpos[j] < window
+ * where qpos[i] = q_pos ? q_pos[i] : q_offset + i (likewise kpos).
+ * A query row with no visible key gets out = 0 and lse = -inf.
+ */
+typedef struct {
+  int64_t batch;           /* B  >= 1                                                    */
+  int64_t seqlen_q;        /* Sq >= 1                                                    */
+  int64_t seqlen_k;        /* Sk >= 1                                                    */
+  int64_t heads_q;         /* Hq >= 1, a multiple of heads_kv                            */
+  int64_t heads_kv;        /* Hkv >= 1; query head h uses kv head h / (Hq / Hkv)          */
+  int64_t head_dim;        /* D: bf16 in {32, 64, 128}; f32 in {16, 32, 64, 128}          */
+  int32_t dtype;           /* cp_dtype_t of q, k, v, out, dout                           */
+  int32_t causal;          /* 0 or 1                                                     */
+  int64_t q_offset;        /* global position of query 0 when q_pos is NULL              */
+  int64_t k_offset;        /* global position of key 0 when k_pos is NULL                */
+  const int32_t* q_pos;    /* NULL or device [Sq] strictly increasing global positions    */
+  const int32_t* k_pos;    /* NULL or device [Sk] strictly increasing global positions    */
+  const int32_t* q_seg;    /* NULL or device [B, Sq] non-decreasing segment ids           */
+  const int32_t* k_seg;    /* NULL or device [B, Sk]; non-NULL iff q_seg is non-NULL     */
+  int64_t window;          /* 0 = no window; > 0 = sliding window width                  */
+  float softmax_scale;     /* 0 -> 1/sqrt(head_dim)                                      */
+} cp_attn_args_t;
+
+/*
+ * Blockwise attention forward.  q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] (dtype);
+ * out [B,Sq,Hq,D] (dtype); lse [B,Hq,Sq] float32, natural log of the row's
+ * sum of exp(scale * q.k) over visible keys.  bf16 inputs are multiplied on the
+ * matrix cores with float32 accumulation; out is rounded to nearest even.
+ * out/lse must not overlap q, k or v (CP_ERR_ALIAS).
+ */
+cp_status_t cp_attn_fwd(const cp_attn_args_t* args, const void* q, const void* k, const void* v,
+                        void* out, float* lse, hipStream_t stream);
+
+/* Workspace bytes cp_attn_bwd needs for args (the per-row dO.O sums). */
+size_t cp_attn_bwd_workspace_size(const cp_attn_args_t* args);
+
+/*
+ * Blockwise attention backward: the gradient of sum(dout * out) with respect to q,
+ * k and v for this block, given the rows' FINAL out and lse (for a ring step these are
+ * the merged values over all blocks, so the per-block gradients add up to the full
+ * gradient).  dq [B,Sq,Hq,D], dk/dv [B,Sk,Hkv,D] float32; dk/dv are summed over the
+ * query heads of each kv group.  accumulate = 1 adds into dq/dk/dv, 0 overwrites
+ * them.  workspace: device memory of at least cp_attn_bwd_workspace_size(args)
+ * bytes, 16-byte aligned, owned by the caller.  The result is deterministic (no
+ * atomics).
+ */
+cp_status_t cp_attn_bwd(const cp_attn_args_t* args, const void* q, const void* k, const void* v,
+                        const void* out, const float* lse, const void* dout,
+                        float* dq, float* dk, float* dv, int32_t accumulate,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Ring-step merge, in place ([H] self-test answers and §"Ring Attention"):
+ *   lse' = log(e^lse_acc + e^lse_blk)
+ *   acc' = acc * e^(lse_acc - lse') + blk * e^(lse_blk - lse')
+ * A part whose lse is -inf has weight 0 (both -inf gives acc' = 0, lse' = -inf).
+ * out_acc [B,S,H,D] float32 (read and written), lse_acc [B,H,S] float32 (read and
+ * written), out_blk [B,S,H,D] of blk_dtype, lse_blk [B,H,S] float32.
+ */
+cp_status_t cp_lse_merge(int64_t batch, int64_t seqlen, int64_t heads, int64_t head_dim,
+                         float* out_acc, float* lse_acc, const void* out_blk,
+                         const float* lse_blk, int32_t blk_dtype, hipStream_t stream);
+
+/*
+ * Ulysses sequence -> head relayout of all P ranks at once, as one local permute
+ * ([H] §"Ulysses", seq_to_head; [MU] the forward all-to-all):
+ *   in  [P][B][S/P][H][D]   (rank s holds sequence slice s, all heads)
+ *   out [P][B][S][H/P][D]   (rank p holds the whole sequence, heads [p*H/P, (p+1)*H/P))
+ *   out[p][b][s*(S/P)+i][hh][d] = in[s][b][i][p*(H/P)+hh][d]
+ * seqlen is the full S; S % P == 0 and H % P == 0 (applied to k/v this is the
+ * degree limit P <= H_kv) else CP_ERR_INVALID.  elem_bytes in {2, 4}.  Bit-exact.
+ * in and out must not overlap (CP_ERR_ALIAS).
+ */
+cp_status_t cp_ulysses_relayout(const void* in, void* out, int64_t P, int64_t batch,
+                                int64_t seqlen, int64_t heads, int64_t head_dim,
+                                int64_t elem_bytes, hipStream_t stream);
+
+/* Exact inverse of cp_ulysses_relayout ([H] §"Ulysses", head_to_seq):
+ *   in [P][B][S][H/P][D] -> out [P][B][S/P][H][D].  Same arguments and errors. */
+cp_status_t cp_ulysses_relayout_inv(const void* in, void* out, int64_t P, int64_t batch,
+                                    int64_t seqlen, int64_t heads, int64_t head_dim,
+                                    int64_t elem_bytes, hipStream_t stream);
+
+/*
+ * Causal load-balancing reorder of whole token rows ([H] §"The zigzag partition";
+ * [MP] reorder strategy 0 = DualChunkSwap).  in/out [B][S][row_bytes].  The sequence
+ * is cut into 2P chunks of S/(2P) rows; the output is, for r = 0..P-1, chunk r then
+ * chunk 2P-1-r, so a contiguous P-way split gives rank r its zigzag pair.
+ * inverse = 1 undoes it.  S % (2P) == 0 else CP_ERR_INVALID; strategy other than 0
+ * -> CP_ERR_UNSUPPORTED (1 = striped is not built) or CP_ERR_INVALID (unknown).
+ * Bit-exact.  in and out must not overlap (CP_ERR_ALIAS).
+ */
+cp_status_t cp_zigzag_reorder(const void* in, void* out, int64_t batch, int64_t seqlen,
+                              int64_t row_bytes, int64_t P, int32_t strategy, int32_t inverse,
+                              hipStream_t stream);
+
+/* Static name of a status code. */
+const char* cp_status_string(cp_status_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* cp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CP_ATTN_H */

@@ -1,0 +1,130 @@
+"""The C ABI without a GPU: the library loads, exports what include/*.h declares,
+and rejects invalid arguments with the documented status codes before touching
+device memory (fake, never-dereferenced pointers are passed)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from context_cp_attn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE_A, FAKE_B, FAKE_C = 1 << 32, 1 << 36, 1 << 40   # 16-byte aligned, far apart
+INVALID, UNSUPPORTED, ALIAS = _lib.CP_ERR_INVALID, _lib.CP_ERR_UNSUPPORTED, _lib.CP_ERR_ALIAS
+
+
+def declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(cp_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_symbols()
+    assert {"cp_attn_fwd", "cp_attn_bwd", "cp_lse_merge", "cp_ulysses_relayout",
+            "cp_ulysses_relayout_inv", "cp_zigzag_reorder"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(_lib.SIGNATURES) == names
+
+
+def test_status_strings():
+    lib = _lib.load()
+    assert [lib.cp_status_string(i).decode() for i in range(5)] == [
+        "CP_OK", "CP_ERR_INVALID", "CP_ERR_UNSUPPORTED", "CP_ERR_ALIAS", "CP_ERR_HIP"]
+
+
+def args(**kw):
+    a = dict(batch=1, seqlen_q=64, seqlen_k=64, heads_q=4, heads_kv=2, head_dim=128, dtype=0,
+             causal=1, q_offset=0, k_offset=0, q_pos=None, k_pos=None, q_seg=None, k_seg=None,
+             window=0, softmax_scale=0.0)
+    a.update(kw)
+    return _lib.AttnArgs(**a)
+
+
+def fwd(a, q=FAKE_A, k=FAKE_B, v=FAKE_C, out=1 << 44, lse=1 << 45):
+    lib = _lib.load()
+    return lib.cp_attn_fwd(ctypes.byref(a), q, k, v, out, lse, None), lib.cp_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(batch=0), INVALID, "sizes must be >= 1"),
+    (dict(seqlen_q=-3), INVALID, "sizes must be >= 1"),
+    (dict(heads_q=6, heads_kv=4), INVALID, "not a multiple"),
+    (dict(dtype=7), INVALID, "unknown dtype"),
+    (dict(causal=2), INVALID, "causal"),
+    (dict(window=-1), INVALID, "window"),
+    (dict(q_seg=FAKE_A), INVALID, "both"),
+    (dict(softmax_scale=-1.0), INVALID, "softmax_scale"),
+    (dict(q_offset=-5), INVALID, "q_offset"),
+    (dict(head_dim=16), UNSUPPORTED, "head_dim"),
+    (dict(head_dim=256, dtype=1), UNSUPPORTED, "head_dim"),
+])
+def test_attn_fwd_rejects(kw, code, msg):
+    st, err = fwd(args(**kw))
+    assert st == code and msg in err
+
+
+def test_attn_fwd_alias_and_alignment():
+    st, err = fwd(args(), out=FAKE_A)       # out == q
+    assert st == ALIAS
+    st, err = fwd(args(), lse=FAKE_C + 64)  # lse inside v
+    assert st == ALIAS
+    st, err = fwd(args(), q=FAKE_A + 2)     # bf16 operands must be 16-byte aligned
+    assert st == INVALID and "aligned" in err
+
+
+def test_attn_bwd_workspace_and_alias():
+    lib = _lib.load()
+    a = args()
+    need = lib.cp_attn_bwd_workspace_size(ctypes.byref(a))
+    assert need >= 4 * 4 * 64 and need % 256 == 0
+    base = [FAKE_A, FAKE_B, FAKE_C, 1 << 41, 1 << 42, 1 << 43, 1 << 44, 1 << 45, 1 << 46]
+    st = lib.cp_attn_bwd(ctypes.byref(a), *base, 0, 1 << 47, need - 1, None)
+    assert st == INVALID and "workspace" in lib.cp_last_error().decode()
+    st = lib.cp_attn_bwd(ctypes.byref(a), *base, 2, 1 << 47, need, None)
+    assert st == INVALID
+    bad = list(base)
+    bad[6] = FAKE_A  # dq over q
+    st = lib.cp_attn_bwd(ctypes.byref(a), *bad, 0, 1 << 47, need, None)
+    assert st == ALIAS
+
+
+def test_relayout_rejects():
+    lib = _lib.load()
+    f = lib.cp_ulysses_relayout
+    assert f(FAKE_A, FAKE_B, 16, 1, 32768, 8, 128, 2, None) == INVALID          # degree > kv heads
+    assert "cannot exceed" in lib.cp_last_error().decode()
+    assert f(FAKE_A, FAKE_B, 4, 1, 30, 8, 16, 4, None) == INVALID               # S % P
+    assert f(FAKE_A, FAKE_B, 4, 1, 32, 8, 16, 3, None) == INVALID               # elem bytes
+    assert f(FAKE_A, FAKE_A + 64, 4, 1, 32, 8, 16, 4, None) == ALIAS            # overlap
+    assert lib.cp_ulysses_relayout_inv(FAKE_A, FAKE_B, 0, 1, 32, 8, 16, 4, None) == INVALID
+
+
+def test_reorder_rejects():
+    lib = _lib.load()
+    f = lib.cp_zigzag_reorder
+    assert f(FAKE_A, FAKE_B, 1, 30, 4, 4, 0, 0, None) == INVALID     # S % 2P
+    assert f(FAKE_A, FAKE_B, 1, 32, 4, 4, 1, 0, None) == UNSUPPORTED  # striped not built
+    assert f(FAKE_A, FAKE_B, 1, 32, 4, 4, 5, 0, None) == INVALID     # unknown strategy
+    assert f(FAKE_A, FAKE_B, 1, 32, 4, 4, 0, 3, None) == INVALID     # inverse flag
+    assert f(FAKE_A, FAKE_A, 1, 32, 4, 4, 0, 0, None) == ALIAS
+
+
+def test_merge_rejects():
+    lib = _lib.load()
+    f = lib.cp_lse_merge
+    assert f(1, 8, 2, 128, FAKE_A, FAKE_B, FAKE_C, 1 << 41, 9, None) == INVALID
+    assert f(1, 8, 2, 12, FAKE_A, FAKE_B, FAKE_C, 1 << 41, 1, None) == UNSUPPORTED
+    assert f(1, 8, 2, 128, FAKE_A, FAKE_B, FAKE_A, 1 << 41, 1, None) == ALIAS
+
+
+def test_python_errors_are_valueerrors():
+    with pytest.raises(ValueError):
+        _lib.check(INVALID)

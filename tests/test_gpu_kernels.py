@@ -1,0 +1,218 @@
+"""Kernel-level parity of the HIP path against the CPU oracle (GPU only).
+
+Sizes span several tiles and a ragged tail; every mask kind, offsets, positions,
+grouped heads and fully masked rows are covered.  Bars: permutations bit-exact;
+attention float32 max-abs 1e-5 (out and lse); bf16 out 1e-2 and lse 1e-3; gradients
+1e-2 * max(1, max|ref|) (bf16) and 1e-5 * max(1, max|ref|) (float32).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import cp_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: dict(out=1e-5, lse=1e-5, grad=1e-5), torch.bfloat16: dict(out=1e-2, lse=1e-3, grad=1e-2)}
+
+
+@pytest.fixture(scope="module")
+def cp():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import context_cp_attn_amd as cp
+    cp.load_library()
+    return cp
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bits of a CPU tensor as an integer numpy array (bf16 -> int16)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy()
+    return t.numpy()
+
+
+def f64(t):
+    return t.detach().cpu().double().numpy()
+
+
+def check_lse(got, ref, tol):
+    got = f64(got)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), "-inf pattern differs"
+    fin = np.isfinite(ref)
+    if fin.any():
+        err = np.abs(got[fin] - ref[fin]).max()
+        assert err <= tol, f"lse max-abs {err} > {tol}"
+
+
+def check_close(got, ref, tol, what):
+    err = np.abs(f64(got) - ref).max() if ref.size else 0.0
+    assert err <= tol, f"{what} max-abs {err} > {tol}"
+
+
+# --------------------------------------------------------------------- permutations
+
+@pytest.mark.parametrize("P,B,S,H,D,dtype", [
+    (4, 1, 32, 8, 16, torch.float32),      # toy
+    (4, 2, 24, 8, 24, torch.bfloat16),     # 96-byte runs
+    (3, 1, 15, 6, 7, torch.float32),       # 56-byte runs
+    (2, 3, 10, 2, 3, torch.bfloat16),      # 6-byte runs
+    (16, 1, 4096, 32, 128, torch.bfloat16),
+])
+def test_ulysses_relayout_bit_exact(cp, P, B, S, H, D, dtype):
+    say(f"relayout P={P} B={B} S={S} H={H} D={D} {dtype}")
+    torch.manual_seed(1)
+    x = torch.randn(P, B, S // P, H, D).to(dtype).cuda()
+    y = cp.ulysses_relayout(x, P)
+    np.testing.assert_array_equal(bits(y), oracle.ulysses_relayout(bits(x)))
+    z = cp.ulysses_relayout_inv(y, P)
+    assert torch.equal(z, x)
+    np.testing.assert_array_equal(bits(z), oracle.ulysses_relayout_inv(bits(y)))
+
+
+@pytest.mark.parametrize("shape,P,dtype", [
+    ((1, 65536), 4, torch.int32),
+    ((2, 48, 3, 5), 3, torch.bfloat16),
+    ((1, 32, 8, 16), 4, torch.float32),
+    ((3, 40, 7), 5, torch.uint8),
+])
+def test_zigzag_reorder_bit_exact(cp, shape, P, dtype):
+    say(f"reorder {shape} P={P} {dtype}")
+    n = int(np.prod(shape))
+    x = (torch.arange(n, dtype=torch.int64) * 2654435761 % 251).to(dtype).reshape(shape).cuda() \
+        if dtype in (torch.int32, torch.uint8) else torch.randn(shape).to(dtype).cuda()
+    y = cp.zigzag_reorder(x, P)
+    np.testing.assert_array_equal(bits(y), oracle.reorder(bits(x), P))
+    z = cp.zigzag_reorder(y, P, inverse=True)
+    np.testing.assert_array_equal(bits(z), oracle.reorder_inv(bits(y), P))
+    assert torch.equal(z, x)
+
+
+# --------------------------------------------------------------------- merge
+
+@pytest.mark.parametrize("blk_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("D", [16, 128])
+def test_lse_merge(cp, blk_dtype, D):
+    say(f"merge D={D} {blk_dtype}")
+    B, S, H = 2, 37, 3
+    g = torch.Generator().manual_seed(2)
+    o1 = torch.randn(B, S, H, D, generator=g)
+    o2 = torch.randn(B, S, H, D, generator=g).to(blk_dtype)
+    l1 = torch.randn(B, H, S, generator=g) * 3
+    l2 = torch.randn(B, H, S, generator=g) * 3
+    l1[0, 0, :5] = -float("inf")
+    l2[0, 0, 3:8] = -float("inf")   # rows 3,4: both empty
+    l2[1, 2, 10:] = -float("inf")
+    acc, lacc = o1.cuda(), l1.cuda()
+    cp.lse_merge(acc, lacc, o2.cuda(), l2.cuda())
+    ref_o, ref_l = oracle.lse_merge(f64(o1), f64(l1), f64(o2), f64(l2))
+    check_lse(lacc, ref_l, 1e-5)
+    check_close(acc, ref_o, 1e-5, "merged out")
+
+
+# --------------------------------------------------------------------- attention
+
+CASES = {
+    # name: (B, Sq, Sk, Hq, Hkv, mask kwargs builder)
+    "causal_square": (1, 300, 300, 4, 2, lambda Sq, Sk: dict()),
+    "noncausal": (2, 200, 333, 2, 2, lambda Sq, Sk: dict(causal=False)),
+    "offsets": (1, 160, 410, 4, 1, lambda Sq, Sk: dict(q_offset=250, k_offset=0)),
+    "zigzag_pos": (1, 256, 256, 2, 2, lambda Sq, Sk: dict(
+        q_pos=np.r_[np.arange(0, 128), np.arange(896, 1024)], k_pos=np.r_[np.arange(384, 512), np.arange(512, 640)])),
+    "packed_window": (1, 520, 520, 4, 2, lambda Sq, Sk: dict(seg=[37, 150, 90, 243], window=64)),
+    "empty_rows": (1, 130, 190, 2, 1, lambda Sq, Sk: dict(q_offset=0, k_offset=64)),
+}
+
+
+def make_case(name, D, dtype, seed=0):
+    B, Sq, Sk, Hq, Hkv, mk = CASES[name]
+    q, k, v, do = cp_inputs.normal_tensors([(B, Sq, Hq, D), (B, Sk, Hkv, D), (B, Sk, Hkv, D), (B, Sq, Hq, D)],
+                                           seed=seed, dtype=dtype)
+    m = mk(Sq, Sk)
+    if "seg" in m:
+        seg = cp_inputs.segment_ids(m.pop("seg"), batch=B)
+        m["q_seg"] = seg
+        m["k_seg"] = seg
+    return (q, k, v, do), m
+
+
+def to_dev(m):
+    out = {}
+    for key, val in m.items():
+        if isinstance(val, np.ndarray):
+            val = torch.from_numpy(val.astype(np.int32))
+        if isinstance(val, torch.Tensor):
+            val = val.to(torch.int32).contiguous().cuda()
+        out[key] = val
+    return out
+
+
+def oracle_mask(m):
+    return {k: (v.numpy() if isinstance(v, torch.Tensor) else v) for k, v in m.items()}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 16), (torch.float32, 128), (torch.bfloat16, 32),
+                                     (torch.bfloat16, 64), (torch.bfloat16, 128)])
+def test_attn_fwd(cp, name, dtype, D):
+    say(f"attn_fwd {name} D={D} {dtype}")
+    (q, k, v, _), m = make_case(name, D, dtype)
+    out, lse = cp.attn_fwd(q.cuda(), k.cuda(), v.cuda(), **to_dev(m))
+    ref_o, ref_l = oracle.attn_fwd(q, k, v, **oracle_mask(m))
+    check_lse(lse, ref_l, TOL[dtype]["lse"])
+    check_close(out, ref_o, TOL[dtype]["out"], "out")
+    empty = np.isneginf(ref_l)
+    if empty.any():  # rows with no visible key are exactly zero
+        o = f64(out).transpose(0, 2, 1, 3)
+        assert np.all(o[empty] == 0)
+
+
+@pytest.mark.parametrize("name", ["causal_square", "offsets", "zigzag_pos", "packed_window", "empty_rows"])
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 16), (torch.float32, 128), (torch.bfloat16, 64),
+                                     (torch.bfloat16, 128)])
+def test_attn_bwd(cp, name, dtype, D):
+    say(f"attn_bwd {name} D={D} {dtype}")
+    (q, k, v, do), m = make_case(name, D, dtype, seed=3)
+    dm = to_dev(m)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    out, lse = cp.attn_fwd(qd, kd, vd, **dm)
+    dq, dk, dv = cp.attn_bwd(qd, kd, vd, out, lse, dod, **dm)
+    om = oracle_mask(m)
+    ref_o, ref_l = oracle.attn_fwd(q, k, v, **om)
+    refs = oracle.attn_bwd(q, k, v, ref_o, ref_l, do, **om)
+    for got, ref, nm in zip((dq, dk, dv), refs, ("dq", "dk", "dv")):
+        check_close(got, ref, TOL[dtype]["grad"] * max(1.0, np.abs(ref).max()), nm)
+    # accumulate adds onto what is there
+    dq2, dk2, dv2 = cp.attn_bwd(qd, kd, vd, out, lse, dod, dq=dq.clone(), dk=dk.clone(), dv=dv.clone(),
+                                accumulate=True, **dm)
+    for a, b in ((dq2, dq), (dk2, dk), (dv2, dv)):
+        torch.testing.assert_close(a, 2 * b, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_deterministic(cp, dtype, D):
+    say(f"determinism {dtype} D={D}")
+    (q, k, v, do), m = make_case("packed_window", D, dtype, seed=4)
+    dm = to_dev(m)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    r1 = cp.attn_fwd(qd, kd, vd, **dm)
+    r2 = cp.attn_fwd(qd, kd, vd, **dm)
+    assert all(torch.equal(a, b) for a, b in zip(r1, r2))
+    g1 = cp.attn_bwd(qd, kd, vd, *r1, dod, **dm)
+    g2 = cp.attn_bwd(qd, kd, vd, *r1, dod, **dm)
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+
+
+def test_single_token_and_gqa_8(cp):
+    say("attn single token / GQA 8")
+    q, k, v = cp_inputs.normal_tensors([(1, 1, 8, 128), (1, 1, 1, 128), (1, 1, 1, 128)], seed=5)
+    out, lse = cp.attn_fwd(q.cuda(), k.cuda(), v.cuda())
+    ref_o, ref_l = oracle.attn_fwd(q, k, v)
+    check_lse(lse, ref_l, 1e-3)
+    check_close(out, ref_o, 1e-2, "out")
