@@ -10,13 +10,6 @@
 #include "cp_attn.h"
 #include "launch.h"
 
-namespace cp {
-// defined in attn_rowwise.hip / attn_bwd_mfma.hip
-hipError_t launch_attn_bwd_rowwise_bf16(const AttnProblem& p, const void* q, const void* k,
-                                        const void* v, const void* out, const float* lse,
-                                        const void* dout, float* dq, float* dk, float* dv,
-                                        int accumulate, float* delta, hipStream_t s);
-}  // namespace cp
 
 namespace {
 

@@ -1,0 +1,512 @@
+// Blockwise attention backward, bf16 in / float32 gradients, on the gfx950 matrix
+// cores.  Deterministic: no atomics; every gradient element is written by one lane.
+//
+// Gradient of sum(dO * O) for O = softmax(scale * Q K^T) V restricted to visible
+// pairs, given the rows' final O and lse (so ring blocks add up to the full
+// gradient):  P = exp(scale*s - lse), Delta_i = dO_i . O_i, dV = P^T dO,
+// dP = dO V^T, dS = P * (dP - Delta), dQ = scale dS K, dK = scale dS^T Q.
+// Attention itself: handbook "Context parallelism: Ring Attention and Ulysses",
+// §"Which operations partition directly"; its gradient is the textbook one.
+//
+// Three launches:
+//  1. delta: Delta = rowsum(dO * O) into the caller's workspace [B,Hq,Sq].
+//  2. dK/dV: a workgroup owns 32*NW keys of one kv head (one wavefront per 32
+//     keys, K and V held as B fragments in registers) and streams query tiles of
+//     every query head of the group through LDS.  S = Q K^T and dP = dO V^T are
+//     computed query-major so that P and dS land directly as B fragments of
+//     dV^T += dO^T P and dK^T += Q^T dS (Q and dO are staged both row-major and
+//     transposed).
+//  3. dQ: a workgroup owns 32*NW queries of one head and streams key tiles:
+//     S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
+// Tiles are skipped / masked exactly as in the forward (empty / partial / full).
+#include "mfma_common.h"
+
+namespace cp {
+namespace {
+
+using namespace mfma;
+
+// ---- 1. Delta --------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void delta_kernel(int64_t rows, int Sq, int Hq,
+                                                    const uint16_t* __restrict__ out,
+                                                    const uint16_t* __restrict__ dout,
+                                                    float* __restrict__ delta) {
+  constexpr int kLanesPerRow = D / 8;
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = t / kLanesPerRow;   // (b, i, h)
+  const int c = int(t % kLanesPerRow);
+  float x = 0.0f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(out + row * D + c * 8);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dout + row * D + c * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      x += bf16_to_f32(uint16_t(a[w] & 0xffff)) * bf16_to_f32(uint16_t(g[w] & 0xffff));
+      x += bf16_to_f32(uint16_t(a[w] >> 16)) * bf16_to_f32(uint16_t(g[w] >> 16));
+    }
+  }
+#pragma unroll
+  for (int o = kLanesPerRow / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  if (row < rows && c == 0) {
+    const int h = int(row % Hq);
+    const int64_t bi = row / Hq;
+    const int i = int(bi % Sq);
+    const int64_t b = bi / Sq;
+    delta[(b * Hq + h) * Sq + i] = x;
+  }
+}
+
+// lse in the base-2 domain; a row with no visible key gets +inf so that every
+// exp2(s*c - lse2) of it is exactly 0.
+CP_DEVICE float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+
+// ---- 2. dK / dV ----------------------------------------------------------------
+template <int D_, int NW_, int BM_>
+struct DkvCfg {
+  static constexpr int D = D_, NW = NW_, BM = BM_;
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kKeys = 32 * NW;
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int QBLK = BM / 32;
+  static constexpr int RLD = D + 8;   // row-major pitch (elements)
+  static constexpr int TLD = BM + 8;  // transposed pitch (elements)
+  static constexpr int kRowElems = BM * RLD;
+  static constexpr int kColElems = D * TLD;
+  // Q rows, Q^T, dO rows, dO^T, then lse2, delta, qpos, qseg
+  static constexpr int kStageBytes = 2 * (kRowElems + kColElems) * 2 + 4 * BM * 4;
+  static constexpr int kLdsBytes = 2 * kStageBytes;
+  using Tile = RowTile<BM, D, kThreads>;
+};
+
+template <class C>
+struct DkvStage {
+  uint16_t* q;
+  uint16_t* qt;
+  uint16_t* g;
+  uint16_t* gt;
+  float* lse2;
+  float* delta;
+  int* qpos;
+  int* qseg;
+  CP_DEVICE DkvStage(uint8_t* base) {
+    q = reinterpret_cast<uint16_t*>(base);
+    qt = q + C::kRowElems;
+    g = qt + C::kColElems;
+    gt = g + C::kRowElems;
+    lse2 = reinterpret_cast<float*>(gt + C::kColElems);
+    delta = lse2 + C::BM;
+    qpos = reinterpret_cast<int*>(delta + C::BM);
+    qseg = qpos + C::BM;
+  }
+};
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void attn_dkdv_kernel(AttnProblem p, const uint16_t* __restrict__ q,
+                                                                const uint16_t* __restrict__ k,
+                                                                const uint16_t* __restrict__ v,
+                                                                const uint16_t* __restrict__ dout,
+                                                                const float* __restrict__ lse,
+                                                                const float* __restrict__ delta,
+                                                                float* __restrict__ dk,
+                                                                float* __restrict__ dv, int accumulate) {
+  __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int kt = blockIdx.x;  // lowest keys first: they see the most queries
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = p.Hq / p.Hkv;
+  const int j0 = kt * C::kKeys;
+  const int wj0 = j0 + wave * 32;
+  const int64_t krs = int64_t(p.Hkv) * C::D;
+  const int64_t qrs = int64_t(p.Hq) * C::D;
+
+  const Span wg_k = k_span(p, b, j0, min(j0 + C::kKeys, p.Sk) - 1);
+  const bool wave_live = wj0 < p.Sk;
+  const Span wv_k = k_span(p, b, min(wj0, p.Sk - 1), min(wj0 + 32, p.Sk) - 1);
+
+  // K and V rows of this lane's key as B fragments (k-slots = head dims)
+  const int key = min(wj0 + l32, p.Sk - 1);
+  const bool key_ok = wj0 + l32 < p.Sk;
+  bf16x8 kf[C::KS], vf[C::KS];
+  {
+    const uint16_t* kr = k + (int64_t(b) * p.Sk + key) * krs + int64_t(g) * C::D;
+    const uint16_t* vr = v + (int64_t(b) * p.Sk + key) * krs + int64_t(g) * C::D;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
+      if (key_ok) {
+        x = *reinterpret_cast<const u32x4*>(kr + s * 16 + hi * 8);
+        y = *reinterpret_cast<const u32x4*>(vr + s * 16 + hi * 8);
+      }
+      kf[s] = __builtin_bit_cast(bf16x8, x);
+      vf[s] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+  const int my_kpos = kpos_at(p, key);
+  const int my_kseg = kseg_at(p, b, key);
+
+  f32x16 dk_acc[C::DB], dv_acc[C::DB];
+#pragma unroll
+  for (int d = 0; d < C::DB; ++d) dk_acc[d] = dv_acc[d] = f32x16{};
+
+  const float c2 = p.scale * kLog2e;
+  const int n_it = (p.Sq + C::BM - 1) / C::BM;
+  const int n_t = G * n_it;  // flattened (query head of the group, query tile)
+
+  auto tile_class = [&](int t, const Span& ksp) {
+    const int i0 = (t % n_it) * C::BM;
+    return classify(p, q_span(p, b, i0, min(i0 + C::BM, p.Sq) - 1), ksp, false);
+  };
+  auto next_tile = [&](int t) {
+    while (t < n_t && tile_class(t, wg_k) == kEmpty) ++t;
+    return t;
+  };
+  typename C::Tile tq, tg;
+  auto load = [&](int t) {
+    const int h = g * G + t / n_it;
+    const int i0 = (t % n_it) * C::BM;
+    tq.load(q + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs, i0, p.Sq);
+    tg.load(dout + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs, i0, p.Sq);
+  };
+  auto store = [&](int t, uint8_t* base) {
+    DkvStage<C> st(base);
+    tq.store_rows(st.q, C::RLD);
+    tq.store_cols(st.qt, C::TLD);
+    tg.store_rows(st.g, C::RLD);
+    tg.store_cols(st.gt, C::TLD);
+    const int h = g * G + t / n_it;
+    const int i0 = (t % n_it) * C::BM;
+    for (int r = tid; r < C::BM; r += C::kThreads) {
+      const int i = i0 + r;
+      const bool ok = i < p.Sq;
+      const int64_t li = (int64_t(b) * p.Hq + h) * p.Sq + i;
+      st.lse2[r] = ok ? lse2_of(lse[li]) : INFINITY;
+      st.delta[r] = ok ? delta[li] : 0.0f;
+      st.qpos[r] = ok ? qpos_at(p, i) : 0;
+      st.qseg[r] = ok ? qseg_at(p, b, i) : 0;
+    }
+  };
+
+  int cur = next_tile(0);
+  if (cur < n_t) {
+    load(cur);
+    store(cur, smem);
+    __syncthreads();
+    int buf = 0;
+    const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
+    while (true) {
+      const int nxt = next_tile(cur + 1);
+      const bool has_next = nxt < n_t;
+      if (has_next) load(nxt);
+      const int wcls = wave_live ? tile_class(cur, wv_k) : kEmpty;
+      if (wcls != kEmpty) {
+        DkvStage<C> st(smem + buf * C::kStageBytes);
+#pragma unroll
+        for (int qb = 0; qb < C::QBLK; ++qb) {
+          f32x16 s = f32x16{}, dp = f32x16{};
+          const int arow = (qb * 32 + perm_row(l32)) * C::RLD + hi * 8;
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            s = mma(ld8(st.q + arow + ks * 16), kf[ks], s);
+            dp = mma(ld8(st.g + arow + ks * 16), vf[ks], dp);
+          }
+          // register r holds query row qb*32 + key_of_reg(r, hi) of this lane's key
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int r0 = qb * 32 + key_of_reg(4 * jj, hi);
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(st.lse2 + r0);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(st.delta + r0);
+            i32x4 qp4 = i32x4{0, 0, 0, 0}, qs4 = i32x4{0, 0, 0, 0};
+            if (wcls == kPartial) {
+              qp4 = *reinterpret_cast<const i32x4*>(st.qpos + r0);
+              qs4 = *reinterpret_cast<const i32x4*>(st.qseg + r0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 4 * jj + i;
+              float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[i]));
+              if (wcls == kPartial && !pair_visible(ms, qp4[i], my_kpos, qs4[i], my_kseg)) pr = 0.0f;
+              s[r] = pr;
+              dp[r] = pr * (dp[r] - d4[i]);
+            }
+          }
+          // dV^T += dO^T P ; dK^T += Q^T dS over the block's two 16-query k-steps
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const bf16x8 pb = to_bf16x8(s, 8 * tt);
+            const bf16x8 sb = to_bf16x8(dp, 8 * tt);
+            const int col = (qb * 2 + tt) * 16 + hi * 8;
+#pragma unroll
+            for (int d = 0; d < C::DB; ++d) {
+              dv_acc[d] = mma(ld8(st.gt + (d * 32 + l32) * C::TLD + col), pb, dv_acc[d]);
+              dk_acc[d] = mma(ld8(st.qt + (d * 32 + l32) * C::TLD + col), sb, dk_acc[d]);
+            }
+          }
+        }
+      }
+      if (has_next) store(nxt, smem + (buf ^ 1) * C::kStageBytes);
+      __syncthreads();
+      if (!has_next) break;
+      cur = nxt;
+      buf ^= 1;
+    }
+  }
+
+  // epilogue: lane holds key column l32, dims d*32 + 8j + 4*hi + (0..3)
+  if (!key_ok) return;
+  float* dkr = dk + ((int64_t(b) * p.Sk + wj0 + l32) * p.Hkv + g) * C::D;
+  float* dvr = dv + ((int64_t(b) * p.Sk + wj0 + l32) * p.Hkv + g) * C::D;
+#pragma unroll
+  for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int off = d * 32 + 8 * j + 4 * hi;
+      f32x4 a{dk_acc[d][4 * j] * p.scale, dk_acc[d][4 * j + 1] * p.scale, dk_acc[d][4 * j + 2] * p.scale,
+              dk_acc[d][4 * j + 3] * p.scale};
+      f32x4 c{dv_acc[d][4 * j], dv_acc[d][4 * j + 1], dv_acc[d][4 * j + 2], dv_acc[d][4 * j + 3]};
+      if (accumulate) {
+        a += *reinterpret_cast<const f32x4*>(dkr + off);
+        c += *reinterpret_cast<const f32x4*>(dvr + off);
+      }
+      *reinterpret_cast<f32x4*>(dkr + off) = a;
+      *reinterpret_cast<f32x4*>(dvr + off) = c;
+    }
+}
+
+// ---- 3. dQ --------------------------------------------------------------------
+template <int D_, int NW_, int BN_>
+struct DqCfg {
+  static constexpr int D = D_, NW = NW_, BN = BN_;
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kRows = 32 * NW;
+  static constexpr int KS = D / 16;
+  static constexpr int KB = BN / 32;
+  static constexpr int DB = D / 32;
+  static constexpr int PT = BN / 16;
+  static constexpr int RLD = D + 8;
+  static constexpr int TLD = BN + 8;
+  static constexpr int kRowElems = BN * RLD;
+  static constexpr int kColElems = D * TLD;
+  // K rows, K^T, V rows, then kpos, kseg
+  static constexpr int kStageBytes = (2 * kRowElems + kColElems) * 2 + 2 * BN * 4;
+  static constexpr int kLdsBytes = 2 * kStageBytes;
+  using Tile = RowTile<BN, D, kThreads>;
+};
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void attn_dq_kernel(AttnProblem p, const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k,
+                                                              const uint16_t* __restrict__ v,
+                                                              const uint16_t* __restrict__ dout,
+                                                              const float* __restrict__ lse,
+                                                              const float* __restrict__ delta,
+                                                              float* __restrict__ dq, int accumulate) {
+  __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int n_qt = (p.Sq + C::kRows - 1) / C::kRows;
+  const int qt = p.causal ? (n_qt - 1 - int(blockIdx.x)) : int(blockIdx.x);
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int g = h / (p.Hq / p.Hkv);
+  const int q0 = qt * C::kRows;
+  const int wq0 = q0 + wave * 32;
+  const int64_t krs = int64_t(p.Hkv) * C::D;
+  const int64_t qrs = int64_t(p.Hq) * C::D;
+
+  const Span wg_q = q_span(p, b, q0, min(q0 + C::kRows, p.Sq) - 1);
+  const bool wave_live = wq0 < p.Sq;
+  const Span wv_q = q_span(p, b, min(wq0, p.Sq - 1), min(wq0 + 32, p.Sq) - 1);
+
+  const int row = min(wq0 + l32, p.Sq - 1);
+  const bool row_ok = wq0 + l32 < p.Sq;
+  bf16x8 qf[C::KS], gf[C::KS];
+  {
+    const uint16_t* qr = q + (int64_t(b) * p.Sq + row) * qrs + int64_t(h) * C::D;
+    const uint16_t* gr = dout + (int64_t(b) * p.Sq + row) * qrs + int64_t(h) * C::D;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
+      if (row_ok) {
+        x = *reinterpret_cast<const u32x4*>(qr + s * 16 + hi * 8);
+        y = *reinterpret_cast<const u32x4*>(gr + s * 16 + hi * 8);
+      }
+      qf[s] = __builtin_bit_cast(bf16x8, x);
+      gf[s] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+  const int64_t li = (int64_t(b) * p.Hq + h) * p.Sq + row;
+  const float my_lse2 = row_ok ? lse2_of(lse[li]) : INFINITY;
+  const float my_delta = row_ok ? delta[li] : 0.0f;
+  const int my_qpos = qpos_at(p, row);
+  const int my_qseg = qseg_at(p, b, row);
+
+  f32x16 dq_acc[C::DB];
+#pragma unroll
+  for (int d = 0; d < C::DB; ++d) dq_acc[d] = f32x16{};
+
+  const float c2 = p.scale * kLog2e;
+  const int n_kt = (p.Sk + C::BN - 1) / C::BN;
+  const uint16_t* kbase = k + int64_t(b) * p.Sk * krs + int64_t(g) * C::D;
+  const uint16_t* vbase = v + int64_t(b) * p.Sk * krs + int64_t(g) * C::D;
+
+  auto tile_class = [&](int kt, const Span& qsp) {
+    const int j0 = kt * C::BN;
+    const int j1 = min(j0 + C::BN, p.Sk) - 1;
+    return classify(p, qsp, k_span(p, b, j0, j1), j1 - j0 + 1 < C::BN);
+  };
+  auto next_tile = [&](int kt) {
+    while (kt < n_kt && tile_class(kt, wg_q) == kEmpty) ++kt;
+    return kt;
+  };
+  typename C::Tile tk, tv;
+  auto stage_ptrs = [&](uint8_t* base, uint16_t*& ks, uint16_t*& kts, uint16_t*& vs, int*& kp, int*& kg) {
+    ks = reinterpret_cast<uint16_t*>(base);
+    kts = ks + C::kRowElems;
+    vs = kts + C::kColElems;
+    kp = reinterpret_cast<int*>(vs + C::kRowElems);
+    kg = kp + C::BN;
+  };
+  auto store = [&](int kt, uint8_t* base) {
+    uint16_t *ks, *kts, *vs;
+    int *kp, *kg;
+    stage_ptrs(base, ks, kts, vs, kp, kg);
+    tk.store_rows(ks, C::RLD);
+    tk.store_cols(kts, C::TLD);
+    tv.store_rows(vs, C::RLD);
+    const int j0 = kt * C::BN;
+    for (int t = tid; t < C::BN; t += C::kThreads) {
+      const int j = j0 + t;
+      const bool ok = j < p.Sk;
+      kp[t] = ok ? kpos_at(p, j) : 0;
+      kg[t] = ok ? kseg_at(p, b, j) : 0;
+    }
+  };
+
+  int cur = next_tile(0);
+  if (cur < n_kt) {
+    tk.load(kbase, krs, cur * C::BN, p.Sk);
+    tv.load(vbase, krs, cur * C::BN, p.Sk);
+    store(cur, smem);
+    __syncthreads();
+    int buf = 0;
+    const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
+    while (true) {
+      const int nxt = next_tile(cur + 1);
+      const bool has_next = nxt < n_kt;
+      if (has_next) {
+        tk.load(kbase, krs, nxt * C::BN, p.Sk);
+        tv.load(vbase, krs, nxt * C::BN, p.Sk);
+      }
+      const int wcls = wave_live ? tile_class(cur, wv_q) : kEmpty;
+      if (wcls != kEmpty) {
+        uint16_t *ks, *kts, *vs;
+        int *kp, *kg;
+        stage_ptrs(smem + buf * C::kStageBytes, ks, kts, vs, kp, kg);
+        f32x16 s[C::KB], dp[C::KB];
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+          s[kb] = f32x16{};
+          dp[kb] = f32x16{};
+          const int arow = (kb * 32 + perm_row(l32)) * C::RLD + hi * 8;
+#pragma unroll
+          for (int kk = 0; kk < C::KS; ++kk) {
+            s[kb] = mma(ld8(ks + arow + kk * 16), qf[kk], s[kb]);
+            dp[kb] = mma(ld8(vs + arow + kk * 16), gf[kk], dp[kb]);
+          }
+        }
+        const int nvalid = p.Sk - cur * C::BN;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int kk0 = kb * 32 + key_of_reg(4 * jj, hi);
+            i32x4 kp4 = i32x4{0, 0, 0, 0}, kg4 = i32x4{0, 0, 0, 0};
+            if (wcls == kPartial) {
+              kp4 = *reinterpret_cast<const i32x4*>(kp + kk0);
+              kg4 = *reinterpret_cast<const i32x4*>(kg + kk0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 4 * jj + i;
+              float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -my_lse2));
+              if (wcls == kPartial &&
+                  !(kk0 + i < nvalid && pair_visible(ms, my_qpos, kp4[i], my_qseg, kg4[i])))
+                pr = 0.0f;
+              dp[kb][r] = pr * (dp[kb][r] - my_delta);
+            }
+          }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int t = 0; t < C::PT; ++t) {
+          const bf16x8 sb = to_bf16x8(dp[t >> 1], 8 * (t & 1));
+#pragma unroll
+          for (int d = 0; d < C::DB; ++d)
+            dq_acc[d] = mma(ld8(kts + (d * 32 + l32) * C::TLD + t * 16 + hi * 8), sb, dq_acc[d]);
+        }
+      }
+      if (has_next) store(nxt, smem + (buf ^ 1) * C::kStageBytes);
+      __syncthreads();
+      if (!has_next) break;
+      cur = nxt;
+      buf ^= 1;
+    }
+  }
+
+  if (!row_ok) return;
+  float* dqr = dq + (int64_t(b) * p.Sq + row) * qrs + int64_t(h) * C::D;
+#pragma unroll
+  for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int off = d * 32 + 8 * j + 4 * hi;
+      f32x4 a{dq_acc[d][4 * j] * p.scale, dq_acc[d][4 * j + 1] * p.scale, dq_acc[d][4 * j + 2] * p.scale,
+              dq_acc[d][4 * j + 3] * p.scale};
+      if (accumulate) a += *reinterpret_cast<const f32x4*>(dqr + off);
+      *reinterpret_cast<f32x4*>(dqr + off) = a;
+    }
+}
+
+template <int D>
+hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const void* v, const void* out,
+                    const float* lse, const void* dout, float* dq, float* dk, float* dv, int accumulate,
+                    float* delta, hipStream_t s) {
+  using U = const uint16_t*;
+  const int64_t rows = int64_t(p.B) * p.Sq * p.Hq;
+  const int64_t threads = rows * (D / 8);
+  hipLaunchKernelGGL(delta_kernel<D>, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, rows, p.Sq,
+                     p.Hq, static_cast<U>(out), static_cast<U>(dout), delta);
+  using KV = DkvCfg<D, 4, 64>;
+  hipLaunchKernelGGL(attn_dkdv_kernel<KV>, dim3((p.Sk + KV::kKeys - 1) / KV::kKeys, p.Hkv, p.B),
+                     dim3(KV::kThreads), 0, s, p, static_cast<U>(q), static_cast<U>(k), static_cast<U>(v),
+                     static_cast<U>(dout), lse, delta, dk, dv, accumulate);
+  using Q = DqCfg<D, 4, 64>;
+  hipLaunchKernelGGL(attn_dq_kernel<Q>, dim3((p.Sq + Q::kRows - 1) / Q::kRows, p.Hq, p.B),
+                     dim3(Q::kThreads), 0, s, p, static_cast<U>(q), static_cast<U>(k), static_cast<U>(v),
+                     static_cast<U>(dout), lse, delta, dq, accumulate);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
+                                const void* out, const float* lse, const void* dout, float* dq,
+                                float* dk, float* dv, int accumulate, float* delta, hipStream_t s) {
+  switch (p.D) {
+    case 128: return launch_d<128>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, s);
+    case 64: return launch_d<64>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, s);
+    case 32: return launch_d<32>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace cp

@@ -1,8 +1,8 @@
 // Row-per-wavefront attention kernels (forward and backward).
 //
 // These serve the float32 problems (small head counts and sequence lengths, e.g.
-// the handbook's toy data), where the bf16 matrix-core path does not apply, and
-// the bf16 backward.  Inputs are float32 or bf16; all arithmetic is float32.  One
+// the handbook's toy data), where the bf16 matrix-core path does not apply.  All
+// arithmetic is float32.  One
 // wavefront owns one row; a lane holds head-dim elements d = lane + 64*t, dot
 // products are wavefront sums, and keys are visited one at a time with the online
 // softmax.
@@ -274,24 +274,6 @@ hipError_t launch_attn_bwd_f32(const AttnProblem& p, const float* q, const float
                                float* dk, float* dv, int accumulate, float* delta, hipStream_t s) {
   return p.D <= 64 ? bwd_nt<float, 1>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, s)
                    : bwd_nt<float, 2>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, s);
-}
-
-// Row-wise backward for bf16 inputs.
-hipError_t launch_attn_bwd_rowwise_bf16(const AttnProblem& p, const void* q, const void* k,
-                                        const void* v, const void* out, const float* lse,
-                                        const void* dout, float* dq, float* dk, float* dv,
-                                        int accumulate, float* delta, hipStream_t s) {
-  using T = uint16_t;
-  return bwd_nt<T, 2>(p, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-                      static_cast<const T*>(out), lse, static_cast<const T*>(dout), dq, dk, dv,
-                      accumulate, delta, s);
-}
-
-// bf16 backward entry point (row-wise kernels).
-hipError_t launch_attn_bwd_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
-                                const void* out, const float* lse, const void* dout, float* dq,
-                                float* dk, float* dv, int accumulate, float* delta, hipStream_t s) {
-  return launch_attn_bwd_rowwise_bf16(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, s);
 }
 
 }  // namespace cp
