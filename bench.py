@@ -1,0 +1,292 @@
+"""Benchmark of the context-parallel attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-legs]
+
+Workload (one "step"): the Ulysses share of llama2-7b (MHA, 32 heads, D=128) at
+32K context with cp=16, every simulated rank on this one GPU:
+
+  forward:  relayout q, k, v  [16][1,2048,32,128] -> [16][1,32768,2,128]  (bf16)
+            16 x attention fwd, one launch per rank at its real shape
+            (q/k/v [1,32768,2,128], causal)
+            inverse relayout of the output
+  backward: relayout dout; 16 x attention bwd (fp32 gradients);
+            inverse relayout of dq, dk, dv (fp32)
+
+value = algorithmic attention FLOPs of the step (fwd 4*D and bwd 8*D per visible
+(query, key, head) triple) / step time, in TFLOP/s.  Inputs are resident in HBM
+before the timed region.  The relayout bandwidth is reported beside it.
+
+Legs timed in the same run (not part of value): the ring share of llama2-7b
+(2048 queries x 32 heads vs 16 zigzag KV blocks, fwd + merge), the 64K-token
+dual-chunk-swap reorder, and the packed + windowed 8K ring share (4 ranks x 4
+steps, fwd + merge + bwd).  The CPU oracle is timed on a bounded sample of the
+step's attention rows (cpu_baseline).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd+bwd TFLOP/s and % bf16 MFMA peak; relayout GB/s on 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E (published)
+
+
+def pairs_causal(S: int) -> int:
+    return S * (S + 1) // 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--no-legs", action="store_true", help="skip the ring / reorder / packed legs")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def sha_of(*paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+class UlyssesStep:
+    """All buffers of the step, allocated once; ``run`` launches one step."""
+
+    P, S, H, D = 16, 32768, 32, 128
+
+    def __init__(self, torch, cp, cp_inputs):
+        P, S, H, D = self.P, self.S, self.H, self.D
+        self.torch, self.cp = torch, cp
+        dev = "cuda"
+        q, k, v, do = cp_inputs.normal_tensors([(1, S, H, D)] * 4, seed=0)
+        # the global [1,S,H,D] sequence split into P contiguous slices = [P][1][S/P][H][D]
+        self.stack = [t.reshape(P, 1, S // P, H, D).to(dev) for t in (q, k, v, do)]
+        bf, f32 = torch.bfloat16, torch.float32
+        sh = (P, 1, S, H // P, D)
+        self.ql, self.kl, self.vl, self.gl = (torch.empty(sh, device=dev, dtype=bf) for _ in range(4))
+        self.ol = torch.empty(sh, device=dev, dtype=bf)
+        self.lse = torch.empty(P, 1, H // P, S, device=dev, dtype=f32)
+        self.out = torch.empty(P, 1, S // P, H, D, device=dev, dtype=bf)
+        self.dql, self.dkl, self.dvl = (torch.empty(sh, device=dev, dtype=f32) for _ in range(3))
+        self.dq, self.dk, self.dv = (torch.empty(P, 1, S // P, H, D, device=dev, dtype=f32) for _ in range(3))
+        self.ws = cp.bwd_workspace(self.ql[0], self.kl[0])
+        hp = H // P
+        self.flops_fwd_rank = 4 * D * hp * pairs_causal(S)
+        self.flops_bwd_rank = 8 * D * hp * pairs_causal(S)
+        self.flops = P * (self.flops_fwd_rank + self.flops_bwd_rank)
+        # bytes moved by the relayouts of one step: one read + one write each
+        bf_bytes = S * H * D * 2  # one whole [P][1][S/P][H][D] bf16 tensor
+        self.relayout_bytes = 5 * 2 * bf_bytes + 3 * 2 * 2 * bf_bytes
+
+    def run(self):
+        cp, P = self.cp, self.P
+        qs, ks, vs, gs = self.stack
+        cp.ulysses_relayout(qs, P, out=self.ql)
+        cp.ulysses_relayout(ks, P, out=self.kl)
+        cp.ulysses_relayout(vs, P, out=self.vl)
+        for p in range(P):
+            cp.attn_fwd(self.ql[p], self.kl[p], self.vl[p], out=self.ol[p], lse=self.lse[p])
+        cp.ulysses_relayout_inv(self.ol, P, out=self.out)
+        cp.ulysses_relayout(gs, P, out=self.gl)
+        for p in range(P):
+            cp.attn_bwd(self.ql[p], self.kl[p], self.vl[p], self.ol[p], self.lse[p], self.gl[p],
+                        dq=self.dql[p], dk=self.dkl[p], dv=self.dvl[p], workspace=self.ws)
+        cp.ulysses_relayout_inv(self.dql, P, out=self.dq)
+        cp.ulysses_relayout_inv(self.dkl, P, out=self.dk)
+        cp.ulysses_relayout_inv(self.dvl, P, out=self.dv)
+
+
+def timed(torch, fn, reps):
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def legs(torch, cp, cp_inputs):
+    """Ring share (llama2-7b, cp=16), 64K reorder and the packed + windowed ring."""
+    out = {}
+    # ring share of llama2-7b: rank 0, 16 zigzag steps of fwd + merge
+    S, H, D, P = 32768, 32, 128, 16
+    q, k, v = (t.cuda() for t in cp_inputs.normal_tensors([(1, S, H, D)] * 3, seed=0))
+    qz, kz, vz = (cp.zigzag_reorder(t, P) for t in (q, k, v))
+    del q, k, v
+    ring = cp.drivers.RingShare(qz, kz, vz, P, 0)
+    ring.forward()
+    with cp._lib.KernelTrace() as tr:
+        ms = timed(torch, ring.forward, 5)
+    fl = 4 * D * H * (2 * P * (S // (2 * P)) ** 2 + S // (2 * P))
+    fwd_ms, n_fwd = tr.results.get("attn_fwd_mfma", (0.0, 1))
+    mg_ms, n_mg = tr.results.get("lse_merge", (0.0, 1))
+    merge_bytes = (S // P) * H * D * (4 + 2 + 4) + 3 * (S // P) * H * 4
+    out["ring_llama2_7b_32k_cp16_rank0"] = {
+        "ms_per_pass": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+        "attn_fwd_mfma_avg_ms": round(fwd_ms / n_fwd, 5),
+        "lse_merge_avg_ms": round(mg_ms / n_mg, 5),
+        "lse_merge_gbps": round(merge_bytes / (mg_ms / n_mg) / 1e6, 1)}
+    del qz, kz, vz, ring
+    # dual-chunk-swap reorder of 64K tokens into 8 chunks: [1,65536,4096] bf16 (512 MiB)
+    x = torch.randn(1, 65536, 4096, device="cuda").bfloat16()
+    y = torch.empty_like(x)
+    cp.zigzag_reorder(x, 4, out=y)
+    with cp._lib.KernelTrace() as tr:
+        timed(torch, lambda: cp.zigzag_reorder(x, 4, out=y), 10)
+    zms, zn = tr.results["zigzag_reorder"]
+    out["reorder_64k_4096_bf16_cp4"] = {"avg_ms": round(zms / zn, 5),
+                                        "gbps": round(2 * x.numel() * 2 / (zms / zn) / 1e6, 1)}
+    del x, y
+    # packed + windowed ring share: 8K, 32 q / 8 kv heads, docs 256..4096, window 4096, cp=4
+    S, Hq, Hkv, P = 8192, 32, 8, 4
+    q, k, v, do = (t.cuda() for t in cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D),
+                                                               (1, S, Hq, D)], seed=0))
+    seg = cp_inputs.segment_ids(cp_inputs.doc_lengths(S)).cuda()
+    qz, kz, vz, dz = (cp.zigzag_reorder(t, P) for t in (q, k, v, do))
+    sz = cp.zigzag_reorder(seg, P)
+    shares = [cp.drivers.RingShare(qz, kz, vz, P, r, seg=sz, window=4096) for r in range(P)]
+    C = S // P
+
+    def packed_pass():
+        dk = torch.zeros(kz.shape, device="cuda")
+        dv = torch.zeros(vz.shape, device="cuda")
+        for r, sh in enumerate(shares):
+            o, l = sh.forward()
+            ob = o.bfloat16()
+            dq = torch.zeros(1, C, Hq, D, device="cuda")
+            sh.backward(ob, l, dz[:, r * C:(r + 1) * C], dq, dk, dv)
+
+    packed_pass()
+    ms = timed(torch, packed_pass, 3)
+    out["packed_window_8k_cp4_all_ranks"] = {"ms_per_pass": round(ms, 3)}
+    return out
+
+
+def cpu_baseline(torch, cp_inputs, budget_s):
+    """The oracle (numpy float64) on a bounded sample of the step's attention rows."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    S, H, D = 32768, 2, 128
+    q, k, v, do = (t.float().numpy().astype(np.float64)
+                   for t in cp_inputs.normal_tensors([(1, S, H, D)] * 4, seed=7))
+    rows = np.arange(S - 1, -1, -7)  # spread over the sequence, heaviest first
+    t0 = time.perf_counter()
+    done_pairs, n = 0, 0
+    for i0 in range(0, len(rows), 64):
+        r = np.sort(rows[i0:i0 + 64])
+        qr, gr = q[:, r], do[:, r]
+        o, l = oracle.attn_fwd(qr, k, v, q_pos=r)
+        oracle.attn_bwd(qr, k, v, o, l, gr, q_pos=r)
+        done_pairs += int((r + 1).sum()) * H
+        n += len(r)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = done_pairs * 12 * D
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} query rows x {H} heads (every 7th row of S=32768 from the end, causal) fwd+bwd in float64 "
+                      f"against all keys, {dt:.1f} s"}
+
+
+def traffic_from_profiles(kernel_sha):
+    """HBM bytes per launch from committed rocprofv3 counters, if they match the source."""
+    p = os.path.join(ROOT, "profiles", "attn_bwd_mfma_counters.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_sha") != kernel_sha:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {a.gpus} is not supported (every simulated "
+              "context-parallel rank runs on the one GPU)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import cp_inputs
+    import context_cp_attn_amd as cp
+    cp.load_library()
+    torch.cuda.set_device(0)
+
+    step = UlyssesStep(torch, cp, cp_inputs)
+    for _ in range(a.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with cp._lib.KernelTrace() as tr:
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(a.steps):
+            step.run()
+        e.record()
+        torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / a.steps
+    value = step.flops / (ms * 1e-3) / 1e12
+    kern = {k_: {"avg_ms": round(t / n, 5), "launches": n} for k_, (t, n) in tr.results.items()}
+    # dominant kernel: the most total time
+    dom = max(tr.results.items(), key=lambda kv: kv[1][0])[0]
+    bwd_ms = tr.results["attn_bwd_mfma"][0] / tr.results["attn_bwd_mfma"][1]
+    fwd_ms = tr.results["attn_fwd_mfma"][0] / tr.results["attn_fwd_mfma"][1]
+    rel_t = sum(tr.results[k_][0] for k_ in ("ulysses_relayout", "ulysses_relayout_inv")) / a.steps
+    src = os.path.join(ROOT, "context_cp_attn_amd", "csrc")
+    bwd_sha = sha_of(os.path.join(src, "attn_bwd_mfma.hip"), os.path.join(src, "mfma_common.h"))
+    if dom == "attn_bwd_mfma":
+        ach = step.flops_bwd_rank / (bwd_ms * 1e-3) / 1e12
+        roof = {"kernel": "attn_bwd_mfma", "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_from_profiles(bwd_sha), "avg_launch_ms": round(bwd_ms, 4),
+                "algorithmic_per_launch": f"8*D*Hq*S(S+1)/2 = {step.flops_bwd_rank:.4e} FLOP"}
+    else:
+        ach = step.flops_fwd_rank / (fwd_ms * 1e-3) / 1e12
+        roof = {"kernel": "attn_fwd_mfma", "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(fwd_ms, 4),
+                "algorithmic_per_launch": f"4*D*Hq*S(S+1)/2 = {step.flops_fwd_rank:.4e} FLOP"}
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "ulysses_llama2_7b_32k_cp16", "global_batch": 1, "seq_len": 32768,
+                   "heads": 32, "head_dim": 128, "cp": 16,
+                   "parallelism": "cp16 Ulysses, all 16 ranks simulated on 1 GPU",
+                   "step": "relayout q,k,v; 16x fwd; relayout_inv out; relayout dout; 16x bwd; "
+                           "relayout_inv dq,dk,dv"},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(step.flops_fwd_rank / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(step.flops_bwd_rank / (bwd_ms * 1e-3) / 1e12, 2),
+        "relayout_gbps": round(step.relayout_bytes / (rel_t * 1e-3) / 1e9, 1),
+        "relayout_pct_hbm_peak": round(100 * step.relayout_bytes / (rel_t * 1e-3) / 1e9 / PEAK_HBM_GBPS, 1),
+        "roofline": roof,
+        "kernels": kern,
+    }
+    if not a.no_legs:
+        res["legs"] = legs(torch, cp, cp_inputs)
+    res["cpu_baseline"] = None if a.no_cpu else cpu_baseline(torch, cp_inputs, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -38,6 +38,11 @@ SIGNATURES = {
     "cp_ulysses_relayout": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp]),
     "cp_ulysses_relayout_inv": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp]),
     "cp_zigzag_reorder": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp]),
+    "cp_prof_enable": (None, [c_i32]),
+    "cp_prof_reset": (None, []),
+    "cp_prof_kernel_count": (c_i32, []),
+    "cp_prof_kernel_name": (ctypes.c_char_p, [c_i32]),
+    "cp_prof_read": (c_i32, [c_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "cp_status_string": (ctypes.c_char_p, [c_i32]),
     "cp_last_error": (ctypes.c_char_p, []),
 }
@@ -74,3 +79,30 @@ class CpError(ValueError):
 def check(status: int) -> None:
     if status != CP_OK:
         raise CpError(status, load().cp_last_error().decode())
+
+
+class KernelTrace:
+    """Per-kernel durations from the library's HIP-event tracing.
+
+        with KernelTrace() as tr:
+            ...launches...
+        tr.results  # {kernel name: (total_ms, launches)}
+    """
+
+    def __enter__(self):
+        lib = load()
+        lib.cp_prof_reset()
+        lib.cp_prof_enable(1)
+        return self
+
+    def __exit__(self, *exc):
+        lib = load()
+        lib.cp_prof_enable(0)
+        self.results = {}
+        for i in range(lib.cp_prof_kernel_count()):
+            ms, n = ctypes.c_double(), ctypes.c_int64()
+            check(lib.cp_prof_read(i, ctypes.byref(ms), ctypes.byref(n)))
+            if n.value:
+                self.results[lib.cp_prof_kernel_name(i).decode()] = (ms.value, n.value)
+        lib.cp_prof_reset()
+        return False

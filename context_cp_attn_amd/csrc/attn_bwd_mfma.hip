@@ -8,18 +8,19 @@
 // Attention itself: handbook "Context parallelism: Ring Attention and Ulysses",
 // §"Which operations partition directly"; its gradient is the textbook one.
 //
-// Three launches:
+// Two launches (the second holds both the dK/dV and the dQ roles):
 //  1. delta: Delta = rowsum(dO * O) into the caller's workspace [B,Hq,Sq].
-//  2. dK/dV: a workgroup owns 32*NW keys of one kv head (one wavefront per 32
-//     keys, K and V held as B fragments in registers) and streams query tiles of
-//     every query head of the group through LDS.  S = Q K^T and dP = dO V^T are
+//  2a. dK/dV role: a workgroup owns 32*NW keys of one kv head (one wavefront per
+//     32 keys, K and V held as B fragments in registers) and streams query tiles
+//     of every query head of the group through LDS.  S = Q K^T and dP = dO V^T are
 //     computed query-major so that P and dS land directly as B fragments of
 //     dV^T += dO^T P and dK^T += Q^T dS (Q and dO are staged both row-major and
 //     transposed).
-//  3. dQ: a workgroup owns 32*NW queries of one head and streams key tiles:
+//  2b. dQ role: a workgroup owns 32*NW queries of one head and streams key tiles:
 //     S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
 // Tiles are skipped / masked exactly as in the forward (empty / partial / full).
 #include "mfma_common.h"
+#include "prof.h"
 
 namespace cp {
 namespace {
@@ -103,23 +104,16 @@ struct DkvStage {
 };
 
 template <class C>
-__global__ __launch_bounds__(C::kThreads) void attn_dkdv_kernel(AttnProblem p, const uint16_t* __restrict__ q,
-                                                                const uint16_t* __restrict__ k,
-                                                                const uint16_t* __restrict__ v,
-                                                                const uint16_t* __restrict__ dout,
-                                                                const float* __restrict__ lse,
-                                                                const float* __restrict__ delta,
-                                                                float* __restrict__ dk,
-                                                                float* __restrict__ dv, int accumulate) {
-  __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
+CP_DEVICE void dkdv_body(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                         const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                         const float* __restrict__ lse, const float* __restrict__ delta,
+                         float* __restrict__ dk, float* __restrict__ dv, int accumulate, uint8_t* smem,
+                         int kt, int g, int b) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int kt = blockIdx.x;  // lowest keys first: they see the most queries
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
   const int G = p.Hq / p.Hkv;
   const int j0 = kt * C::kKeys;
   const int wj0 = j0 + wave * 32;
@@ -300,23 +294,15 @@ struct DqCfg {
 };
 
 template <class C>
-__global__ __launch_bounds__(C::kThreads) void attn_dq_kernel(AttnProblem p, const uint16_t* __restrict__ q,
-                                                              const uint16_t* __restrict__ k,
-                                                              const uint16_t* __restrict__ v,
-                                                              const uint16_t* __restrict__ dout,
-                                                              const float* __restrict__ lse,
-                                                              const float* __restrict__ delta,
-                                                              float* __restrict__ dq, int accumulate) {
-  __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
+CP_DEVICE void dq_body(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                       const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                       const float* __restrict__ lse, const float* __restrict__ delta,
+                       float* __restrict__ dq, int accumulate, uint8_t* smem, int qt, int h, int b) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int n_qt = (p.Sq + C::kRows - 1) / C::kRows;
-  const int qt = p.causal ? (n_qt - 1 - int(blockIdx.x)) : int(blockIdx.x);
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
   const int g = h / (p.Hq / p.Hkv);
   const int q0 = qt * C::kRows;
   const int wq0 = q0 + wave * 32;
@@ -476,6 +462,52 @@ __global__ __launch_bounds__(C::kThreads) void attn_dq_kernel(AttnProblem p, con
     }
 }
 
+// ---- fused dK/dV + dQ launch --------------------------------------------------
+// One grid holds both roles.  Each role's list is ordered heaviest first (causal:
+// low key tiles for dK/dV, high query tiles for dQ, every head interleaved) and
+// the two lists are merged at the ratio of their lengths, so both kinds of work
+// start together and no second launch waits for a tail.
+struct BwdArgs {
+  AttnProblem p;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse;
+  const float* delta;
+  float* dq;
+  float* dk;
+  float* dv;
+  int accumulate;
+  int n_kv;  // dK/dV workgroups = B * Hkv * key tiles
+  int n_q;   // dQ workgroups = B * Hq * query tiles
+};
+
+template <class KV, class Q>
+__global__ __launch_bounds__(KV::kThreads) void attn_bwd_kernel(BwdArgs a) {
+  static_assert(KV::kThreads == Q::kThreads, "roles share the block size");
+  constexpr int kLds = KV::kLdsBytes > Q::kLdsBytes ? KV::kLdsBytes : Q::kLdsBytes;
+  __shared__ __align__(16) uint8_t smem[kLds];
+  const AttnProblem& p = a.p;
+  const int64_t L = blockIdx.x;
+  const int64_t N = int64_t(a.n_kv) + a.n_q;
+  const int64_t before = (L * a.n_kv) / N;  // dK/dV workgroups placed before L
+  const bool kv_role = ((L + 1) * a.n_kv) / N > before;
+  if (kv_role) {
+    const int i = int(before);
+    const int bg = i % (p.B * p.Hkv);
+    dkdv_body<KV>(p, a.q, a.k, a.v, a.dout, a.lse, a.delta, a.dk, a.dv, a.accumulate, smem,
+                  i / (p.B * p.Hkv), bg % p.Hkv, bg / p.Hkv);
+  } else {
+    const int i = int(L - before);
+    const int bh = i % (p.B * p.Hq);
+    const int r = i / (p.B * p.Hq);
+    const int n_qt = (p.Sq + Q::kRows - 1) / Q::kRows;
+    dq_body<Q>(p, a.q, a.k, a.v, a.dout, a.lse, a.delta, a.dq, a.accumulate, smem,
+               p.causal ? n_qt - 1 - r : r, bh % p.Hq, bh / p.Hq);
+  }
+}
+
 template <int D>
 hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const void* v, const void* out,
                     const float* lse, const void* dout, float* dq, float* dk, float* dv, int accumulate,
@@ -483,16 +515,21 @@ hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const vo
   using U = const uint16_t*;
   const int64_t rows = int64_t(p.B) * p.Sq * p.Hq;
   const int64_t threads = rows * (D / 8);
-  hipLaunchKernelGGL(delta_kernel<D>, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, rows, p.Sq,
-                     p.Hq, static_cast<U>(out), static_cast<U>(dout), delta);
+  {
+    ProfScope ps(s, kProfBwdDelta);
+    hipLaunchKernelGGL(delta_kernel<D>, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, rows, p.Sq,
+                       p.Hq, static_cast<U>(out), static_cast<U>(dout), delta);
+  }
   using KV = DkvCfg<D, 4, 64>;
-  hipLaunchKernelGGL(attn_dkdv_kernel<KV>, dim3((p.Sk + KV::kKeys - 1) / KV::kKeys, p.Hkv, p.B),
-                     dim3(KV::kThreads), 0, s, p, static_cast<U>(q), static_cast<U>(k), static_cast<U>(v),
-                     static_cast<U>(dout), lse, delta, dk, dv, accumulate);
   using Q = DqCfg<D, 4, 64>;
-  hipLaunchKernelGGL(attn_dq_kernel<Q>, dim3((p.Sq + Q::kRows - 1) / Q::kRows, p.Hq, p.B),
-                     dim3(Q::kThreads), 0, s, p, static_cast<U>(q), static_cast<U>(k), static_cast<U>(v),
-                     static_cast<U>(dout), lse, delta, dq, accumulate);
+  BwdArgs a{p, static_cast<U>(q), static_cast<U>(k), static_cast<U>(v), static_cast<U>(dout), lse, delta,
+            dq, dk, dv, accumulate,
+            p.B * p.Hkv * ((p.Sk + KV::kKeys - 1) / KV::kKeys),
+            p.B * p.Hq * ((p.Sq + Q::kRows - 1) / Q::kRows)};
+  {
+    ProfScope ps(s, kProfBwdMfma);
+    hipLaunchKernelGGL((attn_bwd_kernel<KV, Q>), dim3(unsigned(a.n_kv + a.n_q)), dim3(KV::kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

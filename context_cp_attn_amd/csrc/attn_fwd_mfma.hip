@@ -23,9 +23,10 @@
 //  * Tiles are classified per workgroup and per wavefront as empty (skipped: no
 //    load, no math), full (no mask) or partial (elementwise mask) from the
 //    extreme positions / segment ids of the tile, which are monotone.
-//  * Causal grids run heaviest query tiles first.
+//  * Causal grids run the heaviest query tiles of every head first.
 #include "common.h"
 #include "launch.h"
+#include "prof.h"
 
 namespace cp {
 namespace {
@@ -196,10 +197,13 @@ __global__ __launch_bounds__(C::kThreads) void attn_fwd_mfma_kernel(AttnProblem 
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
+  // heaviest query tiles of every (batch, head) first
   const int n_qt = (p.Sq + C::kRows - 1) / C::kRows;
-  const int qt = p.causal ? (n_qt - 1 - int(blockIdx.x)) : int(blockIdx.x);
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  const int tile_rank = int(blockIdx.x) / (p.B * p.Hq);
+  const int bh = int(blockIdx.x) - tile_rank * (p.B * p.Hq);
+  const int qt = p.causal ? (n_qt - 1 - tile_rank) : tile_rank;
+  const int h = bh % p.Hq;
+  const int b = bh / p.Hq;
   const int g = h / (p.Hq / p.Hkv);
   const int q0 = qt * C::kRows;
   const int wq0 = q0 + wave * C::kWaveRows;
@@ -394,7 +398,8 @@ __global__ __launch_bounds__(C::kThreads) void attn_fwd_mfma_kernel(AttnProblem 
 template <class C>
 hipError_t launch_cfg(const AttnProblem& p, const void* q, const void* k, const void* v, void* out,
                       float* lse, hipStream_t s) {
-  dim3 grid((p.Sq + C::kRows - 1) / C::kRows, p.Hq, p.B);
+  dim3 grid(unsigned((p.Sq + C::kRows - 1) / C::kRows) * unsigned(p.Hq * p.B));
+  ProfScope ps(s, kProfFwdMfma);
   hipLaunchKernelGGL(attn_fwd_mfma_kernel<C>, grid, dim3(C::kThreads), 0, s, p,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse);

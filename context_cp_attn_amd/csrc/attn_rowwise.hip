@@ -12,6 +12,7 @@
 // log-sum-exp); gradient: the softmax-attention VJP with Delta_i = dO_i . O_i.
 #include "common.h"
 #include "launch.h"
+#include "prof.h"
 
 namespace cp {
 namespace {
@@ -244,6 +245,7 @@ template <typename T, int NT>
 hipError_t fwd_nt(const AttnProblem& p, const T* q, const T* k, const T* v, T* out, float* lse,
                   hipStream_t s) {
   dim3 grid((p.Sq + kWaves - 1) / kWaves, p.Hq, p.B);
+  ProfScope ps(s, kProfFwdRowwise);
   hipLaunchKernelGGL((fwd_rowwise_kernel<T, NT>), grid, dim3(kThreads), 0, s, p, q, k, v, out, lse);
   return hipGetLastError();
 }
@@ -253,6 +255,7 @@ hipError_t bwd_nt(const AttnProblem& p, const T* q, const T* k, const T* v, cons
                   const float* lse, const T* dout, float* dq, float* dk, float* dv, int accumulate,
                   float* delta, hipStream_t s) {
   const int64_t rows = int64_t(p.B) * p.Sq * p.Hq;
+  ProfScope ps(s, kProfBwdRowwise);
   hipLaunchKernelGGL((delta_rowwise_kernel<T, NT>), dim3(unsigned((rows + kWaves - 1) / kWaves)),
                      dim3(kThreads), 0, s, p.B, p.Sq, p.Hq, p.D, out, dout, delta);
   hipLaunchKernelGGL((dq_rowwise_kernel<T, NT>), dim3((p.Sq + kWaves - 1) / kWaves, p.Hq, p.B),

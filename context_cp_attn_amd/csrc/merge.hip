@@ -8,6 +8,7 @@
 // its row in the same instruction before the row's first lane writes the new one.
 #include "common.h"
 #include "launch.h"
+#include "prof.h"
 
 namespace cp {
 namespace {
@@ -71,6 +72,7 @@ hipError_t launch_lse_merge(int64_t B, int64_t S, int64_t H, int64_t D, float* a
                             const void* blk, const float* lse_blk, int blk_is_bf16, hipStream_t s) {
   const int64_t nvec = B * S * H * (D / 4);
   const unsigned grid = unsigned((nvec + kThreads - 1) / kThreads);
+  ProfScope ps(s, kProfLseMerge);
   if (blk_is_bf16)
     hipLaunchKernelGGL(lse_merge_kernel<true>, dim3(grid), dim3(kThreads), 0, s, acc, lse_acc, blk,
                        lse_blk, int(S), int(H), int(D / 4), nvec);

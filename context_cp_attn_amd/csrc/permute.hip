@@ -10,6 +10,7 @@
 // 2P-1-r); a run is one chunk of S/(2P) token rows.
 #include "common.h"
 #include "launch.h"
+#include "prof.h"
 
 namespace cp {
 namespace {
@@ -161,6 +162,7 @@ hipError_t ulysses_vb(const void* in, void* out, int P, int B, int Sp, int64_t r
                       bool inverse, hipStream_t s) {
   using V = typename Vec<VB>::T;
   const int R = int(run_bytes / VB);
+  ProfScope ps(s, inverse ? kProfUlyssesInv : kProfUlysses);
   if (!inverse) {
     const int64_t spans = int64_t(P) * B * P;
     const int bps = blocks_for(spans, int64_t(Sp) * R);
@@ -182,6 +184,7 @@ hipError_t zigzag_vb(const void* in, void* out, int B, int P, int64_t chunk_byte
   const int64_t cv = chunk_bytes / VB;
   const int64_t spans = int64_t(B) * 2 * P;
   const int bps = blocks_for(spans, cv);
+  ProfScope ps(s, kProfZigzag);
   hipLaunchKernelGGL(zigzag_kernel<V>, dim3(unsigned(spans * bps)), dim3(kThreads), 0, s,
                      static_cast<const V*>(in), static_cast<V*>(out), P, cv, inverse ? 1 : 0, bps);
   return hipGetLastError();

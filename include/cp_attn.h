@@ -1,9 +1,10 @@
 /*
  * cp_attn.h — C ABI of the context-parallel attention hot path on one MI355X (gfx950).
  *
- * Every entry point is asynchronous on the caller's HIP stream, allocates no device
- * memory, never synchronizes, and keeps no global state other than a thread-local
- * message describing the last failure.  All tensors are caller-owned, contiguous,
+ * Every compute entry point is asynchronous on the caller's HIP stream, allocates no
+ * device memory, never synchronizes, and keeps no global state other than a
+ * thread-local message describing the last failure (and the optional tracing
+ * events of cp_prof_*).  All tensors are caller-owned, contiguous,
  * row-major device buffers; pointers must stay valid until the stream work ends.
  * Failures are reported by status code (never by abort); cp_last_error() gives the
  * detail.  Validation happens on the host before any launch, so an invalid call
@@ -58,7 +59,7 @@ typedef struct {
   int64_t seqlen_k;        /* Sk >= 1                                                    */
   int64_t heads_q;         /* Hq >= 1, a multiple of heads_kv                            */
   int64_t heads_kv;        /* Hkv >= 1; query head h uses kv head h / (Hq / Hkv)          */
-  int64_t head_dim;        /* D: bf16 in {32, 64, 128}; f32 in {16, 32, 64, 128}          */
+  int64_t head_dim;        /* D: bf16 in {32, 64, 128}; f32 in [1, 128]                  */
   int32_t dtype;           /* cp_dtype_t of q, k, v, out, dout                           */
   int32_t causal;          /* 0 or 1                                                     */
   int64_t q_offset;        /* global position of query 0 when q_pos is NULL              */
@@ -143,6 +144,22 @@ cp_status_t cp_ulysses_relayout_inv(const void* in, void* out, int64_t P, int64_
 cp_status_t cp_zigzag_reorder(const void* in, void* out, int64_t batch, int64_t seqlen,
                               int64_t row_bytes, int64_t P, int32_t strategy, int32_t inverse,
                               hipStream_t stream);
+
+/*
+ * Kernel tracing with HIP events (a measurement aid, off by default).  While
+ * enabled, every kernel launch of the library is bracketed by two events recorded
+ * on its stream; the events are created by the library on first use and reused.
+ * cp_prof_read() waits for all events recorded so far, folds them into per-kernel
+ * totals and returns the total milliseconds and launch count of one kernel id in
+ * [0, cp_prof_kernel_count()) (CP_ERR_INVALID for another id or NULL outputs,
+ * CP_ERR_HIP if an event query fails).  cp_prof_reset() waits for and discards
+ * everything recorded.  Not for concurrent use from several host threads.
+ */
+void        cp_prof_enable(int32_t on);
+void        cp_prof_reset(void);
+int32_t     cp_prof_kernel_count(void);
+const char* cp_prof_kernel_name(int32_t kernel);   /* "" for an unknown id */
+cp_status_t cp_prof_read(int32_t kernel, double* total_ms, int64_t* launches);
 
 /* Static name of a status code. */
 const char* cp_status_string(cp_status_t status);

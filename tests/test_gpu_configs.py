@@ -1,0 +1,269 @@
+"""Parity of the five workloads, end to end through the drivers (GPU only).
+
+Toy: every output element against the oracle.  Full-size workloads run in the
+launch configuration bench.py times; outputs the oracle can compute one by one
+(sampled query rows, the keys at the end of the sequence) are compared element
+by element, the rest through exact properties that hold at any size.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import cp_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cp():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import context_cp_attn_amd as cp
+    cp.load_library()
+    return cp
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def bits(t):
+    t = t.detach().cpu().contiguous()
+    return t.view(torch.int16).numpy() if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def bf16_bits_to_f64(b):
+    return (b.astype(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f64(t):
+    return t.detach().cpu().double().numpy()
+
+
+def max_err(a, b):
+    return float(np.abs(a - b).max())
+
+
+def check_rows(out, lse, ref_o, ref_l, tol_o, tol_l):
+    assert np.array_equal(np.isneginf(lse), np.isneginf(ref_l))
+    fin = np.isfinite(ref_l)
+    assert max_err(lse[fin], ref_l[fin]) <= tol_l
+    assert max_err(out, ref_o) <= tol_o
+
+
+# ------------------------------------------------------------------ toy (fp32)
+
+def test_toy_full_ring_ulysses_reorder(cp):
+    say("toy: full attention, ring (contiguous, zigzag), Ulysses, reorder")
+    q, k, v = cp_inputs.toy_qkv()
+    P, S = 4, 32
+    ref_o, ref_l = oracle.attn_fwd(q, k, v)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o, l = cp.attn_fwd(qd, kd, vd)
+    check_rows(f64(o), f64(l), ref_o, ref_l, 1e-5, 1e-5)
+    # ring, both partitions
+    for layout in ("contiguous", "zigzag"):
+        src = [cp.zigzag_reorder(t, P) for t in (qd, kd, vd)] if layout == "zigzag" else [qd, kd, vd]
+        for r in range(P):
+            acc, lse = cp.drivers.RingShare(*src, P, r, layout).forward()
+            pos = oracle.rank_positions(r, P, S, layout)
+            check_rows(f64(acc), f64(lse), ref_o[:, pos], ref_l[:, :, pos], 1e-5, 1e-5)
+    # Ulysses: 2 heads per rank
+    stack = [t.reshape(P, 1, S // P, 8, 16).cuda() for t in (q, k, v)]
+    out_stack, lses, (ql, kl, vl, _) = cp.drivers.ulysses_forward(*stack, P)
+    np.testing.assert_array_equal(bits(ql), oracle.ulysses_relayout(bits(stack[0])))
+    assert tuple(ql.shape[2:]) == (32, 2, 16)
+    assert max_err(f64(out_stack).reshape(1, S, 8, 16), ref_o) <= 1e-5
+    assert max_err(np.concatenate([f64(x) for x in lses], axis=1), ref_l) <= 1e-5
+    # reorder into 2P = 8 chunks
+    y = cp.zigzag_reorder(qd, P)
+    np.testing.assert_array_equal(bits(y), oracle.reorder(bits(q), P))
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+def test_toy_ring_backward(cp, layout):
+    say(f"toy ring backward {layout}")
+    q, k, v = cp_inputs.toy_qkv()
+    (do,) = cp_inputs.normal_tensors([(1, 32, 8, 16)], seed=9, scale=1.0, dtype=torch.float32)
+    P, S = 4, 32
+    ref_o, ref_l = oracle.attn_fwd(q, k, v)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, ref_o, ref_l, do)
+    dev = [t.cuda() for t in (q, k, v, do)]
+    if layout == "zigzag":
+        dev = [cp.zigzag_reorder(t, P) for t in dev]
+    qd, kd, vd, dd = dev
+    dk, dv = torch.zeros_like(kd), torch.zeros_like(vd)
+    dq = torch.zeros_like(qd)
+    C = S // P
+    for r in range(P):
+        sh = cp.drivers.RingShare(qd, kd, vd, P, r, layout)
+        o, l = sh.forward()
+        sh.backward(o, l, dd[:, r * C:(r + 1) * C], dq[:, r * C:(r + 1) * C], dk, dv)
+    if layout == "zigzag":
+        dq, dk, dv = (cp.zigzag_reorder(t, P, inverse=True) for t in (dq, dk, dv))
+    for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+        assert max_err(f64(got), ref) <= 1e-5 * max(1.0, np.abs(ref).max())
+
+
+# ------------------------------------------------------------------ Ulysses llama2-7b, 32K, cp=16
+
+def test_ulysses_llama2_7b_32k(cp):
+    P, S, H, D = 16, 32768, 32, 128
+    say("ulysses llama2-7b: inputs")
+    q, k, v, do = cp_inputs.normal_tensors([(1, S, H, D)] * 4, seed=0)
+    stack = [t.reshape(P, 1, S // P, H, D) for t in (q, k, v, do)]
+    dev = [t.cuda() for t in stack]
+    say("ulysses llama2-7b: relayout bit-exact")
+    ql = cp.ulysses_relayout(dev[0], P)
+    ref_ql = oracle.ulysses_relayout(bits(stack[0]))
+    np.testing.assert_array_equal(bits(ql), ref_ql)
+    back = cp.ulysses_relayout_inv(ql, P)
+    assert torch.equal(back, dev[0])
+    kl, vl, gl = (cp.ulysses_relayout(t, P) for t in dev[1:])
+    # rank 0's share in the launch shape the benchmark uses
+    o, l = cp.attn_fwd(ql[0], kl[0], vl[0])
+    dq, dk, dv = cp.attn_bwd(ql[0], kl[0], vl[0], o, l, gl[0])
+    torch.cuda.synchronize()
+    say("ulysses llama2-7b: oracle on sampled rows")
+    # the oracle's own rank-0 share (relayout of the input bits)
+    share = [bf16_bits_to_f64(oracle.ulysses_relayout(bits(t))[0]) for t in stack[1:3]]
+    qs = bf16_bits_to_f64(ref_ql[0])
+    gs = bf16_bits_to_f64(oracle.ulysses_relayout(bits(stack[3]))[0])
+    ks, vs = share
+    rows = np.unique(np.r_[0, 1, 127, 128, 129, 4095, 4096, 20000, S - 129, S - 128, np.arange(S - 64, S)])
+    ro, rl = oracle.attn_fwd(qs[:, rows], ks, vs, q_pos=rows)
+    check_rows(f64(o)[:, rows], f64(l)[:, :, rows], ro, rl, 1e-2, 1e-3)
+    rq, _, _ = oracle.attn_bwd(qs[:, rows], ks, vs, ro, rl, gs[:, rows], q_pos=rows)
+    assert max_err(f64(dq)[:, rows], rq) <= 1e-2 * max(1.0, np.abs(rq).max())
+    # keys at the end are seen only by the last queries: exact dk/dv there
+    tail = np.arange(S - 256, S)
+    to, tl = oracle.attn_fwd(qs[:, tail], ks, vs, q_pos=tail)
+    _, tk, tv = oracle.attn_bwd(qs[:, tail], ks, vs, to, tl, gs[:, tail], q_pos=tail)
+    assert max_err(f64(dk)[:, tail], tk[:, tail]) <= 1e-2 * max(1.0, np.abs(tk[:, tail]).max())
+    assert max_err(f64(dv)[:, tail], tv[:, tail]) <= 1e-2 * max(1.0, np.abs(tv[:, tail]).max())
+    # every row's P sums to one: sum_j dV_j = sum_i dO_i
+    sdv = f64(dv).sum(axis=1)
+    sdo = gs.sum(axis=1)
+    assert max_err(sdv, sdo) <= 1e-2 * max(1.0, np.abs(sdo).max())
+
+
+# ------------------------------------------------------------------ ring llama2-7b, 32K, cp=16
+
+def test_ring_llama2_7b_32k_zigzag(cp):
+    P, S, H, D = 16, 32768, 32, 128
+    say("ring llama2-7b: inputs + zigzag reorder")
+    q, k, v = cp_inputs.normal_tensors([(1, S, H, D)] * 3, seed=0)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    qz = cp.zigzag_reorder(qd, P)
+    np.testing.assert_array_equal(bits(qz), oracle.reorder(bits(q), P))
+    kz, vz = cp.zigzag_reorder(kd, P), cp.zigzag_reorder(vd, P)
+    qf, kf, vf = (f64(t) for t in (q, k, v))
+    for r in (0, 7, 15):
+        say(f"ring llama2-7b: rank {r}")
+        acc, lse = cp.drivers.RingShare(qz, kz, vz, P, r).forward()
+        pos = oracle.rank_positions(r, P, S, "zigzag")
+        pick = np.r_[0, 1, 511, 1023, 1024, 1025, 1500, 2047]
+        ro, rl = oracle.attn_fwd(qf[:, pos[pick]], kf, vf, q_pos=pos[pick])
+        check_rows(f64(acc)[:, pick], f64(lse)[:, :, pick], ro, rl, 1e-2, 1e-3)
+
+
+# ------------------------------------------------------------------ Ulysses llama3.1-8b GQA, 64K, cp=4
+
+def test_ulysses_llama31_8b_64k_gqa(cp):
+    P, S, Hq, Hkv, D = 4, 65536, 32, 8, 128
+    say("ulysses llama3.1-8b: inputs")
+    q, k, v, do = cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D), (1, S, Hq, D)], seed=0)
+    say("ulysses llama3.1-8b: relayout")
+    ql = cp.ulysses_relayout(q.reshape(P, 1, S // P, Hq, D).cuda(), P)[0]   # 8 q heads
+    kl = cp.ulysses_relayout(k.reshape(P, 1, S // P, Hkv, D).cuda(), P)[0]  # 2 kv heads
+    vl = cp.ulysses_relayout(v.reshape(P, 1, S // P, Hkv, D).cuda(), P)[0]
+    gl = cp.ulysses_relayout(do.reshape(P, 1, S // P, Hq, D).cuda(), P)[0]
+    assert ql.shape == (1, S, 8, D) and kl.shape == (1, S, 2, D)
+    o, l = cp.attn_fwd(ql, kl, vl)
+    dq, dk, dv = cp.attn_bwd(ql, kl, vl, o, l, gl)
+    torch.cuda.synchronize()
+    say("ulysses llama3.1-8b: oracle on sampled rows")
+    qs, gs = f64(q[:, :, 0:8]), f64(do[:, :, 0:8])      # rank 0 = heads [0, 8) and kv heads [0, 2)
+    ks, vs = f64(k[:, :, 0:2]), f64(v[:, :, 0:2])
+    np.testing.assert_array_equal(bits(ql), bits(q[:, :, 0:8].contiguous()))
+    rows = np.r_[0, 63, 64, 65, 32767, 40000, np.arange(S - 32, S)]
+    ro, rl = oracle.attn_fwd(qs[:, rows], ks, vs, q_pos=rows)
+    check_rows(f64(o)[:, rows], f64(l)[:, :, rows], ro, rl, 1e-2, 1e-3)
+    rq, _, _ = oracle.attn_bwd(qs[:, rows], ks, vs, ro, rl, gs[:, rows], q_pos=rows)
+    assert max_err(f64(dq)[:, rows], rq) <= 1e-2 * max(1.0, np.abs(rq).max())
+    tail = np.arange(S - 128, S)
+    to, tl = oracle.attn_fwd(qs[:, tail], ks, vs, q_pos=tail)
+    _, tk, tv = oracle.attn_bwd(qs[:, tail], ks, vs, to, tl, gs[:, tail], q_pos=tail)
+    assert max_err(f64(dk)[:, tail], tk[:, tail]) <= 1e-2 * max(1.0, np.abs(tk[:, tail]).max())
+    assert max_err(f64(dv)[:, tail], tv[:, tail]) <= 1e-2 * max(1.0, np.abs(tv[:, tail]).max())
+    # group sums: sum_j dV[j, g] = sum over the group's 4 heads of sum_i dO
+    sdo = gs.reshape(1, S, 2, 4, D).sum(axis=(1, 3))
+    assert max_err(f64(dv).sum(axis=1), sdo) <= 1e-2 * max(1.0, np.abs(sdo).max())
+    say("ulysses llama3.1-8b: dual-chunk-swap reorder of 64K tokens")
+    ids = torch.arange(S, dtype=torch.int32)[None].cuda()
+    z = cp.zigzag_reorder(ids, P)
+    np.testing.assert_array_equal(bits(z), oracle.reorder(bits(ids), P))
+    x = torch.randn(1, S, 4096).bfloat16().cuda()
+    y = cp.zigzag_reorder(x, P)
+    np.testing.assert_array_equal(bits(y[:, :, :64]), oracle.reorder(bits(x[:, :, :64]), P))
+    assert torch.equal(cp.zigzag_reorder(y, P, inverse=True), x)
+
+
+# ------------------------------------------------------------------ packed + windowed ring, 8K, cp=4
+
+def _packed_ring(cp, S, Hq, Hkv, D, P, W, lens):
+    q, k, v, do = cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D), (1, S, Hq, D)], seed=0)
+    seg = cp_inputs.segment_ids(lens)
+    dev = [cp.zigzag_reorder(t.cuda(), P) for t in (q, k, v, do, seg)]
+    qz, kz, vz, dz, sz = dev
+    C = S // P
+    outs, lses = [], []
+    dq = torch.zeros(qz.shape, device="cuda")
+    dk, dv = torch.zeros(kz.shape, device="cuda"), torch.zeros(vz.shape, device="cuda")
+    for r in range(P):
+        sh = cp.drivers.RingShare(qz, kz, vz, P, r, seg=sz, window=W)
+        o, l = sh.forward()
+        outs.append(o)
+        lses.append(l)
+        sh.backward(o.bfloat16(), l, dz[:, r * C:(r + 1) * C], dq[:, r * C:(r + 1) * C], dk, dv)
+    grads = [cp.zigzag_reorder(t, P, inverse=True) for t in (dq, dk, dv)]
+    return (q, k, v, do, seg), outs, lses, grads
+
+
+def test_packed_window_small_all_elements(cp):
+    S, Hq, Hkv, D, P, W = 2048, 4, 2, 128, 4, 512
+    lens = cp_inputs.doc_lengths(S, 64, 1024, seed=1)
+    say(f"packed+window small: docs {lens}")
+    (q, k, v, do, seg), outs, lses, grads = _packed_ring(cp, S, Hq, Hkv, D, P, W, lens)
+    m = dict(q_seg=seg, k_seg=seg, window=W)
+    ro, rl = oracle.attn_fwd(q, k, v, **m)
+    for r in range(P):
+        pos = oracle.rank_positions(r, P, S, "zigzag")
+        check_rows(f64(outs[r]), f64(lses[r]), ro[:, pos], rl[:, :, pos], 1e-2, 1e-3)
+    refs = oracle.attn_bwd(q, k, v, ro, rl, do, **m)
+    for got, ref in zip(grads, refs):
+        assert max_err(f64(got), ref) <= 1e-2 * max(1.0, np.abs(ref).max())
+
+
+def test_packed_window_8k(cp):
+    S, Hq, Hkv, D, P, W = 8192, 32, 8, 128, 4, 4096
+    lens = cp_inputs.doc_lengths(S)
+    say(f"packed+window 8K: docs {lens}")
+    (q, k, v, do, seg), outs, lses, grads = _packed_ring(cp, S, Hq, Hkv, D, P, W, lens)
+    m = dict(window=W)
+    segn = seg.numpy()[0]
+    for r in range(P):
+        pos = oracle.rank_positions(r, P, S, "zigzag")
+        pick = np.r_[0, 1, 100, 1023, 1024, 1025, 2047]
+        qr = f64(q)[:, pos[pick]]
+        ro, rl = oracle.attn_fwd(qr, k, v, q_pos=pos[pick], q_seg=segn[pos[pick]][None], k_seg=segn[None], **m)
+        check_rows(f64(outs[r])[:, pick], f64(lses[r])[:, :, pick], ro, rl, 1e-2, 1e-3)
+    # per document and kv head: sum of dV over the document's keys = sum of dO over its queries
+    dv = f64(grads[2])
+    gs = f64(do).reshape(1, S, Hkv, Hq // Hkv, D).sum(axis=3)
+    s0 = 0
+    for n in lens:
+        ref = gs[:, s0:s0 + n].sum(axis=1)
+        assert max_err(dv[:, s0:s0 + n].sum(axis=1), ref) <= 1e-2 * max(1.0, np.abs(ref).max())
+        s0 += n
