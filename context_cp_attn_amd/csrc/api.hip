@@ -71,6 +71,13 @@ cp_status_t check_attn(const cp_attn_args_t* a, const void* q, const void* k, co
     return fail(CP_ERR_INVALID, "softmax_scale must be finite and >= 0 (0 selects 1/sqrt(D))");
   if (a->seqlen_q > INT_MAX || a->seqlen_k > INT_MAX || a->batch > 65535 || a->heads_q > 65535)
     return fail(CP_ERR_UNSUPPORTED, "sizes beyond the launch grid (batch, heads_q <= 65535; seqlen < 2^31)");
+  {
+    // the matrix-core kernels address one batch plane of a tensor with 32-bit offsets
+    const int64_t eb = a->dtype == CP_DTYPE_BF16 ? 2 : 4;
+    if (a->seqlen_q * a->heads_q * a->head_dim * eb >= (int64_t(1) << 31) ||
+        a->seqlen_k * a->heads_kv * a->head_dim * eb >= (int64_t(1) << 31))
+      return fail(CP_ERR_UNSUPPORTED, "one batch of q or k/v exceeds 2^31 bytes");
+  }
   if (!a->q_pos && (a->q_offset < 0 || a->q_offset + a->seqlen_q > INT_MAX))
     return fail(CP_ERR_INVALID, "q_offset %lld: positions must lie in [0, 2^31)", (long long)a->q_offset);
   if (!a->k_pos && (a->k_offset < 0 || a->k_offset + a->seqlen_k > INT_MAX))

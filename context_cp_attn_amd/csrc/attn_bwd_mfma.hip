@@ -162,11 +162,14 @@ CP_DEVICE void dkdv_body(const AttnProblem& p, const uint16_t* __restrict__ q, c
     return t;
   };
   typename C::Tile tq, tg;
+  const uint32_t qrs_bytes = uint32_t(qrs) * 2u;
+  tq.init(qrs_bytes);
+  tg.init(qrs_bytes);
   auto load = [&](int t) {
     const int h = g * G + t / n_it;
     const int i0 = (t % n_it) * C::BM;
-    tq.load(q + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs, i0, p.Sq);
-    tg.load(dout + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs, i0, p.Sq);
+    tq.load(q + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq);
+    tg.load(dout + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq);
   };
   auto store = [&](int t, uint8_t* base) {
     DkvStage<C> st(base);
@@ -238,8 +241,9 @@ CP_DEVICE void dkdv_body(const AttnProblem& p, const uint16_t* __restrict__ q, c
             const int col = (qb * 2 + tt) * 16 + hi * 8;
 #pragma unroll
             for (int d = 0; d < C::DB; ++d) {
-              dv_acc[d] = mma(ld8(st.gt + (d * 32 + l32) * C::TLD + col), pb, dv_acc[d]);
-              dk_acc[d] = mma(ld8(st.qt + (d * 32 + l32) * C::TLD + col), sb, dk_acc[d]);
+              const int off = (d * 32 + l32) * C::TLD + tcol<C::BM>(d * 32 + l32, col);
+              dv_acc[d] = mma(ld8(st.gt + off), pb, dv_acc[d]);
+              dk_acc[d] = mma(ld8(st.qt + off), sb, dk_acc[d]);
             }
           }
         }
@@ -355,6 +359,9 @@ CP_DEVICE void dq_body(const AttnProblem& p, const uint16_t* __restrict__ q, con
     return kt;
   };
   typename C::Tile tk, tv;
+  const uint32_t krs_bytes = uint32_t(krs) * 2u;
+  tk.init(krs_bytes);
+  tv.init(krs_bytes);
   auto stage_ptrs = [&](uint8_t* base, uint16_t*& ks, uint16_t*& kts, uint16_t*& vs, int*& kp, int*& kg) {
     ks = reinterpret_cast<uint16_t*>(base);
     kts = ks + C::kRowElems;
@@ -380,8 +387,8 @@ CP_DEVICE void dq_body(const AttnProblem& p, const uint16_t* __restrict__ q, con
 
   int cur = next_tile(0);
   if (cur < n_kt) {
-    tk.load(kbase, krs, cur * C::BN, p.Sk);
-    tv.load(vbase, krs, cur * C::BN, p.Sk);
+    tk.load(kbase, krs_bytes, cur * C::BN, p.Sk);
+    tv.load(vbase, krs_bytes, cur * C::BN, p.Sk);
     store(cur, smem);
     __syncthreads();
     int buf = 0;
@@ -390,8 +397,8 @@ CP_DEVICE void dq_body(const AttnProblem& p, const uint16_t* __restrict__ q, con
       const int nxt = next_tile(cur + 1);
       const bool has_next = nxt < n_kt;
       if (has_next) {
-        tk.load(kbase, krs, nxt * C::BN, p.Sk);
-        tv.load(vbase, krs, nxt * C::BN, p.Sk);
+        tk.load(kbase, krs_bytes, nxt * C::BN, p.Sk);
+        tv.load(vbase, krs_bytes, nxt * C::BN, p.Sk);
       }
       const int wcls = wave_live ? tile_class(cur, wv_q) : kEmpty;
       if (wcls != kEmpty) {
@@ -437,7 +444,8 @@ CP_DEVICE void dq_body(const AttnProblem& p, const uint16_t* __restrict__ q, con
           const bf16x8 sb = to_bf16x8(dp[t >> 1], 8 * (t & 1));
 #pragma unroll
           for (int d = 0; d < C::DB; ++d)
-            dq_acc[d] = mma(ld8(kts + (d * 32 + l32) * C::TLD + t * 16 + hi * 8), sb, dq_acc[d]);
+            dq_acc[d] = mma(ld8(kts + (d * 32 + l32) * C::TLD + tcol<C::BN>(d * 32 + l32, t * 16 + hi * 8)), sb,
+                            dq_acc[d]);
         }
       }
       if (has_next) store(nxt, smem + (buf ^ 1) * C::kStageBytes);
