@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-legs", action="store_true", help="skip the ring / reorder / packed legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--profile-copy", action="store_true",
+                    help="after the timed steps, run one plain 1 GiB device copy (read 1 GiB + write 1 GiB) "
+                         "that calibrates the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -210,7 +213,7 @@ def cpu_baseline(torch, cp_inputs, budget_s):
 
 def traffic_from_profiles(kernel_sha):
     """HBM bytes per launch from committed rocprofv3 counters, if they match the source."""
-    p = os.path.join(ROOT, "profiles", "attn_bwd_mfma_counters.json")
+    p = os.path.join(ROOT, "profiles", "attn_bwd_mfma_ulysses_llama2_7b_32k_counters.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
@@ -252,7 +255,8 @@ def main():
     fwd_ms = tr.results["attn_fwd_mfma"][0] / tr.results["attn_fwd_mfma"][1]
     rel_t = sum(tr.results[k_][0] for k_ in ("ulysses_relayout", "ulysses_relayout_inv")) / a.steps
     src = os.path.join(ROOT, "context_cp_attn_amd", "csrc")
-    bwd_sha = sha_of(os.path.join(src, "attn_bwd_mfma.hip"), os.path.join(src, "mfma_common.h"))
+    bwd_sha = sha_of(os.path.join(src, "attn_bwd_mfma.hip"), os.path.join(src, "mfma_common.h"),
+                     os.path.join(ROOT, "context_cp_attn_amd", "build.py"))
     if dom == "attn_bwd_mfma":
         ach = step.flops_bwd_rank / (bwd_ms * 1e-3) / 1e12
         roof = {"kernel": "attn_bwd_mfma", "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
@@ -282,6 +286,13 @@ def main():
         "roofline": roof,
         "kernels": kern,
     }
+    if a.profile_copy:
+        src_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst_buf = torch.empty_like(src_buf)
+        torch.cuda.synchronize()
+        dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
     if not a.no_legs:
         res["legs"] = legs(torch, cp, cp_inputs)
     res["cpu_baseline"] = None if a.no_cpu else cpu_baseline(torch, cp_inputs, a.cpu_seconds)

@@ -28,6 +28,9 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed float32 VALU ops are kept out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA sources/results in VGPRs: the backward's dK/dV accumulators otherwise
+    # bounce between AGPRs and VGPRs every iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", INCLUDE, "-I", CSRC,
 ]

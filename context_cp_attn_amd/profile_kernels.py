@@ -1,0 +1,45 @@
+"""Run one attention kernel a few times on synthetic bf16 inputs, for profilers.
+
+    python -m context_cp_attn_amd.profile_kernels {fwd|bwd} [S,Hq,Hkv,D] [--iters N]
+
+Intended under ``rocprofv3 --pmc ...`` or ``--kernel-trace``: the inputs are made
+on the device, the chosen kernel runs ``iters`` times (default 2), and nothing
+else of the library is launched in between.
+"""
+
+from __future__ import annotations
+
+import argparse
+
+import torch
+
+from . import ops
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("which", choices=["fwd", "bwd"])
+    ap.add_argument("shape", nargs="?", default="65536,8,2,128", help="S,Hq,Hkv,D (causal, batch 1)")
+    ap.add_argument("--iters", type=int, default=2)
+    a = ap.parse_args()
+    S, Hq, Hkv, D = (int(x) for x in a.shape.split(","))
+    g = torch.Generator(device="cuda").manual_seed(0)
+    q = torch.randn(1, S, Hq, D, device="cuda", generator=g).mul_(0.5).bfloat16()
+    k = torch.randn(1, S, Hkv, D, device="cuda", generator=g).mul_(0.5).bfloat16()
+    v = torch.randn(1, S, Hkv, D, device="cuda", generator=g).mul_(0.5).bfloat16()
+    out, lse = ops.attn_fwd(q, k, v)
+    if a.which == "bwd":
+        do = torch.randn(q.shape, device="cuda", generator=g).mul_(0.5).bfloat16()
+        ws = ops.bwd_workspace(q, k)
+        grads = [torch.empty(t.shape, device="cuda") for t in (q, k, v)]
+    for i in range(a.iters):
+        if a.which == "fwd":
+            ops.attn_fwd(q, k, v, out=out, lse=lse)
+        else:
+            ops.attn_bwd(q, k, v, out, lse, do, dq=grads[0], dk=grads[1], dv=grads[2], workspace=ws)
+        torch.cuda.synchronize()
+        print(f"{a.which} {S},{Hq},{Hkv},{D} iteration {i} done", flush=True)
+
+
+if __name__ == "__main__":
+    main()
