@@ -8,16 +8,21 @@
 // Attention itself: handbook "Context parallelism: Ring Attention and Ulysses",
 // §"Which operations partition directly"; its gradient is the textbook one.
 //
-// Two launches (the second holds both the dK/dV and the dQ roles):
+// Two launches:
 //  1. delta: Delta = rowsum(dO * O) into the caller's workspace [B,Hq,Sq].
-//  2a. dK/dV role: a workgroup owns 32*NW keys of one kv head (one wavefront per
-//     32 keys, K and V held as B fragments in registers) and streams query tiles
-//     of every query head of the group through LDS.  S = Q K^T and dP = dO V^T are
-//     computed query-major so that P and dS land directly as B fragments of
-//     dV^T += dO^T P and dK^T += Q^T dS (Q and dO are staged both row-major and
-//     transposed).
-//  2b. dQ role: a workgroup owns 32*NW queries of one head and streams key tiles:
-//     S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
+//  2. one grid with three roles, each a workgroup of 8 wavefronts x 32 rows:
+//     dV role — owns 256 keys of a kv head (K as register B fragments) and streams
+//       query tiles of every head of the group: S = Q K^T, P, dV^T += dO^T P;
+//     dK role — same keys (K and V fragments): S, dP = dO V^T, dS, dK^T += Q^T dS;
+//     dQ role — owns 256 queries of a head (Q and dO fragments) and streams key
+//       tiles: S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
+//     Splitting dV from dK recomputes S once more (8 instead of 7 products per
+//     block pair) but keeps every role under 256 registers, so two wavefronts run
+//     per SIMD and one's matrix products overlap the other's elementwise work.
+//     S and dP are computed query-major in the dV/dK roles so P and dS are directly
+//     the B operands of the next products; the tiles used as A operands in both
+//     orientations are staged in LDS row-major and transposed (XOR-swizzled).
+//     The role lists, each heaviest first, are interleaved in one grid.
 // Tiles are skipped / masked exactly as in the forward (empty / partial / full).
 #include "mfma_common.h"
 #include "prof.h"
@@ -62,92 +67,103 @@ __global__ __launch_bounds__(256) void delta_kernel(int64_t rows, int Sq, int Hq
 // exp2(s*c - lse2) of it is exactly 0.
 CP_DEVICE float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
 
-// ---- 2. dK / dV ----------------------------------------------------------------
-template <int D_, int NW_, int BM_>
-struct DkvCfg {
-  static constexpr int D = D_, NW = NW_, BM = BM_;
+// ---- 2. configuration and LDS stages ---------------------------------------------
+template <int D_>
+struct BwdCfg {
+  static constexpr int D = D_;
+  static constexpr int NW = 8;
   static constexpr int kThreads = 64 * NW;
-  static constexpr int kKeys = 32 * NW;
+  static constexpr int kRows = 32 * NW;  // keys (dV/dK roles) or queries (dQ role) per workgroup
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
+  static constexpr int BM = 64;          // query tile of the dV/dK roles
   static constexpr int QBLK = BM / 32;
-  static constexpr int RLD = D + 8;   // row-major pitch (elements)
-  static constexpr int TLD = BM + 8;  // transposed pitch (elements)
-  static constexpr int kRowElems = BM * RLD;
-  static constexpr int kColElems = D * TLD;
-  // Q rows, Q^T, dO rows, dO^T, then lse2, delta, qpos, qseg
-  static constexpr int kStageBytes = 2 * (kRowElems + kColElems) * 2 + 4 * BM * 4;
-  static constexpr int kLdsBytes = 2 * kStageBytes;
-  using Tile = RowTile<BM, D, kThreads>;
+  static constexpr int BN = 64;          // key tile of the dQ role
+  static constexpr int KB = BN / 32;
+  static constexpr int RLD = D + 8;      // row-major pitch (elements)
+  static constexpr int TLDM = BM + 8;    // transposed pitch, query tiles
+  static constexpr int TLDN = BN + 8;    // transposed pitch, key tiles
+  static constexpr int kRowM = BM * RLD, kColM = D * TLDM;
+  static constexpr int kRowN = BN * RLD, kColN = D * TLDN;
+  // dV stage: Q rows, dO^T, lse2, qpos, qseg (the dK stage's delta slot unused)
+  // dK stage: Q rows, dO rows, Q^T, lse2, delta, qpos, qseg
+  static constexpr int kStageK = (2 * kRowM + kColM) * 2 + 4 * BM * 4;
+  // dQ stage: K rows, V rows, K^T, kpos, kseg
+  static constexpr int kStageQ = (2 * kRowN + kColN) * 2 + 2 * BN * 4;
+  static constexpr int kStageMax = kStageK > kStageQ ? kStageK : kStageQ;
+  static constexpr int kLdsBytes = 2 * kStageMax;
+  // 2-row units: every one of the 512 threads stages a share of each tile
+  using TileM = RowTile<BM, D, kThreads, false, 2>;
+  using TileN = RowTile<BN, D, kThreads, false, 2>;
 };
 
+// Pointers into one LDS stage of the dV / dK roles.
 template <class C>
-struct DkvStage {
-  uint16_t* q;
-  uint16_t* qt;
-  uint16_t* g;
-  uint16_t* gt;
+struct QStage {
+  uint16_t* q;     // Q rows   [BM][RLD]
+  uint16_t* g;     // dO rows  [BM][RLD]  (dK role)
+  uint16_t* t;     // dO^T (dV role) or Q^T (dK role) [D][TLDM]
   float* lse2;
-  float* delta;
+  float* delta;    // dK role
   int* qpos;
   int* qseg;
-  CP_DEVICE DkvStage(uint8_t* base) {
+  CP_DEVICE QStage(uint8_t* base, bool with_g) {
     q = reinterpret_cast<uint16_t*>(base);
-    qt = q + C::kRowElems;
-    g = qt + C::kColElems;
-    gt = g + C::kRowElems;
-    lse2 = reinterpret_cast<float*>(gt + C::kColElems);
+    g = q + C::kRowM;
+    t = with_g ? g + C::kRowM : g;
+    lse2 = reinterpret_cast<float*>(t + C::kColM);
     delta = lse2 + C::BM;
     qpos = reinterpret_cast<int*>(delta + C::BM);
     qseg = qpos + C::BM;
   }
 };
 
-template <class C>
-CP_DEVICE void dkdv_body(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                         const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-                         const float* __restrict__ lse, const float* __restrict__ delta,
-                         float* __restrict__ dk, float* __restrict__ dv, int accumulate, uint8_t* smem,
-                         int kt, int g, int b) {
+// Shared skeleton of the dV and dK roles: a workgroup owns keys [j0, j0 + kRows) of
+// kv head g; wavefront w owns keys j0 + 32w + (0..31), one per lane column.
+// kDK selects the dK role (else dV).
+template <class C, bool kDK>
+CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                        const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                        const float* __restrict__ lse, const float* __restrict__ delta,
+                        float* __restrict__ grad, int accumulate, uint8_t* smem, int kt, int g, int b) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int G = p.Hq / p.Hkv;
-  const int j0 = kt * C::kKeys;
+  const int j0 = kt * C::kRows;
   const int wj0 = j0 + wave * 32;
   const int64_t krs = int64_t(p.Hkv) * C::D;
   const int64_t qrs = int64_t(p.Hq) * C::D;
 
-  const Span wg_k = k_span(p, b, j0, min(j0 + C::kKeys, p.Sk) - 1);
+  const Span wg_k = k_span(p, b, j0, min(j0 + C::kRows, p.Sk) - 1);
   const bool wave_live = wj0 < p.Sk;
   const Span wv_k = k_span(p, b, min(wj0, p.Sk - 1), min(wj0 + 32, p.Sk) - 1);
 
-  // K and V rows of this lane's key as B fragments (k-slots = head dims)
+  // K (and V) rows of this lane's key as B fragments (k-slots = head dims)
   const int key = min(wj0 + l32, p.Sk - 1);
   const bool key_ok = wj0 + l32 < p.Sk;
-  bf16x8 kf[C::KS], vf[C::KS];
+  bf16x8 kf[C::KS], vf[kDK ? C::KS : 1];
   {
     const uint16_t* kr = k + (int64_t(b) * p.Sk + key) * krs + int64_t(g) * C::D;
     const uint16_t* vr = v + (int64_t(b) * p.Sk + key) * krs + int64_t(g) * C::D;
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
-      u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
-      if (key_ok) {
-        x = *reinterpret_cast<const u32x4*>(kr + s * 16 + hi * 8);
-        y = *reinterpret_cast<const u32x4*>(vr + s * 16 + hi * 8);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(kr + s * 16 + hi * 8);
+      kf[s] = __builtin_bit_cast(bf16x8, key_ok ? x : u32x4{0, 0, 0, 0});
+      if constexpr (kDK) {
+        const u32x4 y = *reinterpret_cast<const u32x4*>(vr + s * 16 + hi * 8);
+        vf[s] = __builtin_bit_cast(bf16x8, key_ok ? y : u32x4{0, 0, 0, 0});
       }
-      kf[s] = __builtin_bit_cast(bf16x8, x);
-      vf[s] = __builtin_bit_cast(bf16x8, y);
     }
   }
   const int my_kpos = kpos_at(p, key);
   const int my_kseg = kseg_at(p, b, key);
 
-  f32x16 dk_acc[C::DB], dv_acc[C::DB];
+  f32x16 acc[C::DB];
 #pragma unroll
-  for (int d = 0; d < C::DB; ++d) dk_acc[d] = dv_acc[d] = f32x16{};
+  for (int d = 0; d < C::DB; ++d) acc[d] = f32x16{};
 
   const float c2 = p.scale * kLog2e;
   const int n_it = (p.Sq + C::BM - 1) / C::BM;
@@ -161,7 +177,7 @@ CP_DEVICE void dkdv_body(const AttnProblem& p, const uint16_t* __restrict__ q, c
     while (t < n_t && tile_class(t, wg_k) == kEmpty) ++t;
     return t;
   };
-  typename C::Tile tq, tg;
+  typename C::TileM tq, tg;
   const uint32_t qrs_bytes = uint32_t(qrs) * 2u;
   tq.init(qrs_bytes);
   tg.init(qrs_bytes);
@@ -172,11 +188,14 @@ CP_DEVICE void dkdv_body(const AttnProblem& p, const uint16_t* __restrict__ q, c
     tg.load(dout + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq);
   };
   auto store = [&](int t, uint8_t* base) {
-    DkvStage<C> st(base);
+    QStage<C> st(base, kDK);
     tq.store_rows(st.q, C::RLD);
-    tq.store_cols(st.qt, C::TLD);
-    tg.store_rows(st.g, C::RLD);
-    tg.store_cols(st.gt, C::TLD);
+    if constexpr (kDK) {
+      tg.store_rows(st.g, C::RLD);
+      tq.store_cols(st.t, C::TLDM);
+    } else {
+      tg.store_cols(st.t, C::TLDM);
+    }
     const int h = g * G + t / n_it;
     const int i0 = (t % n_it) * C::BM;
     for (int r = tid; r < C::BM; r += C::kThreads) {
@@ -184,7 +203,7 @@ CP_DEVICE void dkdv_body(const AttnProblem& p, const uint16_t* __restrict__ q, c
       const bool ok = i < p.Sq;
       const int64_t li = (int64_t(b) * p.Hq + h) * p.Sq + i;
       st.lse2[r] = ok ? lse2_of(lse[li]) : INFINITY;
-      st.delta[r] = ok ? delta[li] : 0.0f;
+      if constexpr (kDK) st.delta[r] = ok ? delta[li] : 0.0f;
       st.qpos[r] = ok ? qpos_at(p, i) : 0;
       st.qseg[r] = ok ? qseg_at(p, b, i) : 0;
     }
@@ -203,22 +222,24 @@ CP_DEVICE void dkdv_body(const AttnProblem& p, const uint16_t* __restrict__ q, c
       if (has_next) load(nxt);
       const int wcls = wave_live ? tile_class(cur, wv_k) : kEmpty;
       if (wcls != kEmpty) {
-        DkvStage<C> st(smem + buf * C::kStageBytes);
+        QStage<C> st(smem + buf * C::kStageMax, kDK);
 #pragma unroll
         for (int qb = 0; qb < C::QBLK; ++qb) {
+          // S = Q K^T (and dP = dO V^T): lane column = this lane's key,
+          // register r = query row qb*32 + key_of_reg(r, hi)
           f32x16 s = f32x16{}, dp = f32x16{};
           const int arow = (qb * 32 + perm_row(l32)) * C::RLD + hi * 8;
 #pragma unroll
           for (int ks = 0; ks < C::KS; ++ks) {
             s = mma(ld8(st.q + arow + ks * 16), kf[ks], s);
-            dp = mma(ld8(st.g + arow + ks * 16), vf[ks], dp);
+            if constexpr (kDK) dp = mma(ld8(st.g + arow + ks * 16), vf[ks], dp);
           }
-          // register r holds query row qb*32 + key_of_reg(r, hi) of this lane's key
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int r0 = qb * 32 + key_of_reg(4 * jj, hi);
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(st.lse2 + r0);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(st.delta + r0);
+            f32x4 d4 = f32x4{0, 0, 0, 0};
+            if constexpr (kDK) d4 = *reinterpret_cast<const f32x4*>(st.delta + r0);
             i32x4 qp4 = i32x4{0, 0, 0, 0}, qs4 = i32x4{0, 0, 0, 0};
             if (wcls == kPartial) {
               qp4 = *reinterpret_cast<const i32x4*>(st.qpos + r0);
@@ -229,26 +250,24 @@ CP_DEVICE void dkdv_body(const AttnProblem& p, const uint16_t* __restrict__ q, c
               const int r = 4 * jj + i;
               float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[i]));
               if (wcls == kPartial && !pair_visible(ms, qp4[i], my_kpos, qs4[i], my_kseg)) pr = 0.0f;
-              s[r] = pr;
-              dp[r] = pr * (dp[r] - d4[i]);
+              if constexpr (kDK)
+                s[r] = pr * (dp[r] - d4[i]);  // dS
+              else
+                s[r] = pr;                    // P
             }
           }
-          // dV^T += dO^T P ; dK^T += Q^T dS over the block's two 16-query k-steps
+          // dV^T += dO^T P  or  dK^T += Q^T dS, over the block's two 16-query k-steps
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            const bf16x8 pb = to_bf16x8(s, 8 * tt);
-            const bf16x8 sb = to_bf16x8(dp, 8 * tt);
+            const bf16x8 bfrag = to_bf16x8(s, 8 * tt);
             const int col = (qb * 2 + tt) * 16 + hi * 8;
 #pragma unroll
-            for (int d = 0; d < C::DB; ++d) {
-              const int off = (d * 32 + l32) * C::TLD + tcol<C::BM>(d * 32 + l32, col);
-              dv_acc[d] = mma(ld8(st.gt + off), pb, dv_acc[d]);
-              dk_acc[d] = mma(ld8(st.qt + off), sb, dk_acc[d]);
-            }
+            for (int d = 0; d < C::DB; ++d)
+              acc[d] = mma(ld8(st.t + (d * 32 + l32) * C::TLDM + tcol<C::BM>(d * 32 + l32, col)), bfrag, acc[d]);
           }
         }
       }
-      if (has_next) store(nxt, smem + (buf ^ 1) * C::kStageBytes);
+      if (has_next) store(nxt, smem + (buf ^ 1) * C::kStageMax);
       __syncthreads();
       if (!has_next) break;
       cur = nxt;
@@ -258,50 +277,26 @@ CP_DEVICE void dkdv_body(const AttnProblem& p, const uint16_t* __restrict__ q, c
 
   // epilogue: lane holds key column l32, dims d*32 + 8j + 4*hi + (0..3)
   if (!key_ok) return;
-  float* dkr = dk + ((int64_t(b) * p.Sk + wj0 + l32) * p.Hkv + g) * C::D;
-  float* dvr = dv + ((int64_t(b) * p.Sk + wj0 + l32) * p.Hkv + g) * C::D;
+  const float sc = kDK ? p.scale : 1.0f;
+  float* gr = grad + ((int64_t(b) * p.Sk + wj0 + l32) * p.Hkv + g) * C::D;
 #pragma unroll
   for (int d = 0; d < C::DB; ++d)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int off = d * 32 + 8 * j + 4 * hi;
-      f32x4 a{dk_acc[d][4 * j] * p.scale, dk_acc[d][4 * j + 1] * p.scale, dk_acc[d][4 * j + 2] * p.scale,
-              dk_acc[d][4 * j + 3] * p.scale};
-      f32x4 c{dv_acc[d][4 * j], dv_acc[d][4 * j + 1], dv_acc[d][4 * j + 2], dv_acc[d][4 * j + 3]};
-      if (accumulate) {
-        a += *reinterpret_cast<const f32x4*>(dkr + off);
-        c += *reinterpret_cast<const f32x4*>(dvr + off);
-      }
-      *reinterpret_cast<f32x4*>(dkr + off) = a;
-      *reinterpret_cast<f32x4*>(dvr + off) = c;
+      f32x4 a{acc[d][4 * j] * sc, acc[d][4 * j + 1] * sc, acc[d][4 * j + 2] * sc, acc[d][4 * j + 3] * sc};
+      if (accumulate) a += *reinterpret_cast<const f32x4*>(gr + off);
+      *reinterpret_cast<f32x4*>(gr + off) = a;
     }
 }
 
-// ---- 3. dQ --------------------------------------------------------------------
-template <int D_, int NW_, int BN_>
-struct DqCfg {
-  static constexpr int D = D_, NW = NW_, BN = BN_;
-  static constexpr int kThreads = 64 * NW;
-  static constexpr int kRows = 32 * NW;
-  static constexpr int KS = D / 16;
-  static constexpr int KB = BN / 32;
-  static constexpr int DB = D / 32;
-  static constexpr int PT = BN / 16;
-  static constexpr int RLD = D + 8;
-  static constexpr int TLD = BN + 8;
-  static constexpr int kRowElems = BN * RLD;
-  static constexpr int kColElems = D * TLD;
-  // K rows, K^T, V rows, then kpos, kseg
-  static constexpr int kStageBytes = (2 * kRowElems + kColElems) * 2 + 2 * BN * 4;
-  static constexpr int kLdsBytes = 2 * kStageBytes;
-  using Tile = RowTile<BN, D, kThreads>;
-};
-
+// dQ role: a workgroup owns queries [q0, q0 + kRows) of head h; wavefront w owns
+// queries q0 + 32w + (0..31), one per lane column.
 template <class C>
-CP_DEVICE void dq_body(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                        const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-                       const float* __restrict__ lse, const float* __restrict__ delta,
-                       float* __restrict__ dq, int accumulate, uint8_t* smem, int qt, int h, int b) {
+                       const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dq,
+                       int accumulate, uint8_t* smem, int qt, int h, int b) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -325,13 +320,10 @@ CP_DEVICE void dq_body(const AttnProblem& p, const uint16_t* __restrict__ q, con
     const uint16_t* gr = dout + (int64_t(b) * p.Sq + row) * qrs + int64_t(h) * C::D;
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
-      u32x4 x = u32x4{0, 0, 0, 0}, y = u32x4{0, 0, 0, 0};
-      if (row_ok) {
-        x = *reinterpret_cast<const u32x4*>(qr + s * 16 + hi * 8);
-        y = *reinterpret_cast<const u32x4*>(gr + s * 16 + hi * 8);
-      }
-      qf[s] = __builtin_bit_cast(bf16x8, x);
-      gf[s] = __builtin_bit_cast(bf16x8, y);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(qr + s * 16 + hi * 8);
+      const u32x4 y = *reinterpret_cast<const u32x4*>(gr + s * 16 + hi * 8);
+      qf[s] = __builtin_bit_cast(bf16x8, row_ok ? x : u32x4{0, 0, 0, 0});
+      gf[s] = __builtin_bit_cast(bf16x8, row_ok ? y : u32x4{0, 0, 0, 0});
     }
   }
   const int64_t li = (int64_t(b) * p.Hq + h) * p.Sq + row;
@@ -340,9 +332,9 @@ CP_DEVICE void dq_body(const AttnProblem& p, const uint16_t* __restrict__ q, con
   const int my_qpos = qpos_at(p, row);
   const int my_qseg = qseg_at(p, b, row);
 
-  f32x16 dq_acc[C::DB];
+  f32x16 acc[C::DB];
 #pragma unroll
-  for (int d = 0; d < C::DB; ++d) dq_acc[d] = f32x16{};
+  for (int d = 0; d < C::DB; ++d) acc[d] = f32x16{};
 
   const float c2 = p.scale * kLog2e;
   const int n_kt = (p.Sk + C::BN - 1) / C::BN;
@@ -358,30 +350,26 @@ CP_DEVICE void dq_body(const AttnProblem& p, const uint16_t* __restrict__ q, con
     while (kt < n_kt && tile_class(kt, wg_q) == kEmpty) ++kt;
     return kt;
   };
-  typename C::Tile tk, tv;
+  typename C::TileN tk, tv;
   const uint32_t krs_bytes = uint32_t(krs) * 2u;
   tk.init(krs_bytes);
   tv.init(krs_bytes);
-  auto stage_ptrs = [&](uint8_t* base, uint16_t*& ks, uint16_t*& kts, uint16_t*& vs, int*& kp, int*& kg) {
-    ks = reinterpret_cast<uint16_t*>(base);
-    kts = ks + C::kRowElems;
-    vs = kts + C::kColElems;
-    kp = reinterpret_cast<int*>(vs + C::kRowElems);
-    kg = kp + C::BN;
-  };
+  // stage: K rows, V rows, K^T, kpos, kseg
+  auto ks_of = [&](uint8_t* base) { return reinterpret_cast<uint16_t*>(base); };
+  auto vs_of = [&](uint8_t* base) { return ks_of(base) + C::kRowN; };
+  auto kts_of = [&](uint8_t* base) { return vs_of(base) + C::kRowN; };
+  auto kp_of = [&](uint8_t* base) { return reinterpret_cast<int*>(kts_of(base) + C::kColN); };
   auto store = [&](int kt, uint8_t* base) {
-    uint16_t *ks, *kts, *vs;
-    int *kp, *kg;
-    stage_ptrs(base, ks, kts, vs, kp, kg);
-    tk.store_rows(ks, C::RLD);
-    tk.store_cols(kts, C::TLD);
-    tv.store_rows(vs, C::RLD);
+    tk.store_rows(ks_of(base), C::RLD);
+    tk.store_cols(kts_of(base), C::TLDN);
+    tv.store_rows(vs_of(base), C::RLD);
+    int* kp = kp_of(base);
+    int* kg = kp + C::BN;
     const int j0 = kt * C::BN;
     for (int t = tid; t < C::BN; t += C::kThreads) {
-      const int j = j0 + t;
-      const bool ok = j < p.Sk;
-      kp[t] = ok ? kpos_at(p, j) : 0;
-      kg[t] = ok ? kseg_at(p, b, j) : 0;
+      const int j = min(j0 + t, p.Sk - 1);
+      kp[t] = kpos_at(p, j);
+      kg[t] = kseg_at(p, b, j);
     }
   };
 
@@ -402,24 +390,23 @@ CP_DEVICE void dq_body(const AttnProblem& p, const uint16_t* __restrict__ q, con
       }
       const int wcls = wave_live ? tile_class(cur, wv_q) : kEmpty;
       if (wcls != kEmpty) {
-        uint16_t *ks, *kts, *vs;
-        int *kp, *kg;
-        stage_ptrs(smem + buf * C::kStageBytes, ks, kts, vs, kp, kg);
-        f32x16 s[C::KB], dp[C::KB];
+        uint8_t* base = smem + buf * C::kStageMax;
+        const uint16_t* ks = ks_of(base);
+        const uint16_t* vs = vs_of(base);
+        const uint16_t* kts = kts_of(base);
+        const int* kp = kp_of(base);
+        const int* kg = kp + C::BN;
+        const int nvalid = p.Sk - cur * C::BN;
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) {
-          s[kb] = f32x16{};
-          dp[kb] = f32x16{};
+          // S^T = K Q^T and dP^T = V dO^T for 32 keys: lane column = this lane's query
+          f32x16 s = f32x16{}, dp = f32x16{};
           const int arow = (kb * 32 + perm_row(l32)) * C::RLD + hi * 8;
 #pragma unroll
           for (int kk = 0; kk < C::KS; ++kk) {
-            s[kb] = mma(ld8(ks + arow + kk * 16), qf[kk], s[kb]);
-            dp[kb] = mma(ld8(vs + arow + kk * 16), gf[kk], dp[kb]);
+            s = mma(ld8(ks + arow + kk * 16), qf[kk], s);
+            dp = mma(ld8(vs + arow + kk * 16), gf[kk], dp);
           }
-        }
-        const int nvalid = p.Sk - cur * C::BN;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int kk0 = kb * 32 + key_of_reg(4 * jj, hi);
@@ -431,24 +418,25 @@ CP_DEVICE void dq_body(const AttnProblem& p, const uint16_t* __restrict__ q, con
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int r = 4 * jj + i;
-              float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -my_lse2));
+              float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -my_lse2));
               if (wcls == kPartial &&
                   !(kk0 + i < nvalid && pair_visible(ms, my_qpos, kp4[i], my_qseg, kg4[i])))
                 pr = 0.0f;
-              dp[kb][r] = pr * (dp[kb][r] - my_delta);
+              s[r] = pr * (dp[r] - my_delta);  // dS^T
             }
           }
-        // dQ^T += K^T dS^T
+          // dQ^T += K^T dS^T over the block's two 16-key k-steps
 #pragma unroll
-        for (int t = 0; t < C::PT; ++t) {
-          const bf16x8 sb = to_bf16x8(dp[t >> 1], 8 * (t & 1));
+          for (int tt = 0; tt < 2; ++tt) {
+            const bf16x8 sb = to_bf16x8(s, 8 * tt);
+            const int col = (kb * 2 + tt) * 16 + hi * 8;
 #pragma unroll
-          for (int d = 0; d < C::DB; ++d)
-            dq_acc[d] = mma(ld8(kts + (d * 32 + l32) * C::TLD + tcol<C::BN>(d * 32 + l32, t * 16 + hi * 8)), sb,
-                            dq_acc[d]);
+            for (int d = 0; d < C::DB; ++d)
+              acc[d] = mma(ld8(kts + (d * 32 + l32) * C::TLDN + tcol<C::BN>(d * 32 + l32, col)), sb, acc[d]);
+          }
         }
       }
-      if (has_next) store(nxt, smem + (buf ^ 1) * C::kStageBytes);
+      if (has_next) store(nxt, smem + (buf ^ 1) * C::kStageMax);
       __syncthreads();
       if (!has_next) break;
       cur = nxt;
@@ -463,18 +451,17 @@ CP_DEVICE void dq_body(const AttnProblem& p, const uint16_t* __restrict__ q, con
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int off = d * 32 + 8 * j + 4 * hi;
-      f32x4 a{dq_acc[d][4 * j] * p.scale, dq_acc[d][4 * j + 1] * p.scale, dq_acc[d][4 * j + 2] * p.scale,
-              dq_acc[d][4 * j + 3] * p.scale};
+      f32x4 a{acc[d][4 * j] * p.scale, acc[d][4 * j + 1] * p.scale, acc[d][4 * j + 2] * p.scale,
+              acc[d][4 * j + 3] * p.scale};
       if (accumulate) a += *reinterpret_cast<const f32x4*>(dqr + off);
       *reinterpret_cast<f32x4*>(dqr + off) = a;
     }
 }
 
-// ---- fused dK/dV + dQ launch --------------------------------------------------
-// One grid holds both roles.  Each role's list is ordered heaviest first (causal:
-// low key tiles for dK/dV, high query tiles for dQ, every head interleaved) and
-// the two lists are merged at the ratio of their lengths, so both kinds of work
-// start together and no second launch waits for a tail.
+// ---- fused launch ------------------------------------------------------------------
+// Key-side items (dK then dV of each key block, key blocks lowest first = heaviest
+// under a causal mask) and query-side items (query blocks highest first) are merged
+// at the ratio of their counts.
 struct BwdArgs {
   AttnProblem p;
   const uint16_t* q;
@@ -487,32 +474,36 @@ struct BwdArgs {
   float* dk;
   float* dv;
   int accumulate;
-  int n_kv;  // dK/dV workgroups = B * Hkv * key tiles
-  int n_q;   // dQ workgroups = B * Hq * query tiles
+  int n_kv;  // key-side items = 2 * B * Hkv * key blocks
+  int n_q;   // query-side items = B * Hq * query blocks
 };
 
-template <class KV, class Q>
-__global__ __launch_bounds__(KV::kThreads) void attn_bwd_kernel(BwdArgs a) {
-  static_assert(KV::kThreads == Q::kThreads, "roles share the block size");
-  constexpr int kLds = KV::kLdsBytes > Q::kLdsBytes ? KV::kLdsBytes : Q::kLdsBytes;
-  __shared__ __align__(16) uint8_t smem[kLds];
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void attn_bwd_kernel(BwdArgs a) {
+  __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
   const AttnProblem& p = a.p;
   const int64_t L = blockIdx.x;
   const int64_t N = int64_t(a.n_kv) + a.n_q;
-  const int64_t before = (L * a.n_kv) / N;  // dK/dV workgroups placed before L
-  const bool kv_role = ((L + 1) * a.n_kv) / N > before;
-  if (kv_role) {
+  const int64_t before = (L * a.n_kv) / N;  // key-side items placed before L
+  const bool kv_side = ((L + 1) * a.n_kv) / N > before;
+  if (kv_side) {
     const int i = int(before);
-    const int bg = i % (p.B * p.Hkv);
-    dkdv_body<KV>(p, a.q, a.k, a.v, a.dout, a.lse, a.delta, a.dk, a.dv, a.accumulate, smem,
-                  i / (p.B * p.Hkv), bg % p.Hkv, bg / p.Hkv);
+    const int pair = i >> 1;
+    const int bg = pair % (p.B * p.Hkv);
+    const int kt = pair / (p.B * p.Hkv);
+    if ((i & 1) == 0)
+      key_role<C, true>(p, a.q, a.k, a.v, a.dout, a.lse, a.delta, a.dk, a.accumulate, smem, kt, bg % p.Hkv,
+                        bg / p.Hkv);
+    else
+      key_role<C, false>(p, a.q, a.k, a.v, a.dout, a.lse, a.delta, a.dv, a.accumulate, smem, kt, bg % p.Hkv,
+                         bg / p.Hkv);
   } else {
     const int i = int(L - before);
     const int bh = i % (p.B * p.Hq);
     const int r = i / (p.B * p.Hq);
-    const int n_qt = (p.Sq + Q::kRows - 1) / Q::kRows;
-    dq_body<Q>(p, a.q, a.k, a.v, a.dout, a.lse, a.delta, a.dq, a.accumulate, smem,
-               p.causal ? n_qt - 1 - r : r, bh % p.Hq, bh / p.Hq);
+    const int n_qt = (p.Sq + C::kRows - 1) / C::kRows;
+    dq_role<C>(p, a.q, a.k, a.v, a.dout, a.lse, a.delta, a.dq, a.accumulate, smem, p.causal ? n_qt - 1 - r : r,
+               bh % p.Hq, bh / p.Hq);
   }
 }
 
@@ -528,15 +519,14 @@ hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const vo
     hipLaunchKernelGGL(delta_kernel<D>, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, rows, p.Sq,
                        p.Hq, static_cast<U>(out), static_cast<U>(dout), delta);
   }
-  using KV = DkvCfg<D, 4, 64>;
-  using Q = DqCfg<D, 4, 64>;
+  using C = BwdCfg<D>;
   BwdArgs a{p, static_cast<U>(q), static_cast<U>(k), static_cast<U>(v), static_cast<U>(dout), lse, delta,
             dq, dk, dv, accumulate,
-            p.B * p.Hkv * ((p.Sk + KV::kKeys - 1) / KV::kKeys),
-            p.B * p.Hq * ((p.Sq + Q::kRows - 1) / Q::kRows)};
+            2 * p.B * p.Hkv * ((p.Sk + C::kRows - 1) / C::kRows),
+            p.B * p.Hq * ((p.Sq + C::kRows - 1) / C::kRows)};
   {
     ProfScope ps(s, kProfBwdMfma);
-    hipLaunchKernelGGL((attn_bwd_kernel<KV, Q>), dim3(unsigned(a.n_kv + a.n_q)), dim3(KV::kThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_kernel<C>, dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s, a);
   }
   return hipGetLastError();
 }
