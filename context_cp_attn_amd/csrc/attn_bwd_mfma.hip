@@ -167,27 +167,37 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
 
   const float c2 = p.scale * kLog2e;
   const int n_it = (p.Sq + C::BM - 1) / C::BM;
-  const int n_t = G * n_it;  // flattened (query head of the group, query tile)
-
-  auto tile_class = [&](int t, const Span& ksp) {
-    const int i0 = (t % n_it) * C::BM;
+  // A tile is (query head of the group hh, query tile it), walked hh-major with
+  // incremental counters (no integer division in the loop).
+  struct Tq {
+    int hh, it;
+  };
+  auto step = [&](Tq t) {
+    if (++t.it == n_it) {
+      t.it = 0;
+      ++t.hh;
+    }
+    return t;
+  };
+  auto tile_class = [&](Tq t, const Span& ksp) {
+    const int i0 = t.it * C::BM;
     return classify(p, q_span(p, b, i0, min(i0 + C::BM, p.Sq) - 1), ksp, false);
   };
-  auto next_tile = [&](int t) {
-    while (t < n_t && tile_class(t, wg_k) == kEmpty) ++t;
+  auto next_tile = [&](Tq t) {
+    while (t.hh < G && tile_class(t, wg_k) == kEmpty) t = step(t);
     return t;
   };
   typename C::TileM tq, tg;
   const uint32_t qrs_bytes = uint32_t(qrs) * 2u;
   tq.init(qrs_bytes);
   tg.init(qrs_bytes);
-  auto load = [&](int t) {
-    const int h = g * G + t / n_it;
-    const int i0 = (t % n_it) * C::BM;
+  auto load = [&](Tq t) {
+    const int h = g * G + t.hh;
+    const int i0 = t.it * C::BM;
     tq.load(q + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq);
     tg.load(dout + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq);
   };
-  auto store = [&](int t, uint8_t* base) {
+  auto store = [&](Tq t, uint8_t* base) {
     QStage<C> st(base, kDK);
     tq.store_rows(st.q, C::RLD);
     if constexpr (kDK) {
@@ -196,8 +206,8 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
     } else {
       tg.store_cols(st.t, C::TLDM);
     }
-    const int h = g * G + t / n_it;
-    const int i0 = (t % n_it) * C::BM;
+    const int h = g * G + t.hh;
+    const int i0 = t.it * C::BM;
     for (int r = tid; r < C::BM; r += C::kThreads) {
       const int i = i0 + r;
       const bool ok = i < p.Sq;
@@ -209,16 +219,16 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
     }
   };
 
-  int cur = next_tile(0);
-  if (cur < n_t) {
+  Tq cur = next_tile(Tq{0, 0});
+  if (cur.hh < G) {
     load(cur);
     store(cur, smem);
     __syncthreads();
     int buf = 0;
     const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
     while (true) {
-      const int nxt = next_tile(cur + 1);
-      const bool has_next = nxt < n_t;
+      const Tq nxt = next_tile(step(cur));
+      const bool has_next = nxt.hh < G;
       if (has_next) load(nxt);
       const int wcls = wave_live ? tile_class(cur, wv_k) : kEmpty;
       if (wcls != kEmpty) {

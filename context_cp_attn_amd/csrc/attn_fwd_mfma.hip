@@ -12,11 +12,11 @@
 //    wavefront owns 32 rows, held in registers as bf16 MFMA operands.  The register
 //    budget admits two wavefronts per SIMD, so one wave's matrix products overlap
 //    the other's softmax.
-//  * K/V tiles of BN keys stream through LDS, double-buffered: the global loads of
-//    tile t+1 are in flight while tile t is multiplied.  K is stored [key][d]; V is
-//    stored transposed [d][key] so both products read 16-byte operand fragments;
-//    the V tile is loaded with consecutive threads on consecutive key groups, which
-//    makes its transposing LDS stores bank-conflict free.
+//  * K/V tiles of BN keys stream through LDS, double-buffered, by LDS-DMA (buffer
+//    loads that write LDS directly, no staging registers): the DMA of tile t+1 runs
+//    while tile t is multiplied.  Both tiles are stored row-major with an XOR
+//    swizzle of their 16-byte chunks; K rows are read as 16-byte fragments and V^T
+//    fragments with the gfx950 LDS transpose read, conflict-free both ways.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    each lane then holds one query column, so the row max / row sum of the online
 //    softmax need only one exchange between the two 32-lane halves.  The K rows are
@@ -50,14 +50,10 @@ struct FwdCfg {
   static constexpr int KB = BN / 32;  // 32-key blocks of a tile
   static constexpr int DB = D / 32;   // 32-row d blocks of O^T
   static constexpr int PT = BN / 16;  // k-steps of O^T += V^T P^T
-  static constexpr int KLD = D + 8;   // K row pitch in LDS (elements): 16-byte skew per row
-  static constexpr int VLD = BN + 8;  // V^T row pitch in LDS (elements)
-  static constexpr int kKElems = BN * KLD;
-  static constexpr int kVElems = D * VLD;
-  static constexpr int kStageBytes = (kKElems + kVElems) * 2 + BN * 2 * 4;  // + kpos, kseg
+  static constexpr int kTileElems = BN * D;  // swizzled row-major K or V tile
+  static constexpr int kStageBytes = 2 * kTileElems * 2 + BN * 2 * 4;  // K, V, kpos, kseg
   static constexpr int kLdsBytes = 2 * kStageBytes;
-  using KTile = RowTile<BN, D, kThreads, false>;  // stored row-major
-  using VTile = RowTile<BN, D, kThreads, true>;   // stored transposed
+  using Tile = DmaTile<BN, D, kThreads>;
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
 };
 
@@ -77,8 +73,9 @@ __global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_mfma_kernel(AttnProbl
 
   // heaviest query tiles of every (batch, head) first
   const int n_qt = (p.Sq + C::kRows - 1) / C::kRows;
-  const int tile_rank = int(blockIdx.x) / (p.B * p.Hq);
-  const int bh = int(blockIdx.x) - tile_rank * (p.B * p.Hq);
+  const int order = int(blockIdx.x);
+  const int tile_rank = order / (p.B * p.Hq);
+  const int bh = order - tile_rank * (p.B * p.Hq);
   const int qt = p.causal ? (n_qt - 1 - tile_rank) : tile_rank;
   const int h = bh % p.Hq;
   const int b = bh / p.Hq;
@@ -126,22 +123,18 @@ __global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_mfma_kernel(AttnProbl
     while (kt < n_kt && tile_class(kt, wg_q) == kEmpty) ++kt;
     return kt;
   };
-  typename C::KTile tk;
-  typename C::VTile tv;
+  typename C::Tile tk, tv;
   const uint32_t krs_bytes = uint32_t(krs) * 2u;
   tk.init(krs_bytes);
   tv.init(krs_bytes);
-  auto load = [&](int kt) {
-    tk.load(kbase, krs_bytes, kt * C::BN, p.Sk);
-    tv.load(vbase, krs_bytes, kt * C::BN, p.Sk);
-  };
-  auto store = [&](int kt, uint8_t* stage) {
+  // stage layout: K tile, V tile (swizzled row-major), kpos, kseg
+  auto stage_load = [&](int kt, uint8_t* stage) {
     uint16_t* ks = reinterpret_cast<uint16_t*>(stage);
-    uint16_t* vt = ks + C::kKElems;
-    int* kpos = reinterpret_cast<int*>(vt + C::kVElems);
+    uint16_t* vs = ks + C::kTileElems;
+    int* kpos = reinterpret_cast<int*>(vs + C::kTileElems);
     int* kseg = kpos + C::BN;
-    tk.store_rows(ks, C::KLD);
-    tv.store_cols(vt, C::VLD);
+    tk.load(kbase, krs_bytes, kt * C::BN, p.Sk, ks);
+    tv.load(vbase, krs_bytes, kt * C::BN, p.Sk, vs);
     const int j0 = kt * C::BN;
     for (int t = tid; t < C::BN; t += C::kThreads) {
       const int j = min(j0 + t, p.Sk - 1);
@@ -152,22 +145,23 @@ __global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_mfma_kernel(AttnProbl
 
   int cur = next_tile(0);
   if (cur < n_kt) {
-    load(cur);
-    store(cur, smem);
+    stage_load(cur, smem);
+    wait_all();
     __syncthreads();
     int buf = 0;
     const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
     while (true) {
       const int nxt = next_tile(cur + 1);
       const bool has_next = nxt < n_kt;
-      if (has_next) load(nxt);
+      // the DMA of the next tile runs while this one is multiplied
+      if (has_next) stage_load(nxt, smem + (buf ^ 1) * C::kStageBytes);
 
       const int wcls = wave_live ? tile_class(cur, wv_q) : kEmpty;
       if (wcls != kEmpty) {
         const uint8_t* stage = smem + buf * C::kStageBytes;
         const uint16_t* ks_l = reinterpret_cast<const uint16_t*>(stage);
-        const uint16_t* vt_l = ks_l + C::kKElems;
-        const int* kpos_l = reinterpret_cast<const int*>(vt_l + C::kVElems);
+        const uint16_t* vs_l = ks_l + C::kTileElems;
+        const int* kpos_l = reinterpret_cast<const int*>(vs_l + C::kTileElems);
         const int* kseg_l = kpos_l + C::BN;
 
         // S^T = K Q^T
@@ -178,7 +172,7 @@ __global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_mfma_kernel(AttnProbl
         for (int kstep = 0; kstep < C::KS; ++kstep)
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb)
-            s[kb] = mma(ld8(ks_l + (kb * 32 + perm_row(l32)) * C::KLD + kstep * 16 + hi * 8), qf[kstep], s[kb]);
+            s[kb] = mma(ld_row<C::D>(ks_l, kb * 32 + perm_row(l32), 2 * kstep + hi), qf[kstep], s[kb]);
 
         if (wcls == kPartial) {
           const int nvalid = p.Sk - cur * C::BN;
@@ -231,11 +225,11 @@ __global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_mfma_kernel(AttnProbl
           const bf16x8 pf = to_bf16x8(s[t >> 1], 8 * (t & 1));
 #pragma unroll
           for (int db = 0; db < C::DB; ++db)
-            o[db] = mma(ld8(vt_l + (db * 32 + l32) * C::VLD + t * 16 + hi * 8), pf, o[db]);
+            o[db] = mma(ld_tr<C::D>(vs_l, t * 16, db * 32), pf, o[db]);
         }
       }
 
-      if (has_next) store(nxt, smem + (buf ^ 1) * C::kStageBytes);
+      wait_all();
       __syncthreads();
       if (!has_next) break;
       cur = nxt;
@@ -264,9 +258,9 @@ __global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_mfma_kernel(AttnProbl
 template <class C>
 hipError_t launch_cfg(const AttnProblem& p, const void* q, const void* k, const void* v, void* out,
                       float* lse, hipStream_t s) {
-  dim3 grid(unsigned((p.Sq + C::kRows - 1) / C::kRows) * unsigned(p.Hq * p.B));
+  const unsigned n = unsigned((p.Sq + C::kRows - 1) / C::kRows) * unsigned(p.Hq * p.B);
   ProfScope ps(s, kProfFwdMfma);
-  hipLaunchKernelGGL(attn_fwd_mfma_kernel<C>, grid, dim3(C::kThreads), 0, s, p,
+  hipLaunchKernelGGL(attn_fwd_mfma_kernel<C>, dim3(n), dim3(C::kThreads), 0, s, p,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse);
   return hipGetLastError();

@@ -190,5 +190,86 @@ struct RowTile {
   }
 };
 
+
+// ---- row-major LDS tiles filled by LDS-DMA, read as rows or transposed ------------
+// A tile of NR token rows x D dims is stored unpadded, row-major, with the 16-byte
+// chunk c of row r placed at chunk c ^ chunk_xor<D>(r).  The XOR functions make
+// both access patterns bank-conflict free (64 banks x 4 bytes):
+//  * row fragments (8 consecutive dims of one row; 16 lanes read 16 distinct rows,
+//    the A rows of a product loaded with perm_row);
+//  * transposed fragments (8 consecutive rows of one dim) read with
+//    ds_read_b64_tr_b16, where each group of 16 lanes addresses a 4-row x 16-dim
+//    block and lane j receives dim j of the 4 rows.
+template <int D>
+CP_DEVICE constexpr int chunk_xor(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return (r >> 2) & 3;
+}
+
+template <int D>
+CP_DEVICE int rm_elem(int row, int chunk) { return row * D + ((chunk ^ chunk_xor<D>(row)) << 3); }
+
+// 8 consecutive dims (chunk c) of one row
+template <int D>
+CP_DEVICE bf16x8 ld_row(const uint16_t* tile, int row, int c) { return ld8(tile + rm_elem<D>(row, c)); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Transposed fragment: lane l receives rows rbase + 8*(l/32) + e (e = 0..7) of dim
+// dbase + (l % 32) -- the A/B fragment layout with k-slots over rows.
+template <int D>
+CP_DEVICE bf16x8 ld_tr(const uint16_t* tile, int rbase, int dbase) {
+  const int l = int(threadIdx.x) & 63, g = l >> 4, i = l & 15;
+  const int d = dbase + 16 * (g & 1) + 4 * (i & 3);
+  const int r = rbase + 8 * (g >> 1) + (i >> 2);
+  const uint16_t* p0 = tile + r * D + (((d >> 3) ^ chunk_xor<D>(r)) << 3) + (d & 7);
+  const uint16_t* p1 = tile + (r + 4) * D + (((d >> 3) ^ chunk_xor<D>(r + 4)) << 3) + (d & 7);
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p1));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// Stage NR rows x D dims into a swizzled row-major LDS tile with LDS-DMA: each
+// wavefront instruction moves 64 consecutive 16-byte LDS chunks, lane i fetching
+// the global chunk that belongs at LDS chunk i.  Rows at or beyond nrows read as
+// zeros (buffer range check).  Completion is tracked by vmcnt: wait for it before
+// the barrier that publishes the tile.
+template <int NR, int D, int NT>
+struct DmaTile {
+  static constexpr int kChunks = NR * D / 8;
+  static constexpr int kIter = (kChunks + NT - 1) / NT;
+  static_assert(kChunks % 64 == 0 && NT % 64 == 0, "whole wavefronts");
+  uint32_t voff[kIter];
+
+  CP_DEVICE void init(uint32_t row_stride_bytes) {
+#pragma unroll
+    for (int it = 0; it < kIter; ++it) {
+      const int s = it * NT + int(threadIdx.x);
+      const int row = s / (D / 8), slot = s % (D / 8);
+      voff[it] = uint32_t(row) * row_stride_bytes + uint32_t(slot ^ chunk_xor<D>(row)) * 16u;
+    }
+  }
+
+  CP_DEVICE void load(const uint16_t* base, uint32_t row_stride_bytes, int row0, int nrows, uint16_t* lds_tile) const {
+    const uint32_t skip = uint32_t(row0) * row_stride_bytes;
+    const uint32_t valid = uint32_t(nrows - 1 - row0) * row_stride_bytes + uint32_t(D) * 2u;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const uint8_t*>(base) + skip, valid);
+#pragma unroll
+    for (int it = 0; it < kIter; ++it) {
+      const int s0 = it * NT + (int(threadIdx.x) & ~63);  // first chunk of this wavefront
+      if (kChunks % NT == 0 || s0 < kChunks)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(lds_tile + s0 * 8), 16, voff[it], 0, 0, 0);
+    }
+  }
+};
+
+// Wait for every outstanding memory operation of this wavefront (LDS-DMA included).
+CP_DEVICE void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+
 }  // namespace mfma
 }  // namespace cp
