@@ -20,10 +20,14 @@
 //     block pair) but keeps every role under 256 registers, so two wavefronts run
 //     per SIMD and one's matrix products overlap the other's elementwise work.
 //     S and dP are computed query-major in the dV/dK roles so P and dS are directly
-//     the B operands of the next products; the tiles used as A operands in both
-//     orientations are staged in LDS row-major and transposed (XOR-swizzled).
-//     The role lists, each heaviest first, are interleaved in one grid.
+//     the B operands of the next products.  Each LDS stage holds two row-major
+//     tiles (Q and dO, or K and V), XOR-swizzled and filled by LDS-DMA; the
+//     operands needed transposed (dO^T, Q^T, K^T) are read from the same tiles with
+//     the LDS transpose read.  The role lists, each heaviest first, are
+//     interleaved in one grid.
 // Tiles are skipped / masked exactly as in the forward (empty / partial / full).
+#include <type_traits>
+
 #include "mfma_common.h"
 #include "prof.h"
 
@@ -80,38 +84,31 @@ struct BwdCfg {
   static constexpr int QBLK = BM / 32;
   static constexpr int BN = 64;          // key tile of the dQ role
   static constexpr int KB = BN / 32;
-  static constexpr int RLD = D + 8;      // row-major pitch (elements)
-  static constexpr int TLDM = BM + 8;    // transposed pitch, query tiles
-  static constexpr int TLDN = BN + 8;    // transposed pitch, key tiles
-  static constexpr int kRowM = BM * RLD, kColM = D * TLDM;
-  static constexpr int kRowN = BN * RLD, kColN = D * TLDN;
-  // dV stage: Q rows, dO^T, lse2, qpos, qseg (the dK stage's delta slot unused)
-  // dK stage: Q rows, dO rows, Q^T, lse2, delta, qpos, qseg
-  static constexpr int kStageK = (2 * kRowM + kColM) * 2 + 4 * BM * 4;
-  // dQ stage: K rows, V rows, K^T, kpos, kseg
-  static constexpr int kStageQ = (2 * kRowN + kColN) * 2 + 2 * BN * 4;
+  static constexpr int kTileM = BM * D, kTileN = BN * D;  // swizzled row-major tiles
+  // dV / dK stage: Q rows, dO rows, lse2, delta, qpos, qseg
+  static constexpr int kStageK = 2 * kTileM * 2 + 4 * BM * 4;
+  // dQ stage: K rows, V rows, kpos, kseg
+  static constexpr int kStageQ = 2 * kTileN * 2 + 2 * BN * 4;
   static constexpr int kStageMax = kStageK > kStageQ ? kStageK : kStageQ;
   static constexpr int kLdsBytes = 2 * kStageMax;
-  // 2-row units: every one of the 512 threads stages a share of each tile
-  using TileM = RowTile<BM, D, kThreads, false, 2>;
-  using TileN = RowTile<BN, D, kThreads, false, 2>;
+  using TileM = DmaTile<BM, D, kThreads>;
+  using TileN = DmaTile<BN, D, kThreads>;
+  static_assert(BM <= kThreads && BN <= kThreads, "one thread per row of the small arrays");
 };
 
 // Pointers into one LDS stage of the dV / dK roles.
 template <class C>
 struct QStage {
-  uint16_t* q;     // Q rows   [BM][RLD]
-  uint16_t* g;     // dO rows  [BM][RLD]  (dK role)
-  uint16_t* t;     // dO^T (dV role) or Q^T (dK role) [D][TLDM]
+  uint16_t* q;     // Q rows
+  uint16_t* g;     // dO rows
   float* lse2;
   float* delta;    // dK role
   int* qpos;
   int* qseg;
-  CP_DEVICE QStage(uint8_t* base, bool with_g) {
+  CP_DEVICE explicit QStage(uint8_t* base) {
     q = reinterpret_cast<uint16_t*>(base);
-    g = q + C::kRowM;
-    t = with_g ? g + C::kRowM : g;
-    lse2 = reinterpret_cast<float*>(t + C::kColM);
+    g = q + C::kTileM;
+    lse2 = reinterpret_cast<float*>(g + C::kTileM);
     delta = lse2 + C::BM;
     qpos = reinterpret_cast<int*>(delta + C::BM);
     qseg = qpos + C::BM;
@@ -191,59 +188,68 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
   const uint32_t qrs_bytes = uint32_t(qrs) * 2u;
   tq.init(qrs_bytes);
   tg.init(qrs_bytes);
-  auto load = [&](Tq t) {
+  // per-query values of the next tile, fetched early by the first BM threads and
+  // written to LDS after this tile's products
+  float n_lse2 = INFINITY, n_delta = 0.0f;
+  int n_qpos = 0, n_qseg = 0;
+  auto issue = [&](Tq t, uint8_t* base) {
+    QStage<C> st(base);
     const int h = g * G + t.hh;
     const int i0 = t.it * C::BM;
-    tq.load(q + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq);
-    tg.load(dout + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq);
-  };
-  auto store = [&](Tq t, uint8_t* base) {
-    QStage<C> st(base, kDK);
-    tq.store_rows(st.q, C::RLD);
-    if constexpr (kDK) {
-      tg.store_rows(st.g, C::RLD);
-      tq.store_cols(st.t, C::TLDM);
-    } else {
-      tg.store_cols(st.t, C::TLDM);
-    }
-    const int h = g * G + t.hh;
-    const int i0 = t.it * C::BM;
-    for (int r = tid; r < C::BM; r += C::kThreads) {
-      const int i = i0 + r;
+    tq.load(q + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq, st.q);
+    tg.load(dout + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq, st.g);
+    if (tid < C::BM) {
+      const int i = i0 + tid;
       const bool ok = i < p.Sq;
       const int64_t li = (int64_t(b) * p.Hq + h) * p.Sq + i;
-      st.lse2[r] = ok ? lse2_of(lse[li]) : INFINITY;
-      if constexpr (kDK) st.delta[r] = ok ? delta[li] : 0.0f;
-      st.qpos[r] = ok ? qpos_at(p, i) : 0;
-      st.qseg[r] = ok ? qseg_at(p, b, i) : 0;
+      n_lse2 = ok ? lse2_of(lse[li]) : INFINITY;
+      if constexpr (kDK) n_delta = ok ? delta[li] : 0.0f;
+      n_qpos = ok ? qpos_at(p, i) : 0;
+      n_qseg = ok ? qseg_at(p, b, i) : 0;
     }
+  };
+  auto publish = [&](uint8_t* base) {
+    QStage<C> st(base);
+    if (tid < C::BM) {
+      st.lse2[tid] = n_lse2;
+      if constexpr (kDK) st.delta[tid] = n_delta;
+      st.qpos[tid] = n_qpos;
+      st.qseg[tid] = n_qseg;
+    }
+    wait_all();
+    __syncthreads();
   };
 
   Tq cur = next_tile(Tq{0, 0});
   if (cur.hh < G) {
-    load(cur);
-    store(cur, smem);
-    __syncthreads();
+    issue(cur, smem);
+    publish(smem);
     int buf = 0;
     const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
     while (true) {
       const Tq nxt = next_tile(step(cur));
       const bool has_next = nxt.hh < G;
-      if (has_next) load(nxt);
+      uint8_t* nbase = smem + (buf ^ 1) * C::kStageMax;
+      if (has_next) issue(nxt, nbase);
       const int wcls = wave_live ? tile_class(cur, wv_k) : kEmpty;
       if (wcls != kEmpty) {
-        QStage<C> st(smem + buf * C::kStageMax, kDK);
-#pragma unroll
-        for (int qb = 0; qb < C::QBLK; ++qb) {
+        const QStage<C> st(smem + buf * C::kStageMax);
+        // One instantiation for masked tiles, one for full tiles, each branch-free
+        // (the mask goes into the exponent), so a tile's body is one basic block.
+        auto sdp = [&](int qb, f32x16& s, f32x16& dp) {
           // S = Q K^T (and dP = dO V^T): lane column = this lane's key,
           // register r = query row qb*32 + key_of_reg(r, hi)
-          f32x16 s = f32x16{}, dp = f32x16{};
-          const int arow = (qb * 32 + perm_row(l32)) * C::RLD + hi * 8;
+          s = f32x16{};
+          dp = f32x16{};
+          const int arow = qb * 32 + perm_row(l32);
 #pragma unroll
           for (int ks = 0; ks < C::KS; ++ks) {
-            s = mma(ld8(st.q + arow + ks * 16), kf[ks], s);
-            if constexpr (kDK) dp = mma(ld8(st.g + arow + ks * 16), vf[ks], dp);
+            s = mma(ld_row<C::D>(st.q, arow, 2 * ks + hi), kf[ks], s);
+            if constexpr (kDK) dp = mma(ld_row<C::D>(st.g, arow, 2 * ks + hi), vf[ks], dp);
           }
+        };
+        auto soft = [&](int qb, f32x16& s, const f32x16& dp, auto masked) {
+          constexpr bool kMasked = decltype(masked)::value;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int r0 = qb * 32 + key_of_reg(4 * jj, hi);
@@ -251,34 +257,54 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
             f32x4 d4 = f32x4{0, 0, 0, 0};
             if constexpr (kDK) d4 = *reinterpret_cast<const f32x4*>(st.delta + r0);
             i32x4 qp4 = i32x4{0, 0, 0, 0}, qs4 = i32x4{0, 0, 0, 0};
-            if (wcls == kPartial) {
+            if constexpr (kMasked) {
               qp4 = *reinterpret_cast<const i32x4*>(st.qpos + r0);
               qs4 = *reinterpret_cast<const i32x4*>(st.qseg + r0);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int r = 4 * jj + i;
-              float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[i]));
-              if (wcls == kPartial && !pair_visible(ms, qp4[i], my_kpos, qs4[i], my_kseg)) pr = 0.0f;
+              float x = fmaf(s[r], c2, -l4[i]);
+              // a hidden pair gets exponent -inf, so P = 0 exactly
+              if constexpr (kMasked) x = pair_visible(ms, qp4[i], my_kpos, qs4[i], my_kseg) ? x : -INFINITY;
+              const float pr = __builtin_amdgcn_exp2f(x);
               if constexpr (kDK)
                 s[r] = pr * (dp[r] - d4[i]);  // dS
               else
                 s[r] = pr;                    // P
             }
           }
-          // dV^T += dO^T P  or  dK^T += Q^T dS, over the block's two 16-query k-steps
+        };
+        // dV^T += dO^T P  or  dK^T += Q^T dS over the block's two 16-query k-steps;
+        // the A operand (dO^T or Q^T) is read transposed from the row-major tile
+        const uint16_t* at = kDK ? st.q : st.g;
+        auto grad = [&](int qb, const f32x16& s) {
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             const bf16x8 bfrag = to_bf16x8(s, 8 * tt);
-            const int col = (qb * 2 + tt) * 16 + hi * 8;
 #pragma unroll
             for (int d = 0; d < C::DB; ++d)
-              acc[d] = mma(ld8(st.t + (d * 32 + l32) * C::TLDM + tcol<C::BM>(d * 32 + l32, col)), bfrag, acc[d]);
+              acc[d] = mma(ld_tr<C::D>(at, (qb * 2 + tt) * 16, d * 32), bfrag, acc[d]);
           }
-        }
+        };
+        auto body = [&](auto masked) {
+#pragma unroll
+          for (int qb = 0; qb < C::QBLK; ++qb) {
+            f32x16 s, dp;
+            sdp(qb, s, dp);
+            soft(qb, s, dp, masked);
+            grad(qb, s);
+          }
+        };
+        if (wcls == kPartial)
+          body(std::true_type{});
+        else
+          body(std::false_type{});
       }
-      if (has_next) store(nxt, smem + (buf ^ 1) * C::kStageMax);
-      __syncthreads();
+      if (has_next)
+        publish(nbase);
+      else
+        __syncthreads();
       if (!has_next) break;
       cur = nxt;
       buf ^= 1;
@@ -364,90 +390,98 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
   const uint32_t krs_bytes = uint32_t(krs) * 2u;
   tk.init(krs_bytes);
   tv.init(krs_bytes);
-  // stage: K rows, V rows, K^T, kpos, kseg
+  // stage: K rows, V rows, kpos, kseg
   auto ks_of = [&](uint8_t* base) { return reinterpret_cast<uint16_t*>(base); };
-  auto vs_of = [&](uint8_t* base) { return ks_of(base) + C::kRowN; };
-  auto kts_of = [&](uint8_t* base) { return vs_of(base) + C::kRowN; };
-  auto kp_of = [&](uint8_t* base) { return reinterpret_cast<int*>(kts_of(base) + C::kColN); };
-  auto store = [&](int kt, uint8_t* base) {
-    tk.store_rows(ks_of(base), C::RLD);
-    tk.store_cols(kts_of(base), C::TLDN);
-    tv.store_rows(vs_of(base), C::RLD);
-    int* kp = kp_of(base);
-    int* kg = kp + C::BN;
-    const int j0 = kt * C::BN;
-    for (int t = tid; t < C::BN; t += C::kThreads) {
-      const int j = min(j0 + t, p.Sk - 1);
-      kp[t] = kpos_at(p, j);
-      kg[t] = kseg_at(p, b, j);
+  auto vs_of = [&](uint8_t* base) { return ks_of(base) + C::kTileN; };
+  auto kp_of = [&](uint8_t* base) { return reinterpret_cast<int*>(vs_of(base) + C::kTileN); };
+  int n_kpos = 0, n_kseg = 0;
+  auto issue = [&](int kt, uint8_t* base) {
+    tk.load(kbase, krs_bytes, kt * C::BN, p.Sk, ks_of(base));
+    tv.load(vbase, krs_bytes, kt * C::BN, p.Sk, vs_of(base));
+    if (tid < C::BN) {
+      const int j = min(kt * C::BN + tid, p.Sk - 1);
+      n_kpos = kpos_at(p, j);
+      n_kseg = kseg_at(p, b, j);
     }
+  };
+  auto publish = [&](uint8_t* base) {
+    if (tid < C::BN) {
+      int* kp = kp_of(base);
+      kp[tid] = n_kpos;
+      kp[C::BN + tid] = n_kseg;
+    }
+    wait_all();
+    __syncthreads();
   };
 
   int cur = next_tile(0);
   if (cur < n_kt) {
-    tk.load(kbase, krs_bytes, cur * C::BN, p.Sk);
-    tv.load(vbase, krs_bytes, cur * C::BN, p.Sk);
-    store(cur, smem);
-    __syncthreads();
+    issue(cur, smem);
+    publish(smem);
     int buf = 0;
     const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
     while (true) {
       const int nxt = next_tile(cur + 1);
       const bool has_next = nxt < n_kt;
-      if (has_next) {
-        tk.load(kbase, krs_bytes, nxt * C::BN, p.Sk);
-        tv.load(vbase, krs_bytes, nxt * C::BN, p.Sk);
-      }
+      uint8_t* nbase = smem + (buf ^ 1) * C::kStageMax;
+      if (has_next) issue(nxt, nbase);
       const int wcls = wave_live ? tile_class(cur, wv_q) : kEmpty;
       if (wcls != kEmpty) {
         uint8_t* base = smem + buf * C::kStageMax;
         const uint16_t* ks = ks_of(base);
         const uint16_t* vs = vs_of(base);
-        const uint16_t* kts = kts_of(base);
         const int* kp = kp_of(base);
         const int* kg = kp + C::BN;
         const int nvalid = p.Sk - cur * C::BN;
+        auto body = [&](auto masked) {
+          constexpr bool kMasked = decltype(masked)::value;
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-          // S^T = K Q^T and dP^T = V dO^T for 32 keys: lane column = this lane's query
-          f32x16 s = f32x16{}, dp = f32x16{};
-          const int arow = (kb * 32 + perm_row(l32)) * C::RLD + hi * 8;
+          for (int kb = 0; kb < C::KB; ++kb) {
+            // S^T = K Q^T and dP^T = V dO^T for 32 keys: lane column = this lane's query
+            f32x16 s = f32x16{}, dp = f32x16{};
+            const int arow = kb * 32 + perm_row(l32);
 #pragma unroll
-          for (int kk = 0; kk < C::KS; ++kk) {
-            s = mma(ld8(ks + arow + kk * 16), qf[kk], s);
-            dp = mma(ld8(vs + arow + kk * 16), gf[kk], dp);
-          }
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int kk0 = kb * 32 + key_of_reg(4 * jj, hi);
-            i32x4 kp4 = i32x4{0, 0, 0, 0}, kg4 = i32x4{0, 0, 0, 0};
-            if (wcls == kPartial) {
-              kp4 = *reinterpret_cast<const i32x4*>(kp + kk0);
-              kg4 = *reinterpret_cast<const i32x4*>(kg + kk0);
+            for (int kk = 0; kk < C::KS; ++kk) {
+              s = mma(ld_row<C::D>(ks, arow, 2 * kk + hi), qf[kk], s);
+              dp = mma(ld_row<C::D>(vs, arow, 2 * kk + hi), gf[kk], dp);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 4 * jj + i;
-              float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -my_lse2));
-              if (wcls == kPartial &&
-                  !(kk0 + i < nvalid && pair_visible(ms, my_qpos, kp4[i], my_qseg, kg4[i])))
-                pr = 0.0f;
-              s[r] = pr * (dp[r] - my_delta);  // dS^T
+            for (int jj = 0; jj < 4; ++jj) {
+              const int kk0 = kb * 32 + key_of_reg(4 * jj, hi);
+              i32x4 kp4 = i32x4{0, 0, 0, 0}, kg4 = i32x4{0, 0, 0, 0};
+              if constexpr (kMasked) {
+                kp4 = *reinterpret_cast<const i32x4*>(kp + kk0);
+                kg4 = *reinterpret_cast<const i32x4*>(kg + kk0);
+              }
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int r = 4 * jj + i;
+                float x = fmaf(s[r], c2, -my_lse2);
+                if constexpr (kMasked)
+                  x = ((kk0 + i < nvalid) & pair_visible(ms, my_qpos, kp4[i], my_qseg, kg4[i])) ? x : -INFINITY;
+                const float pr = __builtin_amdgcn_exp2f(x);
+                s[r] = pr * (dp[r] - my_delta);  // dS^T
+              }
+            }
+            // dQ^T += K^T dS^T over the block's two 16-key k-steps (K^T read transposed)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+              const bf16x8 sb = to_bf16x8(s, 8 * tt);
+#pragma unroll
+              for (int d = 0; d < C::DB; ++d)
+                acc[d] = mma(ld_tr<C::D>(ks, (kb * 2 + tt) * 16, d * 32), sb, acc[d]);
             }
           }
-          // dQ^T += K^T dS^T over the block's two 16-key k-steps
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const bf16x8 sb = to_bf16x8(s, 8 * tt);
-            const int col = (kb * 2 + tt) * 16 + hi * 8;
-#pragma unroll
-            for (int d = 0; d < C::DB; ++d)
-              acc[d] = mma(ld8(kts + (d * 32 + l32) * C::TLDN + tcol<C::BN>(d * 32 + l32, col)), sb, acc[d]);
-          }
-        }
+        };
+        if (wcls == kPartial)
+          body(std::true_type{});
+        else
+          body(std::false_type{});
       }
-      if (has_next) store(nxt, smem + (buf ^ 1) * C::kStageMax);
-      __syncthreads();
+      if (has_next)
+        publish(nbase);
+      else
+        __syncthreads();
       if (!has_next) break;
       cur = nxt;
       buf ^= 1;

@@ -48,12 +48,12 @@ struct MaskSpec {
   int has_seg;
 };
 
+// Branch-free (bitwise) so that per-element masks compile to compares and selects.
 CP_DEVICE bool pair_visible(const MaskSpec& m, int qp, int kp, int qs, int ks) {
-  bool vis = true;
-  if (m.causal) vis = vis && (kp <= qp);
-  if (m.has_seg) vis = vis && (qs == ks);
-  if (m.window) vis = vis && (qp - kp < m.window);
-  return vis;
+  const bool c = (m.causal == 0) | (kp <= qp);
+  const bool s = (m.has_seg == 0) | (qs == ks);
+  const bool w = (m.window == 0) | (qp - kp < m.window);
+  return c & s & w;
 }
 
 }  // namespace cp
