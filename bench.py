@@ -17,7 +17,8 @@ value = algorithmic attention FLOPs of the step (fwd 4*D and bwd 8*D per visible
 before the timed region.  The relayout bandwidth is reported beside it.
 
 Legs timed in the same run (not part of value): the ring share of llama2-7b
-(2048 queries x 32 heads vs 16 zigzag KV blocks, fwd + merge), the 64K-token
+(2048 queries x 32 heads vs 16 zigzag KV blocks: the fused step with the merge in
+the attention epilogue, and the unfused fwd + merge pair), the 64K-token
 dual-chunk-swap reorder, and the packed + windowed 8K ring share (4 ranks x 4
 steps, fwd + merge + bwd).  The CPU oracle is timed on a bounded sample of the
 step's attention rows (cpu_baseline).
@@ -131,20 +132,29 @@ def legs(torch, cp, cp_inputs):
     q, k, v = (t.cuda() for t in cp_inputs.normal_tensors([(1, S, H, D)] * 3, seed=0))
     qz, kz, vz = (cp.zigzag_reorder(t, P) for t in (q, k, v))
     del q, k, v
-    ring = cp.drivers.RingShare(qz, kz, vz, P, 0)
+    fl = 4 * D * H * (2 * P * (S // (2 * P)) ** 2 + S // (2 * P))
+    merge_bytes = (S // P) * H * D * (4 + 2 + 4) + 3 * (S // P) * H * 4
+    # unfused: attn_fwd writes (out bf16, lse), lse_merge folds them into (acc, lse_acc)
+    ring = cp.drivers.RingShare(qz, kz, vz, P, 0, fused=False)
     ring.forward()
     with cp._lib.KernelTrace() as tr:
         ms = timed(torch, ring.forward, 5)
-    fl = 4 * D * H * (2 * P * (S // (2 * P)) ** 2 + S // (2 * P))
     fwd_ms, n_fwd = tr.results.get("attn_fwd_mfma", (0.0, 1))
     mg_ms, n_mg = tr.results.get("lse_merge", (0.0, 1))
-    merge_bytes = (S // P) * H * D * (4 + 2 + 4) + 3 * (S // P) * H * 4
+    # fused: the merge runs in the attention epilogue
+    ring_f = cp.drivers.RingShare(qz, kz, vz, P, 0, fused=True)
+    ring_f.forward()
+    with cp._lib.KernelTrace() as tr:
+        ms_f = timed(torch, ring_f.forward, 5)
+    fm_ms, n_fm = tr.results.get("attn_fwd_merge_mfma", (0.0, 1))
     out["ring_llama2_7b_32k_cp16_rank0"] = {
-        "ms_per_pass": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+        "fused_ms_per_pass": round(ms_f, 4), "fused_tflops": round(fl / ms_f / 1e9, 2),
+        "attn_fwd_merge_mfma_avg_ms": round(fm_ms / n_fm, 5),
+        "unfused_ms_per_pass": round(ms, 4), "unfused_tflops": round(fl / ms / 1e9, 2),
         "attn_fwd_mfma_avg_ms": round(fwd_ms / n_fwd, 5),
         "lse_merge_avg_ms": round(mg_ms / n_mg, 5),
         "lse_merge_gbps": round(merge_bytes / (mg_ms / n_mg) / 1e6, 1)}
-    del qz, kz, vz, ring
+    del qz, kz, vz, ring, ring_f
     # dual-chunk-swap reorder of 64K tokens into 8 chunks: [1,65536,4096] bf16 (512 MiB)
     x = torch.randn(1, 65536, 4096, device="cuda").bfloat16()
     y = torch.empty_like(x)

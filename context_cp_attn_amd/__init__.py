@@ -4,7 +4,8 @@ Hand-written HIP kernels behind a C ABI (include/cp_attn.h, libcp_attn.so):
 
 * ``attn_fwd`` / ``attn_bwd`` — blockwise causal attention returning (out, lse) at
   given query/key positions, with segment ids, a sliding window and grouped kv heads;
-* ``lse_merge`` — the ring step's log-sum-exp merge;
+* ``lse_merge`` — the ring step's log-sum-exp merge; ``attn_fwd_merge`` — the ring
+  step fused: attention whose epilogue merges into the running (out, lse);
 * ``ulysses_relayout`` / ``ulysses_relayout_inv`` — the sequence<->head exchange of
   all simulated ranks as one local permute;
 * ``zigzag_reorder`` — the zigzag / dual-chunk-swap load-balancing reorder.
@@ -14,6 +15,6 @@ torch provides device memory and the stream; nothing here computes on the CPU.
 """
 
 from ._lib import CpError, load as load_library  # noqa: F401
-from .ops import (attn_fwd, attn_bwd, lse_merge, ulysses_relayout, ulysses_relayout_inv,  # noqa: F401
-                  zigzag_reorder, bwd_workspace)
+from .ops import (attn_fwd, attn_fwd_merge, attn_bwd, lse_merge, ulysses_relayout,  # noqa: F401
+                  ulysses_relayout_inv, zigzag_reorder, bwd_workspace)
 from . import drivers  # noqa: F401

@@ -154,6 +154,34 @@ cp_status_t cp_attn_fwd(const cp_attn_args_t* a, const void* q, const void* k, c
   return hip_status(e, "cp_attn_fwd launch");
 }
 
+cp_status_t cp_attn_fwd_merge(const cp_attn_args_t* a, const void* q, const void* k, const void* v,
+                              float* out_acc, float* lse_acc, hipStream_t stream) {
+  cp::AttnProblem p;
+  cp_status_t st = check_attn(a, q, k, v, &p);
+  if (st != CP_OK) return st;
+  if (!out_acc || !lse_acc) return fail(CP_ERR_INVALID, "out_acc and lse_acc must be non-NULL");
+  if (!aligned(out_acc, 16)) return fail(CP_ERR_INVALID, "out_acc must be 16-byte aligned");
+  const int64_t eb = dtype_bytes(a->dtype);
+  const int64_t qbytes = a->batch * a->seqlen_q * a->heads_q * a->head_dim * eb;
+  const int64_t kbytes = a->batch * a->seqlen_k * a->heads_kv * a->head_dim * eb;
+  const int64_t abytes = a->batch * a->seqlen_q * a->heads_q * a->head_dim * 4;
+  const int64_t lbytes = a->batch * a->heads_q * a->seqlen_q * 4;
+  for (const void* in : {q, k, v}) {
+    const int64_t ib = (in == q) ? qbytes : kbytes;
+    if (overlaps(out_acc, abytes, in, ib) || overlaps(lse_acc, lbytes, in, ib))
+      return fail(CP_ERR_ALIAS, "out_acc/lse_acc overlap an input");
+  }
+  if (overlaps(out_acc, abytes, lse_acc, lbytes)) return fail(CP_ERR_ALIAS, "out_acc overlaps lse_acc");
+  hipError_t e;
+  if (a->dtype == CP_DTYPE_BF16) {
+    e = cp::launch_attn_fwd_merge_bf16(p, q, k, v, out_acc, lse_acc, stream);
+  } else {
+    e = cp::launch_attn_fwd_merge_f32(p, static_cast<const float*>(q), static_cast<const float*>(k),
+                                      static_cast<const float*>(v), out_acc, lse_acc, stream);
+  }
+  return hip_status(e, "cp_attn_fwd_merge launch");
+}
+
 size_t cp_attn_bwd_workspace_size(const cp_attn_args_t* a) {
   if (!a || a->batch < 1 || a->heads_q < 1 || a->seqlen_q < 1) return 0;
   const size_t n = size_t(a->batch) * size_t(a->heads_q) * size_t(a->seqlen_q) * sizeof(float);

@@ -57,14 +57,12 @@ struct FwdCfg {
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
 };
 
-template <class C>
-__global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_mfma_kernel(AttnProblem p,
-                                                                       const uint16_t* __restrict__ q,
-                                                                       const uint16_t* __restrict__ k,
-                                                                       const uint16_t* __restrict__ v,
-                                                                       uint16_t* __restrict__ out,
-                                                                       float* __restrict__ lse) {
-  __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
+// kMerge = false: write out (bf16) and lse.  kMerge = true (fused ring step): merge
+// the block's float32 result into acc [B,Sq,Hq,D] and lse (= lse_acc) in place.
+template <class C, bool kMerge>
+CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                        const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ acc,
+                        float* __restrict__ lse, uint8_t* smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -237,45 +235,100 @@ __global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_mfma_kernel(AttnProbl
     }
   }
 
-  // ---- epilogue: normalise, store out (bf16) and lse (natural log)
+  // ---- epilogue: normalise; store out (bf16) and lse (natural log), or merge
   const float lt = l + other_half(l);
   if (!row_ok) return;
   const bool any = lt > 0.0f;
   const float inv = any ? 1.0f / lt : 0.0f;
-  uint16_t* orow = out + ((int64_t(b) * p.Sq + row) * p.Hq + h) * C::D;
+  const float lse_blk = any ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  const int64_t li = (int64_t(b) * p.Hq + h) * p.Sq + row;
+  const int64_t orow = ((int64_t(b) * p.Sq + row) * p.Hq + h) * C::D;
+  if constexpr (kMerge) {
+    // both 32-lane halves read the row's old lse before either writes the new one
+    const MergeWeights w = merge_weights(lse[li], lse_blk);
+    const float fb = w.wb * inv;
+    float* arow = acc + orow;
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x16& a = o[db];
-      const u32x2 w{pack_bf16x2(a[4 * j] * inv, a[4 * j + 1] * inv),
-                    pack_bf16x2(a[4 * j + 2] * inv, a[4 * j + 3] * inv)};
-      *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * j + 4 * hi) = w;
-    }
-  if (hi == 0) lse[(int64_t(b) * p.Hq + h) * p.Sq + row] = any ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+      for (int j = 0; j < 4; ++j) {
+        const f32x16& a = o[db];
+        f32x4* dst = reinterpret_cast<f32x4*>(arow + db * 32 + 8 * j + 4 * hi);
+        const f32x4 old = *dst;
+        *dst = f32x4{old[0] * w.wa + a[4 * j] * fb, old[1] * w.wa + a[4 * j + 1] * fb,
+                     old[2] * w.wa + a[4 * j + 2] * fb, old[3] * w.wa + a[4 * j + 3] * fb};
+      }
+    if (hi == 0) lse[li] = w.lse;
+  } else {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x16& a = o[db];
+        const u32x2 wv{pack_bf16x2(a[4 * j] * inv, a[4 * j + 1] * inv),
+                       pack_bf16x2(a[4 * j + 2] * inv, a[4 * j + 3] * inv)};
+        *reinterpret_cast<u32x2*>(out + orow + db * 32 + 8 * j + 4 * hi) = wv;
+      }
+    if (hi == 0) lse[li] = lse_blk;
+  }
 }
 
 template <class C>
+__global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_mfma_kernel(AttnProblem p, const uint16_t* q,
+                                                                       const uint16_t* k, const uint16_t* v,
+                                                                       uint16_t* out, float* lse) {
+  __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
+  fwd_body<C, false>(p, q, k, v, out, nullptr, lse, smem);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_merge_mfma_kernel(AttnProblem p, const uint16_t* q,
+                                                                             const uint16_t* k,
+                                                                             const uint16_t* v, float* acc,
+                                                                             float* lse_acc) {
+  __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
+  fwd_body<C, true>(p, q, k, v, nullptr, acc, lse_acc, smem);
+}
+
+template <class C, bool kMerge>
 hipError_t launch_cfg(const AttnProblem& p, const void* q, const void* k, const void* v, void* out,
-                      float* lse, hipStream_t s) {
+                      float* acc, float* lse, hipStream_t s) {
   const unsigned n = unsigned((p.Sq + C::kRows - 1) / C::kRows) * unsigned(p.Hq * p.B);
-  ProfScope ps(s, kProfFwdMfma);
-  hipLaunchKernelGGL(attn_fwd_mfma_kernel<C>, dim3(n), dim3(C::kThreads), 0, s, p,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), lse);
+  const auto* qq = static_cast<const uint16_t*>(q);
+  const auto* kk = static_cast<const uint16_t*>(k);
+  const auto* vv = static_cast<const uint16_t*>(v);
+  if constexpr (kMerge) {
+    ProfScope ps(s, kProfFwdMergeMfma);
+    hipLaunchKernelGGL(attn_fwd_merge_mfma_kernel<C>, dim3(n), dim3(C::kThreads), 0, s, p, qq, kk, vv, acc, lse);
+  } else {
+    ProfScope ps(s, kProfFwdMfma);
+    hipLaunchKernelGGL(attn_fwd_mfma_kernel<C>, dim3(n), dim3(C::kThreads), 0, s, p, qq, kk, vv,
+                       static_cast<uint16_t*>(out), lse);
+  }
   return hipGetLastError();
+}
+
+template <bool kMerge>
+hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const void* v, void* out,
+                    float* acc, float* lse, hipStream_t s) {
+  switch (p.D) {
+    case 128: return launch_cfg<FwdCfg<128, 4, 64>, kMerge>(p, q, k, v, out, acc, lse, s);
+    case 64: return launch_cfg<FwdCfg<64, 4, 64>, kMerge>(p, q, k, v, out, acc, lse, s);
+    case 32: return launch_cfg<FwdCfg<32, 4, 64>, kMerge>(p, q, k, v, out, acc, lse, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
                                 void* out, float* lse, hipStream_t s) {
-  switch (p.D) {
-    case 128: return launch_cfg<FwdCfg<128, 4, 64>>(p, q, k, v, out, lse, s);
-    case 64: return launch_cfg<FwdCfg<64, 4, 64>>(p, q, k, v, out, lse, s);
-    case 32: return launch_cfg<FwdCfg<32, 4, 64>>(p, q, k, v, out, lse, s);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_d<false>(p, q, k, v, out, nullptr, lse, s);
+}
+
+hipError_t launch_attn_fwd_merge_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
+                                      float* acc, float* lse_acc, hipStream_t s) {
+  return launch_d<true>(p, q, k, v, nullptr, acc, lse_acc, s);
 }
 
 }  // namespace cp

@@ -23,7 +23,9 @@ constexpr int kThreads = 64 * kWaves;
 CP_DEVICE int qpos_of(const AttnProblem& p, int i) { return p.q_pos ? p.q_pos[i] : p.q_offset + i; }
 CP_DEVICE int kpos_of(const AttnProblem& p, int j) { return p.k_pos ? p.k_pos[j] : p.k_offset + j; }
 
-template <typename T, int NT>  // NT = ceil(D / 64) elements per lane
+// NT = ceil(D / 64) elements per lane.  kMerge = true (fused ring step): out is the
+// float32 accumulator and lse the accumulator's lse, merged in place.
+template <typename T, int NT, bool kMerge>
 __global__ __launch_bounds__(kThreads) void fwd_rowwise_kernel(AttnProblem p, const T* __restrict__ q,
                                                                const T* __restrict__ k,
                                                                const T* __restrict__ v,
@@ -72,12 +74,26 @@ __global__ __launch_bounds__(kThreads) void fwd_rowwise_kernel(AttnProblem p, co
   }
   T* orow = out + ((int64_t(b) * p.Sq + i) * p.Hq + h) * D;
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  const float lse_blk = l > 0.0f ? m + logf(l) : -INFINITY;
+  const int64_t li = (int64_t(b) * p.Hq + h) * p.Sq + i;
+  if constexpr (kMerge) {
+    static_assert(sizeof(T) == 4, "the accumulator is float32");
+    // every lane reads the old lse (one wave-wide load) before lane 0 writes it
+    const MergeWeights w = merge_weights(lse[li], lse_blk);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int d = lane + 64 * t;
-    if (d < D) Elem<T>::store(orow + d, acc[t] * inv);
+    for (int t = 0; t < NT; ++t) {
+      const int d = lane + 64 * t;
+      if (d < D) orow[d] = orow[d] * w.wa + acc[t] * inv * w.wb;
+    }
+    if (lane == 0) lse[li] = w.lse;
+  } else {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int d = lane + 64 * t;
+      if (d < D) Elem<T>::store(orow + d, acc[t] * inv);
+    }
+    if (lane == 0) lse[li] = lse_blk;
   }
-  if (lane == 0) lse[(int64_t(b) * p.Hq + h) * p.Sq + i] = l > 0.0f ? m + logf(l) : -INFINITY;
 }
 
 // Delta[b,h,i] = sum_d dO[b,i,h,d] * O[b,i,h,d]; one wavefront per row.
@@ -241,12 +257,12 @@ __global__ __launch_bounds__(kThreads) void dkdv_rowwise_kernel(AttnProblem p, c
   }
 }
 
-template <typename T, int NT>
+template <typename T, int NT, bool kMerge>
 hipError_t fwd_nt(const AttnProblem& p, const T* q, const T* k, const T* v, T* out, float* lse,
                   hipStream_t s) {
   dim3 grid((p.Sq + kWaves - 1) / kWaves, p.Hq, p.B);
-  ProfScope ps(s, kProfFwdRowwise);
-  hipLaunchKernelGGL((fwd_rowwise_kernel<T, NT>), grid, dim3(kThreads), 0, s, p, q, k, v, out, lse);
+  ProfScope ps(s, kMerge ? kProfFwdMergeRowwise : kProfFwdRowwise);
+  hipLaunchKernelGGL((fwd_rowwise_kernel<T, NT, kMerge>), grid, dim3(kThreads), 0, s, p, q, k, v, out, lse);
   return hipGetLastError();
 }
 
@@ -269,7 +285,14 @@ hipError_t bwd_nt(const AttnProblem& p, const T* q, const T* k, const T* v, cons
 
 hipError_t launch_attn_fwd_f32(const AttnProblem& p, const float* q, const float* k, const float* v,
                                float* out, float* lse, hipStream_t s) {
-  return p.D <= 64 ? fwd_nt<float, 1>(p, q, k, v, out, lse, s) : fwd_nt<float, 2>(p, q, k, v, out, lse, s);
+  return p.D <= 64 ? fwd_nt<float, 1, false>(p, q, k, v, out, lse, s)
+                   : fwd_nt<float, 2, false>(p, q, k, v, out, lse, s);
+}
+
+hipError_t launch_attn_fwd_merge_f32(const AttnProblem& p, const float* q, const float* k, const float* v,
+                                     float* acc, float* lse_acc, hipStream_t s) {
+  return p.D <= 64 ? fwd_nt<float, 1, true>(p, q, k, v, acc, lse_acc, s)
+                   : fwd_nt<float, 2, true>(p, q, k, v, acc, lse_acc, s);
 }
 
 hipError_t launch_attn_bwd_f32(const AttnProblem& p, const float* q, const float* k, const float* v,

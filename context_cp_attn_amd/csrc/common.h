@@ -56,4 +56,23 @@ CP_DEVICE bool pair_visible(const MaskSpec& m, int qp, int kp, int qs, int ks) {
   return c & s & w;
 }
 
+// Log-sum-exp merge of two parts of a row (handbook "Context parallelism: Ring
+// Attention and Ulysses", self-test answers and the ring merge): the merged
+// lse = log(e^la + e^lb) and the weights e^(la - lse), e^(lb - lse) of the parts.  A
+// part with lse -inf has weight 0; both -inf gives lse = -inf and weights 0.
+struct MergeWeights {
+  float lse, wa, wb;
+};
+CP_DEVICE MergeWeights merge_weights(float la, float lb) {
+  const float mx = fmaxf(la, lb);
+  MergeWeights r{mx, 0.0f, 0.0f};
+  if (mx != -INFINITY) {
+    // computed from the larger part, so it cannot overflow
+    r.lse = mx + log1pf(__expf(fminf(la, lb) - mx));
+    r.wa = la == -INFINITY ? 0.0f : __expf(la - r.lse);
+    r.wb = lb == -INFINITY ? 0.0f : __expf(lb - r.lse);
+  }
+  return r;
+}
+
 }  // namespace cp

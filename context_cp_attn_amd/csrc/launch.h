@@ -24,6 +24,11 @@ hipError_t launch_attn_fwd_bf16(const AttnProblem& p, const void* q, const void*
                                 void* out, float* lse, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const AttnProblem& p, const float* q, const float* k, const float* v,
                                float* out, float* lse, hipStream_t s);
+// fused ring step: the block's result merged into acc [B,Sq,Hq,D] / lse_acc in place
+hipError_t launch_attn_fwd_merge_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
+                                      float* acc, float* lse_acc, hipStream_t s);
+hipError_t launch_attn_fwd_merge_f32(const AttnProblem& p, const float* q, const float* k, const float* v,
+                                     float* acc, float* lse_acc, hipStream_t s);
 
 // backward: delta workspace is [B,Hq,Sq] float32
 hipError_t launch_attn_bwd_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,

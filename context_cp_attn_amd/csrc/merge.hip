@@ -17,11 +17,6 @@ constexpr int kThreads = 256;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
-// weight of a part with log-sum-exp l in a merged row with log-sum-exp m
-CP_DEVICE float part_weight(float l, float m) {
-  return (l == -INFINITY) ? 0.0f : __expf(l - m);
-}
-
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(float* __restrict__ acc,
                                                              float* __restrict__ lse_acc,
@@ -38,17 +33,8 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(float* __restrict__
   const int s = int(bs % S);
   const int64_t b = bs / S;
   const int64_t li = (b * H + h) * int64_t(S) + s;  // lse index [b][h][s]
-  const float la = lse_acc[li];
-  const float lb = lse_blk[li];
-  // log(e^la + e^lb) computed from the larger part; -inf only if both are -inf
-  const float mx = fmaxf(la, lb);
-  float m = mx;
-  if (mx != -INFINITY) m = mx + log1pf(__expf(fminf(la, lb) - mx));
-  float wa = 0.0f, wb = 0.0f;
-  if (m != -INFINITY) {
-    wa = part_weight(la, m);
-    wb = part_weight(lb, m);
-  }
+  const MergeWeights w = merge_weights(lse_acc[li], lse_blk[li]);
+  const float wa = w.wa, wb = w.wb;
   f32x4 a = *reinterpret_cast<const f32x4*>(acc + t * 4);
   f32x4 x;
   if constexpr (kBf16) {
@@ -63,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(float* __restrict__
   o.z = a.z * wa + x.z * wb;
   o.w = a.w * wa + x.w * wb;
   *reinterpret_cast<f32x4*>(acc + t * 4) = o;
-  if (c == 0) lse_acc[li] = m;
+  if (c == 0) lse_acc[li] = w.lse;
 }
 
 }  // namespace

@@ -17,6 +17,8 @@ enum ProfKernel : int {
   kProfUlysses,         // sequence -> head relayout
   kProfUlyssesInv,      // head -> sequence relayout
   kProfZigzag,          // zigzag reorder (either direction)
+  kProfFwdMergeMfma,    // bf16 forward with the ring merge fused into its epilogue
+  kProfFwdMergeRowwise, // float32 forward with the fused ring merge
   kProfCount
 };
 

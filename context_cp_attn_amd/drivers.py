@@ -50,9 +50,10 @@ class RingShare:
     """
 
     def __init__(self, q, k, v, P: int, rank: int, layout="zigzag", seg=None, causal=True,
-                 window=0, scale=0.0):
+                 window=0, scale=0.0, fused=True):
         self.q, self.k, self.v, self.seg = q, k, v, seg
         self.P, self.rank, self.layout = P, rank, layout
+        self.fused = fused  # merge inside the attention epilogue (else attn_fwd + lse_merge)
         self.S = q.shape[1]
         self.C = self.S // P
         self.mask = dict(causal=causal, window=window, scale=scale)
@@ -78,15 +79,19 @@ class RingShare:
         B, _, Hq, D = ql.shape
         acc = torch.zeros(B, C, Hq, D, device=ql.device, dtype=torch.float32)
         lse = torch.full((B, Hq, C), float("-inf"), device=ql.device, dtype=torch.float32)
-        blk_o = torch.empty(B, C, Hq, D, device=ql.device, dtype=ql.dtype)
-        blk_l = torch.empty(B, Hq, C, device=ql.device, dtype=torch.float32)
+        if not self.fused:
+            blk_o = torch.empty(B, C, Hq, D, device=ql.device, dtype=ql.dtype)
+            blk_l = torch.empty(B, Hq, C, device=ql.device, dtype=torch.float32)
         for step in range(P):
             src = (r - step) % P
             if self._skip(src):
                 continue
-            ops.attn_fwd(ql, _block(self.k, src, C), _block(self.v, src, C), out=blk_o, lse=blk_l,
-                         **self._mask(src))
-            ops.lse_merge(acc, lse, blk_o, blk_l)
+            kb, vb = _block(self.k, src, C), _block(self.v, src, C)
+            if self.fused:
+                ops.attn_fwd_merge(ql, kb, vb, acc, lse, **self._mask(src))
+            else:
+                ops.attn_fwd(ql, kb, vb, out=blk_o, lse=blk_l, **self._mask(src))
+                ops.lse_merge(acc, lse, blk_o, blk_l)
         return acc, lse
 
     def backward(self, out, lse, dout, dq, dk, dv):
@@ -105,7 +110,8 @@ class RingShare:
 
 
 def ring_forward_all(q, k, v, P, layout="zigzag", seg=None, **mask):
-    """Every rank's ring forward; returns per-rank (out fp32, lse)."""
+    """Every rank's ring forward; returns per-rank (out fp32, lse).  mask may hold
+    ``fused`` (default True)."""
     return [RingShare(q, k, v, P, r, layout, seg, **mask).forward() for r in range(P)]
 
 

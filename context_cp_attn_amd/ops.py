@@ -85,6 +85,25 @@ def attn_fwd(q, k, v, *, out=None, lse=None, **mask):
     return out, lse
 
 
+def attn_fwd_merge(q, k, v, out_acc, lse_acc, **mask):
+    """Fused ring step, in place: (out_acc, lse_acc) <- merge((out_acc, lse_acc), attn_fwd(q, k, v)).
+
+    out_acc [B,Sq,Hq,D] fp32, lse_acc [B,Hq,Sq] fp32; the block result is merged in
+    fp32.  Same mask keywords as attn_fwd.
+    """
+    _check_qkv(q, k, v)
+    a = make_args(q, k, **mask)
+    B, Sq, Hq, _ = q.shape
+    _dev(out_acc, "out_acc", torch.float32)
+    _dev(lse_acc, "lse_acc", torch.float32)
+    if out_acc.shape != q.shape or lse_acc.shape != (B, Hq, Sq):
+        raise ValueError("out_acc/lse_acc shape mismatch")
+    lib = _lib.load()
+    _lib.check(lib.cp_attn_fwd_merge(ctypes.byref(a), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     out_acc.data_ptr(), lse_acc.data_ptr(), _stream()))
+    return out_acc, lse_acc
+
+
 def bwd_workspace(q, k, **mask) -> torch.Tensor:
     a = make_args(q, k, **mask)
     n = _lib.load().cp_attn_bwd_workspace_size(ctypes.byref(a))

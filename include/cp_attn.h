@@ -82,6 +82,22 @@ typedef struct {
 cp_status_t cp_attn_fwd(const cp_attn_args_t* args, const void* q, const void* k, const void* v,
                         void* out, float* lse, hipStream_t stream);
 
+/*
+ * Fused ring step ([H] §"Ring Attention": each step's block attention folded into
+ * the running result; the merge of cp_lse_merge moved into the attention epilogue).
+ * Computes the attention of q against k/v exactly as cp_attn_fwd, but instead of
+ * writing the block's out/lse it merges them, in float32 (the block output is not
+ * rounded to dtype), into the caller's running result in place:
+ *   lse' = log(e^lse_acc + e^lse_blk)
+ *   acc' = acc * e^(lse_acc - lse') + out_blk * e^(lse_blk - lse')
+ * with the -inf rules of cp_lse_merge (a row with no visible key in this block has
+ * weight 0).  out_acc [B,Sq,Hq,D] float32 (16-byte aligned) and lse_acc [B,Hq,Sq]
+ * float32 are read and written; start a ring with out_acc = 0, lse_acc = -inf.
+ * out_acc/lse_acc must not overlap q, k, v or each other (CP_ERR_ALIAS).
+ */
+cp_status_t cp_attn_fwd_merge(const cp_attn_args_t* args, const void* q, const void* k, const void* v,
+                              float* out_acc, float* lse_acc, hipStream_t stream);
+
 /* Workspace bytes cp_attn_bwd needs for args (the per-row dO.O sums). */
 size_t cp_attn_bwd_workspace_size(const cp_attn_args_t* args);
 

@@ -80,6 +80,22 @@ def test_attn_fwd_alias_and_alignment():
     assert st == INVALID and "aligned" in err
 
 
+def test_attn_fwd_merge_rejects():
+    lib = _lib.load()
+
+    def call(a, acc=1 << 44, lacc=1 << 45, q=FAKE_A):
+        st = lib.cp_attn_fwd_merge(ctypes.byref(a), q, FAKE_B, FAKE_C, acc, lacc, None)
+        return st, lib.cp_last_error().decode()
+
+    assert call(args(batch=0))[0] == INVALID        # shared validation with cp_attn_fwd
+    st, err = call(args(), acc=0)
+    assert st == INVALID and "non-NULL" in err
+    st, err = call(args(), acc=(1 << 44) + 4)        # float32 accumulator read as 16-byte vectors
+    assert st == INVALID and "aligned" in err
+    assert call(args(), acc=FAKE_B)[0] == ALIAS      # accumulator over k
+    assert call(args(), lacc=(1 << 44) + 256)[0] == ALIAS  # lse_acc inside the accumulator
+
+
 def test_attn_bwd_workspace_and_alias():
     lib = _lib.load()
     a = args()

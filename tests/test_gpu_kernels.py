@@ -173,6 +173,33 @@ def test_attn_fwd(cp, name, dtype, D):
         assert np.all(o[empty] == 0)
 
 
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 16), (torch.float32, 128), (torch.bfloat16, 32),
+                                     (torch.bfloat16, 128)])
+def test_attn_fwd_merge(cp, name, dtype, D):
+    """Fused ring step = the oracle's merge of the oracle's block attention into a
+    running (acc, lse) that has -inf rows, finite rows and rows that stay empty."""
+    say(f"attn_fwd_merge {name} D={D} {dtype}")
+    (q, k, v, _), m = make_case(name, D, dtype, seed=6)
+    B, Sq, Hq, _ = q.shape
+    g = torch.Generator().manual_seed(7)
+    acc0 = torch.randn(B, Sq, Hq, D, generator=g)
+    lse0 = torch.randn(B, Hq, Sq, generator=g) * 2 + 3
+    lse0[..., ::5] = -float("inf")
+    acc0[lse0.transpose(1, 2) == -float("inf")] = 0.0   # a ring starts from acc = 0, lse = -inf
+    acc, lacc = acc0.cuda(), lse0.cuda()
+    cp.attn_fwd_merge(q.cuda(), k.cuda(), v.cuda(), acc, lacc, **to_dev(m))
+    blk_o, blk_l = oracle.attn_fwd(q, k, v, **oracle_mask(m))
+    ref_o, ref_l = oracle.lse_merge(f64(acc0), f64(lse0), blk_o, blk_l)
+    check_lse(lacc, ref_l, TOL[dtype]["lse"])
+    check_close(acc, ref_o, TOL[dtype]["out"], "merged out")
+    # and the unfused pair gives the same result within the bar
+    acc2, lacc2 = acc0.cuda(), lse0.cuda()
+    o, l = cp.attn_fwd(q.cuda(), k.cuda(), v.cuda(), **to_dev(m))
+    cp.lse_merge(acc2, lacc2, o, l)
+    check_close(acc, f64(acc2), TOL[dtype]["out"], "fused vs unfused")
+
+
 @pytest.mark.parametrize("name", ["causal_square", "offsets", "zigzag_pos", "packed_window", "empty_rows"])
 @pytest.mark.parametrize("dtype,D", [(torch.float32, 16), (torch.float32, 128), (torch.bfloat16, 64),
                                      (torch.bfloat16, 128)])
