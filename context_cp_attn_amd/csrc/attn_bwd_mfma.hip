@@ -186,8 +186,8 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
   };
   typename C::TileM tq, tg;
   const uint32_t qrs_bytes = uint32_t(qrs) * 2u;
-  tq.init(qrs_bytes);
-  tg.init(qrs_bytes);
+  tq.init(qrs_bytes, tid);
+  tg.init(qrs_bytes, tid);
   // per-query values of the next tile, fetched early by the first BM threads and
   // written to LDS after this tile's products
   float n_lse2 = INFINITY, n_delta = 0.0f;
@@ -388,8 +388,8 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
   };
   typename C::TileN tk, tv;
   const uint32_t krs_bytes = uint32_t(krs) * 2u;
-  tk.init(krs_bytes);
-  tv.init(krs_bytes);
+  tk.init(krs_bytes, tid);
+  tv.init(krs_bytes, tid);
   // stage: K rows, V rows, kpos, kseg
   auto ks_of = [&](uint8_t* base) { return reinterpret_cast<uint16_t*>(base); };
   auto vs_of = [&](uint8_t* base) { return ks_of(base) + C::kTileN; };

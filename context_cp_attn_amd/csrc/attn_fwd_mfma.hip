@@ -41,10 +41,14 @@ using namespace mfma;
 
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
-template <int D_, int NW_, int BN_>
+// NW row wavefronts (32 query rows each) per key group; NS key groups (1 or 2) that
+// take alternate live key tiles of the same rows and combine their partial softmax
+// states at the end (for grids too small to fill the chip with whole tiles).
+template <int D_, int NW_, int BN_, int NS_>
 struct FwdCfg {
-  static constexpr int D = D_, NW = NW_, BN = BN_;
-  static constexpr int kThreads = 64 * NW;
+  static constexpr int D = D_, NW = NW_, BN = BN_, NS = NS_;
+  static constexpr int kGroupThreads = 64 * NW;
+  static constexpr int kThreads = kGroupThreads * NS;
   static constexpr int kRows = 32 * NW;
   static constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
   static constexpr int KB = BN / 32;  // 32-key blocks of a tile
@@ -52,9 +56,12 @@ struct FwdCfg {
   static constexpr int PT = BN / 16;  // k-steps of O^T += V^T P^T
   static constexpr int kTileElems = BN * D;  // swizzled row-major K or V tile
   static constexpr int kStageBytes = 2 * kTileElems * 2 + BN * 2 * 4;  // K, V, kpos, kseg
-  static constexpr int kLdsBytes = 2 * kStageBytes;
-  using Tile = DmaTile<BN, D, kThreads>;
+  static constexpr int kLdsBytes = NS * 2 * kStageBytes;
+  // exchange of the second key group's (o, m, l) per lane, over the stages
+  static constexpr int kXchgBytes = NW * 64 * (DB * 16 + 2) * 4;
+  using Tile = DmaTile<BN, D, kGroupThreads>;
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
+  static_assert(NS == 1 || (NS == 2 && kXchgBytes <= kLdsBytes), "key groups");
 };
 
 // kMerge = false: write out (bf16) and lse.  kMerge = true (fused ring step): merge
@@ -68,6 +75,9 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const int grp = C::NS > 1 ? wave / C::NW : 0;  // key group
+  const int rw = wave % C::NW;                    // row wavefront within the group
+  const int gtid = tid % C::kGroupThreads;
 
   // heaviest query tiles of every (batch, head) first
   const int n_qt = (p.Sq + C::kRows - 1) / C::kRows;
@@ -79,7 +89,7 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
   const int b = bh / p.Hq;
   const int g = h / (p.Hq / p.Hkv);
   const int q0 = qt * C::kRows;
-  const int wq0 = q0 + wave * 32;
+  const int wq0 = q0 + rw * 32;
   const int64_t krs = int64_t(p.Hkv) * C::D;
 
   const uint16_t* kbase = k + int64_t(b) * p.Sk * krs + int64_t(g) * C::D;
@@ -123,8 +133,8 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
   };
   typename C::Tile tk, tv;
   const uint32_t krs_bytes = uint32_t(krs) * 2u;
-  tk.init(krs_bytes);
-  tv.init(krs_bytes);
+  tk.init(krs_bytes, gtid);
+  tv.init(krs_bytes, gtid);
   // stage layout: K tile, V tile (swizzled row-major), kpos, kseg
   auto stage_load = [&](int kt, uint8_t* stage) {
     uint16_t* ks = reinterpret_cast<uint16_t*>(stage);
@@ -134,29 +144,37 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     tk.load(kbase, krs_bytes, kt * C::BN, p.Sk, ks);
     tv.load(vbase, krs_bytes, kt * C::BN, p.Sk, vs);
     const int j0 = kt * C::BN;
-    for (int t = tid; t < C::BN; t += C::kThreads) {
+    for (int t = gtid; t < C::BN; t += C::kGroupThreads) {
       const int j = min(j0 + t, p.Sk - 1);
       kpos[t] = kpos_at(p, j);
       kseg[t] = kseg_at(p, b, j);
     }
   };
+  auto stage_of = [&](int buf) { return smem + (grp * 2 + buf) * C::kStageBytes; };
 
-  int cur = next_tile(0);
-  if (cur < n_kt) {
-    stage_load(cur, smem);
+  // Live tiles are taken in pairs (t0, t1): key group 0 multiplies t0, group 1 t1
+  // (with one group, t1 is unused).  Every wavefront walks the same pair sequence,
+  // so all of them meet the same barriers.
+  int t0 = next_tile(0);
+  int t1 = (C::NS > 1 && t0 < n_kt) ? next_tile(t0 + 1) : n_kt;
+  if (t0 < n_kt) {
+    int cur = grp == 0 ? t0 : t1;
+    if (cur < n_kt) stage_load(cur, stage_of(0));
     wait_all();
     __syncthreads();
     int buf = 0;
     const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
     while (true) {
-      const int nxt = next_tile(cur + 1);
-      const bool has_next = nxt < n_kt;
+      const int n0 = next_tile((C::NS > 1 && t1 < n_kt ? t1 : t0) + 1);
+      const int n1 = (C::NS > 1 && n0 < n_kt) ? next_tile(n0 + 1) : n_kt;
+      const int nxt = grp == 0 ? n0 : n1;
+      const bool has_next = n0 < n_kt;
       // the DMA of the next tile runs while this one is multiplied
-      if (has_next) stage_load(nxt, smem + (buf ^ 1) * C::kStageBytes);
+      if (nxt < n_kt) stage_load(nxt, stage_of(buf ^ 1));
 
-      const int wcls = wave_live ? tile_class(cur, wv_q) : kEmpty;
+      const int wcls = (wave_live && cur < n_kt) ? tile_class(cur, wv_q) : kEmpty;
       if (wcls != kEmpty) {
-        const uint8_t* stage = smem + buf * C::kStageBytes;
+        const uint8_t* stage = stage_of(buf);
         const uint16_t* ks_l = reinterpret_cast<const uint16_t*>(stage);
         const uint16_t* vs_l = ks_l + C::kTileElems;
         const int* kpos_l = reinterpret_cast<const int*>(vs_l + C::kTileElems);
@@ -230,9 +248,39 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
       wait_all();
       __syncthreads();
       if (!has_next) break;
+      t0 = n0;
+      t1 = n1;
       cur = nxt;
       buf ^= 1;
     }
+  }
+
+  if constexpr (C::NS > 1) {
+    // combine the two key groups' partial states of each row (same lane layout):
+    // m = max(m0, m1), o = o0 2^(m0-m) + o1 2^(m1-m), l likewise
+    float* xo = reinterpret_cast<float*>(smem) + rw * (C::DB * 16) * 64 + lane;
+    float* xm = reinterpret_cast<float*>(smem) + C::NW * (C::DB * 16) * 64 + rw * 64 + lane;
+    float* xl = xm + C::NW * 64;
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64] = o[db][r];
+      *xm = m;
+      *xl = l;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = *xm, l1 = *xl;
+    const float mn = fmaxf(m, m1);
+    const float a0 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+    const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mn);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xo[(db * 16 + r) * 64] * a1;
+    l = l * a0 + l1 * a1;
+    m = mn;
   }
 
   // ---- epilogue: normalise; store out (bf16) and lse (natural log), or merge
@@ -308,13 +356,38 @@ hipError_t launch_cfg(const AttnProblem& p, const void* q, const void* k, const 
   return hipGetLastError();
 }
 
+// Workgroup slots of the device at two workgroups per CU (cached per device).
+int wg_slots() {
+  static int slots[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (!slots[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    slots[dev] = 2 * cus;
+  }
+  return slots[dev];
+}
+
+// Fewer query tiles than two rounds of workgroup slots: split each tile's keys over
+// two wavefront groups, so the heaviest (causal) tiles no longer set the time.
+template <int D, bool kMerge>
+hipError_t launch_dim(const AttnProblem& p, const void* q, const void* k, const void* v, void* out,
+                      float* acc, float* lse, hipStream_t s) {
+  const int64_t tiles = int64_t((p.Sq + 127) / 128) * p.Hq * p.B;
+  if (tiles < 2 * int64_t(wg_slots()))
+    return launch_cfg<FwdCfg<D, 4, 64, 2>, kMerge>(p, q, k, v, out, acc, lse, s);
+  return launch_cfg<FwdCfg<D, 4, 64, 1>, kMerge>(p, q, k, v, out, acc, lse, s);
+}
+
 template <bool kMerge>
 hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const void* v, void* out,
                     float* acc, float* lse, hipStream_t s) {
   switch (p.D) {
-    case 128: return launch_cfg<FwdCfg<128, 4, 64>, kMerge>(p, q, k, v, out, acc, lse, s);
-    case 64: return launch_cfg<FwdCfg<64, 4, 64>, kMerge>(p, q, k, v, out, acc, lse, s);
-    case 32: return launch_cfg<FwdCfg<32, 4, 64>, kMerge>(p, q, k, v, out, acc, lse, s);
+    case 128: return launch_dim<128, kMerge>(p, q, k, v, out, acc, lse, s);
+    case 64: return launch_dim<64, kMerge>(p, q, k, v, out, acc, lse, s);
+    case 32: return launch_dim<32, kMerge>(p, q, k, v, out, acc, lse, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -244,11 +244,14 @@ struct DmaTile {
   static constexpr int kIter = (kChunks + NT - 1) / NT;
   static_assert(kChunks % 64 == 0 && NT % 64 == 0, "whole wavefronts");
   uint32_t voff[kIter];
+  int wbase;  // first thread of this wavefront within the NT loading threads
 
-  CP_DEVICE void init(uint32_t row_stride_bytes) {
+  // tid: this thread's index among the NT threads that load the tile together
+  CP_DEVICE void init(uint32_t row_stride_bytes, int tid) {
+    wbase = __builtin_amdgcn_readfirstlane(tid & ~63);
 #pragma unroll
     for (int it = 0; it < kIter; ++it) {
-      const int s = it * NT + int(threadIdx.x);
+      const int s = it * NT + tid;
       const int row = s / (D / 8), slot = s % (D / 8);
       voff[it] = uint32_t(row) * row_stride_bytes + uint32_t(slot ^ chunk_xor<D>(row)) * 16u;
     }
@@ -260,7 +263,7 @@ struct DmaTile {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const uint8_t*>(base) + skip, valid);
 #pragma unroll
     for (int it = 0; it < kIter; ++it) {
-      const int s0 = it * NT + (int(threadIdx.x) & ~63);  // first chunk of this wavefront
+      const int s0 = it * NT + wbase;  // first chunk of this wavefront
       if (kChunks % NT == 0 || s0 < kChunks)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, (__attribute__((address_space(3))) void*)(lds_tile + s0 * 8), 16, voff[it], 0, 0, 0);

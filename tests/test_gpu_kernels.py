@@ -222,6 +222,38 @@ def test_attn_bwd(cp, name, dtype, D):
         torch.testing.assert_close(a, 2 * b, rtol=1e-6, atol=1e-6)
 
 
+@pytest.mark.parametrize("many_tiles", [False, True])
+@pytest.mark.parametrize("masks", ["causal_offset", "packed_window"])
+def test_attn_fwd_grid_variants(cp, many_tiles, masks):
+    """The forward splits each query tile's keys over two wavefront groups when the
+    grid has fewer than 4 query tiles (of 128 rows) per CU, and runs whole tiles
+    otherwise; both variants against the oracle, plain and fused-merge, D=128."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    S, Hq, Hkv, D = 1000, 8, 2, 128
+    tiles_per_batch = ((S + 127) // 128) * Hq
+    B = -(-4 * cus // tiles_per_batch) if many_tiles else 1   # >= 4 tiles per CU, or far fewer
+    say(f"attn_fwd grid variant many_tiles={many_tiles} B={B} {masks}")
+    q, k, v = cp_inputs.normal_tensors([(B, S, Hq, D), (B, S, Hkv, D), (B, S, Hkv, D)], seed=8)
+    if masks == "causal_offset":
+        m = dict(q_offset=S // 3, k_offset=0)
+    else:
+        seg = cp_inputs.random_segment_ids(S, 60, 400, seed=9, batch=B)
+        m = dict(q_seg=seg, k_seg=seg, window=150)
+    dm = to_dev(m)
+    out, lse = cp.attn_fwd(q.cuda(), k.cuda(), v.cuda(), **dm)
+    acc = torch.zeros(B, S, Hq, D, device="cuda")
+    lacc = torch.full((B, Hq, S), float("-inf"), device="cuda")
+    cp.attn_fwd_merge(q.cuda(), k.cuda(), v.cuda(), acc, lacc, **dm)
+    # the oracle on a sample of batches (every batch element runs the same code)
+    bs = sorted({0, B - 1})
+    om = oracle_mask({k_: (v_[bs] if k_ in ("q_seg", "k_seg") else v_) for k_, v_ in m.items()})
+    ref_o, ref_l = oracle.attn_fwd(q[bs], k[bs], v[bs], **om)
+    check_lse(lse[bs], ref_l, 1e-3)
+    check_close(out[bs], ref_o, 1e-2, "out")
+    check_lse(lacc[bs], ref_l, 1e-3)
+    check_close(acc[bs], ref_o, 1e-2, "fused out")
+
+
 @pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)])
 def test_deterministic(cp, dtype, D):
     say(f"determinism {dtype} D={D}")
