@@ -30,38 +30,40 @@ template <> struct Vec<1> { using T = uint8_t; };
 
 // in [P][B][Sp][P][R] (source rank s, batch, row i, destination p, vector r)
 // out [P][B][P][Sp][R] (destination p, batch, source s, row i, vector r)
-// One grid slice per (p, b, s) output span of Sp*R vectors.
+// One grid slice per (s, b) input span of Sp*P*R vectors, read in order; every run of
+// R vectors goes to its destination rank's rows.
 template <typename V>
 __global__ __launch_bounds__(kThreads) void ulysses_fwd_kernel(const V* __restrict__ in,
                                                                V* __restrict__ out, int P, int B,
                                                                int Sp, int R, int blocks_per_span) {
   const int span = blockIdx.x / blocks_per_span;
   const int blk = blockIdx.x - span * blocks_per_span;
-  const int s = span % P;
-  const int pb = span / P;
-  const int b = pb % B;
-  const int p = pb / B;
-  // per-span counts fit in 32 bits (checked by the launcher)
-  const uint32_t n = uint32_t(Sp) * uint32_t(R);
-  const V* src = in + (int64_t(s) * B + b) * Sp * int64_t(P) * R + int64_t(p) * R;
-  V* dst = out + int64_t(span) * n;
+  const int s = span / B;
+  const int b = span - s * B;
   const uint32_t PR = uint32_t(P) * uint32_t(R);
+  const uint32_t n = uint32_t(Sp) * PR;  // fits in 32 bits (checked by the launcher)
+  const V* src = in + int64_t(span) * n;
+  // element (i, p, r) of the span goes to ((p*B + b)*P + s)*Sp*R + i*R + r
+  V* dst = out + (int64_t(b) * P + s) * Sp * int64_t(R);
+  const int64_t pstride = int64_t(B) * P * Sp * R;
   for (uint32_t base = uint32_t(blk) * kThreads * kVPT + threadIdx.x; base < n;
        base += uint32_t(blocks_per_span) * kThreads * kVPT) {
     V vals[kVPT];
 #pragma unroll
     for (int u = 0; u < kVPT; ++u) {
       const uint32_t idx = base + uint32_t(u) * kThreads;
-      if (idx < n) {
-        const uint32_t i = idx / uint32_t(R);
-        const uint32_t r = idx - i * uint32_t(R);
-        vals[u] = __builtin_nontemporal_load(src + int64_t(i) * PR + r);
-      }
+      if (idx < n) vals[u] = __builtin_nontemporal_load(src + idx);
     }
 #pragma unroll
     for (int u = 0; u < kVPT; ++u) {
       const uint32_t idx = base + uint32_t(u) * kThreads;
-      if (idx < n) __builtin_nontemporal_store(vals[u], dst + idx);
+      if (idx < n) {
+        const uint32_t i = idx / PR;
+        const uint32_t rem = idx - i * PR;
+        const uint32_t p = rem / uint32_t(R);
+        const uint32_t r = rem - p * uint32_t(R);
+        __builtin_nontemporal_store(vals[u], dst + int64_t(p) * pstride + int64_t(i) * R + r);
+      }
     }
   }
 }
@@ -164,8 +166,8 @@ hipError_t ulysses_vb(const void* in, void* out, int P, int B, int Sp, int64_t r
   const int R = int(run_bytes / VB);
   ProfScope ps(s, inverse ? kProfUlyssesInv : kProfUlysses);
   if (!inverse) {
-    const int64_t spans = int64_t(P) * B * P;
-    const int bps = blocks_for(spans, int64_t(Sp) * R);
+    const int64_t spans = int64_t(P) * B;
+    const int bps = blocks_for(spans, int64_t(Sp) * P * R);
     hipLaunchKernelGGL(ulysses_fwd_kernel<V>, dim3(unsigned(spans * bps)), dim3(kThreads), 0, s,
                        static_cast<const V*>(in), static_cast<V*>(out), P, B, Sp, R, bps);
   } else {
