@@ -59,6 +59,13 @@ def parse():
     return ap.parse_args()
 
 
+# every file the backward kernel is built from: the committed counter profile is used
+# only while its recorded hash of these still matches
+BWD_SOURCES = [os.path.join(ROOT, "context_cp_attn_amd", *p) for p in (
+    ("csrc", "attn_bwd_mfma.hip"), ("csrc", "mfma_common.h"), ("csrc", "common.h"), ("csrc", "launch.h"),
+    ("build.py",))]
+
+
 def sha_of(*paths):
     h = hashlib.sha256()
     for p in paths:
@@ -264,9 +271,7 @@ def main():
     bwd_ms = tr.results["attn_bwd_mfma"][0] / tr.results["attn_bwd_mfma"][1]
     fwd_ms = tr.results["attn_fwd_mfma"][0] / tr.results["attn_fwd_mfma"][1]
     rel_t = sum(tr.results[k_][0] for k_ in ("ulysses_relayout", "ulysses_relayout_inv")) / a.steps
-    src = os.path.join(ROOT, "context_cp_attn_amd", "csrc")
-    bwd_sha = sha_of(os.path.join(src, "attn_bwd_mfma.hip"), os.path.join(src, "mfma_common.h"),
-                     os.path.join(ROOT, "context_cp_attn_amd", "build.py"))
+    bwd_sha = sha_of(*BWD_SOURCES)
     if dom == "attn_bwd_mfma":
         ach = step.flops_bwd_rank / (bwd_ms * 1e-3) / 1e12
         roof = {"kernel": "attn_bwd_mfma", "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
