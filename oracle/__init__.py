@@ -14,8 +14,8 @@ Everything is a plain, slow restatement of what the pages define, in float64:
 * ``merge`` — the log-sum-exp merge of two partial attentions.
 * ``ulysses`` — the sequence<->head exchange of Ulysses, as the reshape /
   transpose / exchange steps of the handbook, for all ranks at once.
-* ``zigzag`` — the 2P-chunk zigzag (dual-chunk-swap) partition, its reorder and
-  the causal work counts.
+* ``zigzag`` — the 2P-chunk zigzag (dual-chunk-swap) and the striped partitions,
+  their reorders, the automatic choice between them and the causal work counts.
 * ``ring`` — ring attention per rank (forward and blockwise backward).
 
 Pins (checked by ``tests/test_oracle.py`` against facts other than the oracle's
@@ -26,5 +26,6 @@ from .attention import attn_fwd, attn_bwd, visible_mask  # noqa: F401
 from .merge import lse_merge  # noqa: F401
 from .ulysses import seq_to_head, head_to_seq, ulysses_relayout, ulysses_relayout_inv, ulysses_attn  # noqa: F401
 from .zigzag import (chunk_order, reorder, reorder_inv, rank_positions, rank_chunks,  # noqa: F401
-                     work, visible_pairs)
+                     work, visible_pairs, striped_order, reorder_striped, reorder_striped_inv,
+                     auto_strategy, DUAL_CHUNK_SWAP, STRIPED)
 from .ring import ring_fwd, ring_bwd, ring_block_counts  # noqa: F401

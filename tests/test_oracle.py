@@ -260,6 +260,44 @@ def test_reorder_roundtrip_and_layout():
         oracle.reorder(np.zeros((1, 30)), 4)
 
 
+def test_striped_layout_and_roundtrip():
+    S, P = 48, 4
+    x = np.arange(2 * S * 3).reshape(2, S, 3)
+    y = oracle.reorder_striped(x, P)
+    np.testing.assert_array_equal(oracle.reorder_striped_inv(y, P), x)
+    c = S // P
+    seen = []
+    for r in range(P):
+        pos = y[0, c * r:c * (r + 1), 0] // 3        # the tokens a contiguous split hands rank r
+        assert np.all(np.diff(pos) == P) and pos[0] == r   # striped: stride P from r
+        np.testing.assert_array_equal(pos, oracle.rank_positions(r, P, S, "striped"))
+        seen.extend(pos)
+    assert sorted(seen) == list(range(S))             # every token exactly once
+    assert oracle.auto_strategy(packed=True) == oracle.STRIPED
+    assert oracle.auto_strategy(packed=False) == oracle.DUAL_CHUNK_SWAP
+    with pytest.raises(ValueError):
+        oracle.reorder_striped(np.zeros((1, 30)), 4)
+
+
+@pytest.mark.parametrize("S,P", [(32, 4), (1024, 16), (96, 3)])
+def test_striped_exact_pairs_every_rank_every_step(S, P):
+    # query i of rank r sits at r + P*i, key j of block src at src + P*j: visible iff
+    # j < i, or j == i and src <= r
+    c = S // P
+    total = 0
+    for r in range(P):
+        qpos = oracle.rank_positions(r, P, S, "striped")
+        per_rank = 0
+        for s in range(P):
+            src = (r - s) % P
+            n = oracle.visible_pairs(qpos, oracle.rank_positions(src, P, S, "striped"))
+            assert n == c * (c - 1) // 2 + (c if src <= r else 0)
+            per_rank += n
+        assert per_rank == P * c * (c - 1) // 2 + c * (r + 1)
+        total += per_rank
+    assert total == S * (S + 1) // 2
+
+
 def test_ring_counts_match_handbook():
     g = GOLDEN["ring_block_counts"]
     assert oracle.ring_block_counts(g["P"], g["S"], "contiguous") == g["counts"]
@@ -267,7 +305,7 @@ def test_ring_counts_match_handbook():
     assert oracle.ring_block_counts(g["P"], g["S"], "zigzag") == [g["P"]] * g["P"]
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "striped"])
 def test_ring_equals_full_attention_toy(layout):
     q, k, v = cp_inputs.toy_qkv()
     ref_o, ref_l = oracle.attn_fwd(q, k, v)
@@ -276,12 +314,13 @@ def test_ring_equals_full_attention_toy(layout):
         np.testing.assert_allclose(l, ref_l[:, :, qpos], atol=1e-12)
 
 
-def test_ring_packed_window_gqa_equals_full():
+@pytest.mark.parametrize("layout", ["zigzag", "striped"])
+def test_ring_packed_window_gqa_equals_full(layout):
     S, Hq, Hkv, D, P = 48, 4, 2, 4, 3
     q, k, v = rnd(1, S, Hq, D, seed=26), rnd(1, S, Hkv, D, seed=27), rnd(1, S, Hkv, D, seed=28)
     seg = np.repeat([0, 1, 2, 3], [5, 20, 9, 14])[None]
     ref_o, ref_l = oracle.attn_fwd(q, k, v, q_seg=seg, k_seg=seg, window=6)
-    for qpos, o, l in oracle.ring_fwd(q, k, v, P, "zigzag", seg=seg, window=6):
+    for qpos, o, l in oracle.ring_fwd(q, k, v, P, layout, seg=seg, window=6):
         np.testing.assert_allclose(o, ref_o[:, qpos], atol=1e-12)
         np.testing.assert_allclose(l, ref_l[:, :, qpos], atol=1e-12)
 
@@ -361,7 +400,7 @@ def test_backward_invariants():
     np.testing.assert_allclose(dv.sum(axis=1), dout.reshape(B, S, Hkv, 2, D).sum(axis=(1, 3)), atol=1e-12)
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "striped"])
 def test_ring_backward_equals_full(layout):
     S, Hq, Hkv, D, P = 32, 4, 2, 4, 4
     q, k, v = rnd(1, S, Hq, D, seed=41), rnd(1, S, Hkv, D, seed=42), rnd(1, S, Hkv, D, seed=43)
