@@ -20,7 +20,8 @@ Legs timed in the same run (not part of value): the ring share of llama2-7b
 (2048 queries x 32 heads vs 16 zigzag KV blocks: the fused step with the merge in
 the attention epilogue, and the unfused fwd + merge pair), the 64K-token
 dual-chunk-swap reorder, and the packed + windowed 8K ring share (4 ranks x 4
-steps, fwd + merge + bwd).  The CPU oracle is timed on a bounded sample of the
+steps, fused fwd + merge, bwd; striped as chosen automatically for packed
+sequences, and dual-chunk-swap).  The CPU oracle is timed on a bounded sample of the
 step's attention rows (cpu_baseline).
 """
 
@@ -172,28 +173,30 @@ def legs(torch, cp, cp_inputs):
     out["reorder_64k_4096_bf16_cp4"] = {"avg_ms": round(zms / zn, 5),
                                         "gbps": round(2 * x.numel() * 2 / (zms / zn) / 1e6, 1)}
     del x, y
-    # packed + windowed ring share: 8K, 32 q / 8 kv heads, docs 256..4096, window 4096, cp=4
+    # packed + windowed ring share: 8K, 32 q / 8 kv heads, docs 256..4096, window 4096, cp=4,
+    # with the automatic strategy (striped for packed sequences) and with dual-chunk-swap
     S, Hq, Hkv, P = 8192, 32, 8, 4
     q, k, v, do = (t.cuda() for t in cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D),
                                                                (1, S, Hq, D)], seed=0))
     seg = cp_inputs.segment_ids(cp_inputs.doc_lengths(S)).cuda()
-    qz, kz, vz, dz = (cp.zigzag_reorder(t, P) for t in (q, k, v, do))
-    sz = cp.zigzag_reorder(seg, P)
-    shares = [cp.drivers.RingShare(qz, kz, vz, P, r, seg=sz, window=4096) for r in range(P)]
     C = S // P
+    for name, st in (("auto", cp.drivers.auto_strategy(packed=True)), ("dual_chunk_swap", 0)):
+        layout = cp.drivers.LAYOUT_OF_STRATEGY[st]
+        qz, kz, vz, dz, sz = (cp.zigzag_reorder(t, P, strategy=st) for t in (q, k, v, do, seg))
+        shares = [cp.drivers.RingShare(qz, kz, vz, P, r, layout=layout, seg=sz, window=4096) for r in range(P)]
 
-    def packed_pass():
-        dk = torch.zeros(kz.shape, device="cuda")
-        dv = torch.zeros(vz.shape, device="cuda")
-        for r, sh in enumerate(shares):
-            o, l = sh.forward()
-            ob = o.bfloat16()
-            dq = torch.zeros(1, C, Hq, D, device="cuda")
-            sh.backward(ob, l, dz[:, r * C:(r + 1) * C], dq, dk, dv)
+        def packed_pass():
+            dk = torch.zeros(kz.shape, device="cuda")
+            dv = torch.zeros(vz.shape, device="cuda")
+            for r, sh in enumerate(shares):
+                o, l = sh.forward()
+                ob = o.bfloat16()
+                dq = torch.zeros(1, C, Hq, D, device="cuda")
+                sh.backward(ob, l, dz[:, r * C:(r + 1) * C], dq, dk, dv)
 
-    packed_pass()
-    ms = timed(torch, packed_pass, 3)
-    out["packed_window_8k_cp4_all_ranks"] = {"ms_per_pass": round(ms, 3)}
+        packed_pass()
+        ms = timed(torch, packed_pass, 3)
+        out[f"packed_window_8k_cp4_all_ranks_{name}"] = {"strategy": layout, "ms_per_pass": round(ms, 3)}
     return out
 
 

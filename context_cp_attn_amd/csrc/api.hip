@@ -295,17 +295,25 @@ cp_status_t cp_zigzag_reorder(const void* in, void* out, int64_t batch, int64_t 
                               int64_t row_bytes, int64_t P, int32_t strategy, int32_t inverse,
                               hipStream_t stream) {
   if (batch < 1 || seqlen < 1 || row_bytes < 1 || P < 1) return fail(CP_ERR_INVALID, "sizes must be >= 1");
-  if (strategy == 1) return fail(CP_ERR_UNSUPPORTED, "reorder strategy 1 (striped) is not built");
-  if (strategy != 0) return fail(CP_ERR_INVALID, "unknown reorder strategy %d", (int)strategy);
+  if (strategy != 0 && strategy != 1) return fail(CP_ERR_INVALID, "unknown reorder strategy %d", (int)strategy);
   if (inverse != 0 && inverse != 1) return fail(CP_ERR_INVALID, "inverse must be 0 or 1");
-  if (seqlen % (2 * P))
+  if (strategy == 0 && seqlen % (2 * P))
     return fail(CP_ERR_INVALID, "seqlen %lld is not divisible into 2P = %lld chunks", (long long)seqlen,
                 (long long)(2 * P));
+  if (strategy == 1 && seqlen % P)
+    return fail(CP_ERR_INVALID, "seqlen %lld is not divisible by P = %lld", (long long)seqlen, (long long)P);
   if (!in || !out) return fail(CP_ERR_INVALID, "NULL buffer");
   const int64_t bytes = batch * seqlen * row_bytes;
   if (overlaps(in, bytes, out, bytes)) return fail(CP_ERR_ALIAS, "in and out overlap");
-  if (batch * 2 * P >= (int64_t(1) << 31)) return fail(CP_ERR_UNSUPPORTED, "too many chunks");
-  return hip_status(cp::launch_zigzag(in, out, batch, seqlen, row_bytes, P, inverse != 0, stream),
+  if (strategy == 0) {
+    if (batch * 2 * P >= (int64_t(1) << 31)) return fail(CP_ERR_UNSUPPORTED, "too many chunks");
+    return hip_status(cp::launch_zigzag(in, out, batch, seqlen, row_bytes, P, inverse != 0, stream),
+                      "cp_zigzag_reorder launch");
+  }
+  // striped: rows (and so blocks) and row bytes below 2^31
+  if (row_bytes >= (int64_t(1) << 31) || batch * seqlen >= (int64_t(1) << 31))
+    return fail(CP_ERR_UNSUPPORTED, "striped reorder beyond 2^31 rows or 2^31-byte rows");
+  return hip_status(cp::launch_striped(in, out, batch, seqlen, row_bytes, P, inverse != 0, stream),
                     "cp_zigzag_reorder launch");
 }
 

@@ -45,5 +45,7 @@ hipError_t launch_ulysses(const void* in, void* out, int64_t P, int64_t B, int64
                           int64_t D, int64_t eb, bool inverse, hipStream_t s);
 hipError_t launch_zigzag(const void* in, void* out, int64_t B, int64_t S, int64_t row_bytes,
                          int64_t P, bool inverse, hipStream_t s);
+hipError_t launch_striped(const void* in, void* out, int64_t B, int64_t S, int64_t row_bytes, int64_t P,
+                          bool inverse, hipStream_t s);
 
 }  // namespace cp

@@ -1,5 +1,5 @@
-// Data-movement kernels: the Ulysses sequence<->head relayout of all simulated ranks
-// and the zigzag (dual-chunk-swap) reorder.  Both are permutations of contiguous
+// Data-movement kernels: the Ulysses sequence<->head relayout of all simulated ranks,
+// the zigzag (dual-chunk-swap) reorder and the striped reorder.  Both are permutations of contiguous
 // byte runs, so each is a streaming copy: every thread moves VPT vectors of VB bytes,
 // writes are fully coalesced in output order and reads are coalesced within a run.
 //
@@ -8,6 +8,8 @@
 // token: (H/P)*D elements.
 // Zigzag: the same handbook, §"The zigzag partition" (rank r takes chunks r and
 // 2P-1-r); a run is one chunk of S/(2P) token rows.
+// Striped: MaxText PR "Add Packing Support for Context Parallelism (Ring Attention)",
+// reorder strategy 1 (token t to rank t mod P); a run is one token row.
 #include "common.h"
 #include "launch.h"
 #include "prof.h"
@@ -141,6 +143,43 @@ __global__ __launch_bounds__(kThreads) void zigzag_kernel(const V* __restrict__ 
   }
 }
 
+// Striped reorder (token t -> rank t mod P; ranks' shares in rank order), c = S/P:
+// forward, output row r*c + j of a batch takes input row j*P + r; the inverse takes
+// it back.  Each block copies rows_per_block whole output rows (vector v of row o).
+template <typename V>
+__global__ __launch_bounds__(kThreads) void striped_kernel(const V* __restrict__ in, V* __restrict__ out,
+                                                           int S, int P, int RV, int rows_per_block,
+                                                           int64_t rows, int inverse) {
+  const int64_t row0 = int64_t(blockIdx.x) * rows_per_block;
+  const int c = S / P;
+  const int n = rows_per_block * RV;
+  for (int base = threadIdx.x; base < n; base += kThreads * kVPT) {
+    V vals[kVPT];
+    int64_t dst[kVPT];
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const int l = base + u * kThreads;
+      dst[u] = -1;
+      if (l < n) {
+        const int lr = l / RV;
+        const int v = l - lr * RV;
+        const int64_t o = row0 + lr;  // output row over all batches
+        if (o < rows) {
+          const int64_t b = o / S;
+          const int t = int(o - b * S);
+          // forward: t = r*c + j <- j*P + r; inverse: t = j*P + r <- r*c + j
+          const int src_t = inverse ? (t % P) * c + t / P : (t % c) * P + t / c;
+          vals[u] = __builtin_nontemporal_load(in + (b * S + src_t) * RV + v);
+          dst[u] = o * RV + v;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u)
+      if (dst[u] >= 0) __builtin_nontemporal_store(vals[u], out + dst[u]);
+  }
+}
+
 int pick_vec_bytes(int64_t run_bytes, const void* a, const void* b) {
   const uintptr_t al = reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b);
   for (int vb = 16; vb > 1; vb >>= 1)
@@ -192,7 +231,33 @@ hipError_t zigzag_vb(const void* in, void* out, int B, int P, int64_t chunk_byte
   return hipGetLastError();
 }
 
+template <int VB>
+hipError_t striped_vb(const void* in, void* out, int64_t B, int64_t S, int64_t row_bytes, int64_t P,
+                      bool inverse, hipStream_t s) {
+  using V = typename Vec<VB>::T;
+  const int RV = int(row_bytes / VB);
+  // whole rows per block, about kThreads * kVPT vectors each
+  const int rpb = RV >= kThreads * kVPT ? 1 : (kThreads * kVPT) / RV;
+  const int64_t rows = B * S;
+  const int64_t blocks = (rows + rpb - 1) / rpb;
+  ProfScope ps(s, kProfStriped);
+  hipLaunchKernelGGL(striped_kernel<V>, dim3(unsigned(blocks)), dim3(kThreads), 0, s, static_cast<const V*>(in),
+                     static_cast<V*>(out), int(S), int(P), RV, rpb, rows, inverse ? 1 : 0);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_striped(const void* in, void* out, int64_t B, int64_t S, int64_t row_bytes, int64_t P,
+                          bool inverse, hipStream_t s) {
+  switch (pick_vec_bytes(row_bytes, in, out)) {
+    case 16: return striped_vb<16>(in, out, B, S, row_bytes, P, inverse, s);
+    case 8: return striped_vb<8>(in, out, B, S, row_bytes, P, inverse, s);
+    case 4: return striped_vb<4>(in, out, B, S, row_bytes, P, inverse, s);
+    case 2: return striped_vb<2>(in, out, B, S, row_bytes, P, inverse, s);
+    default: return striped_vb<1>(in, out, B, S, row_bytes, P, inverse, s);
+  }
+}
 
 hipError_t launch_ulysses(const void* in, void* out, int64_t P, int64_t B, int64_t S, int64_t H,
                           int64_t D, int64_t eb, bool inverse, hipStream_t s) {

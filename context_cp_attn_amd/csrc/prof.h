@@ -19,6 +19,7 @@ enum ProfKernel : int {
   kProfZigzag,          // zigzag reorder (either direction)
   kProfFwdMergeMfma,    // bf16 forward with the ring merge fused into its epilogue
   kProfFwdMergeRowwise, // float32 forward with the fused ring merge
+  kProfStriped,         // striped reorder (either direction)
   kProfCount
 };
 

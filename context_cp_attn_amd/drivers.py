@@ -22,8 +22,21 @@ import torch
 from . import ops
 
 
+LAYOUT_OF_STRATEGY = {ops.DUAL_CHUNK_SWAP: "zigzag", ops.STRIPED: "striped"}
+
+
+def auto_strategy(packed: bool) -> int:
+    """Reorder strategy chosen automatically from the packing configuration (the
+    MaxText packing PR's AUTO): striped for packed sequences, else dual-chunk-swap."""
+    return ops.STRIPED if packed else ops.DUAL_CHUNK_SWAP
+
+
 def rank_positions(rank: int, P: int, S: int, layout: str = "zigzag", device="cuda") -> torch.Tensor:
     """int32 global positions of the tokens rank ``rank`` holds (increasing)."""
+    if layout == "striped":
+        if S % P:
+            raise ValueError(f"sequence {S} not divisible by {P} ranks")
+        return torch.arange(rank, S, P, dtype=torch.int32).to(device)
     if S % (2 * P):
         raise ValueError(f"sequence {S} not divisible into {2 * P} chunks")
     c = S // (2 * P)
@@ -44,8 +57,9 @@ def _block(t, r, C):
 class RingShare:
     """One rank's ring pass over P KV blocks, forward and backward.
 
-    q, k, v, seg are the whole tensors in the partition's order: for ``zigzag`` the
-    output of ``ops.zigzag_reorder``; for ``contiguous`` the sequence order.  Rank
+    q, k, v, seg are the whole tensors in the partition's order: for ``zigzag`` /
+    ``striped`` the output of ``ops.zigzag_reorder`` with that strategy; for
+    ``contiguous`` the sequence order.  Rank
     r's rows (queries and its own KV block) are slice r of length S/P.
     """
 

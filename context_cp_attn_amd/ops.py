@@ -180,8 +180,13 @@ def ulysses_relayout_inv(y, P, out=None):
     return out
 
 
-def zigzag_reorder(x, P, inverse=False, strategy=0, out=None):
-    """Zigzag (dual-chunk-swap) reorder of x [B][S][...] along S; inverse undoes it."""
+DUAL_CHUNK_SWAP, STRIPED = 0, 1
+
+
+def zigzag_reorder(x, P, inverse=False, strategy=DUAL_CHUNK_SWAP, out=None):
+    """Load-balancing reorder of x [B][S][...] along S into the P ranks' shares in rank
+    order; inverse undoes it.  strategy DUAL_CHUNK_SWAP (zigzag chunks r, 2P-1-r) or
+    STRIPED (tokens r, r+P, ...)."""
     _dev(x, "x")
     if x.dim() < 2:
         raise ValueError("x must be [B][S][...]")

@@ -149,13 +149,15 @@ cp_status_t cp_ulysses_relayout_inv(const void* in, void* out, int64_t P, int64_
                                     int64_t elem_bytes, hipStream_t stream);
 
 /*
- * Causal load-balancing reorder of whole token rows ([H] §"The zigzag partition";
- * [MP] reorder strategy 0 = DualChunkSwap).  in/out [B][S][row_bytes].  The sequence
- * is cut into 2P chunks of S/(2P) rows; the output is, for r = 0..P-1, chunk r then
- * chunk 2P-1-r, so a contiguous P-way split gives rank r its zigzag pair.
- * inverse = 1 undoes it.  S % (2P) == 0 else CP_ERR_INVALID; strategy other than 0
- * -> CP_ERR_UNSUPPORTED (1 = striped is not built) or CP_ERR_INVALID (unknown).
- * Bit-exact.  in and out must not overlap (CP_ERR_ALIAS).
+ * Causal load-balancing reorder of whole token rows.  in/out [B][S][row_bytes]; the
+ * output is the P ranks' shares in rank order, so a contiguous P-way split gives
+ * rank r its share.  inverse = 1 undoes it.  Bit-exact.
+ *   strategy 0 = DualChunkSwap ([H] §"The zigzag partition"; [MP] strategy 0): the
+ *     sequence is cut into 2P chunks of S/(2P) rows and rank r gets chunk r then
+ *     chunk 2P-1-r.  S % (2P) == 0 else CP_ERR_INVALID.
+ *   strategy 1 = Striped ([MP] strategy 1): token t goes to rank t mod P, so rank r
+ *     gets rows r, r+P, r+2P, ...  S % P == 0 else CP_ERR_INVALID.
+ * Another strategy -> CP_ERR_INVALID.  in and out must not overlap (CP_ERR_ALIAS).
  */
 cp_status_t cp_zigzag_reorder(const void* in, void* out, int64_t batch, int64_t seqlen,
                               int64_t row_bytes, int64_t P, int32_t strategy, int32_t inverse,

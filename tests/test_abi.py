@@ -127,7 +127,8 @@ def test_reorder_rejects():
     lib = _lib.load()
     f = lib.cp_zigzag_reorder
     assert f(FAKE_A, FAKE_B, 1, 30, 4, 4, 0, 0, None) == INVALID     # S % 2P
-    assert f(FAKE_A, FAKE_B, 1, 32, 4, 4, 1, 0, None) == UNSUPPORTED  # striped not built
+    assert f(FAKE_A, FAKE_B, 1, 30, 4, 4, 1, 0, None) == INVALID     # striped: S % P
+    assert f(FAKE_A, FAKE_A + 8, 1, 32, 4, 4, 1, 0, None) == ALIAS   # striped: overlap
     assert f(FAKE_A, FAKE_B, 1, 32, 4, 4, 5, 0, None) == INVALID     # unknown strategy
     assert f(FAKE_A, FAKE_B, 1, 32, 4, 4, 0, 3, None) == INVALID     # inverse flag
     assert f(FAKE_A, FAKE_A, 1, 32, 4, 4, 0, 0, None) == ALIAS

@@ -63,8 +63,9 @@ def test_toy_full_ring_ulysses_reorder(cp):
     o, l = cp.attn_fwd(qd, kd, vd)
     check_rows(f64(o), f64(l), ref_o, ref_l, 1e-5, 1e-5)
     # ring, both partitions
-    for layout in ("contiguous", "zigzag"):
-        src = [cp.zigzag_reorder(t, P) for t in (qd, kd, vd)] if layout == "zigzag" else [qd, kd, vd]
+    for layout in ("contiguous", "zigzag", "striped"):
+        st = {"zigzag": 0, "striped": 1}.get(layout)
+        src = [cp.zigzag_reorder(t, P, strategy=st) for t in (qd, kd, vd)] if st is not None else [qd, kd, vd]
         for r in range(P):
             acc, lse = cp.drivers.RingShare(*src, P, r, layout).forward()
             pos = oracle.rank_positions(r, P, S, layout)
@@ -81,7 +82,7 @@ def test_toy_full_ring_ulysses_reorder(cp):
     np.testing.assert_array_equal(bits(y), oracle.reorder(bits(q), P))
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "striped"])
 def test_toy_ring_backward(cp, layout):
     say(f"toy ring backward {layout}")
     q, k, v = cp_inputs.toy_qkv()
@@ -90,8 +91,9 @@ def test_toy_ring_backward(cp, layout):
     ref_o, ref_l = oracle.attn_fwd(q, k, v)
     rq, rk, rv = oracle.attn_bwd(q, k, v, ref_o, ref_l, do)
     dev = [t.cuda() for t in (q, k, v, do)]
-    if layout == "zigzag":
-        dev = [cp.zigzag_reorder(t, P) for t in dev]
+    st = {"zigzag": 0, "striped": 1}.get(layout)
+    if st is not None:
+        dev = [cp.zigzag_reorder(t, P, strategy=st) for t in dev]
     qd, kd, vd, dd = dev
     dk, dv = torch.zeros_like(kd), torch.zeros_like(vd)
     dq = torch.zeros_like(qd)
@@ -100,8 +102,8 @@ def test_toy_ring_backward(cp, layout):
         sh = cp.drivers.RingShare(qd, kd, vd, P, r, layout)
         o, l = sh.forward()
         sh.backward(o, l, dd[:, r * C:(r + 1) * C], dq[:, r * C:(r + 1) * C], dk, dv)
-    if layout == "zigzag":
-        dq, dk, dv = (cp.zigzag_reorder(t, P, inverse=True) for t in (dq, dk, dv))
+    if st is not None:
+        dq, dk, dv = (cp.zigzag_reorder(t, P, inverse=True, strategy=st) for t in (dq, dk, dv))
     for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
         assert max_err(f64(got), ref) <= 1e-5 * max(1.0, np.abs(ref).max())
 
@@ -212,34 +214,38 @@ def test_ulysses_llama31_8b_64k_gqa(cp):
 
 # ------------------------------------------------------------------ packed + windowed ring, 8K, cp=4
 
-def _packed_ring(cp, S, Hq, Hkv, D, P, W, lens):
+def _packed_ring(cp, S, Hq, Hkv, D, P, W, lens, strategy=0):
     q, k, v, do = cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D), (1, S, Hq, D)], seed=0)
     seg = cp_inputs.segment_ids(lens)
-    dev = [cp.zigzag_reorder(t.cuda(), P) for t in (q, k, v, do, seg)]
+    layout = cp.drivers.LAYOUT_OF_STRATEGY[strategy]
+    dev = [cp.zigzag_reorder(t.cuda(), P, strategy=strategy) for t in (q, k, v, do, seg)]
     qz, kz, vz, dz, sz = dev
     C = S // P
     outs, lses = [], []
     dq = torch.zeros(qz.shape, device="cuda")
     dk, dv = torch.zeros(kz.shape, device="cuda"), torch.zeros(vz.shape, device="cuda")
     for r in range(P):
-        sh = cp.drivers.RingShare(qz, kz, vz, P, r, seg=sz, window=W)
+        sh = cp.drivers.RingShare(qz, kz, vz, P, r, layout=layout, seg=sz, window=W)
         o, l = sh.forward()
         outs.append(o)
         lses.append(l)
         sh.backward(o.bfloat16(), l, dz[:, r * C:(r + 1) * C], dq[:, r * C:(r + 1) * C], dk, dv)
-    grads = [cp.zigzag_reorder(t, P, inverse=True) for t in (dq, dk, dv)]
+    grads = [cp.zigzag_reorder(t, P, inverse=True, strategy=strategy) for t in (dq, dk, dv)]
     return (q, k, v, do, seg), outs, lses, grads
 
 
-def test_packed_window_small_all_elements(cp):
+@pytest.mark.parametrize("strategy", ["dual_chunk_swap", "auto"])
+def test_packed_window_small_all_elements(cp, strategy):
     S, Hq, Hkv, D, P, W = 2048, 4, 2, 128, 4, 512
     lens = cp_inputs.doc_lengths(S, 64, 1024, seed=1)
-    say(f"packed+window small: docs {lens}")
-    (q, k, v, do, seg), outs, lses, grads = _packed_ring(cp, S, Hq, Hkv, D, P, W, lens)
+    st = cp.drivers.auto_strategy(packed=True) if strategy == "auto" else 0
+    layout = cp.drivers.LAYOUT_OF_STRATEGY[st]
+    say(f"packed+window small ({strategy} -> {layout}): docs {lens}")
+    (q, k, v, do, seg), outs, lses, grads = _packed_ring(cp, S, Hq, Hkv, D, P, W, lens, strategy=st)
     m = dict(q_seg=seg, k_seg=seg, window=W)
     ro, rl = oracle.attn_fwd(q, k, v, **m)
     for r in range(P):
-        pos = oracle.rank_positions(r, P, S, "zigzag")
+        pos = oracle.rank_positions(r, P, S, layout)
         check_rows(f64(outs[r]), f64(lses[r]), ro[:, pos], rl[:, :, pos], 1e-2, 1e-3)
     refs = oracle.attn_bwd(q, k, v, ro, rl, do, **m)
     for got, ref in zip(grads, refs):

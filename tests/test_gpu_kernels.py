@@ -76,21 +76,29 @@ def test_ulysses_relayout_bit_exact(cp, P, B, S, H, D, dtype):
     np.testing.assert_array_equal(bits(z), oracle.ulysses_relayout_inv(bits(y)))
 
 
+@pytest.mark.parametrize("strategy", [0, 1])
 @pytest.mark.parametrize("shape,P,dtype", [
     ((1, 65536), 4, torch.int32),
     ((2, 48, 3, 5), 3, torch.bfloat16),
     ((1, 32, 8, 16), 4, torch.float32),
     ((3, 40, 7), 5, torch.uint8),
+    ((1, 4096, 4096), 4, torch.bfloat16),
+    ((2, 30, 3), 5, torch.int32),
 ])
-def test_zigzag_reorder_bit_exact(cp, shape, P, dtype):
-    say(f"reorder {shape} P={P} {dtype}")
+def test_reorder_bit_exact(cp, shape, P, dtype, strategy):
+    """strategy 0 = dual-chunk-swap (zigzag), 1 = striped."""
+    if strategy == 0 and shape[1] % (2 * P):
+        pytest.skip("dual-chunk-swap needs S divisible by 2P")
+    say(f"reorder {shape} P={P} {dtype} strategy={strategy}")
     n = int(np.prod(shape))
     x = (torch.arange(n, dtype=torch.int64) * 2654435761 % 251).to(dtype).reshape(shape).cuda() \
         if dtype in (torch.int32, torch.uint8) else torch.randn(shape).to(dtype).cuda()
-    y = cp.zigzag_reorder(x, P)
-    np.testing.assert_array_equal(bits(y), oracle.reorder(bits(x), P))
-    z = cp.zigzag_reorder(y, P, inverse=True)
-    np.testing.assert_array_equal(bits(z), oracle.reorder_inv(bits(y), P))
+    fwd, inv = ((oracle.reorder, oracle.reorder_inv) if strategy == 0
+                else (oracle.reorder_striped, oracle.reorder_striped_inv))
+    y = cp.zigzag_reorder(x, P, strategy=strategy)
+    np.testing.assert_array_equal(bits(y), fwd(bits(x), P))
+    z = cp.zigzag_reorder(y, P, inverse=True, strategy=strategy)
+    np.testing.assert_array_equal(bits(z), inv(bits(y), P))
     assert torch.equal(z, x)
 
 
