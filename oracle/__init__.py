@@ -13,7 +13,8 @@ Everything is a plain, slow restatement of what the pages define, in float64:
   query heads; and its gradient (closed-form VJP).
 * ``merge`` — the log-sum-exp merge of two partial attentions.
 * ``ulysses`` — the sequence<->head exchange of Ulysses, as the reshape /
-  transpose / exchange steps of the handbook, for all ranks at once.
+  transpose / exchange steps of the handbook, for all ranks at once; kv-head
+  replication beyond the kv head count and the Ulysses x ring hybrid (USP).
 * ``zigzag`` — the 2P-chunk zigzag (dual-chunk-swap) and the striped partitions,
   their reorders, the automatic choice between them and the causal work counts.
 * ``ring`` — ring attention per rank (forward and blockwise backward).
@@ -24,7 +25,9 @@ own formulas) are listed in each module's docstring.
 
 from .attention import attn_fwd, attn_bwd, visible_mask  # noqa: F401
 from .merge import lse_merge  # noqa: F401
-from .ulysses import seq_to_head, head_to_seq, ulysses_relayout, ulysses_relayout_inv, ulysses_attn  # noqa: F401
+from .ulysses import (seq_to_head, head_to_seq, ulysses_relayout, ulysses_relayout_inv,  # noqa: F401
+                      ulysses_attn, ulysses_attn_bwd, replicate_heads, sum_replicas, ulysses_relayout_rep,
+                      ulysses_relayout_inv_sum, usp_relayout, usp_relayout_inv, usp_attn)
 from .zigzag import (chunk_order, reorder, reorder_inv, rank_positions, rank_chunks,  # noqa: F401
                      work, visible_pairs, striped_order, reorder_striped, reorder_striped_inv,
                      auto_strategy, DUAL_CHUNK_SWAP, STRIPED)

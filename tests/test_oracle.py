@@ -400,6 +400,59 @@ def test_backward_invariants():
     np.testing.assert_allclose(dv.sum(axis=1), dout.reshape(B, S, Hkv, 2, D).sum(axis=(1, 3)), atol=1e-12)
 
 
+@pytest.mark.parametrize("Hq,Hkv,P,rep", [(8, 2, 4, 2), (8, 2, 8, 4), (8, 4, 8, 2)])
+@pytest.mark.parametrize("masks", ["causal", "packed_window"])
+def test_ulysses_beyond_kv_heads_equals_full(Hq, Hkv, P, rep, masks):
+    """Degree P > kv heads with each kv head replicated rep times by group (handbook
+    exercise): forward and all three gradients equal full attention's."""
+    S, D = 32, 4
+    q, k, v, do = (rnd(1, S, h, D, seed=60 + i) for i, h in enumerate((Hq, Hkv, Hkv, Hq)))
+    m = {} if masks == "causal" else dict(q_seg=np.repeat([0, 1, 2], [9, 13, 10])[None],
+                                          k_seg=np.repeat([0, 1, 2], [9, 13, 10])[None], window=5)
+    ro, rl = oracle.attn_fwd(q, k, v, **m)
+    with pytest.raises(ValueError):
+        oracle.ulysses_attn(q, k, v, P, **m)           # not without replication
+    o, l, _ = oracle.ulysses_attn(q, k, v, P, kv_rep=rep, **m)
+    np.testing.assert_allclose(o, ro, atol=1e-12)
+    np.testing.assert_allclose(l, rl, atol=1e-12)
+    ref = oracle.attn_bwd(q, k, v, ro, rl, do, **m)
+    got = oracle.ulysses_attn_bwd(q, k, v, do, P, kv_rep=rep, **m)
+    for a, b in zip(got, ref):
+        np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+def test_replicate_and_sum_replicas():
+    x = rnd(2, 3, 4, 5, seed=70)
+    y = oracle.replicate_heads(x, 3)
+    assert y.shape == (2, 3, 12, 5)
+    for j in range(12):
+        np.testing.assert_array_equal(y[:, :, j], x[:, :, j // 3])   # head j is kv head j // rep
+    np.testing.assert_allclose(oracle.sum_replicas(y, 3), 3 * x)
+    st = rnd(4, 1, 8, 2, 3, seed=71)                                  # [P][B][S/P][H][D]
+    out = oracle.ulysses_relayout_rep(st, 2)                          # 4 heads over 4 ranks
+    assert out.shape == (4, 1, 32, 1, 3)
+    np.testing.assert_allclose(oracle.ulysses_relayout_inv_sum(out, 2), 2 * st)
+
+
+@pytest.mark.parametrize("Pr,Pu,rep,masks", [(2, 2, 1, "causal"), (2, 4, 2, "causal"), (4, 2, 1, "packed_window"),
+                                             (2, 2, 1, "noncausal")])
+def test_usp_equals_full(Pr, Pu, rep, masks):
+    """Ulysses within groups x zigzag ring across groups (USP) equals full attention."""
+    S, Hq, Hkv, D = 32, 8, 2 if rep > 1 else 4, 4
+    q, k, v = rnd(1, S, Hq, D, seed=72), rnd(1, S, Hkv, D, seed=73), rnd(1, S, Hkv, D, seed=74)
+    m = dict(causal=masks != "noncausal")
+    seg = None
+    if masks == "packed_window":
+        seg = np.repeat([0, 1, 2], [11, 7, 14])[None]
+        m.update(window=6)
+    ro, rl = oracle.attn_fwd(q, k, v, q_seg=seg, k_seg=seg, **m)
+    o, l = oracle.usp_attn(q, k, v, Pr, Pu, kv_rep=rep, seg=seg, **m)
+    np.testing.assert_allclose(o, ro, atol=1e-12)
+    np.testing.assert_allclose(l, rl, atol=1e-12)
+    st = rnd(Pr, Pu, 1, S // (Pr * Pu), Hq, D, seed=75)
+    np.testing.assert_array_equal(oracle.usp_relayout_inv(oracle.usp_relayout(st)), st)
+
+
 @pytest.mark.parametrize("layout", ["contiguous", "zigzag", "striped"])
 def test_ring_backward_equals_full(layout):
     S, Hq, Hkv, D, P = 32, 4, 2, 4, 4
