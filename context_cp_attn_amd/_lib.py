@@ -29,6 +29,15 @@ class AttnArgs(ctypes.Structure):
     ]
 
 
+class RelayoutArgs(ctypes.Structure):
+    """Mirror of cp_relayout_args_t."""
+
+    _fields_ = [
+        ("groups", c_i64), ("P", c_i64), ("batch", c_i64), ("seqlen", c_i64), ("heads", c_i64),
+        ("head_dim", c_i64), ("elem_bytes", c_i64), ("rep", c_i64), ("inverse", c_i32),
+    ]
+
+
 SIGNATURES = {
     "cp_attn_fwd": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "cp_attn_fwd_merge": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
@@ -39,6 +48,7 @@ SIGNATURES = {
     "cp_ulysses_relayout": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp]),
     "cp_ulysses_relayout_inv": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp]),
     "cp_zigzag_reorder": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp]),
+    "cp_ulysses_relayout_ex": (c_i32, [ctypes.POINTER(RelayoutArgs), c_vp, c_vp, c_vp]),
     "cp_prof_enable": (None, [c_i32]),
     "cp_prof_reset": (None, []),
     "cp_prof_kernel_count": (c_i32, []),

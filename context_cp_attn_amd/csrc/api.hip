@@ -256,39 +256,58 @@ cp_status_t cp_lse_merge(int64_t batch, int64_t seqlen, int64_t heads, int64_t h
                     "cp_lse_merge launch");
 }
 
-static cp_status_t relayout(const void* in, void* out, int64_t P, int64_t batch, int64_t seqlen,
-                            int64_t heads, int64_t head_dim, int64_t eb, bool inverse,
-                            hipStream_t stream) {
-  if (P < 1 || batch < 1 || seqlen < 1 || heads < 1 || head_dim < 1)
+static cp_status_t relayout(const cp_relayout_args_t* a, const void* in, void* out, hipStream_t stream) {
+  if (!a) return fail(CP_ERR_INVALID, "args is NULL");
+  const int64_t G = a->groups, P = a->P, batch = a->batch, seqlen = a->seqlen, heads = a->heads,
+                head_dim = a->head_dim, eb = a->elem_bytes, rep = a->rep;
+  if (G < 1 || P < 1 || batch < 1 || seqlen < 1 || heads < 1 || head_dim < 1 || rep < 1)
     return fail(CP_ERR_INVALID, "sizes must be >= 1");
   if (eb != 2 && eb != 4) return fail(CP_ERR_INVALID, "elem_bytes must be 2 or 4 (got %lld)", (long long)eb);
+  if (a->inverse != 0 && a->inverse != 1) return fail(CP_ERR_INVALID, "inverse must be 0 or 1");
   if (seqlen % P)
     return fail(CP_ERR_INVALID, "seqlen %lld is not divisible by the Ulysses degree %lld",
                 (long long)seqlen, (long long)P);
-  if (heads % P)
+  if ((heads * rep) % P)
     return fail(CP_ERR_INVALID,
-                "heads %lld is not divisible by the Ulysses degree %lld (the degree cannot exceed "
-                "the head count; for k/v, the kv head count)",
-                (long long)heads, (long long)P);
+                "heads %lld x rep %lld is not divisible by the Ulysses degree %lld (the degree cannot exceed "
+                "the head count -- for k/v the kv head count -- unless heads are replicated)",
+                (long long)heads, (long long)rep, (long long)P);
+  if (rep > 1 && a->inverse && eb != 4)
+    return fail(CP_ERR_INVALID, "the inverse with replicated heads sums float32 gradients (elem_bytes 4)");
   if (!in || !out) return fail(CP_ERR_INVALID, "NULL buffer");
-  const int64_t bytes = batch * seqlen * heads * head_dim * eb;
-  if (overlaps(in, bytes, out, bytes)) return fail(CP_ERR_ALIAS, "in and out overlap");
-  if ((seqlen / P) * heads * head_dim * eb >= (int64_t(1) << 31) || P * batch * P >= (int64_t(1) << 31))
-    return fail(CP_ERR_UNSUPPORTED, "relayout span exceeds 2^31 bytes");
-  return hip_status(cp::launch_ulysses(in, out, P, batch, seqlen, heads, head_dim, eb, inverse, stream),
-                    "cp_ulysses_relayout launch");
+  const int64_t seq_bytes = G * P * batch * (seqlen / P) * heads * head_dim * eb;  // sequence-sharded side
+  const int64_t head_bytes = seq_bytes * rep;                                      // head-sharded side
+  const int64_t in_bytes = a->inverse ? head_bytes : seq_bytes;
+  const int64_t out_bytes = a->inverse ? seq_bytes : head_bytes;
+  if (overlaps(in, in_bytes, out, out_bytes)) return fail(CP_ERR_ALIAS, "in and out overlap");
+  // one grid slice (32-bit element offsets) per source span [S/P][H] and destination
+  // span [S][H*rep/P]
+  const int64_t seq_span = (seqlen / P) * heads * head_dim * eb;
+  const int64_t head_span = seqlen * (heads * rep / P) * head_dim * eb;
+  if (seq_span >= (int64_t(1) << 31) || head_span >= (int64_t(1) << 31) || P * batch * P >= (int64_t(1) << 31) ||
+      G > 65535)
+    return fail(CP_ERR_UNSUPPORTED, "relayout span exceeds 2^31 bytes or more than 65535 groups");
+  const cp::RelayoutProblem r{G, P, batch, seqlen, heads, head_dim, eb, rep, a->inverse != 0};
+  return hip_status(cp::launch_relayout(r, in, out, stream), "cp_ulysses_relayout launch");
+}
+
+cp_status_t cp_ulysses_relayout_ex(const cp_relayout_args_t* args, const void* in, void* out,
+                                   hipStream_t stream) {
+  return relayout(args, in, out, stream);
 }
 
 cp_status_t cp_ulysses_relayout(const void* in, void* out, int64_t P, int64_t batch, int64_t seqlen,
                                 int64_t heads, int64_t head_dim, int64_t elem_bytes,
                                 hipStream_t stream) {
-  return relayout(in, out, P, batch, seqlen, heads, head_dim, elem_bytes, false, stream);
+  const cp_relayout_args_t a{1, P, batch, seqlen, heads, head_dim, elem_bytes, 1, 0};
+  return relayout(&a, in, out, stream);
 }
 
 cp_status_t cp_ulysses_relayout_inv(const void* in, void* out, int64_t P, int64_t batch,
                                     int64_t seqlen, int64_t heads, int64_t head_dim,
                                     int64_t elem_bytes, hipStream_t stream) {
-  return relayout(in, out, P, batch, seqlen, heads, head_dim, elem_bytes, true, stream);
+  const cp_relayout_args_t a{1, P, batch, seqlen, heads, head_dim, elem_bytes, 1, 1};
+  return relayout(&a, in, out, stream);
 }
 
 cp_status_t cp_zigzag_reorder(const void* in, void* out, int64_t batch, int64_t seqlen,

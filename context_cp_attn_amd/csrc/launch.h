@@ -41,8 +41,12 @@ hipError_t launch_attn_bwd_f32(const AttnProblem& p, const float* q, const float
 // data movement
 hipError_t launch_lse_merge(int64_t B, int64_t S, int64_t H, int64_t D, float* acc, float* lse_acc,
                             const void* blk, const float* lse_blk, int blk_is_bf16, hipStream_t s);
-hipError_t launch_ulysses(const void* in, void* out, int64_t P, int64_t B, int64_t S, int64_t H,
-                          int64_t D, int64_t eb, bool inverse, hipStream_t s);
+// Ulysses relayout of G independent groups (see cp_relayout_args_t); validated sizes.
+struct RelayoutProblem {
+  int64_t G, P, B, S, H, D, eb, rep;
+  bool inverse;
+};
+hipError_t launch_relayout(const RelayoutProblem& r, const void* in, void* out, hipStream_t s);
 hipError_t launch_zigzag(const void* in, void* out, int64_t B, int64_t S, int64_t row_bytes,
                          int64_t P, bool inverse, hipStream_t s);
 hipError_t launch_striped(const void* in, void* out, int64_t B, int64_t S, int64_t row_bytes, int64_t P,

@@ -22,6 +22,7 @@ constexpr int kVPT = 4;  // vectors per thread per pass: loads issued before sto
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int VB> struct Vec;
 template <> struct Vec<16> { using T = u32x4; };
@@ -37,11 +38,14 @@ template <> struct Vec<1> { using T = uint8_t; };
 template <typename V>
 __global__ __launch_bounds__(kThreads) void ulysses_fwd_kernel(const V* __restrict__ in,
                                                                V* __restrict__ out, int P, int B,
-                                                               int Sp, int R, int blocks_per_span) {
+                                                               int Sp, int R, int blocks_per_span,
+                                                               int64_t group_vecs) {
   const int span = blockIdx.x / blocks_per_span;
   const int blk = blockIdx.x - span * blocks_per_span;
   const int s = span / B;
   const int b = span - s * B;
+  in += int64_t(blockIdx.y) * group_vecs;  // independent groups (USP), stacked outermost
+  out += int64_t(blockIdx.y) * group_vecs;
   const uint32_t PR = uint32_t(P) * uint32_t(R);
   const uint32_t n = uint32_t(Sp) * PR;  // fits in 32 bits (checked by the launcher)
   const V* src = in + int64_t(span) * n;
@@ -75,11 +79,14 @@ __global__ __launch_bounds__(kThreads) void ulysses_fwd_kernel(const V* __restri
 template <typename V>
 __global__ __launch_bounds__(kThreads) void ulysses_inv_kernel(const V* __restrict__ in,
                                                                V* __restrict__ out, int P, int B,
-                                                               int Sp, int R, int blocks_per_span) {
+                                                               int Sp, int R, int blocks_per_span,
+                                                               int64_t group_vecs) {
   const int span = blockIdx.x / blocks_per_span;
   const int blk = blockIdx.x - span * blocks_per_span;
   const int s = span / B;
   const int b = span - s * B;
+  in += int64_t(blockIdx.y) * group_vecs;
+  out += int64_t(blockIdx.y) * group_vecs;
   const uint32_t PR = uint32_t(P) * uint32_t(R);
   const uint32_t n = uint32_t(Sp) * PR;  // fits in 32 bits (checked by the launcher)
   V* dst = out + int64_t(span) * n;
@@ -105,6 +112,83 @@ __global__ __launch_bounds__(kThreads) void ulysses_inv_kernel(const V* __restri
       const uint32_t idx = base + uint32_t(u) * kThreads;
       if (idx < n) __builtin_nontemporal_store(vals[u], dst + idx);
     }
+  }
+}
+
+// Relayout with every head replicated rep times (head j of the replicated set is
+// head j / rep; Hl = H*rep/P of them per destination): in [P][B][Sp][H][R1] ->
+// out [P][B][S][Hl][R1], written in output order (one grid slice per (p, b) span).
+template <typename V>
+__global__ __launch_bounds__(kThreads) void ulysses_rep_kernel(const V* __restrict__ in, V* __restrict__ out,
+                                                               int P, int B, int Sp, int H, int Hl, int rep,
+                                                               int R1, int blocks_per_span, int64_t group_in,
+                                                               int64_t group_out) {
+  const int span = blockIdx.x / blocks_per_span;
+  const int blk = blockIdx.x - span * blocks_per_span;
+  const int p = span / B;
+  const int b = span - p * B;
+  in += int64_t(blockIdx.y) * group_in;
+  const uint32_t HR = uint32_t(Hl) * uint32_t(R1);
+  const uint32_t n = uint32_t(Sp) * uint32_t(P) * HR;  // fits in 32 bits (checked by the launcher)
+  V* dst = out + int64_t(blockIdx.y) * group_out + int64_t(span) * n;
+  for (uint32_t base = uint32_t(blk) * kThreads * kVPT + threadIdx.x; base < n;
+       base += uint32_t(blocks_per_span) * kThreads * kVPT) {
+    V vals[kVPT];
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const uint32_t idx = base + uint32_t(u) * kThreads;
+      if (idx < n) {
+        const uint32_t row = idx / HR;
+        const uint32_t rem = idx - row * HR;
+        const uint32_t hh = rem / uint32_t(R1);
+        const uint32_t v = rem - hh * uint32_t(R1);
+        const uint32_t s = row / uint32_t(Sp);
+        const uint32_t i = row - s * uint32_t(Sp);
+        const uint32_t head = (uint32_t(p) * uint32_t(Hl) + hh) / uint32_t(rep);
+        vals[u] = __builtin_nontemporal_load(in + ((int64_t(s) * B + b) * Sp + i) * (int64_t(H) * R1) +
+                                             int64_t(head) * R1 + v);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const uint32_t idx = base + uint32_t(u) * kThreads;
+      if (idx < n) __builtin_nontemporal_store(vals[u], dst + idx);
+    }
+  }
+}
+
+// Inverse of the replicated relayout for float32 gradients: out [P][B][Sp][H][R1]
+// receives, for head h, the sum of its rep copies j = h*rep + t (t = 0..rep-1, in
+// that order) from in [P][B][S][Hl][R1].  One grid slice per (s, b) span.
+template <typename V>
+__global__ __launch_bounds__(kThreads) void ulysses_inv_sum_kernel(const V* __restrict__ in, V* __restrict__ out,
+                                                                   int P, int B, int Sp, int H, int Hl, int rep,
+                                                                   int R1, int blocks_per_span, int64_t group_in,
+                                                                   int64_t group_out) {
+  const int span = blockIdx.x / blocks_per_span;
+  const int blk = blockIdx.x - span * blocks_per_span;
+  const int s = span / B;
+  const int b = span - s * B;
+  in += int64_t(blockIdx.y) * group_in;
+  const uint32_t HR = uint32_t(H) * uint32_t(R1);
+  const uint32_t n = uint32_t(Sp) * HR;
+  V* dst = out + int64_t(blockIdx.y) * group_out + int64_t(span) * n;
+  const int64_t S = int64_t(P) * Sp;
+  for (uint32_t idx = uint32_t(blk) * kThreads + threadIdx.x; idx < n;
+       idx += uint32_t(blocks_per_span) * kThreads) {
+    const uint32_t i = idx / HR;
+    const uint32_t rem = idx - i * HR;
+    const uint32_t h = rem / uint32_t(R1);
+    const uint32_t v = rem - h * uint32_t(R1);
+    V acc{};
+    for (int t = 0; t < rep; ++t) {
+      const uint32_t j = h * uint32_t(rep) + uint32_t(t);
+      const uint32_t p = j / uint32_t(Hl);
+      const uint32_t hh = j - p * uint32_t(Hl);
+      acc += __builtin_nontemporal_load(in + ((int64_t(p) * B + b) * S + int64_t(s) * Sp + i) * (int64_t(Hl) * R1) +
+                                        int64_t(hh) * R1 + v);
+    }
+    __builtin_nontemporal_store(acc, dst + idx);
   }
 }
 
@@ -199,22 +283,52 @@ int blocks_for(int64_t spans, int64_t vecs_per_span) {
 }
 
 template <int VB>
-hipError_t ulysses_vb(const void* in, void* out, int P, int B, int Sp, int64_t run_bytes,
-                      bool inverse, hipStream_t s) {
+hipError_t ulysses_vb(const RelayoutProblem& r, const void* in, void* out, hipStream_t s) {
   using V = typename Vec<VB>::T;
-  const int R = int(run_bytes / VB);
-  ProfScope ps(s, inverse ? kProfUlyssesInv : kProfUlysses);
-  if (!inverse) {
-    const int64_t spans = int64_t(P) * B;
-    const int bps = blocks_for(spans, int64_t(Sp) * P * R);
-    hipLaunchKernelGGL(ulysses_fwd_kernel<V>, dim3(unsigned(spans * bps)), dim3(kThreads), 0, s,
-                       static_cast<const V*>(in), static_cast<V*>(out), P, B, Sp, R, bps);
-  } else {
-    const int64_t spans = int64_t(P) * B;
-    const int bps = blocks_for(spans, int64_t(Sp) * P * R);
-    hipLaunchKernelGGL(ulysses_inv_kernel<V>, dim3(unsigned(spans * bps)), dim3(kThreads), 0, s,
-                       static_cast<const V*>(in), static_cast<V*>(out), P, B, Sp, R, bps);
-  }
+  const int P = int(r.P), B = int(r.B), Sp = int(r.S / r.P);
+  const int R = int((r.H / r.P) * r.D * r.eb / VB);
+  const int64_t group_vecs = r.B * r.S * r.H * r.D * r.eb / VB;  // one group's tensor, either side
+  const int64_t spans = int64_t(P) * B;
+  const int bps = blocks_for(spans * r.G, int64_t(Sp) * P * R);
+  const dim3 grid(unsigned(spans * bps), unsigned(r.G));
+  ProfScope ps(s, r.inverse ? kProfUlyssesInv : kProfUlysses);
+  if (!r.inverse)
+    hipLaunchKernelGGL(ulysses_fwd_kernel<V>, grid, dim3(kThreads), 0, s, static_cast<const V*>(in),
+                       static_cast<V*>(out), P, B, Sp, R, bps, group_vecs);
+  else
+    hipLaunchKernelGGL(ulysses_inv_kernel<V>, grid, dim3(kThreads), 0, s, static_cast<const V*>(in),
+                       static_cast<V*>(out), P, B, Sp, R, bps, group_vecs);
+  return hipGetLastError();
+}
+
+template <int VB>
+hipError_t ulysses_rep_vb(const RelayoutProblem& r, const void* in, void* out, hipStream_t s) {
+  using V = typename Vec<VB>::T;
+  const int P = int(r.P), B = int(r.B), Sp = int(r.S / r.P), H = int(r.H), rep = int(r.rep);
+  const int Hl = int(r.H * r.rep / r.P);
+  const int R1 = int(r.D * r.eb / VB);
+  const int64_t spans = int64_t(P) * B;
+  const int bps = blocks_for(spans * r.G, int64_t(r.S) * Hl * R1);
+  const dim3 grid(unsigned(spans * bps), unsigned(r.G));
+  ProfScope ps(s, kProfUlysses);
+  hipLaunchKernelGGL(ulysses_rep_kernel<V>, grid, dim3(kThreads), 0, s, static_cast<const V*>(in),
+                     static_cast<V*>(out), P, B, Sp, H, Hl, rep, R1, bps, r.P * r.B * Sp * int64_t(H) * R1,
+                     r.P * r.B * r.S * int64_t(Hl) * R1);
+  return hipGetLastError();
+}
+
+template <typename F>  // float or f32x4
+hipError_t ulysses_inv_sum_f(const RelayoutProblem& r, const void* in, void* out, hipStream_t s) {
+  const int P = int(r.P), B = int(r.B), Sp = int(r.S / r.P), H = int(r.H), rep = int(r.rep);
+  const int Hl = int(r.H * r.rep / r.P);
+  const int R1 = int(r.D * 4 / int(sizeof(F)));
+  const int64_t spans = int64_t(P) * B;
+  const int bps = blocks_for(spans * r.G, int64_t(Sp) * H * R1);
+  const dim3 grid(unsigned(spans * bps), unsigned(r.G));
+  ProfScope ps(s, kProfUlyssesInv);
+  hipLaunchKernelGGL(ulysses_inv_sum_kernel<F>, grid, dim3(kThreads), 0, s, static_cast<const F*>(in),
+                     static_cast<F*>(out), P, B, Sp, H, Hl, rep, R1, bps, r.P * r.B * r.S * int64_t(Hl) * R1,
+                     r.P * r.B * Sp * int64_t(H) * R1);
   return hipGetLastError();
 }
 
@@ -259,16 +373,26 @@ hipError_t launch_striped(const void* in, void* out, int64_t B, int64_t S, int64
   }
 }
 
-hipError_t launch_ulysses(const void* in, void* out, int64_t P, int64_t B, int64_t S, int64_t H,
-                          int64_t D, int64_t eb, bool inverse, hipStream_t s) {
-  const int64_t run = (H / P) * D * eb;
-  const int Sp = int(S / P);
-  switch (pick_vec_bytes(run, in, out)) {
-    case 16: return ulysses_vb<16>(in, out, int(P), int(B), Sp, run, inverse, s);
-    case 8: return ulysses_vb<8>(in, out, int(P), int(B), Sp, run, inverse, s);
-    case 4: return ulysses_vb<4>(in, out, int(P), int(B), Sp, run, inverse, s);
-    case 2: return ulysses_vb<2>(in, out, int(P), int(B), Sp, run, inverse, s);
-    default: return ulysses_vb<1>(in, out, int(P), int(B), Sp, run, inverse, s);
+hipError_t launch_relayout(const RelayoutProblem& r, const void* in, void* out, hipStream_t s) {
+  if (r.rep == 1) {
+    switch (pick_vec_bytes((r.H / r.P) * r.D * r.eb, in, out)) {
+      case 16: return ulysses_vb<16>(r, in, out, s);
+      case 8: return ulysses_vb<8>(r, in, out, s);
+      case 4: return ulysses_vb<4>(r, in, out, s);
+      case 2: return ulysses_vb<2>(r, in, out, s);
+      default: return ulysses_vb<1>(r, in, out, s);
+    }
+  }
+  if (r.inverse) {  // float32, copies summed
+    if (pick_vec_bytes(r.D * 4, in, out) == 16) return ulysses_inv_sum_f<f32x4>(r, in, out, s);
+    return ulysses_inv_sum_f<float>(r, in, out, s);
+  }
+  switch (pick_vec_bytes(r.D * r.eb, in, out)) {
+    case 16: return ulysses_rep_vb<16>(r, in, out, s);
+    case 8: return ulysses_rep_vb<8>(r, in, out, s);
+    case 4: return ulysses_rep_vb<4>(r, in, out, s);
+    case 2: return ulysses_rep_vb<2>(r, in, out, s);
+    default: return ulysses_rep_vb<1>(r, in, out, s);
   }
 }
 

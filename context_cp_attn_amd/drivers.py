@@ -129,15 +129,23 @@ def ring_forward_all(q, k, v, P, layout="zigzag", seg=None, **mask):
     return [RingShare(q, k, v, P, r, layout, seg, **mask).forward() for r in range(P)]
 
 
-def ulysses_forward(q_stack, k_stack, v_stack, P, **mask):
+def _kv_relayout(x_stack, P, kv_rep):
+    if kv_rep == 1:
+        return ops.ulysses_relayout(x_stack, P)
+    return ops.ulysses_relayout_ex(x_stack.unsqueeze(0), P, rep=kv_rep)[0]
+
+
+def ulysses_forward(q_stack, k_stack, v_stack, P, kv_rep=1, **mask):
     """q_stack [P][B][S/P][Hq][D], k/v [P][B][S/P][Hkv][D] (rank s holds sequence slice s).
 
-    Returns (out_stack [P][B][S/P][Hq][D], lse [P][B][Hq/P][S], the relayouted q, k, v):
-    rank p attends over the whole sequence with q heads [p*Hq/P, (p+1)*Hq/P).
+    Returns (out_stack [P][B][S/P][Hq][D], lse [P][B][Hq/P][S], the relayouted q, k, v
+    and per-rank outputs): rank p attends over the whole sequence with q heads
+    [p*Hq/P, (p+1)*Hq/P).  kv_rep > 1 replicates every kv head by group before the
+    exchange, for a degree up to Hkv * kv_rep.
     """
     ql = ops.ulysses_relayout(q_stack, P)
-    kl = ops.ulysses_relayout(k_stack, P)
-    vl = ops.ulysses_relayout(v_stack, P)
+    kl = _kv_relayout(k_stack, P, kv_rep)
+    vl = _kv_relayout(v_stack, P, kv_rep)
     outs, lses = [], []
     for p in range(P):
         o, l = ops.attn_fwd(ql[p], kl[p], vl[p], **mask)
@@ -145,3 +153,57 @@ def ulysses_forward(q_stack, k_stack, v_stack, P, **mask):
         lses.append(l)
     out_l = torch.stack(outs)
     return ops.ulysses_relayout_inv(out_l, P), torch.stack(lses), (ql, kl, vl, out_l)
+
+
+def ulysses_backward(relayouted, lse, dout_stack, P, kv_rep=1, **mask):
+    """Gradients through Ulysses, from ``ulysses_forward``'s relayouted tensors and lse.
+
+    Returns (dq, dk, dv) stacks [P][B][S/P][H][D] float32 in the sequence-sharded
+    layout; with kv_rep > 1 each kv head's gradient is the sum over its copies.
+    """
+    ql, kl, vl, out_l = relayouted
+    gl = ops.ulysses_relayout(dout_stack, P)
+    ws = ops.bwd_workspace(ql[0], kl[0], **mask)
+    grads = [ops.attn_bwd(ql[p], kl[p], vl[p], out_l[p], lse[p], gl[p], workspace=ws, **mask) for p in range(P)]
+    dql, dkl, dvl = (torch.stack([g[i] for g in grads]) for i in range(3))
+    dq = ops.ulysses_relayout_inv(dql, P)
+    if kv_rep == 1:
+        return dq, ops.ulysses_relayout_inv(dkl, P), ops.ulysses_relayout_inv(dvl, P)
+    inv = lambda t: ops.ulysses_relayout_ex(t.unsqueeze(0), P, rep=kv_rep, inverse=True)[0]
+    return dq, inv(dkl), inv(dvl)
+
+
+def usp_forward(q, k, v, Pr, Pu, kv_rep=1, seg=None, causal=True, window=0, scale=0.0):
+    """Ulysses within groups of Pu ranks x ring attention across Pr groups, all
+    Pr*Pu ranks on one GPU.  q [1,S,Hq,D], k/v [1,S,Hkv,D] in sequence order.
+
+    The sequence is zigzag-reordered for the Pr groups; group r's share is split
+    contiguously over its Pu ranks and exchanged inside the group (heads slice u to
+    rank (r, u)); rank (r, u) then runs the ring over the groups' blocks of its head
+    slice with the fused step.  Returns (out [1,S,Hq,D] float32 in sequence order,
+    lse [Pr][Pu][1][Hq/Pu][S/Pr] per rank).
+    """
+    if q.shape[0] != 1:
+        raise ValueError("usp_forward takes batch 1")
+    S = q.shape[1]
+    Sr, Sl = S // Pr, S // (Pr * Pu)
+    stack = lambda t: ops.zigzag_reorder(t, Pr).view(Pr, Pu, 1, Sl, t.shape[2], t.shape[3])
+    ql = ops.ulysses_relayout_ex(stack(q), Pu, groups=Pr)
+    kl = ops.ulysses_relayout_ex(stack(k), Pu, groups=Pr, rep=kv_rep)
+    vl = ops.ulysses_relayout_ex(stack(v), Pu, groups=Pr, rep=kv_rep)
+    pos = [rank_positions(r, Pr, S, "zigzag", q.device) for r in range(Pr)]
+    sz = None if seg is None else ops.zigzag_reorder(seg, Pr)
+    Hl = ql.shape[4]
+    acc = torch.zeros(ql.shape, device=q.device, dtype=torch.float32)
+    lse = torch.full((Pr, Pu, 1, Hl, Sr), float("-inf"), device=q.device, dtype=torch.float32)
+    for r in range(Pr):
+        for u in range(Pu):
+            for step in range(Pr):
+                src = (r - step) % Pr
+                m = dict(causal=causal, window=window, scale=scale, q_pos=pos[r], k_pos=pos[src])
+                if sz is not None:
+                    m.update(q_seg=sz[:, r * Sr:(r + 1) * Sr].contiguous(), k_seg=sz[:, src * Sr:(src + 1) * Sr].contiguous())
+                ops.attn_fwd_merge(ql[r, u], kl[src, u], vl[src, u], acc[r, u], lse[r, u], **m)
+    back = ops.ulysses_relayout_ex(acc, Pu, groups=Pr, inverse=True)   # [Pr][Pu][1][Sl][Hq][D]
+    out = ops.zigzag_reorder(back.view(1, S, back.shape[4], back.shape[5]), Pr, inverse=True)
+    return out, lse

@@ -180,6 +180,37 @@ def ulysses_relayout_inv(y, P, out=None):
     return out
 
 
+def ulysses_relayout_ex(x, P, *, groups=1, rep=1, inverse=False, out=None):
+    """General Ulysses relayout of ``groups`` independent groups with every head
+    replicated ``rep`` times (head j of the replicated set = head j // rep).
+
+    forward: x [G][P][B][S/P][H][D] -> [G][P][B][S][H*rep/P][D]
+    inverse: x [G][P][B][S][H*rep/P][D] -> [G][P][B][S/P][H][D]; with rep > 1 the
+    copies of each head are summed (float32 gradients).
+    """
+    _dev(x, "x")
+    if x.dim() != 6 or x.shape[0] != groups or x.shape[1] != P:
+        raise ValueError("x must be [G][P][B][...][...][D]")
+    G, _, B, s_in, h_in, D = x.shape
+    if not inverse:
+        S, H = s_in * P, h_in
+        if (H * rep) % P:
+            raise _lib.CpError(_lib.CP_ERR_INVALID, f"heads {H} x rep {rep} not divisible by {P}")
+        shape = (G, P, B, S, H * rep // P, D)
+    else:
+        S, H = s_in, h_in * P // rep
+        if S % P or (h_in * P) % rep:
+            raise _lib.CpError(_lib.CP_ERR_INVALID, "sequence or replicated heads not divisible")
+        shape = (G, P, B, S // P, H, D)
+    out = torch.empty(shape, device=x.device, dtype=x.dtype) if out is None else _dev(out, "out", x.dtype)
+    if tuple(out.shape) != shape:
+        raise ValueError(f"out must be {shape}")
+    a = _lib.RelayoutArgs(groups=G, P=P, batch=B, seqlen=S, heads=H, head_dim=D, elem_bytes=x.element_size(),
+                          rep=rep, inverse=int(bool(inverse)))
+    _lib.check(_lib.load().cp_ulysses_relayout_ex(ctypes.byref(a), x.data_ptr(), out.data_ptr(), _stream()))
+    return out
+
+
 DUAL_CHUNK_SWAP, STRIPED = 0, 1
 
 

@@ -149,6 +149,39 @@ cp_status_t cp_ulysses_relayout_inv(const void* in, void* out, int64_t P, int64_
                                     int64_t elem_bytes, hipStream_t stream);
 
 /*
+ * General Ulysses relayout ([H] §"Ulysses" and §Exercises: a degree above the kv
+ * head count by replicating each kv head by group before the exchange, or Ulysses
+ * within groups combined with ring attention across them, as in USP; [MU] names
+ * the Ulysses x ring hybrid).  G independent groups stacked outermost (the ring
+ * groups of USP; 1 for plain Ulysses); within a group P ranks, seqlen = the group's
+ * whole sequence S, heads = H of the sequence-sharded tensor, each replicated rep
+ * times (head j of the replicated set is head j / rep; H' = H*rep).
+ *   inverse = 0: in [G][P][B][S/P][H][D] -> out [G][P][B][S][H'/P][D]
+ *     out[g][p][b][s*(S/P)+i][hh][d] = in[g][s][b][i][(p*H'/P + hh) / rep][d]
+ *   inverse = 1: in [G][P][B][S][H'/P][D] -> out [G][P][B][S/P][H][D]: the exact
+ *     inverse for rep = 1; for rep > 1 each head receives the sum of its rep copies
+ *     (copies t = 0..rep-1 added in that order; the gradient of the replication),
+ *     float32 only (elem_bytes 4).
+ * S % P == 0 and (H*rep) % P == 0, elem_bytes in {2, 4}, G <= 65535, else
+ * CP_ERR_INVALID / CP_ERR_UNSUPPORTED.  Bit-exact except for the sums.  in and out
+ * must not overlap (CP_ERR_ALIAS).  cp_ulysses_relayout(_inv) are G = 1, rep = 1.
+ */
+typedef struct {
+  int64_t groups;      /* G >= 1                                                   */
+  int64_t P;           /* Ulysses degree within a group                            */
+  int64_t batch;       /* B >= 1                                                   */
+  int64_t seqlen;      /* S: the sequence one group covers                         */
+  int64_t heads;       /* H: heads of the sequence-sharded tensor                  */
+  int64_t head_dim;    /* D                                                        */
+  int64_t elem_bytes;  /* 2 or 4                                                   */
+  int64_t rep;         /* >= 1: copies of every head                               */
+  int32_t inverse;     /* 0: sequence -> heads; 1: heads -> sequence               */
+} cp_relayout_args_t;
+
+cp_status_t cp_ulysses_relayout_ex(const cp_relayout_args_t* args, const void* in, void* out,
+                                   hipStream_t stream);
+
+/*
  * Causal load-balancing reorder of whole token rows.  in/out [B][S][row_bytes]; the
  * output is the P ranks' shares in rank order, so a contiguous P-way split gives
  * rank r its share.  inverse = 1 undoes it.  Bit-exact.

@@ -76,6 +76,72 @@ def test_ulysses_relayout_bit_exact(cp, P, B, S, H, D, dtype):
     np.testing.assert_array_equal(bits(z), oracle.ulysses_relayout_inv(bits(y)))
 
 
+@pytest.mark.parametrize("G,P,B,S,H,D,dtype,rep", [
+    (1, 4, 1, 64, 2, 128, torch.bfloat16, 2),     # kv heads replicated 2x (degree 2x the kv heads)
+    (1, 8, 2, 64, 2, 64, torch.bfloat16, 4),
+    (3, 2, 1, 32, 4, 16, torch.float32, 1),      # USP groups
+    (2, 4, 1, 128, 2, 128, torch.bfloat16, 2),   # groups and replication
+    (1, 3, 1, 12, 1, 7, torch.float32, 3),       # odd head size: 4-byte vectors
+])
+def test_relayout_ex(cp, G, P, B, S, H, D, dtype, rep):
+    say(f"relayout_ex G={G} P={P} B={B} S={S} H={H} D={D} {dtype} rep={rep}")
+    torch.manual_seed(2)
+    x = torch.randn(G, P, B, S // P, H, D).to(dtype).cuda()
+    y = cp.ulysses_relayout_ex(x, P, groups=G, rep=rep)
+    ref = np.stack([oracle.ulysses_relayout_rep(bits(x[g]), rep) for g in range(G)])
+    np.testing.assert_array_equal(bits(y), ref)
+    if rep == 1:
+        z = cp.ulysses_relayout_ex(y, P, groups=G, inverse=True)
+        assert torch.equal(z, x)
+        np.testing.assert_array_equal(bits(z), oracle.usp_relayout_inv(bits(y)))
+    # inverse with copies summed (float32 gradients)
+    g32 = torch.randn(y.shape, generator=torch.Generator().manual_seed(3)).cuda()
+    z = cp.ulysses_relayout_ex(g32, P, groups=G, rep=rep, inverse=True)
+    ref = np.stack([oracle.ulysses_relayout_inv_sum(f64(g32[g]), rep) for g in range(G)])
+    check_close(z, ref, 1e-5 * max(1.0, np.abs(ref).max()), "inverse sum")
+
+
+@pytest.mark.parametrize("Hq,Hkv,P", [(8, 2, 4), (8, 2, 8)])
+def test_ulysses_beyond_kv_heads(cp, Hq, Hkv, P):
+    """Degree P above the kv head count by replicating kv heads: out, lse and all
+    gradients against the oracle's full attention."""
+    S, D, rep = 512, 128, P // Hkv
+    say(f"ulysses Hq={Hq} Hkv={Hkv} P={P} rep={rep}")
+    q, k, v, do = cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D), (1, S, Hq, D)], seed=11)
+    st = lambda t: t.reshape(P, 1, S // P, t.shape[2], D).cuda()
+    out, lse, rel = cp.drivers.ulysses_forward(st(q), st(k), st(v), P, kv_rep=rep)
+    ro, rl = oracle.attn_fwd(q, k, v)
+    check_close(out.reshape(1, S, Hq, D), ro, 1e-2, "out")
+    check_lse(torch.cat(list(lse), dim=1), rl, 1e-3)
+    dq, dk, dv = cp.drivers.ulysses_backward(rel, lse, st(do), P, kv_rep=rep)
+    refs = oracle.attn_bwd(q, k, v, ro, rl, do)
+    for got, ref, nm in zip((dq, dk, dv), refs, ("dq", "dk", "dv")):
+        check_close(got.reshape(ref.shape), ref, 1e-2 * max(1.0, np.abs(ref).max()), nm)
+
+
+@pytest.mark.parametrize("Pr,Pu,Hkv,masks,dtype", [
+    (2, 4, 2, "causal", torch.bfloat16),          # kv heads replicated inside the groups
+    (4, 2, 2, "packed_window", torch.bfloat16),
+    (2, 2, 8, "causal", torch.float32),
+])
+def test_usp_forward(cp, Pr, Pu, Hkv, masks, dtype):
+    """Ulysses within groups x zigzag ring across groups against full attention."""
+    S, Hq = 1024, 8
+    D = 128 if dtype == torch.bfloat16 else 32
+    rep = max(1, Pu // Hkv)
+    say(f"usp Pr={Pr} Pu={Pu} Hkv={Hkv} rep={rep} {masks} {dtype}")
+    q, k, v = cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D)], seed=12, dtype=dtype)
+    seg, window = None, 0
+    if masks == "packed_window":
+        seg = cp_inputs.random_segment_ids(S, 40, 300, seed=13)
+        window = 100
+    out, _ = cp.drivers.usp_forward(q.cuda(), k.cuda(), v.cuda(), Pr, Pu, kv_rep=rep,
+                                    seg=None if seg is None else seg.cuda(), window=window)
+    sm = {} if seg is None else dict(q_seg=seg.numpy(), k_seg=seg.numpy())
+    ro, rl = oracle.attn_fwd(q, k, v, window=window, **sm)
+    check_close(out, ro, TOL[dtype]["out"], "usp out")
+
+
 @pytest.mark.parametrize("strategy", [0, 1])
 @pytest.mark.parametrize("shape,P,dtype", [
     ((1, 65536), 4, torch.int32),
