@@ -18,6 +18,7 @@ Everything is a plain, slow restatement of what the pages define, in float64:
 * ``zigzag`` — the 2P-chunk zigzag (dual-chunk-swap) and the striped partitions,
   their reorders, the automatic choice between them and the causal work counts.
 * ``ring`` — ring attention per rank (forward and blockwise backward).
+* ``padding`` — padding a sequence at its end to a multiple of the CP degree.
 
 Pins (checked by ``tests/test_oracle.py`` against facts other than the oracle's
 own formulas) are listed in each module's docstring.
@@ -32,3 +33,4 @@ from .zigzag import (chunk_order, reorder, reorder_inv, rank_positions, rank_chu
                      work, visible_pairs, striped_order, reorder_striped, reorder_striped_inv,
                      auto_strategy, DUAL_CHUNK_SWAP, STRIPED)
 from .ring import ring_fwd, ring_bwd, ring_block_counts  # noqa: F401
+from .padding import padded_length, pad_rows, pad_segments  # noqa: F401

@@ -473,3 +473,37 @@ def test_inputs_recipe():
     assert q.shape == (1, 32, 8, 16) and q.dtype == torch.float32
     lens = cp_inputs.doc_lengths(8192)
     assert sum(lens) == 8192 and all(256 <= n <= 4096 for n in lens[:-1])
+
+
+# ---------------------------------------------------------------- padding to a multiple of P
+
+@pytest.mark.parametrize("masks", ["causal", "noncausal", "packed_window"])
+def test_end_padding_leaves_real_rows_unchanged(masks):
+    """Padding at the end (zeros, positions continuing, pads in a segment of their own)
+    changes no real row: plain attention, zigzag ring and Ulysses on the padded
+    sequence equal unpadded full attention on the real rows."""
+    S, Hq, Hkv, D, P = 29, 4, 2, 4, 4
+    q, k, v = rnd(1, S, Hq, D, seed=80), rnd(1, S, Hkv, D, seed=81), rnd(1, S, Hkv, D, seed=82)
+    m = dict(causal=masks != "noncausal")
+    seg = np.repeat([0, 1, 2], [8, 12, 9])[None] if masks == "packed_window" else None
+    if masks == "packed_window":
+        m["window"] = 5
+    ro, rl = oracle.attn_fwd(q, k, v, q_seg=seg, k_seg=seg, **m)
+    Sp = oracle.padded_length(S, 2 * P)
+    assert Sp == 32
+    qp, kp, vp = (oracle.pad_rows(t, Sp) for t in (q, k, v))
+    assert np.all(qp[:, S:] == 0) and np.array_equal(qp[:, :S], q)
+    segp = oracle.pad_segments(seg if seg is not None else np.zeros((1, S), np.int64), Sp)
+    assert np.all(segp[:, S:] == segp[:, :S].max() + 1)
+    sm = dict(q_seg=segp, k_seg=segp) if (seg is not None or not m["causal"]) else {}
+    o, l = oracle.attn_fwd(qp, kp, vp, **sm, **m)
+    np.testing.assert_allclose(o[:, :S], ro, atol=1e-12)
+    np.testing.assert_allclose(l[:, :, :S], rl, atol=1e-12)
+    for qpos, o, l in oracle.ring_fwd(qp, kp, vp, P, "zigzag", seg=sm.get("q_seg"), **m):
+        real = qpos < S
+        np.testing.assert_allclose(o[:, real], ro[:, qpos[real]], atol=1e-12)
+        np.testing.assert_allclose(l[:, :, real], rl[:, :, qpos[real]], atol=1e-12)
+    if not sm:
+        o, l, _ = oracle.ulysses_attn(qp, kp, vp, 2, **m)
+        np.testing.assert_allclose(o[:, :S], ro, atol=1e-12)
+    np.testing.assert_array_equal(oracle.pad_rows(qp, S), q)   # truncation undoes it
