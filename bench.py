@@ -21,8 +21,9 @@ Legs timed in the same run (not part of value): the ring share of llama2-7b
 the attention epilogue, and the unfused fwd + merge pair), the 64K-token
 dual-chunk-swap reorder, and the packed + windowed 8K ring share (4 ranks x 4
 steps, fused fwd + merge, bwd; striped as chosen automatically for packed
-sequences, and dual-chunk-swap).  The CPU oracle is timed on a bounded sample of the
-step's attention rows (cpu_baseline).
+sequences, and dual-chunk-swap), and llama3.1-8b at 16K on 16 ranks beyond its 8 kv
+heads (Ulysses 8 x ring 2, and Ulysses 16 with kv heads replicated).  The CPU oracle
+is timed on a bounded sample of the step's attention rows (cpu_baseline).
 """
 
 from __future__ import annotations
@@ -197,6 +198,22 @@ def legs(torch, cp, cp_inputs):
         packed_pass()
         ms = timed(torch, packed_pass, 3)
         out[f"packed_window_8k_cp4_all_ranks_{name}"] = {"strategy": layout, "ms_per_pass": round(ms, 3)}
+    # beyond the kv head count, llama3.1-8b (32 q / 8 kv heads) at 16K tokens on 16 ranks:
+    # Ulysses 8 within groups x ring 2 across them (USP), and Ulysses 16 with kv heads
+    # replicated 2x; forward of all ranks, algorithmic causal FLOPs of the whole sequence
+    S, Hq, Hkv = 16384, 32, 8
+    q, k, v = (t.cuda() for t in cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D)], seed=0))
+    fl = 4 * D * Hq * S * (S + 1) / 2
+    usp = lambda: cp.drivers.usp_forward(q, k, v, 2, 8)
+    usp()
+    ms = timed(torch, usp, 3)
+    out["usp_llama31_8b_16k_ulysses8_ring2_fwd"] = {"ms_per_pass": round(ms, 3), "tflops": round(fl / ms / 1e9, 2)}
+    P = 16
+    st = lambda t: t.reshape(P, 1, S // P, t.shape[2], D)
+    uly = lambda: cp.drivers.ulysses_forward(st(q), st(k), st(v), P, kv_rep=2)
+    uly()
+    ms = timed(torch, uly, 3)
+    out["ulysses16_kv_rep2_llama31_8b_16k_fwd"] = {"ms_per_pass": round(ms, 3), "tflops": round(fl / ms / 1e9, 2)}
     return out
 
 

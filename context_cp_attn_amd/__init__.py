@@ -9,7 +9,8 @@ Hand-written HIP kernels behind a C ABI (include/cp_attn.h, libcp_attn.so):
 * ``ulysses_relayout`` / ``ulysses_relayout_inv`` — the sequence<->head exchange of
   all simulated ranks as one local permute; ``ulysses_relayout_ex`` adds groups
   (Ulysses x ring, USP) and kv-head replication beyond the kv head count;
-* ``zigzag_reorder`` — the zigzag / dual-chunk-swap load-balancing reorder.
+* ``zigzag_reorder`` — the zigzag / dual-chunk-swap (or striped) load-balancing
+  reorder; ``pad_rows`` — end padding of a sequence to a multiple of the CP degree.
 
 ``drivers`` simulates the P ranks' ring and Ulysses shares on one GPU.
 torch provides device memory and the stream; nothing here computes on the CPU.
@@ -17,5 +18,5 @@ torch provides device memory and the stream; nothing here computes on the CPU.
 
 from ._lib import CpError, load as load_library  # noqa: F401
 from .ops import (attn_fwd, attn_fwd_merge, attn_bwd, lse_merge, ulysses_relayout,  # noqa: F401
-                  ulysses_relayout_inv, ulysses_relayout_ex, zigzag_reorder, bwd_workspace)
+                  ulysses_relayout_inv, ulysses_relayout_ex, zigzag_reorder, pad_rows, bwd_workspace)
 from . import drivers  # noqa: F401

@@ -49,6 +49,7 @@ SIGNATURES = {
     "cp_ulysses_relayout_inv": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp]),
     "cp_zigzag_reorder": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp]),
     "cp_ulysses_relayout_ex": (c_i32, [ctypes.POINTER(RelayoutArgs), c_vp, c_vp, c_vp]),
+    "cp_pad_rows": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, ctypes.c_uint32, c_vp]),
     "cp_prof_enable": (None, [c_i32]),
     "cp_prof_reset": (None, []),
     "cp_prof_kernel_count": (c_i32, []),

@@ -336,4 +336,18 @@ cp_status_t cp_zigzag_reorder(const void* in, void* out, int64_t batch, int64_t 
                     "cp_zigzag_reorder launch");
 }
 
+cp_status_t cp_pad_rows(const void* in, void* out, int64_t batch, int64_t seqlen, int64_t seqlen_out,
+                        int64_t row_bytes, uint32_t fill, hipStream_t stream) {
+  if (batch < 1 || seqlen < 1 || seqlen_out < 1 || row_bytes < 1) return fail(CP_ERR_INVALID, "sizes must be >= 1");
+  if (fill != 0 && row_bytes % 4)
+    return fail(CP_ERR_INVALID, "a non-zero fill word needs rows of whole 32-bit words (row_bytes %lld)",
+                (long long)row_bytes);
+  if (!in || !out) return fail(CP_ERR_INVALID, "NULL buffer");
+  if (overlaps(in, batch * seqlen * row_bytes, out, batch * seqlen_out * row_bytes))
+    return fail(CP_ERR_ALIAS, "in and out overlap");
+  if (batch > 65535 * 64) return fail(CP_ERR_UNSUPPORTED, "batch too large");
+  return hip_status(cp::launch_pad_rows(in, out, batch, seqlen, seqlen_out, row_bytes, fill, stream),
+                    "cp_pad_rows launch");
+}
+
 }  // extern "C"

@@ -47,6 +47,8 @@ struct RelayoutProblem {
   bool inverse;
 };
 hipError_t launch_relayout(const RelayoutProblem& r, const void* in, void* out, hipStream_t s);
+hipError_t launch_pad_rows(const void* in, void* out, int64_t B, int64_t S, int64_t S_out, int64_t row_bytes,
+                           uint32_t fill, hipStream_t s);
 hipError_t launch_zigzag(const void* in, void* out, int64_t B, int64_t S, int64_t row_bytes,
                          int64_t P, bool inverse, hipStream_t s);
 hipError_t launch_striped(const void* in, void* out, int64_t B, int64_t S, int64_t row_bytes, int64_t P,

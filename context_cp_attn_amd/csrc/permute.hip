@@ -10,6 +10,8 @@
 // 2P-1-r); a run is one chunk of S/(2P) token rows.
 // Striped: MaxText PR "Add Packing Support for Context Parallelism (Ring Attention)",
 // reorder strategy 1 (token t to rank t mod P); a run is one token row.
+// Padding: transformers PR "[distributed] Context parallel module, with Ulysses",
+// "What this PR brings" (sequences padded at their end to a multiple of the CP size).
 #include "common.h"
 #include "launch.h"
 #include "prof.h"
@@ -264,6 +266,36 @@ __global__ __launch_bounds__(kThreads) void striped_kernel(const V* __restrict__
   }
 }
 
+// Pad (or truncate) every batch's sequence to S_out rows: rows t < min(S, S_out) are
+// copied, rows t >= S are filled with a repeated 32-bit word.  Output-ordered, one
+// grid slice per batch.  Vectors of VB bytes; fill is the word pattern as a vector.
+template <typename V>
+__global__ __launch_bounds__(kThreads) void pad_rows_kernel(const V* __restrict__ in, V* __restrict__ out,
+                                                            int64_t S, int64_t S_out, int64_t RV, V fill,
+                                                            int blocks_per_span) {
+  const int b = blockIdx.x / blocks_per_span;
+  const int blk = blockIdx.x - b * blocks_per_span;
+  const int64_t n = S_out * RV;
+  const int64_t copy = (S < S_out ? S : S_out) * RV;  // vectors of real rows
+  const V* src = in + int64_t(b) * S * RV;
+  V* dst = out + int64_t(b) * n;
+  for (int64_t base = int64_t(blk) * kThreads * kVPT + threadIdx.x; base < n;
+       base += int64_t(blocks_per_span) * kThreads * kVPT) {
+    V vals[kVPT];
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const int64_t idx = base + int64_t(u) * kThreads;
+      vals[u] = fill;
+      if (idx < copy) vals[u] = __builtin_nontemporal_load(src + idx);
+    }
+#pragma unroll
+    for (int u = 0; u < kVPT; ++u) {
+      const int64_t idx = base + int64_t(u) * kThreads;
+      if (idx < n) __builtin_nontemporal_store(vals[u], dst + idx);
+    }
+  }
+}
+
 int pick_vec_bytes(int64_t run_bytes, const void* a, const void* b) {
   const uintptr_t al = reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b);
   for (int vb = 16; vb > 1; vb >>= 1)
@@ -371,6 +403,39 @@ hipError_t launch_striped(const void* in, void* out, int64_t B, int64_t S, int64
     case 2: return striped_vb<2>(in, out, B, S, row_bytes, P, inverse, s);
     default: return striped_vb<1>(in, out, B, S, row_bytes, P, inverse, s);
   }
+}
+
+hipError_t launch_pad_rows(const void* in, void* out, int64_t B, int64_t S, int64_t S_out, int64_t row_bytes,
+                           uint32_t fill, hipStream_t s) {
+  // fill words need 4-byte vectors at least; a zero fill admits any width
+  int vb = pick_vec_bytes(row_bytes, in, out);
+  if (fill != 0 && vb < 4) vb = 4;  // row_bytes % 4 == 0 is checked by the caller
+  const int64_t RV = row_bytes / vb;
+  const int bps = blocks_for(B, S_out * RV);
+  ProfScope ps(s, kProfPadRows);
+  const dim3 grid(unsigned(B * bps));
+  switch (vb) {
+    case 16:
+      hipLaunchKernelGGL(pad_rows_kernel<u32x4>, grid, dim3(kThreads), 0, s, static_cast<const u32x4*>(in),
+                         static_cast<u32x4*>(out), S, S_out, RV, u32x4{fill, fill, fill, fill}, bps);
+      break;
+    case 8:
+      hipLaunchKernelGGL(pad_rows_kernel<u32x2>, grid, dim3(kThreads), 0, s, static_cast<const u32x2*>(in),
+                         static_cast<u32x2*>(out), S, S_out, RV, u32x2{fill, fill}, bps);
+      break;
+    case 4:
+      hipLaunchKernelGGL(pad_rows_kernel<uint32_t>, grid, dim3(kThreads), 0, s, static_cast<const uint32_t*>(in),
+                         static_cast<uint32_t*>(out), S, S_out, RV, fill, bps);
+      break;
+    case 2:
+      hipLaunchKernelGGL(pad_rows_kernel<uint16_t>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(in),
+                         static_cast<uint16_t*>(out), S, S_out, RV, uint16_t(0), bps);
+      break;
+    default:
+      hipLaunchKernelGGL(pad_rows_kernel<uint8_t>, grid, dim3(kThreads), 0, s, static_cast<const uint8_t*>(in),
+                         static_cast<uint8_t*>(out), S, S_out, RV, uint8_t(0), bps);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_relayout(const RelayoutProblem& r, const void* in, void* out, hipStream_t s) {

@@ -20,6 +20,7 @@ enum ProfKernel : int {
   kProfFwdMergeMfma,    // bf16 forward with the ring merge fused into its epilogue
   kProfFwdMergeRowwise, // float32 forward with the fused ring merge
   kProfStriped,         // striped reorder (either direction)
+  kProfPadRows,         // sequence padding / truncation
   kProfCount
 };
 

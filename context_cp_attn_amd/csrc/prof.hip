@@ -26,7 +26,7 @@ int64_t g_count[kProfCount];
 const char* const kNames[kProfCount] = {
     "attn_fwd_mfma", "attn_fwd_rowwise", "attn_bwd_delta", "attn_bwd_mfma", "attn_bwd_rowwise",
     "lse_merge", "ulysses_relayout", "ulysses_relayout_inv", "zigzag_reorder", "attn_fwd_merge_mfma",
-    "attn_fwd_merge_rowwise", "striped_reorder"};
+    "attn_fwd_merge_rowwise", "striped_reorder", "pad_rows"};
 
 hipEvent_t take_event() {
   if (!g_free.empty()) {

@@ -31,6 +31,25 @@ def auto_strategy(packed: bool) -> int:
     return ops.STRIPED if packed else ops.DUAL_CHUNK_SWAP
 
 
+def padded_length(S: int, multiple: int) -> int:
+    return -(-S // multiple) * multiple
+
+
+def pad_sequence(x, multiple: int):
+    """Pad x [B][S][...] at its end with zero rows to a multiple of ``multiple`` (the
+    CP degree, or 2P for the zigzag chunks).  Pad tokens take positions S, S+1, ...;
+    under a causal mask no real query sees them.  Returns (x_padded, S)."""
+    S = x.shape[1]
+    return ops.pad_rows(x, padded_length(S, multiple)), S
+
+
+def pad_segments(seg, multiple: int, pad_id: int):
+    """Pad int32 segment ids [B][S] to a multiple, the pad tokens in segment
+    ``pad_id`` (an id no real token has), so that no real query sees a pad key
+    without a causal mask either."""
+    return ops.pad_rows(seg, padded_length(seg.shape[1], multiple), fill=pad_id)
+
+
 def rank_positions(rank: int, P: int, S: int, layout: str = "zigzag", device="cuda") -> torch.Tensor:
     """int32 global positions of the tokens rank ``rank`` holds (increasing)."""
     if layout == "striped":

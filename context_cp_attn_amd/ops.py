@@ -211,6 +211,24 @@ def ulysses_relayout_ex(x, P, *, groups=1, rep=1, inverse=False, out=None):
     return out
 
 
+def pad_rows(x, seqlen_out, fill=0, out=None):
+    """x [B][S][...] -> [B][seqlen_out][...]: the first min(S, seqlen_out) rows
+    copied, rows beyond S filled with the 32-bit word ``fill`` (0 for data, a fresh
+    segment id for int32 segment ids); seqlen_out < S truncates."""
+    _dev(x, "x")
+    if x.dim() < 2:
+        raise ValueError("x must be [B][S][...]")
+    B, S = x.shape[0], x.shape[1]
+    row_bytes = (x[0, 0].numel() if x.dim() > 2 else 1) * x.element_size()
+    shape = (B, seqlen_out) + tuple(x.shape[2:])
+    out = torch.empty(shape, device=x.device, dtype=x.dtype) if out is None else _dev(out, "out", x.dtype)
+    if tuple(out.shape) != shape:
+        raise ValueError(f"out must be {shape}")
+    _lib.check(_lib.load().cp_pad_rows(x.data_ptr(), out.data_ptr(), B, S, seqlen_out, row_bytes,
+                                       int(fill) & 0xFFFFFFFF, _stream()))
+    return out
+
+
 DUAL_CHUNK_SWAP, STRIPED = 0, 1
 
 

@@ -197,6 +197,20 @@ cp_status_t cp_zigzag_reorder(const void* in, void* out, int64_t batch, int64_t 
                               hipStream_t stream);
 
 /*
+ * Sequence padding to a multiple of the context-parallel degree ([HF] "What this
+ * PR brings": sequences padded at their end before the masks are built; embeddings
+ * zeros, positions continuing).  in [B][seqlen][row_bytes] -> out
+ * [B][seqlen_out][row_bytes]: rows t < min(seqlen, seqlen_out) copied, rows
+ * t >= seqlen filled with the 32-bit word `fill` repeated (0 for data; a fresh
+ * segment id for int32 segment ids, so no real query sees a pad key);
+ * seqlen_out < seqlen truncates (removes the padding of an output).  A non-zero
+ * fill needs row_bytes % 4 == 0 (CP_ERR_INVALID).  Bit-exact.  in and out must
+ * not overlap (CP_ERR_ALIAS).
+ */
+cp_status_t cp_pad_rows(const void* in, void* out, int64_t batch, int64_t seqlen, int64_t seqlen_out,
+                        int64_t row_bytes, uint32_t fill, hipStream_t stream);
+
+/*
  * Kernel tracing with HIP events (a measurement aid, off by default).  While
  * enabled, every kernel launch of the library is bracketed by two events recorded
  * on its stream; the events are created by the library on first use and reused.

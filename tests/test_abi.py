@@ -142,6 +142,15 @@ def test_merge_rejects():
     assert f(1, 8, 2, 128, FAKE_A, FAKE_B, FAKE_A, 1 << 41, 1, None) == ALIAS
 
 
+def test_pad_rows_rejects():
+    lib = _lib.load()
+    f = lib.cp_pad_rows
+    assert f(FAKE_A, FAKE_B, 0, 8, 16, 4, 0, None) == INVALID          # batch
+    assert f(FAKE_A, FAKE_B, 1, 8, 16, 6, 7, None) == INVALID          # fill word needs 4-byte rows
+    assert f(FAKE_A, FAKE_A + 16, 1, 8, 16, 4, 0, None) == ALIAS
+    assert f(0, FAKE_B, 1, 8, 16, 4, 0, None) == INVALID
+
+
 def test_python_errors_are_valueerrors():
     with pytest.raises(ValueError):
         _lib.check(INVALID)

@@ -142,6 +142,52 @@ def test_usp_forward(cp, Pr, Pu, Hkv, masks, dtype):
     check_close(out, ro, TOL[dtype]["out"], "usp out")
 
 
+@pytest.mark.parametrize("shape,S_out,fill,dtype", [
+    ((1, 1001, 32, 128), 1008, 0, torch.bfloat16),
+    ((2, 37), 40, 7, torch.int32),          # segment ids: pads get id 7
+    ((3, 10, 5), 16, 0, torch.uint8),
+    ((1, 1008, 8), 1001, 0, torch.float32),  # truncation removes padding
+])
+def test_pad_rows(cp, shape, S_out, fill, dtype):
+    say(f"pad_rows {shape} -> {S_out} fill={fill} {dtype}")
+    n = int(np.prod(shape))
+    x = (torch.arange(n, dtype=torch.int64) % 251).to(dtype).reshape(shape) if dtype in (torch.int32, torch.uint8) \
+        else torch.randn(shape).to(dtype)
+    y = cp.pad_rows(x.cuda(), S_out, fill=fill)
+    np.testing.assert_array_equal(bits(y), oracle.pad_rows(bits(x), S_out, fill=fill))
+
+
+@pytest.mark.parametrize("scheme,causal", [("ring", True), ("ring", False), ("ulysses", True)])
+def test_padded_sequence_attention(cp, scheme, causal):
+    """A sequence no CP degree divides, padded at its end: the real rows of the ring
+    (zigzag) or Ulysses result equal unpadded full attention's."""
+    S, Hq, Hkv, D, P = 1001, 4, 4, 128, 4
+    say(f"padded {scheme} causal={causal} S={S} P={P}")
+    q, k, v = cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D)], seed=14)
+    ro, rl = oracle.attn_fwd(q, k, v, causal=causal)
+    mult = 2 * P if scheme == "ring" else P
+    (qp, S0), (kp, _), (vp, _) = (cp.drivers.pad_sequence(t.cuda(), mult) for t in (q, k, v))
+    Sp = qp.shape[1]
+    assert S0 == S and Sp % mult == 0
+    if scheme == "ring":
+        seg = None
+        if not causal:   # pads in a segment of their own
+            seg = cp.drivers.pad_segments(torch.zeros(1, S, dtype=torch.int32, device="cuda"), mult, pad_id=1)
+            seg = cp.zigzag_reorder(seg, P)
+        qz, kz, vz = (cp.zigzag_reorder(t, P) for t in (qp, kp, vp))
+        for r in range(P):
+            acc, lse = cp.drivers.RingShare(qz, kz, vz, P, r, seg=seg, causal=causal).forward()
+            pos = oracle.rank_positions(r, P, Sp, "zigzag")
+            real = pos < S
+            check_close(acc[:, real], ro[:, pos[real]], 1e-2, f"rank {r} out")
+            check_lse(lse[:, :, real], rl[:, :, pos[real]], 1e-3)
+    else:
+        st = lambda t: t.reshape(P, 1, Sp // P, t.shape[2], D)
+        out, lse, _ = cp.drivers.ulysses_forward(st(qp), st(kp), st(vp), P)
+        check_close(out.reshape(1, Sp, Hq, D)[:, :S], ro, 1e-2, "out")
+        check_lse(torch.cat(list(lse), dim=1)[:, :, :S], rl, 1e-3)
+
+
 @pytest.mark.parametrize("strategy", [0, 1])
 @pytest.mark.parametrize("shape,P,dtype", [
     ((1, 65536), 4, torch.int32),
