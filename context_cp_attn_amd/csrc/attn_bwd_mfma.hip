@@ -90,6 +90,7 @@ struct BwdCfg {
   // dQ stage: K rows, V rows, kpos, kseg
   static constexpr int kStageQ = 2 * kTileN * 2 + 2 * BN * 4;
   static constexpr int kStageMax = kStageK > kStageQ ? kStageK : kStageQ;
+  static constexpr int kAhead = 3;  // LDS operand reads issued this many products ahead
   static constexpr int kLdsBytes = 2 * kStageMax;
   using TileM = DmaTile<BM, D, kThreads>;
   using TileN = DmaTile<BN, D, kThreads>;
@@ -242,11 +243,16 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
           s = f32x16{};
           dp = f32x16{};
           const int arow = qb * 32 + perm_row(l32);
-#pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks) {
-            s = mma(ld_row<C::D>(st.q, arow, 2 * ks + hi), kf[ks], s);
-            if constexpr (kDK) dp = mma(ld_row<C::D>(st.g, arow, 2 * ks + hi), vf[ks], dp);
-          }
+          // dK role: products alternate S (even) and dP (odd) over the k-steps
+          constexpr int kStep = kDK ? 2 : 1;
+          pipelined_products<kStep * C::KS, C::kAhead>(
+              [&](int i) { return ld_row<C::D>((i % kStep) ? st.g : st.q, arow, 2 * (i / kStep) + hi); },
+              [&](int i, bf16x8 f) {
+                if (i % kStep)
+                  dp = mma(f, vf[i / kStep], dp);
+                else
+                  s = mma(f, kf[i / kStep], s);
+              });
         };
         auto soft = [&](int qb, f32x16& s, const f32x16& dp, auto masked) {
           constexpr bool kMasked = decltype(masked)::value;
@@ -279,13 +285,10 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
         // the A operand (dO^T or Q^T) is read transposed from the row-major tile
         const uint16_t* at = kDK ? st.q : st.g;
         auto grad = [&](int qb, const f32x16& s) {
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const bf16x8 bfrag = to_bf16x8(s, 8 * tt);
-#pragma unroll
-            for (int d = 0; d < C::DB; ++d)
-              acc[d] = mma(ld_tr<C::D>(at, (qb * 2 + tt) * 16, d * 32), bfrag, acc[d]);
-          }
+          const bf16x8 bfrag[2] = {to_bf16x8(s, 0), to_bf16x8(s, 8)};
+          pipelined_products<2 * C::DB, C::kAhead>(
+              [&](int i) { return ld_tr<C::D>(at, (qb * 2 + i / C::DB) * 16, (i % C::DB) * 32); },
+              [&](int i, bf16x8 f) { acc[i % C::DB] = mma(f, bfrag[i / C::DB], acc[i % C::DB]); });
         };
         auto body = [&](auto masked) {
 #pragma unroll
@@ -440,11 +443,14 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
             // S^T = K Q^T and dP^T = V dO^T for 32 keys: lane column = this lane's query
             f32x16 s = f32x16{}, dp = f32x16{};
             const int arow = kb * 32 + perm_row(l32);
-#pragma unroll
-            for (int kk = 0; kk < C::KS; ++kk) {
-              s = mma(ld_row<C::D>(ks, arow, 2 * kk + hi), qf[kk], s);
-              dp = mma(ld_row<C::D>(vs, arow, 2 * kk + hi), gf[kk], dp);
-            }
+            pipelined_products<2 * C::KS, C::kAhead>(
+                [&](int i) { return ld_row<C::D>((i & 1) ? vs : ks, arow, 2 * (i >> 1) + hi); },
+                [&](int i, bf16x8 f) {
+                  if (i & 1)
+                    dp = mma(f, gf[i >> 1], dp);
+                  else
+                    s = mma(f, qf[i >> 1], s);
+                });
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
               const int kk0 = kb * 32 + key_of_reg(4 * jj, hi);
@@ -464,13 +470,10 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
               }
             }
             // dQ^T += K^T dS^T over the block's two 16-key k-steps (K^T read transposed)
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-              const bf16x8 sb = to_bf16x8(s, 8 * tt);
-#pragma unroll
-              for (int d = 0; d < C::DB; ++d)
-                acc[d] = mma(ld_tr<C::D>(ks, (kb * 2 + tt) * 16, d * 32), sb, acc[d]);
-            }
+            const bf16x8 sb[2] = {to_bf16x8(s, 0), to_bf16x8(s, 8)};
+            pipelined_products<2 * C::DB, C::kAhead>(
+                [&](int i) { return ld_tr<C::D>(ks, (kb * 2 + i / C::DB) * 16, (i % C::DB) * 32); },
+                [&](int i, bf16x8 f) { acc[i % C::DB] = mma(f, sb[i / C::DB], acc[i % C::DB]); });
           }
         };
         if (wcls == kPartial)

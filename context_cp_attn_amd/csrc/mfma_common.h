@@ -271,6 +271,29 @@ struct DmaTile {
   }
 };
 
+// Issue N matrix products whose A operands come from LDS with each operand read
+// kAhead products ahead of its use: load(i) returns product i's fragment, mul(i, f)
+// issues it.  Scheduling fences keep the order, so the reads are in flight while
+// earlier products run instead of each product waiting for its own read.
+template <int N, int kAhead, class Load, class Mul>
+CP_DEVICE void pipelined_products(Load&& load, Mul&& mul) {
+  if constexpr (kAhead == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) mul(i, load(i));
+  } else {
+    bf16x8 frag[kAhead + 1];
+#pragma unroll
+    for (int i = 0; i < kAhead && i < N; ++i) frag[i] = load(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (i + kAhead < N) frag[(i + kAhead) % (kAhead + 1)] = load(i + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(i, frag[i % (kAhead + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // Wait for every outstanding memory operation of this wavefront (LDS-DMA included).
 CP_DEVICE void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
