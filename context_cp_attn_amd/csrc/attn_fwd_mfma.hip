@@ -59,6 +59,7 @@ struct FwdCfg {
   static constexpr int kLdsBytes = NS * 2 * kStageBytes;
   // exchange of the second key group's (o, m, l) per lane, over the stages
   static constexpr int kXchgBytes = NW * 64 * (DB * 16 + 2) * 4;
+  static constexpr int kAhead = 2;  // LDS operand reads issued ahead of their product
   using Tile = DmaTile<BN, D, kGroupThreads>;
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
   static_assert(NS == 1 || (NS == 2 && kXchgBytes <= kLdsBytes), "key groups");
@@ -180,15 +181,13 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
         const int* kpos_l = reinterpret_cast<const int*>(vs_l + C::kTileElems);
         const int* kseg_l = kpos_l + C::BN;
 
-        // S^T = K Q^T
+        // S^T = K Q^T (K rows read ahead of their products)
         f32x16 s[C::KB];
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-        for (int kstep = 0; kstep < C::KS; ++kstep)
-#pragma unroll
-          for (int kb = 0; kb < C::KB; ++kb)
-            s[kb] = mma(ld_row<C::D>(ks_l, kb * 32 + perm_row(l32), 2 * kstep + hi), qf[kstep], s[kb]);
+        pipelined_products<C::KS * C::KB, C::kAhead>(
+            [&](int i) { return ld_row<C::D>(ks_l, (i % C::KB) * 32 + perm_row(l32), 2 * (i / C::KB) + hi); },
+            [&](int i, bf16x8 f) { s[i % C::KB] = mma(f, qf[i / C::KB], s[i % C::KB]); });
 
         if (wcls == kPartial) {
           const int nvalid = p.Sk - cur * C::BN;
@@ -235,14 +234,13 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
           }
         l += rs;
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T (V^T fragments read ahead of their products)
+        bf16x8 pf[C::PT];
 #pragma unroll
-        for (int t = 0; t < C::PT; ++t) {
-          const bf16x8 pf = to_bf16x8(s[t >> 1], 8 * (t & 1));
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db)
-            o[db] = mma(ld_tr<C::D>(vs_l, t * 16, db * 32), pf, o[db]);
-        }
+        for (int t = 0; t < C::PT; ++t) pf[t] = to_bf16x8(s[t >> 1], 8 * (t & 1));
+        pipelined_products<C::PT * C::DB, C::kAhead>(
+            [&](int i) { return ld_tr<C::D>(vs_l, (i / C::DB) * 16, (i % C::DB) * 32); },
+            [&](int i, bf16x8 f) { o[i % C::DB] = mma(f, pf[i / C::DB], o[i % C::DB]); });
       }
 
       wait_all();
