@@ -80,9 +80,9 @@ struct BwdCfg {
   static constexpr int kRows = 32 * NW;  // keys (dV/dK roles) or queries (dQ role) per workgroup
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int BM = 64;          // query tile of the dV/dK roles
+  static constexpr int BM = 128;         // query tile of the dV/dK roles
   static constexpr int QBLK = BM / 32;
-  static constexpr int BN = 64;          // key tile of the dQ role
+  static constexpr int BN = 128;         // key tile of the dQ role
   static constexpr int KB = BN / 32;
   static constexpr int kTileM = BM * D, kTileN = BN * D;  // swizzled row-major tiles
   // dV / dK stage: Q rows, dO rows, lse2, delta, qpos, qseg
