@@ -31,6 +31,8 @@
 //    load, no math), full (no mask) or partial (elementwise mask) from the
 //    extreme positions / segment ids of the tile, which are monotone.
 //  * Causal grids run the heaviest query tiles of every head first.
+#include <type_traits>
+
 #include "mfma_common.h"
 #include "prof.h"
 
@@ -163,9 +165,11 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     if (cur < n_kt) stage_load(cur, stage_of(0));
     wait_all();
     __syncthreads();
-    int buf = 0;
     const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
-    while (true) {
+    // one tile per call, the stage index a compile-time constant (the loop below
+    // alternates 0 and 1), so the swizzled LDS addresses of each stage are fixed
+    auto iter = [&](auto bufc) -> bool {
+      constexpr int buf = decltype(bufc)::value;
       const int n0 = next_tile((C::NS > 1 && t1 < n_kt ? t1 : t0) + 1);
       const int n1 = (C::NS > 1 && n0 < n_kt) ? next_tile(n0 + 1) : n_kt;
       const int nxt = grp == 0 ? n0 : n1;
@@ -245,11 +249,12 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
 
       wait_all();
       __syncthreads();
-      if (!has_next) break;
       t0 = n0;
       t1 = n1;
       cur = nxt;
-      buf ^= 1;
+      return has_next;
+    };
+    while (iter(std::integral_constant<int, 0>{}) && iter(std::integral_constant<int, 1>{})) {
     }
   }
 
