@@ -142,6 +142,30 @@ def test_merge_rejects():
     assert f(1, 8, 2, 128, FAKE_A, FAKE_B, FAKE_A, 1 << 41, 1, None) == ALIAS
 
 
+def test_relayout_ex_rejects():
+    lib = _lib.load()
+
+    def call(inp=FAKE_A, out=FAKE_B, **kw):
+        a = dict(groups=1, P=4, batch=1, seqlen=32, heads=8, head_dim=16, elem_bytes=2, rep=1, inverse=0)
+        a.update(kw)
+        st = lib.cp_ulysses_relayout_ex(ctypes.byref(_lib.RelayoutArgs(**a)), inp, out, None)
+        return st, lib.cp_last_error().decode()
+
+    assert call(groups=0)[0] == INVALID
+    assert call(rep=0)[0] == INVALID
+    assert call(seqlen=30)[0] == INVALID                          # S % P
+    st, err = call(heads=2, P=4)                                    # 2 heads over 4 ranks, no replication
+    assert st == INVALID and "replicated" in err
+    assert call(heads=2, P=4, rep=2, inverse=1)[0] == INVALID       # replica sums need float32
+    assert call(elem_bytes=3)[0] == INVALID
+    assert call(inverse=2)[0] == INVALID
+    assert call(groups=70000)[0] == UNSUPPORTED
+    # the head side is rep times the sequence side: an output just past the input's
+    # end still overlaps when it is the larger side
+    assert call(out=FAKE_A + 32 * 8 * 16 * 2 - 16)[0] == ALIAS
+    assert lib.cp_ulysses_relayout_ex(None, FAKE_A, FAKE_B, None) == INVALID
+
+
 def test_pad_rows_rejects():
     lib = _lib.load()
     f = lib.cp_pad_rows
