@@ -133,6 +133,37 @@ def timed(torch, fn, reps):
     return s.elapsed_time(e) / reps
 
 
+def packed_work(seg, P, layout, window, D):
+    """Visible (query, key) pairs per head of a causal packed + windowed sequence
+    (counted from the segment ids: a query sees the keys of its own document no
+    further back than the window), and the fraction of the forward's query-tile x
+    key-tile blocks that hold no visible pair over all P ranks' P ring steps."""
+    import numpy as np
+    S = seg.shape[0]
+    start = np.zeros(S, dtype=np.int64)
+    for t in range(1, S):
+        start[t] = start[t - 1] if seg[t] == seg[t - 1] else t
+    i = np.arange(S)
+    pairs = int(np.sum(np.minimum(i - start + 1, window)))
+    # the kernel's tiles: 128 query rows x 64 keys of one rank pair
+    C = S // P
+    if layout == "striped":
+        pos = [np.arange(r, S, P) for r in range(P)]
+    else:
+        c = S // (2 * P)
+        pos = [np.r_[np.arange(r * c, (r + 1) * c), np.arange((2 * P - 1 - r) * c, (2 * P - r) * c)] for r in range(P)]
+    empty = total = 0
+    for r in range(P):
+        for src in range(P):
+            qp, kp = pos[r], pos[src]
+            vis = (kp[None, :] <= qp[:, None]) & (seg[qp][:, None] == seg[kp][None, :]) & \
+                  (qp[:, None] - kp[None, :] < window)
+            blk = vis.reshape(C // 128, 128, C // 64, 64).any(axis=(1, 3))
+            empty += int((~blk).sum())
+            total += blk.size
+    return pairs, empty / total
+
+
 def legs(torch, cp, cp_inputs):
     """Ring share (llama2-7b, cp=16), 64K reorder and the packed + windowed ring."""
     out = {}
@@ -197,7 +228,11 @@ def legs(torch, cp, cp_inputs):
 
         packed_pass()
         ms = timed(torch, packed_pass, 3)
-        out[f"packed_window_8k_cp4_all_ranks_{name}"] = {"strategy": layout, "ms_per_pass": round(ms, 3)}
+        pairs, skipped = packed_work(seg[0].cpu().numpy(), P, layout, 4096, D)
+        fl = 12 * D * Hq * pairs  # forward 4*D + backward 8*D per visible pair and head
+        out[f"packed_window_8k_cp4_all_ranks_{name}"] = {
+            "strategy": layout, "ms_per_pass": round(ms, 3), "visible_pairs_per_head": pairs,
+            "tflops": round(fl / ms / 1e9, 2), "fwd_tiles_skipped_frac": round(skipped, 4)}
     # beyond the kv head count, llama3.1-8b (32 q / 8 kv heads) at 16K tokens on 16 ranks:
     # Ulysses 8 within groups x ring 2 across them (USP), and Ulysses 16 with kv heads
     # replicated 2x; forward of all ranks, algorithmic causal FLOPs of the whole sequence
