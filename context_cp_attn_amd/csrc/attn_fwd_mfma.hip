@@ -75,7 +75,7 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
                         float* __restrict__ lse, uint8_t* smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int grp = C::NS > 1 ? wave / C::NW : 0;  // key group
