@@ -165,15 +165,19 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
 
   const float c2 = p.scale * kLog2e;
   const int n_it = (p.Sq + C::BM - 1) / C::BM;
-  // A tile is (query head of the group hh, query tile it), walked hh-major with
-  // incremental counters (no integer division in the loop).
+  // A tile is (query head of the group hh, query tile it).  Query tiles are walked
+  // from the last one down, the heads of the group innermost: every workgroup of
+  // this role starts at the end of the sequence and sweeps down at about the same
+  // pace, so the workgroups resident together read the same Q / dO tiles and the
+  // caches serve most of them (walked upward from their own diagonals they would
+  // spread over all of Q and dO at once).
   struct Tq {
     int hh, it;
   };
   auto step = [&](Tq t) {
-    if (++t.it == n_it) {
-      t.it = 0;
-      ++t.hh;
+    if (++t.hh == G) {
+      t.hh = 0;
+      --t.it;
     }
     return t;
   };
@@ -182,7 +186,7 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
     return classify(p, q_span(p, b, i0, min(i0 + C::BM, p.Sq) - 1), ksp, false);
   };
   auto next_tile = [&](Tq t) {
-    while (t.hh < G && tile_class(t, wg_k) == kEmpty) t = step(t);
+    while (t.it >= 0 && tile_class(t, wg_k) == kEmpty) t = step(t);
     return t;
   };
   typename C::TileM tq, tg;
@@ -221,15 +225,15 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
     __syncthreads();
   };
 
-  Tq cur = next_tile(Tq{0, 0});
-  if (cur.hh < G) {
+  Tq cur = next_tile(Tq{0, n_it - 1});
+  if (cur.it >= 0) {
     issue(cur, smem);
     publish(smem);
     int buf = 0;
     const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
     while (true) {
       const Tq nxt = next_tile(step(cur));
-      const bool has_next = nxt.hh < G;
+      const bool has_next = nxt.it >= 0;
       uint8_t* nbase = smem + (buf ^ 1) * C::kStageMax;
       if (has_next) issue(nxt, nbase);
       const int wcls = wave_live ? tile_class(cur, wv_k) : kEmpty;
@@ -508,7 +512,8 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
 // ---- fused launch ------------------------------------------------------------------
 // Key-side items (dK then dV of each key block, key blocks lowest first = heaviest
 // under a causal mask) and query-side items (query blocks highest first) are merged
-// at the ratio of their counts.
+// at the ratio of their counts, then rotated within each round of 8 workgroups so
+// that every XCD receives a fair share of each role.
 struct BwdArgs {
   AttnProblem p;
   const uint16_t* q;
@@ -529,8 +534,14 @@ template <class C>
 __global__ __launch_bounds__(C::kThreads) void attn_bwd_kernel(BwdArgs a) {
   __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
   const AttnProblem& p = a.p;
-  const int64_t L = blockIdx.x;
   const int64_t N = int64_t(a.n_kv) + a.n_q;
+  // Workgroups go to the 8 XCDs round-robin by index.  Within each round of 8
+  // consecutive workgroups the items are rotated by the round number, so that the
+  // periodic role pattern of the interleaved list cannot alias with the XCD index
+  // (at a 1:2 key/query ratio it would put every dK item on the even XCDs).
+  const int64_t u = blockIdx.x / 8;
+  const int64_t width = N - 8 * u < 8 ? N - 8 * u : 8;
+  const int64_t L = 8 * u + (blockIdx.x % 8 + u) % width;
   const int64_t before = (L * a.n_kv) / N;  // key-side items placed before L
   const bool kv_side = ((L + 1) * a.n_kv) / N > before;
   if (kv_side) {
