@@ -351,6 +351,9 @@ def main():
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(step.flops_fwd_rank / (fwd_ms * 1e-3) / 1e12, 2),
         "bwd_tflops": round(step.flops_bwd_rank / (bwd_ms * 1e-3) / 1e12, 2),
+        # the FlashAttention papers count the backward as 10*D per pair (QK^T recomputed);
+        # printed for comparison only, never used in value or roofline
+        "bwd_tflops_fa_convention_10D": round(step.flops_bwd_rank * 10 / 8 / (bwd_ms * 1e-3) / 1e12, 2),
         "relayout_gbps": round(step.relayout_bytes / (rel_t * 1e-3) / 1e9, 1),
         "relayout_pct_hbm_peak": round(100 * step.relayout_bytes / (rel_t * 1e-3) / 1e9 / PEAK_HBM_GBPS, 1),
         "roofline": roof,
