@@ -42,6 +42,7 @@ SIGNATURES = {
     "cp_attn_fwd": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "cp_attn_fwd_merge": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "cp_attn_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(AttnArgs)]),
+    "cp_attn_check_args": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp]),
     "cp_attn_bwd": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                             c_vp, c_i32, c_vp, ctypes.c_size_t, c_vp]),
     "cp_lse_merge": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp]),

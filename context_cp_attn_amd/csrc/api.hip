@@ -45,6 +45,12 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int64_t dtype_bytes(int32_t dt) { return dt == CP_DTYPE_BF16 ? 2 : 4; }
 
+// bf16 problems with these head dims run on the matrix-core kernels; other bf16
+// head dims up to 128 run on the row-per-wavefront kernels.
+bool mfma_path(const cp_attn_args_t* a) {
+  return a->dtype == CP_DTYPE_BF16 && (a->head_dim == 32 || a->head_dim == 64 || a->head_dim == 128);
+}
+
 // Shared validation of cp_attn_fwd / cp_attn_bwd arguments; fills the device problem.
 cp_status_t check_attn(const cp_attn_args_t* a, const void* q, const void* k, const void* v,
                        cp::AttnProblem* p) {
@@ -82,15 +88,15 @@ cp_status_t check_attn(const cp_attn_args_t* a, const void* q, const void* k, co
     return fail(CP_ERR_INVALID, "q_offset %lld: positions must lie in [0, 2^31)", (long long)a->q_offset);
   if (!a->k_pos && (a->k_offset < 0 || a->k_offset + a->seqlen_k > INT_MAX))
     return fail(CP_ERR_INVALID, "k_offset %lld: positions must lie in [0, 2^31)", (long long)a->k_offset);
-  if (a->dtype == CP_DTYPE_BF16) {
-    if (a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
-      return fail(CP_ERR_UNSUPPORTED, "bf16 attention is built for head_dim 32, 64, 128 (got %lld)",
-                  (long long)a->head_dim);
+  if (a->head_dim > 128)
+    return fail(CP_ERR_UNSUPPORTED, "attention is built for head_dim <= 128 (got %lld)",
+                (long long)a->head_dim);
+  if (mfma_path(a)) {
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
       return fail(CP_ERR_INVALID, "bf16 q, k, v must be 16-byte aligned");
-  } else if (a->head_dim > 128) {
-    return fail(CP_ERR_UNSUPPORTED, "float32 attention is built for head_dim <= 128 (got %lld)",
-                (long long)a->head_dim);
+  } else if (!aligned(q, dtype_bytes(a->dtype)) || !aligned(k, dtype_bytes(a->dtype)) ||
+             !aligned(v, dtype_bytes(a->dtype))) {
+    return fail(CP_ERR_INVALID, "q, k, v must be aligned to their element size");
   }
   p->B = int(a->batch);
   p->Sq = int(a->seqlen_q);
@@ -144,9 +150,12 @@ cp_status_t cp_attn_fwd(const cp_attn_args_t* a, const void* q, const void* k, c
   }
   if (overlaps(out, qbytes, lse, lbytes)) return fail(CP_ERR_ALIAS, "out overlaps lse");
   hipError_t e;
-  if (a->dtype == CP_DTYPE_BF16) {
-    if (!aligned(out, 16)) return fail(CP_ERR_INVALID, "bf16 out must be 16-byte aligned");
+  if (!aligned(out, mfma_path(a) ? 16 : eb) || !aligned(lse, 4))
+    return fail(CP_ERR_INVALID, "out or lse is misaligned");
+  if (mfma_path(a)) {
     e = cp::launch_attn_fwd_bf16(p, q, k, v, out, lse, stream);
+  } else if (a->dtype == CP_DTYPE_BF16) {
+    e = cp::launch_attn_fwd_rowwise_bf16(p, q, k, v, out, lse, stream);
   } else {
     e = cp::launch_attn_fwd_f32(p, static_cast<const float*>(q), static_cast<const float*>(k),
                                 static_cast<const float*>(v), static_cast<float*>(out), lse, stream);
@@ -160,7 +169,7 @@ cp_status_t cp_attn_fwd_merge(const cp_attn_args_t* a, const void* q, const void
   cp_status_t st = check_attn(a, q, k, v, &p);
   if (st != CP_OK) return st;
   if (!out_acc || !lse_acc) return fail(CP_ERR_INVALID, "out_acc and lse_acc must be non-NULL");
-  if (!aligned(out_acc, 16)) return fail(CP_ERR_INVALID, "out_acc must be 16-byte aligned");
+  if (!aligned(out_acc, mfma_path(a) ? 16 : 4)) return fail(CP_ERR_INVALID, "out_acc is misaligned");
   const int64_t eb = dtype_bytes(a->dtype);
   const int64_t qbytes = a->batch * a->seqlen_q * a->heads_q * a->head_dim * eb;
   const int64_t kbytes = a->batch * a->seqlen_k * a->heads_kv * a->head_dim * eb;
@@ -173,13 +182,29 @@ cp_status_t cp_attn_fwd_merge(const cp_attn_args_t* a, const void* q, const void
   }
   if (overlaps(out_acc, abytes, lse_acc, lbytes)) return fail(CP_ERR_ALIAS, "out_acc overlaps lse_acc");
   hipError_t e;
-  if (a->dtype == CP_DTYPE_BF16) {
+  if (!aligned(lse_acc, 4)) return fail(CP_ERR_INVALID, "lse_acc is misaligned");
+  if (mfma_path(a)) {
     e = cp::launch_attn_fwd_merge_bf16(p, q, k, v, out_acc, lse_acc, stream);
+  } else if (a->dtype == CP_DTYPE_BF16) {
+    e = cp::launch_attn_fwd_merge_rowwise_bf16(p, q, k, v, out_acc, lse_acc, stream);
   } else {
     e = cp::launch_attn_fwd_merge_f32(p, static_cast<const float*>(q), static_cast<const float*>(k),
                                       static_cast<const float*>(v), out_acc, lse_acc, stream);
   }
   return hip_status(e, "cp_attn_fwd_merge launch");
+}
+
+cp_status_t cp_attn_check_args(const cp_attn_args_t* a, int32_t* flags, hipStream_t stream) {
+  if (!a) return fail(CP_ERR_INVALID, "args is NULL");
+  if (!flags || !aligned(flags, 4)) return fail(CP_ERR_INVALID, "flags must be a non-NULL, 4-byte aligned int32");
+  if (a->batch < 1 || a->seqlen_q < 1 || a->seqlen_k < 1 || a->seqlen_q > INT_MAX || a->seqlen_k > INT_MAX ||
+      a->batch > INT_MAX)
+    return fail(CP_ERR_INVALID, "sizes must be >= 1 and seqlens < 2^31");
+  if ((a->q_seg == nullptr) != (a->k_seg == nullptr))
+    return fail(CP_ERR_INVALID, "q_seg and k_seg must both be given or both be NULL");
+  const hipError_t e = cp::launch_check_args(a->q_pos, a->k_pos, a->q_seg, a->k_seg, a->batch, a->seqlen_q,
+                                             a->seqlen_k, flags, stream);
+  return hip_status(e, "cp_attn_check_args launch");
 }
 
 size_t cp_attn_bwd_workspace_size(const cp_attn_args_t* a) {
@@ -222,10 +247,14 @@ cp_status_t cp_attn_bwd(const cp_attn_args_t* a, const void* q, const void* k, c
   }
   float* delta = static_cast<float*>(workspace);
   hipError_t e;
-  if (a->dtype == CP_DTYPE_BF16) {
-    if (!aligned(out, 16) || !aligned(dout, 16))
-      return fail(CP_ERR_INVALID, "bf16 out and dout must be 16-byte aligned");
+  if (!aligned(out, mfma_path(a) ? 16 : eb) || !aligned(dout, mfma_path(a) ? 16 : eb))
+    return fail(CP_ERR_INVALID, "out or dout is misaligned");
+  if (!aligned(lse, 4) || !aligned(dq, 4) || !aligned(dk, 4) || !aligned(dv, 4))
+    return fail(CP_ERR_INVALID, "lse or a gradient buffer is misaligned");
+  if (mfma_path(a)) {
     e = cp::launch_attn_bwd_bf16(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, stream);
+  } else if (a->dtype == CP_DTYPE_BF16) {
+    e = cp::launch_attn_bwd_rowwise_bf16(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, stream);
   } else {
     e = cp::launch_attn_bwd_f32(p, static_cast<const float*>(q), static_cast<const float*>(k),
                                 static_cast<const float*>(v), static_cast<const float*>(out), lse,

@@ -1,8 +1,10 @@
 // Row-per-wavefront attention kernels (forward and backward).
 //
 // These serve the float32 problems (small head counts and sequence lengths, e.g.
-// the handbook's toy data), where the bf16 matrix-core path does not apply.  All
-// arithmetic is float32.  One
+// the handbook's toy data) and bf16 head dims the matrix-core kernels are not
+// built for (any D <= 128 other than 32, 64, 128, e.g. 16).  All arithmetic is
+// float32; bf16 inputs are widened on load and the bf16 output is rounded to
+// nearest even.  One
 // wavefront owns one row; a lane holds head-dim elements d = lane + 64*t, dot
 // products are wavefront sums, and keys are visited one at a time with the online
 // softmax.
@@ -10,6 +12,8 @@
 // Definition: handbook "Context parallelism: Ring Attention and Ulysses",
 // §"Which operations partition directly" (attention with offsets returning the
 // log-sum-exp); gradient: the softmax-attention VJP with Delta_i = dO_i . O_i.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "prof.h"
@@ -25,11 +29,14 @@ CP_DEVICE int kpos_of(const AttnProblem& p, int j) { return p.k_pos ? p.k_pos[j]
 
 // NT = ceil(D / 64) elements per lane.  kMerge = true (fused ring step): out is the
 // float32 accumulator and lse the accumulator's lse, merged in place.
+template <typename T, bool kMerge>
+using OutT = typename std::conditional<kMerge, float, T>::type;
+
 template <typename T, int NT, bool kMerge>
 __global__ __launch_bounds__(kThreads) void fwd_rowwise_kernel(AttnProblem p, const T* __restrict__ q,
                                                                const T* __restrict__ k,
                                                                const T* __restrict__ v,
-                                                               T* __restrict__ out,
+                                                               OutT<T, kMerge>* __restrict__ out,
                                                                float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -72,12 +79,11 @@ __global__ __launch_bounds__(kThreads) void fwd_rowwise_kernel(AttnProblem p, co
     }
     m = mn;
   }
-  T* orow = out + ((int64_t(b) * p.Sq + i) * p.Hq + h) * D;
+  OutT<T, kMerge>* orow = out + ((int64_t(b) * p.Sq + i) * p.Hq + h) * D;
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   const float lse_blk = l > 0.0f ? m + logf(l) : -INFINITY;
   const int64_t li = (int64_t(b) * p.Hq + h) * p.Sq + i;
   if constexpr (kMerge) {
-    static_assert(sizeof(T) == 4, "the accumulator is float32");
     // every lane reads the old lse (one wave-wide load) before lane 0 writes it
     const MergeWeights w = merge_weights(lse[li], lse_blk);
 #pragma unroll
@@ -258,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_rowwise_kernel(AttnProblem p, c
 }
 
 template <typename T, int NT, bool kMerge>
-hipError_t fwd_nt(const AttnProblem& p, const T* q, const T* k, const T* v, T* out, float* lse,
+hipError_t fwd_nt(const AttnProblem& p, const T* q, const T* k, const T* v, OutT<T, kMerge>* out, float* lse,
                   hipStream_t s) {
   dim3 grid((p.Sq + kWaves - 1) / kWaves, p.Hq, p.B);
   ProfScope ps(s, kMerge ? kProfFwdMergeRowwise : kProfFwdRowwise);
@@ -300,6 +306,28 @@ hipError_t launch_attn_bwd_f32(const AttnProblem& p, const float* q, const float
                                float* dk, float* dv, int accumulate, float* delta, hipStream_t s) {
   return p.D <= 64 ? bwd_nt<float, 1>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, s)
                    : bwd_nt<float, 2>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, s);
+}
+
+hipError_t launch_attn_fwd_rowwise_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
+                                        void* out, float* lse, hipStream_t s) {
+  using U = const uint16_t*;
+  return p.D <= 64 ? fwd_nt<uint16_t, 1, false>(p, U(q), U(k), U(v), static_cast<uint16_t*>(out), lse, s)
+                   : fwd_nt<uint16_t, 2, false>(p, U(q), U(k), U(v), static_cast<uint16_t*>(out), lse, s);
+}
+
+hipError_t launch_attn_fwd_merge_rowwise_bf16(const AttnProblem& p, const void* q, const void* k,
+                                              const void* v, float* acc, float* lse_acc, hipStream_t s) {
+  using U = const uint16_t*;
+  return p.D <= 64 ? fwd_nt<uint16_t, 1, true>(p, U(q), U(k), U(v), acc, lse_acc, s)
+                   : fwd_nt<uint16_t, 2, true>(p, U(q), U(k), U(v), acc, lse_acc, s);
+}
+
+hipError_t launch_attn_bwd_rowwise_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
+                                        const void* out, const float* lse, const void* dout, float* dq,
+                                        float* dk, float* dv, int accumulate, float* delta, hipStream_t s) {
+  using U = const uint16_t*;
+  return p.D <= 64 ? bwd_nt<uint16_t, 1>(p, U(q), U(k), U(v), U(out), lse, U(dout), dq, dk, dv, accumulate, delta, s)
+                   : bwd_nt<uint16_t, 2>(p, U(q), U(k), U(v), U(out), lse, U(dout), dq, dk, dv, accumulate, delta, s);
 }
 
 }  // namespace cp

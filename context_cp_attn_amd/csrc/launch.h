@@ -30,6 +30,16 @@ hipError_t launch_attn_fwd_merge_bf16(const AttnProblem& p, const void* q, const
 hipError_t launch_attn_fwd_merge_f32(const AttnProblem& p, const float* q, const float* k, const float* v,
                                      float* acc, float* lse_acc, hipStream_t s);
 
+// bf16 head dims without a matrix-core kernel (D <= 128 other than 32, 64, 128):
+// the row-per-wavefront kernels with bf16 loads / stores
+hipError_t launch_attn_fwd_rowwise_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
+                                        void* out, float* lse, hipStream_t s);
+hipError_t launch_attn_fwd_merge_rowwise_bf16(const AttnProblem& p, const void* q, const void* k,
+                                              const void* v, float* acc, float* lse_acc, hipStream_t s);
+hipError_t launch_attn_bwd_rowwise_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
+                                        const void* out, const float* lse, const void* dout, float* dq,
+                                        float* dk, float* dv, int accumulate, float* delta, hipStream_t s);
+
 // backward: delta workspace is [B,Hq,Sq] float32
 hipError_t launch_attn_bwd_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
                                 const void* out, const float* lse, const void* dout, float* dq,
@@ -37,6 +47,10 @@ hipError_t launch_attn_bwd_bf16(const AttnProblem& p, const void* q, const void*
 hipError_t launch_attn_bwd_f32(const AttnProblem& p, const float* q, const float* k, const float* v,
                                const float* out, const float* lse, const float* dout, float* dq,
                                float* dk, float* dv, int accumulate, float* delta, hipStream_t s);
+
+// precondition check of the position / segment arrays; writes a violation bit mask
+hipError_t launch_check_args(const int* q_pos, const int* k_pos, const int* q_seg, const int* k_seg, int64_t B,
+                             int64_t Sq, int64_t Sk, int* flags, hipStream_t s);
 
 // data movement
 hipError_t launch_lse_merge(int64_t B, int64_t S, int64_t H, int64_t D, float* acc, float* lse_acc,

@@ -9,10 +9,10 @@ namespace cp {
 
 enum ProfKernel : int {
   kProfFwdMfma = 0,     // bf16 attention forward (matrix cores)
-  kProfFwdRowwise,      // float32 attention forward
+  kProfFwdRowwise,      // row-per-wavefront forward (float32, bf16 head dims without MFMA kernel)
   kProfBwdDelta,        // bf16 backward pre-pass: Delta = rowsum(dO * O)
   kProfBwdMfma,         // bf16 backward: dK/dV and dQ roles in one grid
-  kProfBwdRowwise,      // float32 backward (delta, dQ, dK/dV)
+  kProfBwdRowwise,      // row-per-wavefront backward (delta, dQ, dK/dV)
   kProfLseMerge,        // ring-step log-sum-exp merge
   kProfUlysses,         // sequence -> head relayout
   kProfUlyssesInv,      // head -> sequence relayout

@@ -7,10 +7,16 @@ synchronizing.  All arithmetic happens in the HIP kernels of libcp_attn.
 from __future__ import annotations
 
 import ctypes
+import os
 
 import torch
 
 from . import _lib
+
+# CP_ATTN_DEBUG=1: every attention call first checks its position / segment arrays
+# on the device (cp_attn_check_args), synchronizes, and raises ValueError on a
+# violation.  Off by default: the check costs a synchronization per call.
+DEBUG = os.environ.get("CP_ATTN_DEBUG", "0") == "1"
 
 _DT = {torch.bfloat16: _lib.CP_DTYPE_BF16, torch.float32: _lib.CP_DTYPE_F32}
 
@@ -59,6 +65,33 @@ def make_args(q, k, *, causal=True, q_offset=0, k_offset=0, q_pos=None, k_pos=No
                          int(window), float(scale))
 
 
+_CHECK_BITS = {
+    1: "q_pos must be strictly increasing and >= 0",
+    2: "k_pos must be strictly increasing and >= 0",
+    4: "q_seg must be non-decreasing along each batch row",
+    8: "k_seg must be non-decreasing along each batch row",
+}
+
+
+def check_attn_args(q, k, **mask) -> list[str]:
+    """The preconditions the attention kernels rely on, checked on the device.
+
+    Returns one message per violated rule (empty list: all hold).  Synchronizes.
+    """
+    a = make_args(q, k, **mask)
+    flags = torch.empty(1, device=q.device, dtype=torch.int32)
+    _lib.check(_lib.load().cp_attn_check_args(ctypes.byref(a), flags.data_ptr(), _stream()))
+    f = int(flags.item())
+    return [msg for bit, msg in _CHECK_BITS.items() if f & bit]
+
+
+def _debug_check(q, k, mask):
+    if DEBUG:
+        errs = check_attn_args(q, k, **mask)
+        if errs:
+            raise ValueError("; ".join(errs))
+
+
 def _check_qkv(q, k, v):
     _dev(q, "q")
     _dev(k, "k", q.dtype)
@@ -74,6 +107,7 @@ def attn_fwd(q, k, v, *, out=None, lse=None, **mask):
     """
     _check_qkv(q, k, v)
     a = make_args(q, k, **mask)
+    _debug_check(q, k, mask)
     B, Sq, Hq, _ = q.shape
     out = torch.empty_like(q) if out is None else _dev(out, "out", q.dtype)
     lse = torch.empty(B, Hq, Sq, device=q.device, dtype=torch.float32) if lse is None else _dev(lse, "lse", torch.float32)
@@ -93,6 +127,7 @@ def attn_fwd_merge(q, k, v, out_acc, lse_acc, **mask):
     """
     _check_qkv(q, k, v)
     a = make_args(q, k, **mask)
+    _debug_check(q, k, mask)
     B, Sq, Hq, _ = q.shape
     _dev(out_acc, "out_acc", torch.float32)
     _dev(lse_acc, "lse_acc", torch.float32)
@@ -118,6 +153,7 @@ def attn_bwd(q, k, v, out, lse, dout, *, dq=None, dk=None, dv=None, accumulate=F
     _dev(dout, "dout", q.dtype)
     _dev(lse, "lse", torch.float32)
     a = make_args(q, k, **mask)
+    _debug_check(q, k, mask)
     f32 = dict(device=q.device, dtype=torch.float32)
     if accumulate and (dq is None or dk is None or dv is None):
         raise ValueError("accumulate needs dq, dk and dv")

@@ -59,7 +59,7 @@ typedef struct {
   int64_t seqlen_k;        /* Sk >= 1                                                    */
   int64_t heads_q;         /* Hq >= 1, a multiple of heads_kv                            */
   int64_t heads_kv;        /* Hkv >= 1; query head h uses kv head h / (Hq / Hkv)          */
-  int64_t head_dim;        /* D: bf16 in {32, 64, 128}; f32 in [1, 128]                  */
+  int64_t head_dim;        /* D in [1, 128] (bf16 32/64/128 on the matrix cores)         */
   int32_t dtype;           /* cp_dtype_t of q, k, v, out, dout                           */
   int32_t causal;          /* 0 or 1                                                     */
   int64_t q_offset;        /* global position of query 0 when q_pos is NULL              */
@@ -75,8 +75,10 @@ typedef struct {
 /*
  * Blockwise attention forward.  q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] (dtype);
  * out [B,Sq,Hq,D] (dtype); lse [B,Hq,Sq] float32, natural log of the row's
- * sum of exp(scale * q.k) over visible keys.  bf16 inputs are multiplied on the
- * matrix cores with float32 accumulation; out is rounded to nearest even.
+ * sum of exp(scale * q.k) over visible keys.  bf16 inputs with D in {32, 64, 128}
+ * are multiplied on the matrix cores (q, k, v, out 16-byte aligned); other D run on
+ * row-per-wavefront kernels (element-aligned buffers).  Accumulation is float32;
+ * a bf16 out is rounded to nearest even.  D > 128 gives CP_ERR_UNSUPPORTED.
  * out/lse must not overlap q, k or v (CP_ERR_ALIAS).
  */
 cp_status_t cp_attn_fwd(const cp_attn_args_t* args, const void* q, const void* k, const void* v,
@@ -91,7 +93,7 @@ cp_status_t cp_attn_fwd(const cp_attn_args_t* args, const void* q, const void* k
  *   lse' = log(e^lse_acc + e^lse_blk)
  *   acc' = acc * e^(lse_acc - lse') + out_blk * e^(lse_blk - lse')
  * with the -inf rules of cp_lse_merge (a row with no visible key in this block has
- * weight 0).  out_acc [B,Sq,Hq,D] float32 (16-byte aligned) and lse_acc [B,Hq,Sq]
+ * weight 0).  out_acc [B,Sq,Hq,D] float32 (16-byte aligned on the matrix-core path) and lse_acc [B,Hq,Sq]
  * float32 are read and written; start a ring with out_acc = 0, lse_acc = -inf.
  * out_acc/lse_acc must not overlap q, k, v or each other (CP_ERR_ALIAS).
  */
@@ -115,6 +117,18 @@ cp_status_t cp_attn_bwd(const cp_attn_args_t* args, const void* q, const void* k
                         const void* out, const float* lse, const void* dout,
                         float* dq, float* dk, float* dv, int32_t accumulate,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Debug check of the preconditions on args' arrays that the attention kernels rely
+ * on but the host cannot see: q_pos / k_pos strictly increasing and >= 0 (the block
+ * positions of [H] §"Ring Attention"), q_seg / k_seg non-decreasing along each of the
+ * B rows (the per-token segment ids of [MP]).  Two small kernels on `stream` clear
+ * *flags and set bit 0 (q_pos), 1 (k_pos), 2 (q_seg) or 3 (k_seg) for each array
+ * that breaks its rule; NULL arrays are skipped, 0 means all hold.  flags: caller-
+ * owned device int32, 4-byte aligned.  Asynchronous; read flags after the stream
+ * work ends.  CP_ERR_INVALID for a NULL args/flags or invalid sizes.
+ */
+cp_status_t cp_attn_check_args(const cp_attn_args_t* args, int32_t* flags, hipStream_t stream);
 
 /*
  * Ring-step merge, in place ([H] self-test answers and §"Ring Attention"):

@@ -63,7 +63,7 @@ def fwd(a, q=FAKE_A, k=FAKE_B, v=FAKE_C, out=1 << 44, lse=1 << 45):
     (dict(q_seg=FAKE_A), INVALID, "both"),
     (dict(softmax_scale=-1.0), INVALID, "softmax_scale"),
     (dict(q_offset=-5), INVALID, "q_offset"),
-    (dict(head_dim=16), UNSUPPORTED, "head_dim"),
+    (dict(head_dim=256), UNSUPPORTED, "head_dim"),
     (dict(head_dim=256, dtype=1), UNSUPPORTED, "head_dim"),
 ])
 def test_attn_fwd_rejects(kw, code, msg):
@@ -78,6 +78,28 @@ def test_attn_fwd_alias_and_alignment():
     assert st == ALIAS
     st, err = fwd(args(), q=FAKE_A + 2)     # bf16 operands must be 16-byte aligned
     assert st == INVALID and "aligned" in err
+    # head dims without a matrix-core kernel only need element alignment
+    st, err = fwd(args(head_dim=16), q=FAKE_A + 1)
+    assert st == INVALID and "aligned" in err
+    st, err = fwd(args(head_dim=16), out=(1 << 44) + 1)
+    assert st == INVALID and "misaligned" in err
+
+
+def test_attn_check_args_rejects():
+    lib = _lib.load()
+
+    def call(a, flags=1 << 44):
+        st = lib.cp_attn_check_args(None if a is None else ctypes.byref(a), flags, None)
+        return st, lib.cp_last_error().decode()
+
+    assert call(None)[0] == INVALID
+    st, err = call(args(), flags=0)
+    assert st == INVALID and "flags" in err
+    st, err = call(args(), flags=(1 << 44) + 2)
+    assert st == INVALID and "aligned" in err
+    assert call(args(seqlen_k=0))[0] == INVALID
+    st, err = call(args(k_seg=FAKE_A))
+    assert st == INVALID and "both" in err
 
 
 def test_attn_fwd_merge_rejects():

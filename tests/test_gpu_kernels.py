@@ -279,7 +279,8 @@ def oracle_mask(m):
 
 @pytest.mark.parametrize("name", list(CASES))
 @pytest.mark.parametrize("dtype,D", [(torch.float32, 16), (torch.float32, 128), (torch.bfloat16, 32),
-                                     (torch.bfloat16, 64), (torch.bfloat16, 128)])
+                                     (torch.bfloat16, 64), (torch.bfloat16, 128),
+                                     (torch.bfloat16, 16), (torch.bfloat16, 96)])  # row-per-wavefront bf16
 def test_attn_fwd(cp, name, dtype, D):
     say(f"attn_fwd {name} D={D} {dtype}")
     (q, k, v, _), m = make_case(name, D, dtype)
@@ -295,7 +296,7 @@ def test_attn_fwd(cp, name, dtype, D):
 
 @pytest.mark.parametrize("name", list(CASES))
 @pytest.mark.parametrize("dtype,D", [(torch.float32, 16), (torch.float32, 128), (torch.bfloat16, 32),
-                                     (torch.bfloat16, 128)])
+                                     (torch.bfloat16, 128), (torch.bfloat16, 16)])
 def test_attn_fwd_merge(cp, name, dtype, D):
     """Fused ring step = the oracle's merge of the oracle's block attention into a
     running (acc, lse) that has -inf rows, finite rows and rows that stay empty."""
@@ -322,7 +323,7 @@ def test_attn_fwd_merge(cp, name, dtype, D):
 
 @pytest.mark.parametrize("name", ["causal_square", "offsets", "zigzag_pos", "packed_window", "empty_rows"])
 @pytest.mark.parametrize("dtype,D", [(torch.float32, 16), (torch.float32, 128), (torch.bfloat16, 64),
-                                     (torch.bfloat16, 128)])
+                                     (torch.bfloat16, 128), (torch.bfloat16, 16)])
 def test_attn_bwd(cp, name, dtype, D):
     say(f"attn_bwd {name} D={D} {dtype}")
     (q, k, v, do), m = make_case(name, D, dtype, seed=3)
@@ -340,6 +341,64 @@ def test_attn_bwd(cp, name, dtype, D):
                                 accumulate=True, **dm)
     for a, b in ((dq2, dq), (dk2, dk), (dv2, dv)):
         torch.testing.assert_close(a, 2 * b, rtol=1e-6, atol=1e-6)
+
+
+def _expected_flags(B, qp, kp, qs, ks):
+    """The rules of cp_attn_check_args written with numpy."""
+    f = 0
+    for bit, pos in ((1, qp), (2, kp)):
+        if pos is not None and ((np.diff(pos) <= 0).any() or (pos < 0).any()):
+            f |= bit
+    for bit, seg in ((4, qs), (8, ks)):
+        if seg is not None and (np.diff(seg.reshape(B, -1), axis=1) < 0).any():
+            f |= bit
+    return f
+
+
+def test_check_attn_args(cp, monkeypatch):
+    """Violation bits of the device check equal the numpy rules, bit for bit; the
+    CP_ATTN_DEBUG mode raises before launching on a violation."""
+    say("check_attn_args")
+    from context_cp_attn_amd import ops
+    B, Sq, Sk = 2, 700, 515
+    q = torch.zeros(B, Sq, 2, 16, device="cuda")
+    k = torch.zeros(B, Sk, 1, 16, device="cuda")
+    rng = np.random.default_rng(11)
+    seen = set()
+    for trial in range(40):
+        # strictly increasing positions / non-decreasing ids (each row of the segment
+        # ids restarts, which is allowed), then up to one planted defect per array
+        qp = np.cumsum(rng.integers(1, 4, Sq)) - 1
+        kp = np.cumsum(rng.integers(1, 4, Sk)) + 7
+        qs = np.concatenate([np.sort(rng.integers(0, 5, Sq)) for _ in range(B)])
+        ks = np.concatenate([np.sort(rng.integers(0, 5, Sk)) for _ in range(B)])
+        for arr in (qp, kp, qs, ks):
+            kind = rng.integers(0, 4)
+            i = int(rng.integers(0, arr.size - 1))
+            if kind == 1:
+                arr[i + 1] = arr[i]            # a repeat: breaks strictness only
+            elif kind == 2:
+                arr[i + 1] = arr[i] - 1        # a step down
+            elif kind == 3:
+                arr[0] = -1 - int(rng.integers(0, 3))   # a negative first entry
+        want = _expected_flags(B, qp, kp, qs, ks)
+        seen.add(want)
+        t = lambda x: torch.from_numpy(x.astype(np.int32)).cuda()
+        msgs = cp.check_attn_args(q, k, q_pos=t(qp), k_pos=t(kp), q_seg=t(qs), k_seg=t(ks))
+        got = sum(bit for bit, msg in ops._CHECK_BITS.items() if msg in msgs)
+        assert got == want, (trial, got, want)
+    assert 0 in seen and len(seen) > 4
+    # NULL arrays are skipped
+    assert cp.check_attn_args(q, k) == []
+    # debug mode: a violation raises before any launch; valid arrays run normally
+    monkeypatch.setattr(ops, "DEBUG", True)
+    v = torch.zeros_like(k)
+    bad = torch.arange(Sq, dtype=torch.int32, device="cuda").flip(0).contiguous()
+    with pytest.raises(ValueError, match="q_pos"):
+        cp.attn_fwd(q, k, v, q_pos=bad)
+    out, lse = cp.attn_fwd(q, k, v, q_pos=torch.arange(Sq, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.isfinite(lse).all()
 
 
 @pytest.mark.parametrize("many_tiles", [False, True])
