@@ -96,6 +96,7 @@ class UlyssesStep:
         self.dql, self.dkl, self.dvl = (torch.empty(sh, device=dev, dtype=f32) for _ in range(3))
         self.dq, self.dk, self.dv = (torch.empty(P, 1, S // P, H, D, device=dev, dtype=f32) for _ in range(3))
         self.ws = cp.bwd_workspace(self.ql[0], self.kl[0])
+        self.fws = cp.fwd_workspace(self.ql[0], self.kl[0])   # None when the forward does not split
         hp = H // P
         self.flops_fwd_rank = 4 * D * hp * pairs_causal(S)
         self.flops_bwd_rank = 8 * D * hp * pairs_causal(S)
@@ -111,7 +112,7 @@ class UlyssesStep:
         cp.ulysses_relayout(ks, P, out=self.kl)
         cp.ulysses_relayout(vs, P, out=self.vl)
         for p in range(P):
-            cp.attn_fwd(self.ql[p], self.kl[p], self.vl[p], out=self.ol[p], lse=self.lse[p])
+            cp.attn_fwd(self.ql[p], self.kl[p], self.vl[p], out=self.ol[p], lse=self.lse[p], workspace=self.fws)
         cp.ulysses_relayout_inv(self.ol, P, out=self.out)
         cp.ulysses_relayout(gs, P, out=self.gl)
         for p in range(P):

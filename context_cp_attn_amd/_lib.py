@@ -41,6 +41,9 @@ class RelayoutArgs(ctypes.Structure):
 SIGNATURES = {
     "cp_attn_fwd": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "cp_attn_fwd_merge": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "cp_attn_fwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(AttnArgs)]),
+    "cp_attn_fwd_ws": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t,
+                               c_vp]),
     "cp_attn_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(AttnArgs)]),
     "cp_attn_check_args": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp]),
     "cp_attn_bwd": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,

@@ -133,12 +133,37 @@ const char* cp_status_string(cp_status_t st) {
 
 const char* cp_last_error(void) { return g_last_error.c_str(); }
 
-cp_status_t cp_attn_fwd(const cp_attn_args_t* a, const void* q, const void* k, const void* v,
-                        void* out, float* lse, hipStream_t stream) {
+namespace {
+
+// Workspace bytes of the split forward for args, 0 where it does not apply (the
+// problem is invalid, not on the matrix-core path, or large enough to fill the
+// current device with whole query tiles).
+size_t fwd_workspace_bytes(const cp_attn_args_t* a) {
+  if (!a || a->batch < 1 || a->seqlen_q < 1 || a->seqlen_k < 1 || a->heads_q < 1 || a->batch > 65535 ||
+      a->heads_q > 65535 || a->seqlen_q > INT_MAX || a->seqlen_k > INT_MAX || !mfma_path(a))
+    return 0;
+  cp::AttnProblem p{};
+  p.B = int(a->batch);
+  p.Sq = int(a->seqlen_q);
+  p.Sk = int(a->seqlen_k);
+  p.Hq = int(a->heads_q);
+  p.D = int(a->head_dim);
+  if (!cp::fwd_split_applies(p)) return 0;
+  return (cp::fwd_split_workspace_bytes(p) + 255) & ~size_t(255);
+}
+
+cp_status_t fwd_impl(const cp_attn_args_t* a, const void* q, const void* k, const void* v, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, bool with_ws, hipStream_t stream) {
   cp::AttnProblem p;
   cp_status_t st = check_attn(a, q, k, v, &p);
   if (st != CP_OK) return st;
   if (!out || !lse) return fail(CP_ERR_INVALID, "out and lse must be non-NULL");
+  const size_t need = with_ws ? fwd_workspace_bytes(a) : 0;
+  if (need) {
+    if (!workspace || workspace_bytes < need)
+      return fail(CP_ERR_INVALID, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    if (!aligned(workspace, 16)) return fail(CP_ERR_INVALID, "workspace must be 16-byte aligned");
+  }
   const int64_t eb = dtype_bytes(a->dtype);
   const int64_t qbytes = a->batch * a->seqlen_q * a->heads_q * a->head_dim * eb;
   const int64_t kbytes = a->batch * a->seqlen_k * a->heads_kv * a->head_dim * eb;
@@ -149,10 +174,19 @@ cp_status_t cp_attn_fwd(const cp_attn_args_t* a, const void* q, const void* k, c
       return fail(CP_ERR_ALIAS, "out/lse overlap an input");
   }
   if (overlaps(out, qbytes, lse, lbytes)) return fail(CP_ERR_ALIAS, "out overlaps lse");
+  if (need) {
+    const void* bufs[] = {q, k, v, out, lse};
+    const int64_t bytes[] = {qbytes, kbytes, kbytes, qbytes, lbytes};
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(workspace, int64_t(need), bufs[i], bytes[i]))
+        return fail(CP_ERR_ALIAS, "the workspace overlaps an input or output");
+  }
   hipError_t e;
   if (!aligned(out, mfma_path(a) ? 16 : eb) || !aligned(lse, 4))
     return fail(CP_ERR_INVALID, "out or lse is misaligned");
-  if (mfma_path(a)) {
+  if (need) {
+    e = cp::launch_attn_fwd_split_bf16(p, q, k, v, out, lse, static_cast<float*>(workspace), stream);
+  } else if (mfma_path(a)) {
     e = cp::launch_attn_fwd_bf16(p, q, k, v, out, lse, stream);
   } else if (a->dtype == CP_DTYPE_BF16) {
     e = cp::launch_attn_fwd_rowwise_bf16(p, q, k, v, out, lse, stream);
@@ -161,6 +195,20 @@ cp_status_t cp_attn_fwd(const cp_attn_args_t* a, const void* q, const void* k, c
                                 static_cast<const float*>(v), static_cast<float*>(out), lse, stream);
   }
   return hip_status(e, "cp_attn_fwd launch");
+}
+
+}  // namespace
+
+cp_status_t cp_attn_fwd(const cp_attn_args_t* a, const void* q, const void* k, const void* v, void* out,
+                        float* lse, hipStream_t stream) {
+  return fwd_impl(a, q, k, v, out, lse, nullptr, 0, false, stream);
+}
+
+size_t cp_attn_fwd_workspace_size(const cp_attn_args_t* a) { return fwd_workspace_bytes(a); }
+
+cp_status_t cp_attn_fwd_ws(const cp_attn_args_t* a, const void* q, const void* k, const void* v, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fwd_impl(a, q, k, v, out, lse, workspace, workspace_bytes, true, stream);
 }
 
 cp_status_t cp_attn_fwd_merge(const cp_attn_args_t* a, const void* q, const void* k, const void* v,

@@ -46,11 +46,15 @@ constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 // NW row wavefronts (32 query rows each) per key group; NS key groups (1 or 2) that
 // take alternate live key tiles of the same rows and combine their partial softmax
 // states at the end (for grids too small to fill the chip with whole tiles).
-template <int D_, int NW_, int BN_, int NS_>
+// SPLIT: the NS = 2 key groups of a query tile are two workgroups instead of one
+// (workgroup 2t + g is group g of tile t); each writes its partial (out, lse) to a
+// float32 workspace and a second kernel combines the pair.
+template <int D_, int NW_, int BN_, int NS_, bool SPLIT_ = false>
 struct FwdCfg {
   static constexpr int D = D_, NW = NW_, BN = BN_, NS = NS_;
+  static constexpr bool SPLIT = SPLIT_;
   static constexpr int kGroupThreads = 64 * NW;
-  static constexpr int kThreads = kGroupThreads * NS;
+  static constexpr int kThreads = SPLIT ? kGroupThreads : kGroupThreads * NS;
   static constexpr int kRows = 32 * NW;
   static constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
   static constexpr int KB = BN / 32;  // 32-key blocks of a tile
@@ -58,33 +62,37 @@ struct FwdCfg {
   static constexpr int PT = BN / 16;  // k-steps of O^T += V^T P^T
   static constexpr int kTileElems = BN * D;  // swizzled row-major K or V tile
   static constexpr int kStageBytes = 2 * kTileElems * 2 + BN * 2 * 4;  // K, V, kpos, kseg
-  static constexpr int kLdsBytes = NS * 2 * kStageBytes;
+  static constexpr int kLdsBytes = (SPLIT ? 1 : NS) * 2 * kStageBytes;
   // exchange of the second key group's (o, m, l) per lane, over the stages
   static constexpr int kXchgBytes = NW * 64 * (DB * 16 + 2) * 4;
   static constexpr int kAhead = 2;  // LDS operand reads issued ahead of their product
   using Tile = DmaTile<BN, D, kGroupThreads>;
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
-  static_assert(NS == 1 || (NS == 2 && kXchgBytes <= kLdsBytes), "key groups");
+  static_assert(NS == 1 || (NS == 2 && (SPLIT || kXchgBytes <= kLdsBytes)), "key groups");
+  static_assert(!SPLIT || NS == 2, "a split pairs two key groups");
 };
 
 // kMerge = false: write out (bf16) and lse.  kMerge = true (fused ring step): merge
 // the block's float32 result into acc [B,Sq,Hq,D] and lse (= lse_acc) in place.
+// C::SPLIT: out / lse are ignored; the group's partial result goes to part_o
+// [2][B,Sq,Hq,D] and part_l [2][B,Hq,Sq] (float32, normalised, natural-log lse).
 template <class C, bool kMerge>
 CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ acc,
-                        float* __restrict__ lse, uint8_t* smem) {
+                        float* __restrict__ lse, uint8_t* smem, float* __restrict__ part_o = nullptr,
+                        float* __restrict__ part_l = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int grp = C::NS > 1 ? wave / C::NW : 0;  // key group
+  const int grp = C::SPLIT ? int(blockIdx.x & 1) : C::NS > 1 ? wave / C::NW : 0;  // key group
   const int rw = wave % C::NW;                    // row wavefront within the group
   const int gtid = tid % C::kGroupThreads;
 
   // heaviest query tiles of every (batch, head) first
   const int n_qt = (p.Sq + C::kRows - 1) / C::kRows;
-  const int order = int(blockIdx.x);
+  const int order = C::SPLIT ? int(blockIdx.x >> 1) : int(blockIdx.x);
   const int tile_rank = order / (p.B * p.Hq);
   const int bh = order - tile_rank * (p.B * p.Hq);
   const int qt = p.causal ? (n_qt - 1 - tile_rank) : tile_rank;
@@ -153,7 +161,7 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
       kseg[t] = kseg_at(p, b, j);
     }
   };
-  auto stage_of = [&](int buf) { return smem + (grp * 2 + buf) * C::kStageBytes; };
+  auto stage_of = [&](int buf) { return smem + ((C::SPLIT ? 0 : grp) * 2 + buf) * C::kStageBytes; };
 
   // Live tiles are taken in pairs (t0, t1): key group 0 multiplies t0, group 1 t1
   // (with one group, t1 is unused).  Every wavefront walks the same pair sequence,
@@ -258,7 +266,7 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     }
   }
 
-  if constexpr (C::NS > 1) {
+  if constexpr (C::NS > 1 && !C::SPLIT) {
     // combine the two key groups' partial states of each row (same lane layout):
     // m = max(m0, m1), o = o0 2^(m0-m) + o1 2^(m1-m), l likewise
     float* xo = reinterpret_cast<float*>(smem) + rw * (C::DB * 16) * 64 + lane;
@@ -294,7 +302,21 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
   const float lse_blk = any ? (m + __log2f(lt)) * kLn2 : -INFINITY;
   const int64_t li = (int64_t(b) * p.Hq + h) * p.Sq + row;
   const int64_t orow = ((int64_t(b) * p.Sq + row) * p.Hq + h) * C::D;
-  if constexpr (kMerge) {
+  if constexpr (C::SPLIT) {
+    // this group's normalised partial; a group with no visible key writes o = 0,
+    // lse = -inf (weight 0 in the combine)
+    const int64_t plane = int64_t(p.B) * p.Sq * p.Hq * C::D;
+    float* prow = part_o + grp * plane + orow;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x16& a = o[db];
+        *reinterpret_cast<f32x4*>(prow + db * 32 + 8 * j + 4 * hi) =
+            f32x4{a[4 * j] * inv, a[4 * j + 1] * inv, a[4 * j + 2] * inv, a[4 * j + 3] * inv};
+      }
+    if (hi == 0) part_l[grp * (int64_t(p.B) * p.Hq * p.Sq) + li] = lse_blk;
+  } else if constexpr (kMerge) {
     // both 32-lane halves read the row's old lse before either writes the new one
     const MergeWeights w = merge_weights(lse[li], lse_blk);
     const float fb = w.wb * inv;
@@ -341,6 +363,46 @@ __global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_merge_mfma_kernel(Att
   fwd_body<C, true>(p, q, k, v, nullptr, acc, lse_acc, smem);
 }
 
+template <class C>
+__global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_split_kernel(AttnProblem p, const uint16_t* q,
+                                                                        const uint16_t* k, const uint16_t* v,
+                                                                        float* part_o, float* part_l) {
+  __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
+  fwd_body<C, false>(p, q, k, v, nullptr, nullptr, nullptr, smem, part_o, part_l);
+}
+
+// out = merge of the two partials of every (row, head), rounded to bf16, and the
+// merged lse: the ring-step merge rule applied to the two key halves (weights
+// e^(lse_g - lse), a -inf half has weight 0; both -inf gives out = 0, lse = -inf).
+// One thread per 8 consecutive elements of a row.
+template <int D>
+__global__ __launch_bounds__(256) void split_combine_kernel(int64_t rows, int Sq, int Hq, const float* part_o,
+                                                            const float* part_l, uint16_t* out, float* lse) {
+  constexpr int kPer = D / 8;
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = t / kPer;  // (b, i, h) row of out
+  if (row >= rows) return;
+  const int c = int(t % kPer);
+  const int h = int(row % Hq);
+  const int64_t bi = row / Hq;
+  const int i = int(bi % Sq);
+  const int64_t b = bi / Sq;
+  const int64_t li = (b * Hq + h) * Sq + i;
+  const MergeWeights w = merge_weights(part_l[li], part_l[rows + li]);
+  const int64_t e = row * D + c * 8;
+  const int64_t plane = rows * D;
+  const f32x4 a0 = *reinterpret_cast<const f32x4*>(part_o + e);
+  const f32x4 a1 = *reinterpret_cast<const f32x4*>(part_o + e + 4);
+  const f32x4 b0 = *reinterpret_cast<const f32x4*>(part_o + plane + e);
+  const f32x4 b1 = *reinterpret_cast<const f32x4*>(part_o + plane + e + 4);
+  const u32x4 r{pack_bf16x2(a0[0] * w.wa + b0[0] * w.wb, a0[1] * w.wa + b0[1] * w.wb),
+                pack_bf16x2(a0[2] * w.wa + b0[2] * w.wb, a0[3] * w.wa + b0[3] * w.wb),
+                pack_bf16x2(a1[0] * w.wa + b1[0] * w.wb, a1[1] * w.wa + b1[1] * w.wb),
+                pack_bf16x2(a1[2] * w.wa + b1[2] * w.wb, a1[3] * w.wa + b1[3] * w.wb)};
+  *reinterpret_cast<u32x4*>(out + e) = r;
+  if (c == 0) lse[li] = w.lse;
+}
+
 template <class C, bool kMerge>
 hipError_t launch_cfg(const AttnProblem& p, const void* q, const void* k, const void* v, void* out,
                       float* acc, float* lse, hipStream_t s) {
@@ -356,6 +418,24 @@ hipError_t launch_cfg(const AttnProblem& p, const void* q, const void* k, const 
     hipLaunchKernelGGL(attn_fwd_mfma_kernel<C>, dim3(n), dim3(C::kThreads), 0, s, p, qq, kk, vv,
                        static_cast<uint16_t*>(out), lse);
   }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_split(const AttnProblem& p, const void* q, const void* k, const void* v, void* out, float* lse,
+                        float* ws, hipStream_t s) {
+  using C = FwdCfg<D, 4, 64, 2, true>;
+  const int64_t rows = int64_t(p.B) * p.Sq * p.Hq;
+  float* part_o = ws;
+  float* part_l = ws + 2 * rows * D;
+  const unsigned n = 2u * unsigned((p.Sq + C::kRows - 1) / C::kRows) * unsigned(p.Hq * p.B);
+  ProfScope ps(s, kProfFwdMfma);
+  hipLaunchKernelGGL(attn_fwd_split_kernel<C>, dim3(n), dim3(C::kThreads), 0, s, p,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), part_o, part_l);
+  const int64_t threads = rows * (D / 8);
+  hipLaunchKernelGGL(split_combine_kernel<D>, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, rows, p.Sq,
+                     p.Hq, part_o, part_l, static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
 }
 
@@ -396,6 +476,31 @@ hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const vo
 }
 
 }  // namespace
+
+// The combine pass moves 10 bytes per output element (two float32 partials in, bf16
+// out); with fewer than 8192 keys that is no longer small next to the attention of
+// the row (a 2048-key causal block measured slower split than unsplit).
+constexpr int kSplitMinKeys = 8192;
+
+bool fwd_split_applies(const AttnProblem& p) {
+  const int64_t tiles = int64_t((p.Sq + 127) / 128) * p.Hq * p.B;
+  return p.Sk >= kSplitMinKeys && tiles < 2 * int64_t(wg_slots());
+}
+
+size_t fwd_split_workspace_bytes(const AttnProblem& p) {
+  const int64_t rows = int64_t(p.B) * p.Sq * p.Hq;
+  return size_t(2 * rows * p.D + 2 * rows) * sizeof(float);
+}
+
+hipError_t launch_attn_fwd_split_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
+                                      void* out, float* lse, float* ws, hipStream_t s) {
+  switch (p.D) {
+    case 128: return launch_split<128>(p, q, k, v, out, lse, ws, s);
+    case 64: return launch_split<64>(p, q, k, v, out, lse, ws, s);
+    case 32: return launch_split<32>(p, q, k, v, out, lse, ws, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_attn_fwd_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
                                 void* out, float* lse, hipStream_t s) {

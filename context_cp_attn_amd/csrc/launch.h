@@ -24,6 +24,13 @@ hipError_t launch_attn_fwd_bf16(const AttnProblem& p, const void* q, const void*
                                 void* out, float* lse, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const AttnProblem& p, const float* q, const float* k, const float* v,
                                float* out, float* lse, hipStream_t s);
+// the same forward with each query tile's keys split over two workgroups whose
+// float32 partials (ws, fwd_split_workspace_bytes) a second kernel combines; used
+// when fwd_split_applies (too few query tiles to fill the device twice)
+bool fwd_split_applies(const AttnProblem& p);
+size_t fwd_split_workspace_bytes(const AttnProblem& p);
+hipError_t launch_attn_fwd_split_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
+                                      void* out, float* lse, float* ws, hipStream_t s);
 // fused ring step: the block's result merged into acc [B,Sq,Hq,D] / lse_acc in place
 hipError_t launch_attn_fwd_merge_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
                                       float* acc, float* lse_acc, hipStream_t s);

@@ -100,10 +100,19 @@ def _check_qkv(q, k, v):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
 
 
-def attn_fwd(q, k, v, *, out=None, lse=None, **mask):
+def fwd_workspace(q, k, **mask) -> torch.Tensor | None:
+    """Workspace for attn_fwd's split path on this problem (None if it does not split)."""
+    n = _lib.load().cp_attn_fwd_workspace_size(ctypes.byref(make_args(q, k, **mask)))
+    return torch.empty(n, device=q.device, dtype=torch.uint8) if n else None
+
+
+def attn_fwd(q, k, v, *, out=None, lse=None, workspace=None, **mask):
     """(out [B,Sq,Hq,D] q.dtype, lse [B,Hq,Sq] fp32) of one attention block.
 
     mask keywords: causal, q_offset, k_offset, q_pos, k_pos, q_seg, k_seg, window, scale.
+    workspace: None allocates what cp_attn_fwd_workspace_size asks for (the split
+    path for small grids); a uint8 tensor is used as given; False calls cp_attn_fwd,
+    which never splits.
     """
     _check_qkv(q, k, v)
     a = make_args(q, k, **mask)
@@ -114,8 +123,16 @@ def attn_fwd(q, k, v, *, out=None, lse=None, **mask):
     if out.shape != q.shape or lse.shape != (B, Hq, Sq):
         raise ValueError("out/lse shape mismatch")
     lib = _lib.load()
-    _lib.check(lib.cp_attn_fwd(ctypes.byref(a), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                               out.data_ptr(), lse.data_ptr(), _stream()))
+    if workspace is False:
+        _lib.check(lib.cp_attn_fwd(ctypes.byref(a), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                   out.data_ptr(), lse.data_ptr(), _stream()))
+        return out, lse
+    if workspace is None:
+        n = lib.cp_attn_fwd_workspace_size(ctypes.byref(a))
+        workspace = torch.empty(n, device=q.device, dtype=torch.uint8) if n else None
+    ws_ptr, ws_n = (None, 0) if workspace is None else (_dev(workspace, "workspace").data_ptr(), workspace.numel())
+    _lib.check(lib.cp_attn_fwd_ws(ctypes.byref(a), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  out.data_ptr(), lse.data_ptr(), ws_ptr, ws_n, _stream()))
     return out, lse
 
 

@@ -85,6 +85,24 @@ cp_status_t cp_attn_fwd(const cp_attn_args_t* args, const void* q, const void* k
                         void* out, float* lse, hipStream_t stream);
 
 /*
+ * The same forward with a caller-owned workspace, which lets the library split the
+ * keys of every query tile over two workgroups when the problem has too few query
+ * tiles (of 128 rows) to fill the current device twice and at least 8192 keys (bf16,
+ * head_dim 32/64/128); the two float32 partial
+ * results are then merged with the ring-step rule of cp_lse_merge ([H] §"Ring
+ * Attention": the merge of two blocks of keys) by a second kernel.  Same results
+ * as cp_attn_fwd within the bf16 tolerance (out is rounded once, after the merge).
+ * cp_attn_fwd_workspace_size gives the bytes needed for args on the current
+ * device (0: no split, workspace may be NULL); the workspace must be 16-byte
+ * aligned and must not overlap q, k, v, out or lse (CP_ERR_ALIAS), otherwise as
+ * cp_attn_fwd.
+ */
+size_t cp_attn_fwd_workspace_size(const cp_attn_args_t* args);
+cp_status_t cp_attn_fwd_ws(const cp_attn_args_t* args, const void* q, const void* k, const void* v,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
  * Fused ring step ([H] §"Ring Attention": each step's block attention folded into
  * the running result; the merge of cp_lse_merge moved into the attention epilogue).
  * Computes the attention of q against k/v exactly as cp_attn_fwd, but instead of

@@ -85,6 +85,35 @@ def test_attn_fwd_alias_and_alignment():
     assert st == INVALID and "misaligned" in err
 
 
+def test_attn_fwd_workspace_rules():
+    lib = _lib.load()
+    size = lambda a: lib.cp_attn_fwd_workspace_size(ctypes.byref(a))
+    small = args(seqlen_k=8192)                      # 4 query tiles, 8192 keys: the split applies
+    rows = 1 * 64 * 4
+    assert size(args(seqlen_k=8191)) == 0            # too few keys to pay for the combine
+    assert size(small) >= 2 * rows * 128 * 4 + 2 * rows * 4 and size(small) % 256 == 0
+    assert size(args(dtype=1)) == 0                  # float32: row-per-wavefront path
+    assert size(args(head_dim=16)) == 0              # bf16 without a matrix-core kernel
+    assert size(args(seqlen_q=1 << 17, heads_q=16, heads_kv=2)) == 0   # fills the device
+    assert size(args(batch=0)) == 0
+
+    def call(a, ws, nbytes):
+        st = lib.cp_attn_fwd_ws(ctypes.byref(a), FAKE_A, FAKE_B, FAKE_C, 1 << 44, 1 << 45, ws, nbytes, None)
+        return st, lib.cp_last_error().decode()
+
+    need = size(small)
+    ws = 1 << 46
+    st, err = call(small, ws, need - 1)
+    assert st == INVALID and "workspace" in err
+    st, err = call(small, 0, need)
+    assert st == INVALID and "workspace" in err
+    st, err = call(small, ws + 8, need)
+    assert st == INVALID and "aligned" in err
+    st, err = call(small, FAKE_B - 256, need)        # over k
+    assert st == ALIAS
+    assert call(args(batch=0), ws, need)[0] == INVALID   # shared validation
+
+
 def test_attn_check_args_rejects():
     lib = _lib.load()
 

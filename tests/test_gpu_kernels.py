@@ -404,9 +404,11 @@ def test_check_attn_args(cp, monkeypatch):
 @pytest.mark.parametrize("many_tiles", [False, True])
 @pytest.mark.parametrize("masks", ["causal_offset", "packed_window"])
 def test_attn_fwd_grid_variants(cp, many_tiles, masks):
-    """The forward splits each query tile's keys over two wavefront groups when the
-    grid has fewer than 4 query tiles (of 128 rows) per CU, and runs whole tiles
-    otherwise; both variants against the oracle, plain and fused-merge, D=128."""
+    """The forward splits each query tile's keys over two wavefront groups of one
+    workgroup when the grid has fewer than 4 query tiles (of 128 rows) per CU, and
+    runs whole tiles otherwise; both variants against the oracle, plain (with and
+    without a workspace: with 1000 keys cp_attn_fwd_ws does not split) and
+    fused-merge, D=128."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     S, Hq, Hkv, D = 1000, 8, 2, 128
     tiles_per_batch = ((S + 127) // 128) * Hq
@@ -419,7 +421,8 @@ def test_attn_fwd_grid_variants(cp, many_tiles, masks):
         seg = cp_inputs.random_segment_ids(S, 60, 400, seed=9, batch=B)
         m = dict(q_seg=seg, k_seg=seg, window=150)
     dm = to_dev(m)
-    out, lse = cp.attn_fwd(q.cuda(), k.cuda(), v.cuda(), **dm)
+    out, lse = cp.attn_fwd(q.cuda(), k.cuda(), v.cuda(), **dm)                      # workspace path
+    out1, lse1 = cp.attn_fwd(q.cuda(), k.cuda(), v.cuda(), workspace=False, **dm)   # cp_attn_fwd
     acc = torch.zeros(B, S, Hq, D, device="cuda")
     lacc = torch.full((B, Hq, S), float("-inf"), device="cuda")
     cp.attn_fwd_merge(q.cuda(), k.cuda(), v.cuda(), acc, lacc, **dm)
@@ -429,8 +432,43 @@ def test_attn_fwd_grid_variants(cp, many_tiles, masks):
     ref_o, ref_l = oracle.attn_fwd(q[bs], k[bs], v[bs], **om)
     check_lse(lse[bs], ref_l, 1e-3)
     check_close(out[bs], ref_o, 1e-2, "out")
+    check_lse(lse1[bs], ref_l, 1e-3)
+    check_close(out1[bs], ref_o, 1e-2, "out without workspace")
     check_lse(lacc[bs], ref_l, 1e-3)
     check_close(acc[bs], ref_o, 1e-2, "fused out")
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("masks", ["causal_offset", "empty_rows", "packed_window"])
+def test_attn_fwd_split(cp, D, masks):
+    """cp_attn_fwd_ws on a grid small enough to split the keys of every query tile
+    over two workgroups (>= 8192 keys, a ragged last key tile): the combined result
+    against the oracle, and against cp_attn_fwd (no workspace)."""
+    Sq, Sk, Hq, Hkv = 300, 8400, 4, 2
+    say(f"attn_fwd split D={D} {masks}")
+    q, k, v = cp_inputs.normal_tensors([(1, Sq, Hq, D), (1, Sk, Hkv, D), (1, Sk, Hkv, D)], seed=12)
+    if masks == "causal_offset":      # the last rows see every key
+        m = dict(q_offset=Sk - 150, k_offset=0)
+    elif masks == "empty_rows":       # rows 0..99 precede every key
+        m = dict(q_offset=0, k_offset=100)
+    else:                             # queries at positions 8000.. inside packed documents
+        kseg = cp_inputs.random_segment_ids(Sk, 500, 3000, seed=13)
+        qpos = np.arange(8000, 8000 + Sq)
+        m = dict(q_pos=qpos, k_pos=np.arange(Sk), q_seg=kseg[:, 8000:8000 + Sq].contiguous(), k_seg=kseg,
+                 window=2500)
+    dm = to_dev(m)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    ws = cp.fwd_workspace(qd, kd, **dm)
+    assert ws is not None
+    out, lse = cp.attn_fwd(qd, kd, vd, workspace=ws, **dm)
+    out1, lse1 = cp.attn_fwd(qd, kd, vd, workspace=False, **dm)
+    ref_o, ref_l = oracle.attn_fwd(q, k, v, **oracle_mask(m))
+    check_lse(lse, ref_l, 1e-3)
+    check_close(out, ref_o, 1e-2, "split out")
+    empty = np.isneginf(ref_l)
+    if empty.any():
+        assert np.all(f64(out).transpose(0, 2, 1, 3)[empty] == 0)
+    check_close(out, f64(out1), 1e-2, "split vs unsplit")
 
 
 @pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)])
