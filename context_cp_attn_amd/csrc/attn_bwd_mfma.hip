@@ -185,8 +185,16 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
     const int i0 = t.it * C::BM;
     return classify(p, q_span(p, b, i0, min(i0 + C::BM, p.Sq) - 1), ksp, false);
   };
+  // the query tiles live for this key block lie in [it_lo, it_hi); the walk stays
+  // inside (queries wholly after the keys' window / segments are a suffix, those
+  // wholly before the keys a prefix)
+  auto qtile_span = [&](int it) { return q_span(p, b, it * C::BM, min(it * C::BM + C::BM, p.Sq) - 1); };
+  const int it_hi = first_true(0, n_it, [&](int it) { return keys_before(p, qtile_span(it), wg_k); });
+  const int it_lo = first_true(0, it_hi, [&](int it) { return !keys_after(p, qtile_span(it), wg_k); });
   auto next_tile = [&](Tq t) {
-    while (t.it >= 0 && tile_class(t, wg_k) == kEmpty) t = step(t);
+    if (t.it >= it_hi) t = Tq{0, it_hi - 1};
+    while (t.it >= it_lo && tile_class(t, wg_k) == kEmpty) t = step(t);
+    if (t.it < it_lo) t.it = -1;
     return t;
   };
   typename C::TileM tq, tg;
@@ -389,9 +397,14 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
     const int j1 = min(j0 + C::BN, p.Sk) - 1;
     return classify(p, qsp, k_span(p, b, j0, j1), j1 - j0 + 1 < C::BN);
   };
+  // the key tiles live for this query block lie in [kt_lo, kt_hi)
+  auto ktile_span = [&](int kt) { return k_span(p, b, kt * C::BN, min(kt * C::BN + C::BN, p.Sk) - 1); };
+  const int kt_lo = first_true(0, n_kt, [&](int kt) { return !keys_before(p, wg_q, ktile_span(kt)); });
+  const int kt_hi = first_true(kt_lo, n_kt, [&](int kt) { return keys_after(p, wg_q, ktile_span(kt)); });
   auto next_tile = [&](int kt) {
-    while (kt < n_kt && tile_class(kt, wg_q) == kEmpty) ++kt;
-    return kt;
+    kt = max(kt, kt_lo);
+    while (kt < kt_hi && tile_class(kt, wg_q) == kEmpty) ++kt;
+    return kt < kt_hi ? kt : n_kt;
   };
   typename C::TileN tk, tv;
   const uint32_t krs_bytes = uint32_t(krs) * 2u;

@@ -138,9 +138,14 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     const int j1 = min(j0 + C::BN, p.Sk) - 1;
     return classify(p, qsp, k_span(p, b, j0, j1), j1 - j0 + 1 < C::BN);
   };
+  // the workgroup's live key tiles lie in [kt_lo, kt_hi); the walk stays inside
+  auto tile_span = [&](int kt) { return k_span(p, b, kt * C::BN, min(kt * C::BN + C::BN, p.Sk) - 1); };
+  const int kt_lo = first_true(0, n_kt, [&](int kt) { return !keys_before(p, wg_q, tile_span(kt)); });
+  const int kt_hi = first_true(kt_lo, n_kt, [&](int kt) { return keys_after(p, wg_q, tile_span(kt)); });
   auto next_tile = [&](int kt) {
-    while (kt < n_kt && tile_class(kt, wg_q) == kEmpty) ++kt;
-    return kt;
+    kt = max(kt, kt_lo);
+    while (kt < kt_hi && tile_class(kt, wg_q) == kEmpty) ++kt;
+    return kt < kt_hi ? kt : n_kt;
   };
   typename C::Tile tk, tv;
   const uint32_t krs_bytes = uint32_t(krs) * 2u;

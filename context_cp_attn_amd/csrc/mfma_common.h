@@ -78,6 +78,32 @@ CP_DEVICE int classify(const AttnProblem& p, const Span& q, const Span& k, bool 
   return full ? kFull : kPartial;
 }
 
+// With positions strictly increasing and segment ids non-decreasing along q and
+// along k (the documented preconditions the tile classification above already
+// relies on), the key runs wholly before a query run's window / segments form a
+// prefix of the key tiles, and those wholly after its causal horizon / segments a
+// suffix: the live tiles of a run lie in one contiguous range, found by bisection
+// instead of classifying every empty tile.
+CP_DEVICE bool keys_before(const AttnProblem& p, const Span& q, const Span& k) {
+  return (p.window && q.pos_lo - k.pos_hi >= p.window) || (p.q_seg && k.seg_hi < q.seg_lo);
+}
+CP_DEVICE bool keys_after(const AttnProblem& p, const Span& q, const Span& k) {
+  return (p.causal && k.pos_lo > q.pos_hi) || (p.q_seg && k.seg_lo > q.seg_hi);
+}
+
+// Smallest x in [lo, hi) with pred(x), else hi; pred must be false ... false true ... true.
+template <class Pred>
+CP_DEVICE int first_true(int lo, int hi, Pred&& pred) {
+  while (lo < hi) {
+    const int mid = lo + (hi - lo) / 2;
+    if (pred(mid))
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return lo;
+}
+
 // ---- transposed LDS tiles: [D][ld] with NR tokens per row --------------------------
 // The 8-token column groups of row d are XOR-swizzled by (d >> 4): stores of the
 // 4-token x 8-dim register units then hit distinct banks, while a 16-byte read of
