@@ -218,7 +218,8 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
               const i32x4 kg4 = *reinterpret_cast<const i32x4*>(kseg_l + kk0);
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const bool vis = (kk0 + i < nvalid) && pair_visible(ms, qp, kp4[i], qs, kg4[i]);
+                // bitwise &: a short-circuit && here became one branch per element
+                const bool vis = (kk0 + i < nvalid) & pair_visible(ms, qp, kp4[i], qs, kg4[i]);
                 s[kb][4 * jj + i] = vis ? s[kb][4 * jj + i] : -INFINITY;
               }
             }
