@@ -439,15 +439,16 @@ def test_attn_fwd_grid_variants(cp, many_tiles, masks):
 
 
 @pytest.mark.parametrize("D", [32, 64, 128])
-@pytest.mark.parametrize("masks", ["causal_offset", "empty_rows", "packed_window"])
+@pytest.mark.parametrize("masks", ["causal_offset", "empty_rows", "packed_window", "batch2"])
 def test_attn_fwd_split(cp, D, masks):
     """cp_attn_fwd_ws on a grid small enough to split the keys of every query tile
     over two workgroups (>= 8192 keys, a ragged last key tile): the combined result
     against the oracle, and against cp_attn_fwd (no workspace)."""
     Sq, Sk, Hq, Hkv = 300, 8400, 4, 2
+    B = 2 if masks == "batch2" else 1
     say(f"attn_fwd split D={D} {masks}")
-    q, k, v = cp_inputs.normal_tensors([(1, Sq, Hq, D), (1, Sk, Hkv, D), (1, Sk, Hkv, D)], seed=12)
-    if masks == "causal_offset":      # the last rows see every key
+    q, k, v = cp_inputs.normal_tensors([(B, Sq, Hq, D), (B, Sk, Hkv, D), (B, Sk, Hkv, D)], seed=12)
+    if masks in ("causal_offset", "batch2"):   # the last rows see every key
         m = dict(q_offset=Sk - 150, k_offset=0)
     elif masks == "empty_rows":       # rows 0..99 precede every key
         m = dict(q_offset=0, k_offset=100)
