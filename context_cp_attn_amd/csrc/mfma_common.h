@@ -104,118 +104,12 @@ CP_DEVICE int first_true(int lo, int hi, Pred&& pred) {
   return lo;
 }
 
-// ---- transposed LDS tiles: [D][ld] with NR tokens per row --------------------------
-// The 8-token column groups of row d are XOR-swizzled by (d >> 4): stores of the
-// 4-token x 8-dim register units then hit distinct banks, while a 16-byte read of
-// 8 consecutive tokens stays contiguous.  tcol gives the element column of the
-// 8-token group starting at token key8 (a multiple of 8) in row d.
-template <int NR>
-CP_DEVICE int tcol(int d, int key8) {
-  static_assert(NR % 8 == 0 && ((NR / 8) & (NR / 8 - 1)) == 0, "power-of-two groups");
-  return (((key8 >> 3) ^ ((d >> 4) & (NR / 8 - 1))) << 3);
-}
-
-// ---- a tile of NR token rows x D dims (bf16): global -> registers -> LDS ----------
-// Rows are fetched with buffer loads through a resource rebased at the tile's first
-// row whose size ends at the last valid row: rows past the end read as zeros in
-// hardware, so the loads need neither selects nor 64-bit address arithmetic.
-//
-// Work unit = R rows x 8 dims (R 16-byte loads; R = 4, or 2 to spread a tile over
-// more threads with fewer registers).  Two thread -> unit maps:
-//  * kKeysFast = false: consecutive threads take consecutive 8-dim columns of the
-//    same 4 rows (row-major stores are conflict-free; transposed stores go through
-//    the tcol swizzle);
-//  * kKeysFast = true: consecutive threads take consecutive 4-row groups (only
-//    transposed stores; conflict-free without a swizzle, so reads use tcol_plain).
+// ---- buffer resources ---------------------------------------------------------------
+// A raw buffer resource over nbytes from base: loads past the end read as zeros in
+// hardware, so ragged tiles need neither selects nor 64-bit address arithmetic.
 CP_DEVICE __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(nbytes), 0x00020000);
 }
-
-template <int NR, int D, int NT, bool kKeysFast = false, int R = 4>
-struct RowTile {
-  static_assert(R == 4 || (R == 2 && !kKeysFast), "2-row units are d8-fast only");
-  static constexpr int kUnits = (NR / R) * (D / 8);
-  static constexpr int kIter = (kUnits + NT - 1) / NT;
-  static_assert(NR % R == 0 && D % 8 == 0, "tile shape");
-  u32x4 r[kIter][R];
-  uint32_t voff[kIter][R];  // byte offset of each loaded row piece within the tile
-
-  static CP_DEVICE int unit_row(int u) { return (kKeysFast ? u % (NR / R) : u / (D / 8)) * R; }
-  static CP_DEVICE int unit_d8(int u) { return kKeysFast ? u / (NR / R) : u % (D / 8); }
-  static CP_DEVICE bool unit_ok(int u) { return kUnits % NT == 0 || u < kUnits; }
-
-  CP_DEVICE void init(uint32_t row_stride_bytes) {
-#pragma unroll
-    for (int it = 0; it < kIter; ++it) {
-      const int u = int(threadIdx.x) + it * NT;
-#pragma unroll
-      for (int e = 0; e < R; ++e)
-        voff[it][e] = uint32_t(unit_row(u) + e) * row_stride_bytes + uint32_t(unit_d8(u)) * 16u;
-    }
-  }
-
-  // base: the token rows' first element (row 0); nrows valid rows of row_stride_bytes
-  CP_DEVICE void load(const uint16_t* base, uint32_t row_stride_bytes, int row0, int nrows) {
-    const uint32_t skip = uint32_t(row0) * row_stride_bytes;
-    const uint32_t valid = uint32_t(nrows - 1 - row0) * row_stride_bytes + uint32_t(D) * 2u;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const uint8_t*>(base) + skip, valid);
-#pragma unroll
-    for (int it = 0; it < kIter; ++it) {
-      if (unit_ok(int(threadIdx.x) + it * NT)) {
-#pragma unroll
-        for (int e = 0; e < R; ++e)
-          r[it][e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[it][e], 0, 0));
-      }
-    }
-  }
-
-  CP_DEVICE void store_rows(uint16_t* lds, int ld) const {
-#pragma unroll
-    for (int it = 0; it < kIter; ++it) {
-      const int u = int(threadIdx.x) + it * NT;
-      if (unit_ok(u)) {
-        const int r0 = unit_row(u), d8 = unit_d8(u);
-#pragma unroll
-        for (int e = 0; e < R; ++e) *reinterpret_cast<u32x4*>(lds + (r0 + e) * ld + d8 * 8) = r[it][e];
-      }
-    }
-  }
-
-  // transposed: row d of the LDS tile holds dim d of the NR tokens (swizzled with
-  // tcol unless kKeysFast)
-  CP_DEVICE void store_cols(uint16_t* lds, int ld) const {
-#pragma unroll
-    for (int it = 0; it < kIter; ++it) {
-      const int u = int(threadIdx.x) + it * NT;
-      if (unit_ok(u)) {
-        const int r0 = unit_row(u), d8 = unit_d8(u);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {  // dims 2w, 2w+1 live in 32-bit word w
-          const int d0 = d8 * 8 + 2 * w, d1 = d0 + 1;
-          if constexpr (R == 4) {
-            const uint32_t a0 = r[it][0][w], a1 = r[it][1][w], a2 = r[it][2][w], a3 = r[it][3][w];
-            const u32x2 lo{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-            const u32x2 hi{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-            if (kKeysFast) {
-              *reinterpret_cast<u32x2*>(lds + d0 * ld + r0) = lo;
-              *reinterpret_cast<u32x2*>(lds + d1 * ld + r0) = hi;
-            } else {
-              const int sub = r0 & 7;
-              *reinterpret_cast<u32x2*>(lds + d0 * ld + tcol<NR>(d0, r0) + sub) = lo;
-              *reinterpret_cast<u32x2*>(lds + d1 * ld + tcol<NR>(d1, r0) + sub) = hi;
-            }
-          } else {
-            const uint32_t a0 = r[it][0][w], a1 = r[it][1][w];
-            const int sub = r0 & 7;
-            *reinterpret_cast<uint32_t*>(lds + d0 * ld + tcol<NR>(d0, r0) + sub) = (a0 & 0xffffu) | (a1 << 16);
-            *reinterpret_cast<uint32_t*>(lds + d1 * ld + tcol<NR>(d1, r0) + sub) = (a0 >> 16) | (a1 & 0xffff0000u);
-          }
-        }
-      }
-    }
-  }
-};
-
 
 // ---- row-major LDS tiles filled by LDS-DMA, read as rows or transposed ------------
 // A tile of NR token rows x D dims is stored unpadded, row-major, with the 16-byte
