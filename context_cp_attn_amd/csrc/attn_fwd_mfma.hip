@@ -29,8 +29,14 @@
 //    same max in numerator and denominator, and keeps P <= 2^8.
 //  * Tiles are classified per workgroup and per wavefront as empty (skipped: no
 //    load, no math), full (no mask) or partial (elementwise mask) from the
-//    extreme positions / segment ids of the tile, which are monotone.
+//    extreme positions / segment ids of the tile, which are monotone; a
+//    workgroup's walk is confined to the bisected range of key tiles that can hold
+//    a visible pair.
 //  * Causal grids run the heaviest query tiles of every head first.
+//  * Grids with fewer query tiles than two rounds of workgroup slots split each
+//    tile's live key tiles over two key groups: two wavefront groups of one
+//    workgroup combining through LDS, or (with a workspace and >= 8192 keys) two
+//    workgroups whose float32 partials a combine kernel merges.
 #include <type_traits>
 
 #include "mfma_common.h"
