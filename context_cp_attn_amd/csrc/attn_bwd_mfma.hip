@@ -91,7 +91,10 @@ struct BwdCfg {
   static constexpr int kStageQ = 2 * kTileN * 2 + 2 * BN * 4;
   static constexpr int kStageMax = kStageK > kStageQ ? kStageK : kStageQ;
   static constexpr int kAhead = 3;  // LDS operand reads issued this many products ahead
-  static constexpr int kLdsBytes = 2 * kStageMax;
+  // spans of up to kSpanTiles query tiles (dV / dK roles) or key tiles (dQ role),
+  // cached when they come from position / segment arrays
+  static constexpr int kSpanTiles = 1024;
+  static constexpr int kLdsBytes = 2 * kStageMax + kSpanTiles * 16;
   using TileM = DmaTile<BM, D, kThreads>;
   using TileN = DmaTile<BN, D, kThreads>;
   static_assert(BM <= kThreads && BN <= kThreads, "one thread per row of the small arrays");
@@ -181,14 +184,28 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
     }
     return t;
   };
-  auto tile_class = [&](Tq t, const Span& ksp) {
-    const int i0 = t.it * C::BM;
-    return classify(p, q_span(p, b, i0, min(i0 + C::BM, p.Sq) - 1), ksp, false);
+  // Spans of the query tiles: with position or segment arrays each is two dependent
+  // global loads, so they are loaded once, in parallel, into LDS.
+  const bool span_cached = (p.q_pos != nullptr || p.q_seg != nullptr) && n_it <= C::kSpanTiles;
+  i32x4* span_l = reinterpret_cast<i32x4*>(smem + 2 * C::kStageMax);
+  if (span_cached) {
+    for (int t = tid; t < n_it; t += C::kThreads) {
+      const Span s = q_span(p, b, t * C::BM, min(t * C::BM + C::BM, p.Sq) - 1);
+      span_l[t] = i32x4{s.pos_lo, s.pos_hi, s.seg_lo, s.seg_hi};
+    }
+    __syncthreads();
+  }
+  auto qtile_span = [&](int it) {
+    if (span_cached) {
+      const i32x4 x = span_l[it];
+      return Span{x[0], x[1], x[2], x[3]};
+    }
+    return q_span(p, b, it * C::BM, min(it * C::BM + C::BM, p.Sq) - 1);
   };
+  auto tile_class = [&](Tq t, const Span& ksp) { return classify(p, qtile_span(t.it), ksp, false); };
   // the query tiles live for this key block lie in [it_lo, it_hi); the walk stays
   // inside (queries wholly after the keys' window / segments are a suffix, those
   // wholly before the keys a prefix)
-  auto qtile_span = [&](int it) { return q_span(p, b, it * C::BM, min(it * C::BM + C::BM, p.Sq) - 1); };
   const int it_hi = first_true(0, n_it, [&](int it) { return keys_before(p, qtile_span(it), wg_k); });
   const int it_lo = first_true(0, it_hi, [&](int it) { return !keys_after(p, qtile_span(it), wg_k); });
   auto next_tile = [&](Tq t) {
@@ -392,13 +409,27 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
   const uint16_t* kbase = k + int64_t(b) * p.Sk * krs + int64_t(g) * C::D;
   const uint16_t* vbase = v + int64_t(b) * p.Sk * krs + int64_t(g) * C::D;
 
+  // spans of the key tiles, cached in LDS when they come from arrays (as above)
+  const bool span_cached = (p.k_pos != nullptr || p.k_seg != nullptr) && n_kt <= C::kSpanTiles;
+  i32x4* span_l = reinterpret_cast<i32x4*>(smem + 2 * C::kStageMax);
+  if (span_cached) {
+    for (int t = tid; t < n_kt; t += C::kThreads) {
+      const Span s = k_span(p, b, t * C::BN, min(t * C::BN + C::BN, p.Sk) - 1);
+      span_l[t] = i32x4{s.pos_lo, s.pos_hi, s.seg_lo, s.seg_hi};
+    }
+    __syncthreads();
+  }
+  auto ktile_span = [&](int kt) {
+    if (span_cached) {
+      const i32x4 x = span_l[kt];
+      return Span{x[0], x[1], x[2], x[3]};
+    }
+    return k_span(p, b, kt * C::BN, min(kt * C::BN + C::BN, p.Sk) - 1);
+  };
   auto tile_class = [&](int kt, const Span& qsp) {
-    const int j0 = kt * C::BN;
-    const int j1 = min(j0 + C::BN, p.Sk) - 1;
-    return classify(p, qsp, k_span(p, b, j0, j1), j1 - j0 + 1 < C::BN);
+    return classify(p, qsp, ktile_span(kt), kt * C::BN + C::BN > p.Sk);
   };
   // the key tiles live for this query block lie in [kt_lo, kt_hi)
-  auto ktile_span = [&](int kt) { return k_span(p, b, kt * C::BN, min(kt * C::BN + C::BN, p.Sk) - 1); };
   const int kt_lo = first_true(0, n_kt, [&](int kt) { return !keys_before(p, wg_q, ktile_span(kt)); });
   const int kt_hi = first_true(kt_lo, n_kt, [&](int kt) { return keys_after(p, wg_q, ktile_span(kt)); });
   auto next_tile = [&](int kt) {

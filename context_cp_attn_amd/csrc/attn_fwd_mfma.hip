@@ -68,13 +68,17 @@ struct FwdCfg {
   static constexpr int PT = BN / 16;  // k-steps of O^T += V^T P^T
   static constexpr int kTileElems = BN * D;  // swizzled row-major K or V tile
   static constexpr int kStageBytes = 2 * kTileElems * 2 + BN * 2 * 4;  // K, V, kpos, kseg
-  static constexpr int kLdsBytes = (SPLIT ? 1 : NS) * 2 * kStageBytes;
+  static constexpr int kStagesBytes = (SPLIT ? 1 : NS) * 2 * kStageBytes;
+  // spans of up to kSpanTiles key tiles, cached when they come from position /
+  // segment arrays (a span is then two dependent global loads)
+  static constexpr int kSpanTiles = 512;
+  static constexpr int kLdsBytes = kStagesBytes + kSpanTiles * 16;
   // exchange of the second key group's (o, m, l) per lane, over the stages
   static constexpr int kXchgBytes = NW * 64 * (DB * 16 + 2) * 4;
   static constexpr int kAhead = 2;  // LDS operand reads issued ahead of their product
   using Tile = DmaTile<BN, D, kGroupThreads>;
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
-  static_assert(NS == 1 || (NS == 2 && (SPLIT || kXchgBytes <= kLdsBytes)), "key groups");
+  static_assert(NS == 1 || (NS == 2 && (SPLIT || kXchgBytes <= kStagesBytes)), "key groups");
   static_assert(!SPLIT || NS == 2, "a split pairs two key groups");
 };
 
@@ -139,15 +143,37 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
   const float c2 = p.scale * kLog2e;
   const int n_kt = (p.Sk + C::BN - 1) / C::BN;
 
+  // Spans of the key tiles.  With position or segment arrays each one is two
+  // dependent global loads, which the walk and the per-wave classification would
+  // wait for at every tile; all tiles' spans are then loaded once, in parallel,
+  // into LDS (for up to kSpanTiles tiles).
+  const bool span_cached = (p.k_pos != nullptr || p.k_seg != nullptr) && n_kt <= C::kSpanTiles;
+  i32x4* span_l = reinterpret_cast<i32x4*>(smem + C::kStagesBytes);
+  if (span_cached) {
+    for (int t = tid; t < n_kt; t += C::kThreads) {
+      const Span s = k_span(p, b, t * C::BN, min(t * C::BN + C::BN, p.Sk) - 1);
+      span_l[t] = i32x4{s.pos_lo, s.pos_hi, s.seg_lo, s.seg_hi};
+    }
+    __syncthreads();
+  }
+  auto tile_span = [&](int kt) {
+    if (span_cached) {
+      const i32x4 x = span_l[kt];
+      return Span{x[0], x[1], x[2], x[3]};
+    }
+    return k_span(p, b, kt * C::BN, min(kt * C::BN + C::BN, p.Sk) - 1);
+  };
   auto tile_class = [&](int kt, const Span& qsp) {
-    const int j0 = kt * C::BN;
-    const int j1 = min(j0 + C::BN, p.Sk) - 1;
-    return classify(p, qsp, k_span(p, b, j0, j1), j1 - j0 + 1 < C::BN);
+    return classify(p, qsp, tile_span(kt), kt * C::BN + C::BN > p.Sk);
   };
   // the workgroup's live key tiles lie in [kt_lo, kt_hi); the walk stays inside
-  auto tile_span = [&](int kt) { return k_span(p, b, kt * C::BN, min(kt * C::BN + C::BN, p.Sk) - 1); };
   const int kt_lo = first_true(0, n_kt, [&](int kt) { return !keys_before(p, wg_q, tile_span(kt)); });
   const int kt_hi = first_true(kt_lo, n_kt, [&](int kt) { return keys_after(p, wg_q, tile_span(kt)); });
+  if constexpr (kMerge) {
+    // no key of this block is visible to these rows: merging a weight-0 block
+    // leaves the running result as it is, so nothing is read or written
+    if (kt_lo >= kt_hi) return;
+  }
   auto next_tile = [&](int kt) {
     kt = max(kt, kt_lo);
     while (kt < kt_hi && tile_class(kt, wg_q) == kEmpty) ++kt;

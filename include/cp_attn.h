@@ -112,7 +112,9 @@ cp_status_t cp_attn_fwd_ws(const cp_attn_args_t* args, const void* q, const void
  *   acc' = acc * e^(lse_acc - lse') + out_blk * e^(lse_blk - lse')
  * with the -inf rules of cp_lse_merge (a row with no visible key in this block has
  * weight 0).  out_acc [B,Sq,Hq,D] float32 (16-byte aligned on the matrix-core path) and lse_acc [B,Hq,Sq]
- * float32 are read and written; start a ring with out_acc = 0, lse_acc = -inf.
+ * float32 are read and written; start a ring with out_acc = 0, lse_acc = -inf (rows
+ * whose query tile sees no key of the block may be left untouched, which is the
+ * same result for every state such a ring reaches).
  * out_acc/lse_acc must not overlap q, k, v or each other (CP_ERR_ALIAS).
  */
 cp_status_t cp_attn_fwd_merge(const cp_attn_args_t* args, const void* q, const void* k, const void* v,
