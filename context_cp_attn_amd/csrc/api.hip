@@ -257,8 +257,9 @@ cp_status_t cp_attn_check_args(const cp_attn_args_t* a, int32_t* flags, hipStrea
 
 size_t cp_attn_bwd_workspace_size(const cp_attn_args_t* a) {
   if (!a || a->batch < 1 || a->heads_q < 1 || a->seqlen_q < 1) return 0;
-  const size_t n = size_t(a->batch) * size_t(a->heads_q) * size_t(a->seqlen_q) * sizeof(float);
-  return (n + 255) & ~size_t(255);
+  // two row arrays: delta and the base-2 lse
+  const int64_t rows = a->batch * a->heads_q * a->seqlen_q;
+  return size_t(2 * cp::bwd_row_plane(rows)) * sizeof(float);
 }
 
 cp_status_t cp_attn_bwd(const cp_attn_args_t* a, const void* q, const void* k, const void* v,

@@ -36,12 +36,19 @@ namespace {
 
 using namespace mfma;
 
-// ---- 1. Delta --------------------------------------------------------------------
+// lse in the base-2 domain; a row with no visible key gets +inf so that every
+// exp2(s*c - lse2) of it is exactly 0.
+CP_DEVICE float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+
+// ---- 1. Delta (and the base-2 lse) ----------------------------------------------
+// Both row arrays [B,Hq,Sq] go to the workspace, where the main kernel's key roles
+// copy a query tile's values straight into LDS.
 template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(int64_t rows, int Sq, int Hq,
                                                     const uint16_t* __restrict__ out,
                                                     const uint16_t* __restrict__ dout,
-                                                    float* __restrict__ delta) {
+                                                    const float* __restrict__ lse,
+                                                    float* __restrict__ delta, float* __restrict__ lse2) {
   constexpr int kLanesPerRow = D / 8;
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t row = t / kLanesPerRow;   // (b, i, h)
@@ -63,13 +70,22 @@ __global__ __launch_bounds__(256) void delta_kernel(int64_t rows, int Sq, int Hq
     const int64_t bi = row / Hq;
     const int i = int(bi % Sq);
     const int64_t b = bi / Sq;
-    delta[(b * Hq + h) * Sq + i] = x;
+    const int64_t li = (b * Hq + h) * Sq + i;
+    delta[li] = x;
+    lse2[li] = lse2_of(lse[li]);
   }
 }
 
-// lse in the base-2 domain; a row with no visible key gets +inf so that every
-// exp2(s*c - lse2) of it is exactly 0.
-CP_DEVICE float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+// 128 consecutive dwords of src from element first (valid of them exist; the rest
+// read as 0) into lds, copied by one wavefront with two LDS-DMA loads.
+CP_DEVICE void dma_dwords128(const void* src, int64_t first, int valid, void* lds, int lane) {
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(reinterpret_cast<const uint8_t*>(src) + first * 4, uint32_t(valid > 0 ? valid : 0) * 4u);
+  uint8_t* dst = static_cast<uint8_t*>(lds);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 4, lane * 4, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 256), 4,
+                                          lane * 4 + 256, 0, 0, 0);
+}
 
 // ---- 2. configuration and LDS stages ---------------------------------------------
 template <int D_>
@@ -125,7 +141,7 @@ struct QStage {
 template <class C, bool kDK>
 CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-                        const float* __restrict__ lse, const float* __restrict__ delta,
+                        const float* __restrict__ lse2, const float* __restrict__ delta,
                         float* __restrict__ grad, int accumulate, uint8_t* smem, int kt, int g, int b) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -218,34 +234,33 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
   const uint32_t qrs_bytes = uint32_t(qrs) * 2u;
   tq.init(qrs_bytes, tid);
   tg.init(qrs_bytes, tid);
-  // per-query values of the next tile, fetched early by the first BM threads and
-  // written to LDS after this tile's products
-  float n_lse2 = INFINITY, n_delta = 0.0f;
-  int n_qpos = 0, n_qseg = 0;
+  // The tile's per-query values go straight into the stage: lse2 and delta by
+  // LDS-DMA from the workspace, positions / segment ids by LDS-DMA from their
+  // arrays, or written as offset + row / 0 when there are none.  Rows past the end
+  // read as 0; their Q and dO rows are zero as well, so they add nothing.
+  static_assert(C::BM == 128, "dma_dwords128 copies one 128-row tile");
   auto issue = [&](Tq t, uint8_t* base) {
     QStage<C> st(base);
     const int h = g * G + t.hh;
     const int i0 = t.it * C::BM;
     tq.load(q + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq, st.q);
     tg.load(dout + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq, st.g);
-    if (tid < C::BM) {
-      const int i = i0 + tid;
-      const bool ok = i < p.Sq;
-      const int64_t li = (int64_t(b) * p.Hq + h) * p.Sq + i;
-      n_lse2 = ok ? lse2_of(lse[li]) : INFINITY;
-      if constexpr (kDK) n_delta = ok ? delta[li] : 0.0f;
-      n_qpos = ok ? qpos_at(p, i) : 0;
-      n_qseg = ok ? qseg_at(p, b, i) : 0;
+    const int64_t li0 = (int64_t(b) * p.Hq + h) * p.Sq + i0;
+    const int wave = tid >> 6;
+    if (wave == 0) dma_dwords128(lse2, li0, p.Sq - i0, st.lse2, lane);
+    if (kDK && wave == 1) dma_dwords128(delta, li0, p.Sq - i0, st.delta, lane);
+    if (p.q_pos) {
+      if (wave == 2) dma_dwords128(p.q_pos, i0, p.Sq - i0, st.qpos, lane);
+    } else if (tid < C::BM) {
+      st.qpos[tid] = p.q_offset + i0 + tid;
+    }
+    if (p.q_seg) {
+      if (wave == 3) dma_dwords128(p.q_seg, int64_t(b) * p.Sq + i0, p.Sq - i0, st.qseg, lane);
+    } else if (tid < C::BM) {
+      st.qseg[tid] = 0;
     }
   };
-  auto publish = [&](uint8_t* base) {
-    QStage<C> st(base);
-    if (tid < C::BM) {
-      st.lse2[tid] = n_lse2;
-      if constexpr (kDK) st.delta[tid] = n_delta;
-      st.qpos[tid] = n_qpos;
-      st.qseg[tid] = n_qseg;
-    }
+  auto publish = [&](uint8_t*) {
     wait_all();
     __syncthreads();
   };
@@ -363,7 +378,7 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
 template <class C>
 CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                        const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-                       const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dq,
+                       const float* __restrict__ lse2, const float* __restrict__ delta, float* __restrict__ dq,
                        int accumulate, uint8_t* smem, int qt, int h, int b) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -395,7 +410,7 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
     }
   }
   const int64_t li = (int64_t(b) * p.Hq + h) * p.Sq + row;
-  const float my_lse2 = row_ok ? lse2_of(lse[li]) : INFINITY;
+  const float my_lse2 = row_ok ? lse2[li] : INFINITY;
   const float my_delta = row_ok ? delta[li] : 0.0f;
   const int my_qpos = qpos_at(p, row);
   const int my_qseg = qseg_at(p, b, row);
@@ -445,22 +460,27 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
   auto ks_of = [&](uint8_t* base) { return reinterpret_cast<uint16_t*>(base); };
   auto vs_of = [&](uint8_t* base) { return ks_of(base) + C::kTileN; };
   auto kp_of = [&](uint8_t* base) { return reinterpret_cast<int*>(vs_of(base) + C::kTileN); };
-  int n_kpos = 0, n_kseg = 0;
+  // key positions / segment ids of the tile straight into the stage (as in the
+  // key roles); keys past the end are masked by their index
+  static_assert(C::BN == 128, "dma_dwords128 copies one 128-key tile");
   auto issue = [&](int kt, uint8_t* base) {
     tk.load(kbase, krs_bytes, kt * C::BN, p.Sk, ks_of(base));
     tv.load(vbase, krs_bytes, kt * C::BN, p.Sk, vs_of(base));
-    if (tid < C::BN) {
-      const int j = min(kt * C::BN + tid, p.Sk - 1);
-      n_kpos = kpos_at(p, j);
-      n_kseg = kseg_at(p, b, j);
+    int* kp = kp_of(base);
+    const int j0 = kt * C::BN;
+    const int wave = tid >> 6;
+    if (p.k_pos) {
+      if (wave == 0) dma_dwords128(p.k_pos, j0, p.Sk - j0, kp, lane);
+    } else if (tid < C::BN) {
+      kp[tid] = p.k_offset + j0 + tid;
+    }
+    if (p.k_seg) {
+      if (wave == 1) dma_dwords128(p.k_seg, int64_t(b) * p.Sk + j0, p.Sk - j0, kp + C::BN, lane);
+    } else if (tid < C::BN) {
+      kp[C::BN + tid] = 0;
     }
   };
-  auto publish = [&](uint8_t* base) {
-    if (tid < C::BN) {
-      int* kp = kp_of(base);
-      kp[tid] = n_kpos;
-      kp[C::BN + tid] = n_kseg;
-    }
+  auto publish = [&](uint8_t*) {
     wait_all();
     __syncthreads();
   };
@@ -564,8 +584,8 @@ struct BwdArgs {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* lse;
-  const float* delta;
+  const float* lse2;   // [B,Hq,Sq] base-2 lse (workspace)
+  const float* delta;  // [B,Hq,Sq] (workspace)
   float* dq;
   float* dk;
   float* dv;
@@ -594,17 +614,17 @@ __global__ __launch_bounds__(C::kThreads) void attn_bwd_kernel(BwdArgs a) {
     const int bg = pair % (p.B * p.Hkv);
     const int kt = pair / (p.B * p.Hkv);
     if ((i & 1) == 0)
-      key_role<C, true>(p, a.q, a.k, a.v, a.dout, a.lse, a.delta, a.dk, a.accumulate, smem, kt, bg % p.Hkv,
+      key_role<C, true>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dk, a.accumulate, smem, kt, bg % p.Hkv,
                         bg / p.Hkv);
     else
-      key_role<C, false>(p, a.q, a.k, a.v, a.dout, a.lse, a.delta, a.dv, a.accumulate, smem, kt, bg % p.Hkv,
+      key_role<C, false>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dv, a.accumulate, smem, kt, bg % p.Hkv,
                          bg / p.Hkv);
   } else {
     const int i = int(L - before);
     const int bh = i % (p.B * p.Hq);
     const int r = i / (p.B * p.Hq);
     const int n_qt = (p.Sq + C::kRows - 1) / C::kRows;
-    dq_role<C>(p, a.q, a.k, a.v, a.dout, a.lse, a.delta, a.dq, a.accumulate, smem, p.causal ? n_qt - 1 - r : r,
+    dq_role<C>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dq, a.accumulate, smem, p.causal ? n_qt - 1 - r : r,
                bh % p.Hq, bh / p.Hq);
   }
 }
@@ -616,13 +636,14 @@ hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const vo
   using U = const uint16_t*;
   const int64_t rows = int64_t(p.B) * p.Sq * p.Hq;
   const int64_t threads = rows * (D / 8);
+  float* lse2 = delta + bwd_row_plane(rows);
   {
     ProfScope ps(s, kProfBwdDelta);
     hipLaunchKernelGGL(delta_kernel<D>, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, rows, p.Sq,
-                       p.Hq, static_cast<U>(out), static_cast<U>(dout), delta);
+                       p.Hq, static_cast<U>(out), static_cast<U>(dout), lse, delta, lse2);
   }
   using C = BwdCfg<D>;
-  BwdArgs a{p, static_cast<U>(q), static_cast<U>(k), static_cast<U>(v), static_cast<U>(dout), lse, delta,
+  BwdArgs a{p, static_cast<U>(q), static_cast<U>(k), static_cast<U>(v), static_cast<U>(dout), lse2, delta,
             dq, dk, dv, accumulate,
             2 * p.B * p.Hkv * ((p.Sk + C::kRows - 1) / C::kRows),
             p.B * p.Hq * ((p.Sq + C::kRows - 1) / C::kRows)};

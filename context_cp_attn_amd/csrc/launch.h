@@ -47,7 +47,9 @@ hipError_t launch_attn_bwd_rowwise_bf16(const AttnProblem& p, const void* q, con
                                         const void* out, const float* lse, const void* dout, float* dq,
                                         float* dk, float* dv, int accumulate, float* delta, hipStream_t s);
 
-// backward: delta workspace is [B,Hq,Sq] float32
+// backward workspace: delta [B,Hq,Sq] float32, then (bf16 matrix-core path) the
+// base-2 lse [B,Hq,Sq] float32 starting bwd_row_plane(rows) floats in
+inline int64_t bwd_row_plane(int64_t rows) { return (rows + 63) / 64 * 64; }
 hipError_t launch_attn_bwd_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
                                 const void* out, const float* lse, const void* dout, float* dq,
                                 float* dk, float* dv, int accumulate, float* delta, hipStream_t s);

@@ -120,7 +120,8 @@ cp_status_t cp_attn_fwd_ws(const cp_attn_args_t* args, const void* q, const void
 cp_status_t cp_attn_fwd_merge(const cp_attn_args_t* args, const void* q, const void* k, const void* v,
                               float* out_acc, float* lse_acc, hipStream_t stream);
 
-/* Workspace bytes cp_attn_bwd needs for args (the per-row dO.O sums). */
+/* Workspace bytes cp_attn_bwd needs for args: two float32 arrays of the rows
+   [B,Hq,Sq], the per-row dO.O sums and the rows' lse in base 2. */
 size_t cp_attn_bwd_workspace_size(const cp_attn_args_t* args);
 
 /*
