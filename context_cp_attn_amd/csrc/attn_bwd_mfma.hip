@@ -76,16 +76,6 @@ __global__ __launch_bounds__(256) void delta_kernel(int64_t rows, int Sq, int Hq
   }
 }
 
-// 128 consecutive dwords of src from element first (valid of them exist; the rest
-// read as 0) into lds, copied by one wavefront with two LDS-DMA loads.
-CP_DEVICE void dma_dwords128(const void* src, int64_t first, int valid, void* lds, int lane) {
-  const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(reinterpret_cast<const uint8_t*>(src) + first * 4, uint32_t(valid > 0 ? valid : 0) * 4u);
-  uint8_t* dst = static_cast<uint8_t*>(lds);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 4, lane * 4, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 256), 4,
-                                          lane * 4 + 256, 0, 0, 0);
-}
 
 // ---- 2. configuration and LDS stages ---------------------------------------------
 template <int D_>
@@ -238,7 +228,7 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
   // LDS-DMA from the workspace, positions / segment ids by LDS-DMA from their
   // arrays, or written as offset + row / 0 when there are none.  Rows past the end
   // read as 0; their Q and dO rows are zero as well, so they add nothing.
-  static_assert(C::BM == 128, "dma_dwords128 copies one 128-row tile");
+  static_assert(C::BM % 64 == 0, "whole wavefronts of rows");
   auto issue = [&](Tq t, uint8_t* base) {
     QStage<C> st(base);
     const int h = g * G + t.hh;
@@ -247,15 +237,15 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
     tg.load(dout + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq, st.g);
     const int64_t li0 = (int64_t(b) * p.Hq + h) * p.Sq + i0;
     const int wave = tid >> 6;
-    if (wave == 0) dma_dwords128(lse2, li0, p.Sq - i0, st.lse2, lane);
-    if (kDK && wave == 1) dma_dwords128(delta, li0, p.Sq - i0, st.delta, lane);
+    if (wave == 0) dma_dwords<C::BM>(lse2, li0, p.Sq - i0, st.lse2, lane);
+    if (kDK && wave == 1) dma_dwords<C::BM>(delta, li0, p.Sq - i0, st.delta, lane);
     if (p.q_pos) {
-      if (wave == 2) dma_dwords128(p.q_pos, i0, p.Sq - i0, st.qpos, lane);
+      if (wave == 2) dma_dwords<C::BM>(p.q_pos, i0, p.Sq - i0, st.qpos, lane);
     } else if (tid < C::BM) {
       st.qpos[tid] = p.q_offset + i0 + tid;
     }
     if (p.q_seg) {
-      if (wave == 3) dma_dwords128(p.q_seg, int64_t(b) * p.Sq + i0, p.Sq - i0, st.qseg, lane);
+      if (wave == 3) dma_dwords<C::BM>(p.q_seg, int64_t(b) * p.Sq + i0, p.Sq - i0, st.qseg, lane);
     } else if (tid < C::BM) {
       st.qseg[tid] = 0;
     }
@@ -462,7 +452,7 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
   auto kp_of = [&](uint8_t* base) { return reinterpret_cast<int*>(vs_of(base) + C::kTileN); };
   // key positions / segment ids of the tile straight into the stage (as in the
   // key roles); keys past the end are masked by their index
-  static_assert(C::BN == 128, "dma_dwords128 copies one 128-key tile");
+  static_assert(C::BN % 64 == 0, "whole wavefronts of keys");
   auto issue = [&](int kt, uint8_t* base) {
     tk.load(kbase, krs_bytes, kt * C::BN, p.Sk, ks_of(base));
     tv.load(vbase, krs_bytes, kt * C::BN, p.Sk, vs_of(base));
@@ -470,12 +460,12 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
     const int j0 = kt * C::BN;
     const int wave = tid >> 6;
     if (p.k_pos) {
-      if (wave == 0) dma_dwords128(p.k_pos, j0, p.Sk - j0, kp, lane);
+      if (wave == 0) dma_dwords<C::BN>(p.k_pos, j0, p.Sk - j0, kp, lane);
     } else if (tid < C::BN) {
       kp[tid] = p.k_offset + j0 + tid;
     }
     if (p.k_seg) {
-      if (wave == 1) dma_dwords128(p.k_seg, int64_t(b) * p.Sk + j0, p.Sk - j0, kp + C::BN, lane);
+      if (wave == 1) dma_dwords<C::BN>(p.k_seg, int64_t(b) * p.Sk + j0, p.Sk - j0, kp + C::BN, lane);
     } else if (tid < C::BN) {
       kp[C::BN + tid] = 0;
     }

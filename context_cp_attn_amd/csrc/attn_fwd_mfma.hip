@@ -191,11 +191,19 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     int* kseg = kpos + C::BN;
     tk.load(kbase, krs_bytes, kt * C::BN, p.Sk, ks);
     tv.load(vbase, krs_bytes, kt * C::BN, p.Sk, vs);
+    // key positions / segment ids: LDS-DMA from their arrays (one row wavefront of
+    // the group each), or written as offset + index / 0; keys past the end are
+    // masked by their index
     const int j0 = kt * C::BN;
-    for (int t = gtid; t < C::BN; t += C::kGroupThreads) {
-      const int j = min(j0 + t, p.Sk - 1);
-      kpos[t] = kpos_at(p, j);
-      kseg[t] = kseg_at(p, b, j);
+    if (p.k_pos) {
+      if (rw == 0) dma_dwords<C::BN>(p.k_pos, j0, p.Sk - j0, kpos, lane);
+    } else {
+      for (int t = gtid; t < C::BN; t += C::kGroupThreads) kpos[t] = p.k_offset + j0 + t;
+    }
+    if (p.k_seg) {
+      if (rw == 1 % C::NW) dma_dwords<C::BN>(p.k_seg, int64_t(b) * p.Sk + j0, p.Sk - j0, kseg, lane);
+    } else {
+      for (int t = gtid; t < C::BN; t += C::kGroupThreads) kseg[t] = 0;
     }
   };
   auto stage_of = [&](int buf) { return smem + ((C::SPLIT ? 0 : grp) * 2 + buf) * C::kStageBytes; };
