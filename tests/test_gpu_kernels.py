@@ -472,6 +472,32 @@ def test_attn_fwd_split(cp, D, masks):
     check_close(out, f64(out1), 1e-2, "split vs unsplit")
 
 
+@pytest.mark.parametrize("Sq,Sk", [(1, 1), (1, 300), (300, 1), (33, 65), (1, 8193)])
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.bfloat16, 16),
+                                     (torch.float32, 16)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_attn_tiny_and_ragged(cp, Sq, Sk, dtype, D, causal):
+    """Degenerate shapes: one query row, one key, lengths one past a tile, and a
+    single row against 8193 keys (the split forward with one ragged key tile);
+    forward (with and without a workspace) and backward against the oracle.  With
+    causal masking and q_offset = Sk - Sq (>= 0) every row sees a key."""
+    say(f"attn tiny Sq={Sq} Sk={Sk} D={D} {dtype} causal={causal}")
+    q, k, v, do = cp_inputs.normal_tensors([(1, Sq, 2, D), (1, Sk, 1, D), (1, Sk, 1, D), (1, Sq, 2, D)],
+                                           seed=21, dtype=dtype)
+    m = dict(causal=causal, q_offset=max(Sk - Sq, 0))
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    out, lse = cp.attn_fwd(qd, kd, vd, **m)
+    out1, lse1 = cp.attn_fwd(qd, kd, vd, workspace=False, **m)
+    dq, dk, dv = cp.attn_bwd(qd, kd, vd, out, lse, dod, **m)
+    ref_o, ref_l = oracle.attn_fwd(q, k, v, **m)
+    refs = oracle.attn_bwd(q, k, v, ref_o, ref_l, do, **m)
+    for o_, l_, nm in ((out, lse, "ws"), (out1, lse1, "no ws")):
+        check_lse(l_, ref_l, TOL[dtype]["lse"])
+        check_close(o_, ref_o, TOL[dtype]["out"], f"out ({nm})")
+    for got, ref, nm in zip((dq, dk, dv), refs, ("dq", "dk", "dv")):
+        check_close(got, ref, TOL[dtype]["grad"] * max(1.0, np.abs(ref).max()), nm)
+
+
 @pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)])
 def test_deterministic(cp, dtype, D):
     say(f"determinism {dtype} D={D}")
