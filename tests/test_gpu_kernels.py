@@ -64,6 +64,7 @@ def check_close(got, ref, tol, what):
     (3, 1, 15, 6, 7, torch.float32),       # 56-byte runs
     (2, 3, 10, 2, 3, torch.bfloat16),      # 6-byte runs
     (16, 1, 4096, 32, 128, torch.bfloat16),
+    (1, 2, 9, 3, 5, torch.float32),         # degree 1: a plain copy
 ])
 def test_ulysses_relayout_bit_exact(cp, P, B, S, H, D, dtype):
     say(f"relayout P={P} B={B} S={S} H={H} D={D} {dtype}")
@@ -71,6 +72,8 @@ def test_ulysses_relayout_bit_exact(cp, P, B, S, H, D, dtype):
     x = torch.randn(P, B, S // P, H, D).to(dtype).cuda()
     y = cp.ulysses_relayout(x, P)
     np.testing.assert_array_equal(bits(y), oracle.ulysses_relayout(bits(x)))
+    if P == 1:
+        assert torch.equal(y, x)
     z = cp.ulysses_relayout_inv(y, P)
     assert torch.equal(z, x)
     np.testing.assert_array_equal(bits(z), oracle.ulysses_relayout_inv(bits(y)))
@@ -196,6 +199,7 @@ def test_padded_sequence_attention(cp, scheme, causal):
     ((3, 40, 7), 5, torch.uint8),
     ((1, 4096, 4096), 4, torch.bfloat16),
     ((2, 30, 3), 5, torch.int32),
+    ((2, 6, 3), 1, torch.float32),          # one rank: the identity
 ])
 def test_reorder_bit_exact(cp, shape, P, dtype, strategy):
     """strategy 0 = dual-chunk-swap (zigzag), 1 = striped."""
@@ -209,6 +213,8 @@ def test_reorder_bit_exact(cp, shape, P, dtype, strategy):
                 else (oracle.reorder_striped, oracle.reorder_striped_inv))
     y = cp.zigzag_reorder(x, P, strategy=strategy)
     np.testing.assert_array_equal(bits(y), fwd(bits(x), P))
+    if P == 1:
+        assert torch.equal(y, x)
     z = cp.zigzag_reorder(y, P, inverse=True, strategy=strategy)
     np.testing.assert_array_equal(bits(z), inv(bits(y), P))
     assert torch.equal(z, x)
