@@ -303,12 +303,15 @@ int pick_vec_bytes(int64_t run_bytes, const void* a, const void* b) {
   return 1;
 }
 
-// Blocks per span so that the whole grid holds about 8 resident blocks per CU
-// (256 CUs) while a span never gets more blocks than it has work.
+// Blocks per span so that the whole grid has about 16384 blocks (64 per CU of 256;
+// a 256 MiB bf16 tensor then takes one pass of kThreads * kVPT 16-byte vectors per
+// block) while a span never gets more blocks than it has work.  Measured on the
+// llama2-7b relayout shapes and the 64K-token reorder against 2048 / 4096 / 8192
+// blocks: +2% (bf16 relayout) to +10% (float32 inverse), e.g. 5.5 -> 6.1 TB/s.
 int blocks_for(int64_t spans, int64_t vecs_per_span) {
   const int64_t per_block = int64_t(kThreads) * kVPT;
   int64_t need = (vecs_per_span + per_block - 1) / per_block;
-  int64_t want = (2048 + spans - 1) / spans;
+  int64_t want = (16384 + spans - 1) / spans;
   if (want < 1) want = 1;
   int64_t bps = need < want ? need : want;
   return int(bps < 1 ? 1 : bps);
