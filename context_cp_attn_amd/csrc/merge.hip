@@ -3,9 +3,10 @@
 // §"Ring Attention": lse = log(e^lse1 + e^lse2), o = o1 e^(lse1-lse) + o2 e^(lse2-lse).
 //
 // HBM-bound streaming kernel: each thread owns 4 consecutive float32 of one
-// (b, s, h) row of the accumulator (16-byte loads and stores); the D/4 threads of a
-// row sit in one wavefront (D/4 divides 64), so every lane reads the old lse_acc of
-// its row in the same instruction before the row's first lane writes the new one.
+// (b, s, h) row of the accumulator (16-byte loads and stores), for two rows apart; the
+// D/4 threads of a row sit in one wavefront (D/4 divides 64), so every lane reads the
+// old lse_acc of its row in the same instruction before the row's first lane writes
+// the new one.
 #include "common.h"
 #include "launch.h"
 #include "prof.h"
@@ -17,39 +18,63 @@ constexpr int kThreads = 256;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
-template <bool kBf16>
+constexpr int kVPT = 2;  // vectors per thread: both loads issued before the stores
+
+// I: index type; 32-bit when the sizes allow (64-bit division is a long instruction
+// sequence, and this kernel does a row / column split per 16 bytes moved).
+template <bool kBf16, typename I>
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(float* __restrict__ acc,
                                                              float* __restrict__ lse_acc,
                                                              const void* __restrict__ blk,
                                                              const float* __restrict__ lse_blk,
-                                                             int S, int H, int D4,
-                                                             int64_t nvec) {
-  const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  if (t >= nvec) return;
-  const int64_t row = t / D4;            // (b, s, h) row index in [B*S*H]
-  const int c = int(t - row * D4);       // which 4-float column group
-  const int h = int(row % H);
-  const int64_t bs = row / H;
-  const int s = int(bs % S);
-  const int64_t b = bs / S;
-  const int64_t li = (b * H + h) * int64_t(S) + s;  // lse index [b][h][s]
-  const MergeWeights w = merge_weights(lse_acc[li], lse_blk[li]);
-  const float wa = w.wa, wb = w.wb;
-  f32x4 a = *reinterpret_cast<const f32x4*>(acc + t * 4);
-  f32x4 x;
-  if constexpr (kBf16) {
-    const u16x4 r = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(blk) + t * 4);
-    x = f32x4{bf16_to_f32(r.x), bf16_to_f32(r.y), bf16_to_f32(r.z), bf16_to_f32(r.w)};
-  } else {
-    x = *reinterpret_cast<const f32x4*>(static_cast<const float*>(blk) + t * 4);
+                                                             I S, I H, I D4, I nvec) {
+  // vectors t0 + u * kThreads, u < kVPT; the D4 lanes of a row are consecutive
+  // threads of one wavefront for every u
+  const I t0 = I(blockIdx.x) * I(kThreads * kVPT) + I(threadIdx.x);
+  f32x4 a[kVPT], x[kVPT];
+  MergeWeights w[kVPT];
+  I li[kVPT];
+#pragma unroll
+  for (int u = 0; u < kVPT; ++u) {
+    const I t = t0 + I(u * kThreads);
+    if (t >= nvec) continue;
+    const I row = t / D4;  // (b, s, h) row index in [B*S*H]
+    const I h = row % H;
+    const I bs = row / H;
+    const I sI = bs % S;
+    const I b = bs / S;
+    li[u] = (b * H + h) * S + sI;  // lse index [b][h][s]
+    w[u] = merge_weights(lse_acc[li[u]], lse_blk[li[u]]);
+    a[u] = *reinterpret_cast<const f32x4*>(acc + int64_t(t) * 4);
+    if constexpr (kBf16) {
+      const u16x4 r = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(blk) + int64_t(t) * 4);
+      x[u] = f32x4{bf16_to_f32(r.x), bf16_to_f32(r.y), bf16_to_f32(r.z), bf16_to_f32(r.w)};
+    } else {
+      x[u] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(blk) + int64_t(t) * 4);
+    }
   }
-  f32x4 o;
-  o.x = a.x * wa + x.x * wb;
-  o.y = a.y * wa + x.y * wb;
-  o.z = a.z * wa + x.z * wb;
-  o.w = a.w * wa + x.w * wb;
-  *reinterpret_cast<f32x4*>(acc + t * 4) = o;
-  if (c == 0) lse_acc[li] = w.lse;
+#pragma unroll
+  for (int u = 0; u < kVPT; ++u) {
+    const I t = t0 + I(u * kThreads);
+    if (t >= nvec) continue;
+    const float wa = w[u].wa, wb = w[u].wb;
+    f32x4 o;
+    o.x = a[u].x * wa + x[u].x * wb;
+    o.y = a[u].y * wa + x[u].y * wb;
+    o.z = a[u].z * wa + x[u].z * wb;
+    o.w = a[u].w * wa + x[u].w * wb;
+    *reinterpret_cast<f32x4*>(acc + int64_t(t) * 4) = o;
+    if (t % D4 == 0) lse_acc[li[u]] = w[u].lse;
+  }
+}
+
+template <bool kBf16, typename I>
+void launch_merge_t(int64_t B, int64_t S, int64_t H, int64_t D, float* acc, float* lse_acc, const void* blk,
+                    const float* lse_blk, hipStream_t s) {
+  const int64_t nvec = B * S * H * (D / 4);
+  const unsigned grid = unsigned((nvec + kThreads * kVPT - 1) / (kThreads * kVPT));
+  hipLaunchKernelGGL((lse_merge_kernel<kBf16, I>), dim3(grid), dim3(kThreads), 0, s, acc, lse_acc, blk, lse_blk,
+                     I(S), I(H), I(D / 4), I(nvec));
 }
 
 }  // namespace
@@ -57,14 +82,20 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(float* __restrict__
 hipError_t launch_lse_merge(int64_t B, int64_t S, int64_t H, int64_t D, float* acc, float* lse_acc,
                             const void* blk, const float* lse_blk, int blk_is_bf16, hipStream_t s) {
   const int64_t nvec = B * S * H * (D / 4);
-  const unsigned grid = unsigned((nvec + kThreads - 1) / kThreads);
+  // 32-bit indices while every vector index (and the last block's overhang) fits
+  const bool small = nvec + kThreads * kVPT < (int64_t(1) << 31);
   ProfScope ps(s, kProfLseMerge);
-  if (blk_is_bf16)
-    hipLaunchKernelGGL(lse_merge_kernel<true>, dim3(grid), dim3(kThreads), 0, s, acc, lse_acc, blk,
-                       lse_blk, int(S), int(H), int(D / 4), nvec);
-  else
-    hipLaunchKernelGGL(lse_merge_kernel<false>, dim3(grid), dim3(kThreads), 0, s, acc, lse_acc,
-                       blk, lse_blk, int(S), int(H), int(D / 4), nvec);
+  if (blk_is_bf16) {
+    if (small)
+      launch_merge_t<true, uint32_t>(B, S, H, D, acc, lse_acc, blk, lse_blk, s);
+    else
+      launch_merge_t<true, int64_t>(B, S, H, D, acc, lse_acc, blk, lse_blk, s);
+  } else {
+    if (small)
+      launch_merge_t<false, uint32_t>(B, S, H, D, acc, lse_acc, blk, lse_blk, s);
+    else
+      launch_merge_t<false, int64_t>(B, S, H, D, acc, lse_acc, blk, lse_blk, s);
+  }
   return hipGetLastError();
 }
 
