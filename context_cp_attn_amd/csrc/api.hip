@@ -323,6 +323,8 @@ cp_status_t cp_lse_merge(int64_t batch, int64_t seqlen, int64_t heads, int64_t h
     return fail(CP_ERR_UNSUPPORTED, "merge is built for head_dim in {4,8,16,32,64,128,256} (got %lld)",
                 (long long)head_dim);
   if (!out_acc || !lse_acc || !out_blk || !lse_blk) return fail(CP_ERR_INVALID, "NULL buffer");
+  if (batch * seqlen * heads > ((int64_t(1) << 31) - 512) / (head_dim / 4))
+    return fail(CP_ERR_UNSUPPORTED, "merge of 2^31 - 512 or more 16-byte vectors (out_acc of 32 GiB or more)");
   if (!aligned(out_acc, 16) || !aligned(out_blk, blk_dtype == CP_DTYPE_BF16 ? 8 : 16))
     return fail(CP_ERR_INVALID, "out_acc must be 16-byte aligned, out_blk 8 (bf16) / 16 (f32)");
   const int64_t rows = batch * seqlen * heads;

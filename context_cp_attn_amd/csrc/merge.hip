@@ -20,8 +20,9 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kVPT = 2;  // vectors per thread: both loads issued before the stores
 
-// I: index type; 32-bit when the sizes allow (64-bit division is a long instruction
-// sequence, and this kernel does a row / column split per 16 bytes moved).
+// I: index type, 32-bit (a 64-bit division is a long instruction sequence, and this
+// kernel does a row / column split per 16 bytes moved; the entry point rejects sizes
+// whose vector indices would not fit).
 template <bool kBf16, typename I>
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(float* __restrict__ acc,
                                                              float* __restrict__ lse_acc,
@@ -81,21 +82,12 @@ void launch_merge_t(int64_t B, int64_t S, int64_t H, int64_t D, float* acc, floa
 
 hipError_t launch_lse_merge(int64_t B, int64_t S, int64_t H, int64_t D, float* acc, float* lse_acc,
                             const void* blk, const float* lse_blk, int blk_is_bf16, hipStream_t s) {
-  const int64_t nvec = B * S * H * (D / 4);
-  // 32-bit indices while every vector index (and the last block's overhang) fits
-  const bool small = nvec + kThreads * kVPT < (int64_t(1) << 31);
+  // the caller keeps B*S*H*D/4 + 512 below 2^31, so every vector index fits
   ProfScope ps(s, kProfLseMerge);
-  if (blk_is_bf16) {
-    if (small)
-      launch_merge_t<true, uint32_t>(B, S, H, D, acc, lse_acc, blk, lse_blk, s);
-    else
-      launch_merge_t<true, int64_t>(B, S, H, D, acc, lse_acc, blk, lse_blk, s);
-  } else {
-    if (small)
-      launch_merge_t<false, uint32_t>(B, S, H, D, acc, lse_acc, blk, lse_blk, s);
-    else
-      launch_merge_t<false, int64_t>(B, S, H, D, acc, lse_acc, blk, lse_blk, s);
-  }
+  if (blk_is_bf16)
+    launch_merge_t<true, uint32_t>(B, S, H, D, acc, lse_acc, blk, lse_blk, s);
+  else
+    launch_merge_t<false, uint32_t>(B, S, H, D, acc, lse_acc, blk, lse_blk, s);
   return hipGetLastError();
 }
 

@@ -158,6 +158,8 @@ cp_status_t cp_attn_check_args(const cp_attn_args_t* args, int32_t* flags, hipSt
  * A part whose lse is -inf has weight 0 (both -inf gives acc' = 0, lse' = -inf).
  * out_acc [B,S,H,D] float32 (read and written), lse_acc [B,H,S] float32 (read and
  * written), out_blk [B,S,H,D] of blk_dtype, lse_blk [B,H,S] float32.
+ * CP_ERR_UNSUPPORTED when out_acc holds 32 GiB or more (B*S*H*D/4 >= 2^31 - 512
+ * 16-byte vectors: the kernel indexes with 32-bit integers).
  */
 cp_status_t cp_lse_merge(int64_t batch, int64_t seqlen, int64_t heads, int64_t head_dim,
                          float* out_acc, float* lse_acc, const void* out_blk,

@@ -191,6 +191,9 @@ def test_merge_rejects():
     assert f(1, 8, 2, 128, FAKE_A, FAKE_B, FAKE_C, 1 << 41, 9, None) == INVALID
     assert f(1, 8, 2, 12, FAKE_A, FAKE_B, FAKE_C, 1 << 41, 1, None) == UNSUPPORTED
     assert f(1, 8, 2, 128, FAKE_A, FAKE_B, FAKE_A, 1 << 41, 1, None) == ALIAS
+    # 32 GiB of accumulator and beyond: 32-bit vector indices would overflow
+    assert f(1, 1 << 21, 32, 128, FAKE_A, FAKE_B, FAKE_C, 1 << 41, 1, None) == UNSUPPORTED
+    assert "32 GiB" in lib.cp_last_error().decode()
 
 
 def test_relayout_ex_rejects():
