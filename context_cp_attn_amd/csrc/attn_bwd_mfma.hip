@@ -214,9 +214,12 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
   // wholly before the keys a prefix)
   const int it_hi = first_true(0, n_it, [&](int it) { return keys_before(p, qtile_span(it), wg_k); });
   const int it_lo = first_true(0, it_hi, [&](int it) { return !keys_after(p, qtile_span(it), wg_k); });
+  // without a window or segment ids every query tile of [it_lo, it_hi) holds a
+  // visible pair (the keys' first position is visible to its last query)
+  const bool dense = !p.window && !p.q_seg;
   auto next_tile = [&](Tq t) {
     if (t.it >= it_hi) t = Tq{0, it_hi - 1};
-    while (t.it >= it_lo && tile_class(t, wg_k) == kEmpty) t = step(t);
+    while (!dense && t.it >= it_lo && tile_class(t, wg_k) == kEmpty) t = step(t);
     if (t.it < it_lo) t.it = -1;
     return t;
   };
@@ -437,9 +440,11 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
   // the key tiles live for this query block lie in [kt_lo, kt_hi)
   const int kt_lo = first_true(0, n_kt, [&](int kt) { return !keys_before(p, wg_q, ktile_span(kt)); });
   const int kt_hi = first_true(kt_lo, n_kt, [&](int kt) { return keys_after(p, wg_q, ktile_span(kt)); });
+  // dense as in the key roles: no classification inside [kt_lo, kt_hi)
+  const bool dense = !p.window && !p.q_seg;
   auto next_tile = [&](int kt) {
     kt = max(kt, kt_lo);
-    while (kt < kt_hi && tile_class(kt, wg_q) == kEmpty) ++kt;
+    while (!dense && kt < kt_hi && tile_class(kt, wg_q) == kEmpty) ++kt;
     return kt < kt_hi ? kt : n_kt;
   };
   typename C::TileN tk, tv;

@@ -174,9 +174,13 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     // leaves the running result as it is, so nothing is read or written
     if (kt_lo >= kt_hi) return;
   }
+  // Without a window or segment ids every tile of [kt_lo, kt_hi) holds a visible
+  // pair (its first key is visible to the run's last query, positions increasing),
+  // so the walk needs no classification there.
+  const bool dense = !p.window && !p.q_seg;
   auto next_tile = [&](int kt) {
     kt = max(kt, kt_lo);
-    while (kt < kt_hi && tile_class(kt, wg_q) == kEmpty) ++kt;
+    while (!dense && kt < kt_hi && tile_class(kt, wg_q) == kEmpty) ++kt;
     return kt < kt_hi ? kt : n_kt;
   };
   typename C::Tile tk, tv;
