@@ -223,6 +223,19 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
     if (t.it < it_lo) t.it = -1;
     return t;
   };
+  // This wavefront's class of a query tile; dense problems by range (along the
+  // query tile index: empty ... empty, partial ..., full ... full; query rows past
+  // the end add nothing, so no tile is ragged here)
+  int it_wlo = 0, it_wfull = 0;
+  if (dense && wave_live && p.causal) {
+    it_wlo = first_true(it_lo, it_hi, [&](int it) { return !(wv_k.pos_lo > qtile_span(it).pos_hi); });
+    it_wfull = first_true(it_wlo, it_hi, [&](int it) { return qtile_span(it).pos_lo >= wv_k.pos_hi; });
+  }
+  auto wave_class = [&](Tq t) {
+    if (!dense) return tile_class(t, wv_k);
+    if (!wave_live || t.it < it_wlo) return int(kEmpty);
+    return t.it >= it_wfull ? int(kFull) : int(kPartial);
+  };
   typename C::TileM tq, tg;
   const uint32_t qrs_bytes = uint32_t(qrs) * 2u;
   tq.init(qrs_bytes, tid);
@@ -269,7 +282,7 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
       const bool has_next = nxt.it >= 0;
       uint8_t* nbase = smem + (buf ^ 1) * C::kStageMax;
       if (has_next) issue(nxt, nbase);
-      const int wcls = wave_live ? tile_class(cur, wv_k) : kEmpty;
+      const int wcls = wave_class(cur);
       if (wcls != kEmpty) {
         const QStage<C> st(smem + buf * C::kStageMax);
         // One instantiation for masked tiles, one for full tiles, each branch-free
@@ -447,6 +460,18 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
     while (!dense && kt < kt_hi && tile_class(kt, wg_q) == kEmpty) ++kt;
     return kt < kt_hi ? kt : n_kt;
   };
+  // this wavefront's class of a key tile; dense problems by range (full ... full,
+  // partial ..., empty ...; the last tile is partial when ragged)
+  int kt_full = n_kt, kt_wend = n_kt;
+  if (dense && wave_live && p.causal) {
+    kt_wend = first_true(kt_lo, kt_hi, [&](int kt) { return ktile_span(kt).pos_lo > wv_q.pos_hi; });
+    kt_full = first_true(kt_lo, kt_wend, [&](int kt) { return ktile_span(kt).pos_hi > wv_q.pos_lo; });
+  }
+  auto wave_class = [&](int kt) {
+    if (!dense) return tile_class(kt, wv_q);
+    if (!wave_live || kt >= kt_wend) return int(kEmpty);
+    return (kt < kt_full && kt * C::BN + C::BN <= p.Sk) ? int(kFull) : int(kPartial);
+  };
   typename C::TileN tk, tv;
   const uint32_t krs_bytes = uint32_t(krs) * 2u;
   tk.init(krs_bytes, tid);
@@ -491,7 +516,7 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
       const bool has_next = nxt < n_kt;
       uint8_t* nbase = smem + (buf ^ 1) * C::kStageMax;
       if (has_next) issue(nxt, nbase);
-      const int wcls = wave_live ? tile_class(cur, wv_q) : kEmpty;
+      const int wcls = wave_class(cur);
       if (wcls != kEmpty) {
         uint8_t* base = smem + buf * C::kStageMax;
         const uint16_t* ks = ks_of(base);
