@@ -204,9 +204,10 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     } else {
       for (int t = gtid; t < C::BN; t += C::kGroupThreads) kpos[t] = p.k_offset + j0 + t;
     }
+    // (segment ids are compared only when q_seg is given: no fill otherwise)
     if (p.k_seg) {
       if (rw == 1 % C::NW) dma_dwords<C::BN>(p.k_seg, int64_t(b) * p.Sk + j0, p.Sk - j0, kseg, lane);
-    } else {
+    } else if (p.q_seg) {
       for (int t = gtid; t < C::BN; t += C::kGroupThreads) kseg[t] = 0;
     }
   };
