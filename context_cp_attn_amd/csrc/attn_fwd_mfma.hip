@@ -183,6 +183,28 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     while (!dense && kt < kt_hi && tile_class(kt, wg_q) == kEmpty) ++kt;
     return kt < kt_hi ? kt : n_kt;
   };
+  // This wavefront's class of a tile.  Dense problems are classified by range: along
+  // the tile index the class runs full ... full, partial ... partial, empty ...
+  // (positions increase), so two bisections per wavefront replace the per-tile
+  // classification; the last tile is partial when ragged.
+  int kt_full = n_kt, kt_wend = n_kt;
+  if (dense && wave_live && p.causal) {
+    kt_wend = first_true(kt_lo, kt_hi, [&](int kt) { return tile_span(kt).pos_lo > wv_q.pos_hi; });
+    kt_full = first_true(kt_lo, kt_wend, [&](int kt) { return tile_span(kt).pos_hi > wv_q.pos_lo; });
+  }
+  auto wave_class = [&](int kt) {
+    if (!dense) return tile_class(kt, wv_q);
+    if (!wave_live || kt >= kt_wend) return int(kEmpty);
+    return (kt < kt_full && kt * C::BN + C::BN <= p.Sk) ? int(kFull) : int(kPartial);
+  };
+  // Dense causal problems: the tiles below kt_wg_full are full for every row of the
+  // workgroup (positions increase), so no wavefront masks them and their key
+  // positions are not needed in LDS.
+  int kt_wg_full = kt_lo;
+  if (dense && p.causal && !p.k_pos)
+    kt_wg_full = first_true(kt_lo, kt_hi, [&](int kt) {
+      return kt * C::BN + C::BN > p.Sk || tile_span(kt).pos_hi > wg_q.pos_lo;
+    });
   typename C::Tile tk, tv;
   const uint32_t krs_bytes = uint32_t(krs) * 2u;
   tk.init(krs_bytes, gtid);
@@ -201,7 +223,7 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     const int j0 = kt * C::BN;
     if (p.k_pos) {
       if (rw == 0) dma_dwords<C::BN>(p.k_pos, j0, p.Sk - j0, kpos, lane);
-    } else {
+    } else if (kt >= kt_wg_full) {
       for (int t = gtid; t < C::BN; t += C::kGroupThreads) kpos[t] = p.k_offset + j0 + t;
     }
     // (segment ids are compared only when q_seg is given: no fill otherwise)
@@ -235,7 +257,7 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
       // the DMA of the next tile runs while this one is multiplied
       if (nxt < n_kt) stage_load(nxt, stage_of(buf ^ 1));
 
-      const int wcls = (wave_live && cur < n_kt) ? tile_class(cur, wv_q) : kEmpty;
+      const int wcls = (wave_live && cur < n_kt) ? wave_class(cur) : kEmpty;
       if (wcls != kEmpty) {
         const uint8_t* stage = stage_of(buf);
         const uint16_t* ks_l = reinterpret_cast<const uint16_t*>(stage);
