@@ -2,11 +2,12 @@
 // Handbook "Context parallelism: Ring Attention and Ulysses", self-test answers and
 // §"Ring Attention": lse = log(e^lse1 + e^lse2), o = o1 e^(lse1-lse) + o2 e^(lse2-lse).
 //
-// HBM-bound streaming kernel: each thread owns 4 consecutive float32 of one
-// (b, s, h) row of the accumulator (16-byte loads and stores), for two rows apart; the
+// HBM-bound streaming kernel: each thread moves two 16-byte vectors (4 consecutive
+// float32 of a (b, s, h) row of the accumulator each, kThreads vectors apart); the
 // D/4 threads of a row sit in one wavefront (D/4 divides 64), so every lane reads the
 // old lse_acc of its row in the same instruction before the row's first lane writes
-// the new one.
+// the new one.  Index math is 32-bit (a 64-bit division is a long instruction
+// sequence); the entry point rejects sizes whose vector indices would not fit.
 #include "common.h"
 #include "launch.h"
 #include "prof.h"
@@ -20,10 +21,9 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kVPT = 2;  // vectors per thread: both loads issued before the stores
 
-// I: index type, 32-bit (a 64-bit division is a long instruction sequence, and this
-// kernel does a row / column split per 16 bytes moved; the entry point rejects sizes
-// whose vector indices would not fit).
-template <bool kBf16, typename I>
+using I = uint32_t;
+
+template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(float* __restrict__ acc,
                                                              float* __restrict__ lse_acc,
                                                              const void* __restrict__ blk,
@@ -69,12 +69,12 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(float* __restrict__
   }
 }
 
-template <bool kBf16, typename I>
+template <bool kBf16>
 void launch_merge_t(int64_t B, int64_t S, int64_t H, int64_t D, float* acc, float* lse_acc, const void* blk,
                     const float* lse_blk, hipStream_t s) {
   const int64_t nvec = B * S * H * (D / 4);
   const unsigned grid = unsigned((nvec + kThreads * kVPT - 1) / (kThreads * kVPT));
-  hipLaunchKernelGGL((lse_merge_kernel<kBf16, I>), dim3(grid), dim3(kThreads), 0, s, acc, lse_acc, blk, lse_blk,
+  hipLaunchKernelGGL((lse_merge_kernel<kBf16>), dim3(grid), dim3(kThreads), 0, s, acc, lse_acc, blk, lse_blk,
                      I(S), I(H), I(D / 4), I(nvec));
 }
 
@@ -85,9 +85,9 @@ hipError_t launch_lse_merge(int64_t B, int64_t S, int64_t H, int64_t D, float* a
   // the caller keeps B*S*H*D/4 + 512 below 2^31, so every vector index fits
   ProfScope ps(s, kProfLseMerge);
   if (blk_is_bf16)
-    launch_merge_t<true, uint32_t>(B, S, H, D, acc, lse_acc, blk, lse_blk, s);
+    launch_merge_t<true>(B, S, H, D, acc, lse_acc, blk, lse_blk, s);
   else
-    launch_merge_t<false, uint32_t>(B, S, H, D, acc, lse_acc, blk, lse_blk, s);
+    launch_merge_t<false>(B, S, H, D, acc, lse_acc, blk, lse_blk, s);
   return hipGetLastError();
 }
 
