@@ -276,7 +276,7 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
     issue(cur, smem);
     publish(smem);
     int buf = 0;
-    const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
+    const MaskSpec ms = make_mask_spec(p.causal, p.window, p.q_seg != nullptr);
     while (true) {
       const Tq nxt = next_tile(step(cur));
       const bool has_next = nxt.it >= 0;
@@ -510,7 +510,7 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
     issue(cur, smem);
     publish(smem);
     int buf = 0;
-    const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
+    const MaskSpec ms = make_mask_spec(p.causal, p.window, p.q_seg != nullptr);
     while (true) {
       const int nxt = next_tile(cur + 1);
       const bool has_next = nxt < n_kt;

@@ -245,7 +245,7 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     if (cur < n_kt) stage_load(cur, stage_of(0));
     wait_all();
     __syncthreads();
-    const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
+    const MaskSpec ms = make_mask_spec(p.causal, p.window, p.q_seg != nullptr);
     // one tile per call, the stage index a compile-time constant (the loop below
     // alternates 0 and 1), so the swizzled LDS addresses of each stage are fixed
     auto iter = [&](auto bufc) -> bool {

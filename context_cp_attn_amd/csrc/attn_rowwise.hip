@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kThreads) void fwd_rowwise_kernel(AttnProblem p, co
   if (i >= p.Sq) return;
   const int g = h / (p.Hq / p.Hkv);
   const int D = p.D;
-  const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
+  const MaskSpec ms = make_mask_spec(p.causal, p.window, p.q_seg != nullptr);
   const T* qr = q + ((int64_t(b) * p.Sq + i) * p.Hq + h) * D;
   float qv[NT], acc[NT];
 #pragma unroll
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void dq_rowwise_kernel(AttnProblem p, con
   if (i >= p.Sq) return;
   const int g = h / (p.Hq / p.Hkv);
   const int D = p.D;
-  const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
+  const MaskSpec ms = make_mask_spec(p.causal, p.window, p.q_seg != nullptr);
   const int64_t qrow = ((int64_t(b) * p.Sq + i) * p.Hq + h) * D;
   float qv[NT], gv[NT], acc[NT];
 #pragma unroll
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_rowwise_kernel(AttnProblem p, c
   if (j >= p.Sk) return;
   const int G = p.Hq / p.Hkv;
   const int D = p.D;
-  const MaskSpec ms{p.causal, p.window, p.q_seg != nullptr};
+  const MaskSpec ms = make_mask_spec(p.causal, p.window, p.q_seg != nullptr);
   const int64_t krow = ((int64_t(b) * p.Sk + j) * p.Hkv + g) * D;
   float kv[NT], vv[NT], ak[NT], av[NT];
 #pragma unroll

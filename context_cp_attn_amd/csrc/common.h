@@ -41,19 +41,33 @@ CP_DEVICE float wave_sum(float x) {
 }
 
 // ---- visibility of a (query, key) pair -------------------------------------------
-// Positions are int32 global token indices; segments int32 document ids.
+// Positions are global token indices in [0, 2^31); segments int32 document ids.  The
+// key at kp is visible to the query at qp iff kp <= qp (causal), qp - kp < window
+// (when a window is given) and both carry the same segment id (when given).  With
+// d = qp - kp in (-2^31, 2^31) the two position rules are one unsigned range test,
+// (d - lo) mod 2^32 < span:
+//   causal:     lo = 0,          span = window, or 2^31 without one (d >= 0);
+//   not causal: lo = 1 - 2^31,   span = window - lo (d < window), or 2^32 - 1 (any d).
 struct MaskSpec {
-  int causal;
-  int window;        // 0 = none
+  uint32_t lo, span;
   int has_seg;
 };
 
+inline __host__ __device__ MaskSpec make_mask_spec(int causal, int window, int has_seg) {
+  const uint32_t lo = causal ? 0u : 1u - (1u << 31);
+  uint32_t span;
+  if (causal)
+    span = window ? uint32_t(window) : (1u << 31);
+  else
+    span = window ? uint32_t(window) - lo : 0xffffffffu;
+  return MaskSpec{lo, span, has_seg};
+}
+
 // Branch-free (bitwise) so that per-element masks compile to compares and selects.
 CP_DEVICE bool pair_visible(const MaskSpec& m, int qp, int kp, int qs, int ks) {
-  const bool c = (m.causal == 0) | (kp <= qp);
-  const bool s = (m.has_seg == 0) | (qs == ks);
-  const bool w = (m.window == 0) | (qp - kp < m.window);
-  return c & s & w;
+  const bool pos = uint32_t(qp) - uint32_t(kp) - m.lo < m.span;
+  const bool seg = (m.has_seg == 0) | (qs == ks);
+  return pos & seg;
 }
 
 // Log-sum-exp merge of two parts of a row (handbook "Context parallelism: Ring
