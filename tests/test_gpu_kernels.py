@@ -253,6 +253,13 @@ CASES = {
         q_pos=np.r_[np.arange(0, 128), np.arange(896, 1024)], k_pos=np.r_[np.arange(384, 512), np.arange(512, 640)])),
     "packed_window": (1, 520, 520, 4, 2, lambda Sq, Sk: dict(seg=[37, 150, 90, 243], window=64)),
     "empty_rows": (1, 130, 190, 2, 1, lambda Sq, Sk: dict(q_offset=0, k_offset=64)),
+    # a window without the causal mask: every later key is visible, earlier ones only
+    # within the window (qpos - kpos < 37)
+    "noncausal_window": (1, 210, 260, 2, 1, lambda Sq, Sk: dict(causal=False, window=37, q_offset=40)),
+    # a window of 1: each row sees only the key at its own position
+    "window_1": (1, 150, 150, 2, 2, lambda Sq, Sk: dict(window=1)),
+    # offsets and a window that leaves the first rows with no visible key
+    "offset_window": (1, 140, 300, 2, 1, lambda Sq, Sk: dict(q_offset=20, k_offset=100, window=50)),
 }
 
 
@@ -327,7 +334,8 @@ def test_attn_fwd_merge(cp, name, dtype, D):
     check_close(acc, f64(acc2), TOL[dtype]["out"], "fused vs unfused")
 
 
-@pytest.mark.parametrize("name", ["causal_square", "offsets", "zigzag_pos", "packed_window", "empty_rows"])
+@pytest.mark.parametrize("name", ["causal_square", "offsets", "zigzag_pos", "packed_window", "empty_rows",
+                                  "noncausal_window", "window_1", "offset_window"])
 @pytest.mark.parametrize("dtype,D", [(torch.float32, 16), (torch.float32, 128), (torch.bfloat16, 64),
                                      (torch.bfloat16, 128), (torch.bfloat16, 16)])
 def test_attn_bwd(cp, name, dtype, D):
