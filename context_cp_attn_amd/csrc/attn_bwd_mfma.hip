@@ -127,8 +127,10 @@ struct QStage {
 
 // Shared skeleton of the dV and dK roles: a workgroup owns keys [j0, j0 + kRows) of
 // kv head g; wavefront w owns keys j0 + 32w + (0..31), one per lane column.
-// kDK selects the dK role (else dV).
-template <class C, bool kDK>
+// kDK selects the dK role (else dV); kLane enables the one-tile-per-lane
+// classification of windowed or segmented problems (a separate instance, so that
+// the dense kernel's register allocation does not carry it).
+template <class C, bool kDK, bool kLane>
 CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                         const float* __restrict__ lse2, const float* __restrict__ delta,
@@ -217,8 +219,34 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
   // without a window or segment ids every query tile of [it_lo, it_hi) holds a
   // visible pair (the keys' first position is visible to its last query)
   const bool dense = !p.window && !p.q_seg;
+  // other problems with at most 64 query tiles in [it_lo, it_hi) classify them all
+  // at once, one tile per lane (the class does not depend on the head): bit masks
+  // over it - it_lo of the live tiles and of this wavefront's full / partial ones
+  const bool lane_cls = kLane && !dense && it_hi - it_lo <= 64;
+  uint64_t live_m = 0, wfull_m = 0, wpart_m = 0;
+  if (lane_cls) {
+    const int it = it_lo + lane;
+    int cg = kEmpty, cw = kEmpty;
+    if (it < it_hi) {
+      const Span qs = qtile_span(it);
+      cg = classify(p, qs, wg_k, false);
+      if (wave_live) cw = classify(p, qs, wv_k, false);
+    }
+    live_m = __ballot(cg != kEmpty);
+    wfull_m = __ballot(cw == kFull);
+    wpart_m = __ballot(cw == kPartial);
+  }
   auto next_tile = [&](Tq t) {
     if (t.it >= it_hi) t = Tq{0, it_hi - 1};
+    if (lane_cls) {
+      if (t.it < it_lo) return Tq{t.hh, -1};
+      // live tiles at or below t.it; t.it itself keeps its head, a lower one starts at head 0
+      const int sh = t.it - it_lo;
+      const uint64_t m = live_m & (sh == 63 ? ~uint64_t(0) : (uint64_t(2) << sh) - 1);
+      if (!m) return Tq{t.hh, -1};
+      const int it = it_lo + 63 - int(__builtin_clzll(m));
+      return it == t.it ? t : Tq{0, it};
+    }
     while (!dense && t.it >= it_lo && tile_class(t, wg_k) == kEmpty) t = step(t);
     if (t.it < it_lo) t.it = -1;
     return t;
@@ -232,6 +260,10 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
     it_wfull = first_true(it_wlo, it_hi, [&](int it) { return qtile_span(it).pos_lo >= wv_k.pos_hi; });
   }
   auto wave_class = [&](Tq t) {
+    if (lane_cls) {
+      const uint64_t bit = uint64_t(1) << (t.it - it_lo);
+      return (wfull_m & bit) ? int(kFull) : (wpart_m & bit) ? int(kPartial) : int(kEmpty);
+    }
     if (!dense) return tile_class(t, wv_k);
     if (!wave_live || t.it < it_wlo) return int(kEmpty);
     return t.it >= it_wfull ? int(kFull) : int(kPartial);
@@ -381,7 +413,7 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
 
 // dQ role: a workgroup owns queries [q0, q0 + kRows) of head h; wavefront w owns
 // queries q0 + 32w + (0..31), one per lane column.
-template <class C>
+template <class C, bool kLane>
 CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                        const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                        const float* __restrict__ lse2, const float* __restrict__ delta, float* __restrict__ dq,
@@ -455,8 +487,29 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
   const int kt_hi = first_true(kt_lo, n_kt, [&](int kt) { return keys_after(p, wg_q, ktile_span(kt)); });
   // dense as in the key roles: no classification inside [kt_lo, kt_hi)
   const bool dense = !p.window && !p.q_seg;
+  // other problems with at most 64 key tiles in the range: all classified at once,
+  // one tile per lane, as in the key roles
+  const bool lane_cls = kLane && !dense && kt_hi - kt_lo <= 64;
+  uint64_t live_m = 0, wfull_m = 0, wpart_m = 0;
+  if (lane_cls) {
+    const int kt = kt_lo + lane;
+    int cg = kEmpty, cw = kEmpty;
+    if (kt < kt_hi) {
+      const Span ks = ktile_span(kt);
+      const bool ragged = kt * C::BN + C::BN > p.Sk;
+      cg = classify(p, wg_q, ks, ragged);
+      if (wave_live) cw = classify(p, wv_q, ks, ragged);
+    }
+    live_m = __ballot(cg != kEmpty);
+    wfull_m = __ballot(cw == kFull);
+    wpart_m = __ballot(cw == kPartial);
+  }
   auto next_tile = [&](int kt) {
     kt = max(kt, kt_lo);
+    if (lane_cls) {
+      const uint64_t m = kt < kt_hi ? live_m >> (kt - kt_lo) : 0;
+      return m ? kt + int(__builtin_ctzll(m)) : n_kt;
+    }
     while (!dense && kt < kt_hi && tile_class(kt, wg_q) == kEmpty) ++kt;
     return kt < kt_hi ? kt : n_kt;
   };
@@ -468,6 +521,10 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
     kt_full = first_true(kt_lo, kt_wend, [&](int kt) { return ktile_span(kt).pos_hi > wv_q.pos_lo; });
   }
   auto wave_class = [&](int kt) {
+    if (lane_cls) {
+      const uint64_t bit = uint64_t(1) << (kt - kt_lo);
+      return (wfull_m & bit) ? int(kFull) : (wpart_m & bit) ? int(kPartial) : int(kEmpty);
+    }
     if (!dense) return tile_class(kt, wv_q);
     if (!wave_live || kt >= kt_wend) return int(kEmpty);
     return (kt < kt_full && kt * C::BN + C::BN <= p.Sk) ? int(kFull) : int(kPartial);
@@ -614,7 +671,7 @@ struct BwdArgs {
   int n_q;   // query-side items = B * Hq * query blocks
 };
 
-template <class C>
+template <class C, bool kLane>
 __global__ __launch_bounds__(C::kThreads) void attn_bwd_kernel(BwdArgs a) {
   __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
   const AttnProblem& p = a.p;
@@ -634,17 +691,17 @@ __global__ __launch_bounds__(C::kThreads) void attn_bwd_kernel(BwdArgs a) {
     const int bg = pair % (p.B * p.Hkv);
     const int kt = pair / (p.B * p.Hkv);
     if ((i & 1) == 0)
-      key_role<C, true>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dk, a.accumulate, smem, kt, bg % p.Hkv,
+      key_role<C, true, kLane>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dk, a.accumulate, smem, kt, bg % p.Hkv,
                         bg / p.Hkv);
     else
-      key_role<C, false>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dv, a.accumulate, smem, kt, bg % p.Hkv,
+      key_role<C, false, kLane>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dv, a.accumulate, smem, kt, bg % p.Hkv,
                          bg / p.Hkv);
   } else {
     const int i = int(L - before);
     const int bh = i % (p.B * p.Hq);
     const int r = i / (p.B * p.Hq);
     const int n_qt = (p.Sq + C::kRows - 1) / C::kRows;
-    dq_role<C>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dq, a.accumulate, smem, p.causal ? n_qt - 1 - r : r,
+    dq_role<C, kLane>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dq, a.accumulate, smem, p.causal ? n_qt - 1 - r : r,
                bh % p.Hq, bh / p.Hq);
   }
 }
@@ -669,7 +726,10 @@ hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const vo
             p.B * p.Hq * ((p.Sq + C::kRows - 1) / C::kRows)};
   {
     ProfScope ps(s, kProfBwdMfma);
-    hipLaunchKernelGGL(attn_bwd_kernel<C>, dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s, a);
+    if (p.window || p.q_seg)
+      hipLaunchKernelGGL((attn_bwd_kernel<C, true>), dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_bwd_kernel<C, false>), dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -86,7 +86,9 @@ struct FwdCfg {
 // the block's float32 result into acc [B,Sq,Hq,D] and lse (= lse_acc) in place.
 // C::SPLIT: out / lse are ignored; the group's partial result goes to part_o
 // [2][B,Sq,Hq,D] and part_l [2][B,Hq,Sq] (float32, normalised, natural-log lse).
-template <class C, bool kMerge>
+// kLane enables the one-tile-per-lane classification of windowed or segmented
+// problems (its own instance, so that dense problems run without its per-tile tests).
+template <class C, bool kMerge, bool kLane>
 CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ acc,
                         float* __restrict__ lse, uint8_t* smem, float* __restrict__ part_o = nullptr,
@@ -178,8 +180,31 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
   // pair (its first key is visible to the run's last query, positions increasing),
   // so the walk needs no classification there.
   const bool dense = !p.window && !p.q_seg;
+  // Other problems with at most 64 tiles in [kt_lo, kt_hi) classify them all at once,
+  // one tile per lane: ballots give the workgroup's live tiles and this wavefront's
+  // full and partial tiles as bit masks over kt - kt_lo, and the walk becomes a bit
+  // scan.
+  const bool lane_cls = kLane && !dense && kt_hi - kt_lo <= 64;
+  uint64_t live_m = 0, wfull_m = 0, wpart_m = 0;
+  if (lane_cls) {
+    const int kt = kt_lo + lane;
+    int cg = kEmpty, cw = kEmpty;
+    if (kt < kt_hi) {
+      const Span ks = tile_span(kt);
+      const bool ragged = kt * C::BN + C::BN > p.Sk;
+      cg = classify(p, wg_q, ks, ragged);
+      if (wave_live) cw = classify(p, wv_q, ks, ragged);
+    }
+    live_m = __ballot(cg != kEmpty);
+    wfull_m = __ballot(cw == kFull);
+    wpart_m = __ballot(cw == kPartial);
+  }
   auto next_tile = [&](int kt) {
     kt = max(kt, kt_lo);
+    if (lane_cls) {
+      const uint64_t m = kt < kt_hi ? live_m >> (kt - kt_lo) : 0;
+      return m ? kt + int(__builtin_ctzll(m)) : n_kt;
+    }
     while (!dense && kt < kt_hi && tile_class(kt, wg_q) == kEmpty) ++kt;
     return kt < kt_hi ? kt : n_kt;
   };
@@ -193,6 +218,10 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     kt_full = first_true(kt_lo, kt_wend, [&](int kt) { return tile_span(kt).pos_hi > wv_q.pos_lo; });
   }
   auto wave_class = [&](int kt) {
+    if (lane_cls) {
+      const uint64_t bit = uint64_t(1) << (kt - kt_lo);
+      return (wfull_m & bit) ? int(kFull) : (wpart_m & bit) ? int(kPartial) : int(kEmpty);
+    }
     if (!dense) return tile_class(kt, wv_q);
     if (!wave_live || kt >= kt_wend) return int(kEmpty);
     return (kt < kt_full && kt * C::BN + C::BN <= p.Sk) ? int(kFull) : int(kPartial);
@@ -419,29 +448,29 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
   }
 }
 
-template <class C>
+template <class C, bool kLane>
 __global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_mfma_kernel(AttnProblem p, const uint16_t* q,
                                                                        const uint16_t* k, const uint16_t* v,
                                                                        uint16_t* out, float* lse) {
   __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
-  fwd_body<C, false>(p, q, k, v, out, nullptr, lse, smem);
+  fwd_body<C, false, kLane>(p, q, k, v, out, nullptr, lse, smem);
 }
 
-template <class C>
+template <class C, bool kLane>
 __global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_merge_mfma_kernel(AttnProblem p, const uint16_t* q,
                                                                              const uint16_t* k,
                                                                              const uint16_t* v, float* acc,
                                                                              float* lse_acc) {
   __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
-  fwd_body<C, true>(p, q, k, v, nullptr, acc, lse_acc, smem);
+  fwd_body<C, true, kLane>(p, q, k, v, nullptr, acc, lse_acc, smem);
 }
 
-template <class C>
+template <class C, bool kLane>
 __global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_split_kernel(AttnProblem p, const uint16_t* q,
                                                                         const uint16_t* k, const uint16_t* v,
                                                                         float* part_o, float* part_l) {
   __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
-  fwd_body<C, false>(p, q, k, v, nullptr, nullptr, nullptr, smem, part_o, part_l);
+  fwd_body<C, false, kLane>(p, q, k, v, nullptr, nullptr, nullptr, smem, part_o, part_l);
 }
 
 // out = merge of the two partials of every (row, head), rounded to bf16, and the
@@ -483,13 +512,22 @@ hipError_t launch_cfg(const AttnProblem& p, const void* q, const void* k, const 
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   const auto* vv = static_cast<const uint16_t*>(v);
+  const bool masked = p.window || p.q_seg;
   if constexpr (kMerge) {
     ProfScope ps(s, kProfFwdMergeMfma);
-    hipLaunchKernelGGL(attn_fwd_merge_mfma_kernel<C>, dim3(n), dim3(C::kThreads), 0, s, p, qq, kk, vv, acc, lse);
+    if (masked)
+      hipLaunchKernelGGL((attn_fwd_merge_mfma_kernel<C, true>), dim3(n), dim3(C::kThreads), 0, s, p, qq, kk, vv,
+                         acc, lse);
+    else
+      hipLaunchKernelGGL((attn_fwd_merge_mfma_kernel<C, false>), dim3(n), dim3(C::kThreads), 0, s, p, qq, kk, vv,
+                         acc, lse);
   } else {
     ProfScope ps(s, kProfFwdMfma);
-    hipLaunchKernelGGL(attn_fwd_mfma_kernel<C>, dim3(n), dim3(C::kThreads), 0, s, p, qq, kk, vv,
-                       static_cast<uint16_t*>(out), lse);
+    auto* o = static_cast<uint16_t*>(out);
+    if (masked)
+      hipLaunchKernelGGL((attn_fwd_mfma_kernel<C, true>), dim3(n), dim3(C::kThreads), 0, s, p, qq, kk, vv, o, lse);
+    else
+      hipLaunchKernelGGL((attn_fwd_mfma_kernel<C, false>), dim3(n), dim3(C::kThreads), 0, s, p, qq, kk, vv, o, lse);
   }
   return hipGetLastError();
 }
@@ -502,10 +540,16 @@ hipError_t launch_split(const AttnProblem& p, const void* q, const void* k, cons
   float* part_o = ws;
   float* part_l = ws + 2 * rows * D;
   const unsigned n = 2u * unsigned((p.Sq + C::kRows - 1) / C::kRows) * unsigned(p.Hq * p.B);
+  const auto* qq = static_cast<const uint16_t*>(q);
+  const auto* kk = static_cast<const uint16_t*>(k);
+  const auto* vv = static_cast<const uint16_t*>(v);
   ProfScope ps(s, kProfFwdMfma);
-  hipLaunchKernelGGL(attn_fwd_split_kernel<C>, dim3(n), dim3(C::kThreads), 0, s, p,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), part_o, part_l);
+  if (p.window || p.q_seg)
+    hipLaunchKernelGGL((attn_fwd_split_kernel<C, true>), dim3(n), dim3(C::kThreads), 0, s, p, qq, kk, vv, part_o,
+                       part_l);
+  else
+    hipLaunchKernelGGL((attn_fwd_split_kernel<C, false>), dim3(n), dim3(C::kThreads), 0, s, p, qq, kk, vv, part_o,
+                       part_l);
   const int64_t threads = rows * (D / 8);
   hipLaunchKernelGGL(split_combine_kernel<D>, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, rows, p.Sq,
                      p.Hq, part_o, part_l, static_cast<uint16_t*>(out), lse);
