@@ -357,6 +357,45 @@ def test_attn_bwd(cp, name, dtype, D):
         torch.testing.assert_close(a, 2 * b, rtol=1e-6, atol=1e-6)
 
 
+@pytest.mark.parametrize("masks", ["long_docs", "long_window"])
+def test_attn_long_masked_ranges(cp, masks):
+    """Segmented or windowed problems whose workgroups see more than 64 tiles: the
+    kernels classify ranges of up to 64 tiles at once (one per lane) and walk longer
+    ones tile by tile.  Documents of 400 and 8600 tokens put both kinds in one
+    launch of the forward (64-key tiles: up to 134 in a range) and of the backward
+    (128-row tiles: up to 68); a 7000-token window without segment ids gives the
+    forward up to 110.  Forward through the two-workgroup split (workspace), the
+    in-workgroup split (none) and the fused ring step; backward; all against the
+    oracle, bf16, D=128."""
+    S, Hq, Hkv, D = 9000, 2, 1, 128
+    say(f"attn long masked ranges {masks}")
+    q, k, v, do = cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D), (1, S, Hq, D)],
+                                           seed=31, dtype=torch.bfloat16)
+    if masks == "long_docs":
+        seg = cp_inputs.segment_ids([400, 8600], batch=1)
+        m = dict(q_seg=seg, k_seg=seg)
+    else:
+        m = dict(window=7000)
+    dm = to_dev(m)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    ws = cp.fwd_workspace(qd, kd, **dm)
+    assert ws is not None
+    out, lse = cp.attn_fwd(qd, kd, vd, workspace=ws, **dm)
+    out1, lse1 = cp.attn_fwd(qd, kd, vd, workspace=False, **dm)
+    acc = torch.zeros(1, S, Hq, D, device="cuda")
+    lacc = torch.full((1, Hq, S), float("-inf"), device="cuda")
+    cp.attn_fwd_merge(qd, kd, vd, acc, lacc, **dm)
+    dq, dk, dv = cp.attn_bwd(qd, kd, vd, out, lse, dod, **dm)
+    om = oracle_mask(m)
+    ref_o, ref_l = oracle.attn_fwd(q, k, v, **om)
+    for o_, l_, nm in ((out, lse, "split"), (out1, lse1, "unsplit"), (acc, lacc, "fused")):
+        check_lse(l_, ref_l, 1e-3)
+        check_close(o_, ref_o, 1e-2, f"{nm} out")
+    refs = oracle.attn_bwd(q, k, v, ref_o, ref_l, do, **om)
+    for got, ref, nm in zip((dq, dk, dv), refs, ("dq", "dk", "dv")):
+        check_close(got, ref, TOL[torch.bfloat16]["grad"] * max(1.0, np.abs(ref).max()), nm)
+
+
 def _expected_flags(B, qp, kp, qs, ks):
     """The rules of cp_attn_check_args written with numpy."""
     f = 0
