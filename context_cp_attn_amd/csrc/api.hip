@@ -77,6 +77,19 @@ cp_status_t check_attn(const cp_attn_args_t* a, const void* q, const void* k, co
     return fail(CP_ERR_INVALID, "softmax_scale must be finite and >= 0 (0 selects 1/sqrt(D))");
   if (a->seqlen_q > INT_MAX || a->seqlen_k > INT_MAX || a->batch > 65535 || a->heads_q > 65535)
     return fail(CP_ERR_UNSUPPORTED, "sizes beyond the launch grid (batch, heads_q <= 65535; seqlen < 2^31)");
+  if (a->head_dim > 128)
+    return fail(CP_ERR_UNSUPPORTED, "attention is built for head_dim <= 128 (got %lld)",
+                (long long)a->head_dim);
+  {
+    // grid sizes and (batch, head, tile) indices are 32-bit: batch * heads_q * seqlen
+    // (the longer of the two) rows at most 2^31 - 1; batch * heads_q < 2^32 here, so
+    // the test divides instead of multiplying
+    const int64_t bh = a->batch * a->heads_q;
+    const int64_t s = a->seqlen_q > a->seqlen_k ? a->seqlen_q : a->seqlen_k;
+    if (bh > INT_MAX / s)
+      return fail(CP_ERR_UNSUPPORTED, "batch * heads_q * seqlen = %lld * %lld * %lld rows: 2^31 or more",
+                  (long long)a->batch, (long long)a->heads_q, (long long)s);
+  }
   {
     // the matrix-core kernels address one batch plane of a tensor with 32-bit offsets
     const int64_t eb = a->dtype == CP_DTYPE_BF16 ? 2 : 4;
@@ -88,9 +101,6 @@ cp_status_t check_attn(const cp_attn_args_t* a, const void* q, const void* k, co
     return fail(CP_ERR_INVALID, "q_offset %lld: positions must lie in [0, 2^31)", (long long)a->q_offset);
   if (!a->k_pos && (a->k_offset < 0 || a->k_offset + a->seqlen_k > INT_MAX))
     return fail(CP_ERR_INVALID, "k_offset %lld: positions must lie in [0, 2^31)", (long long)a->k_offset);
-  if (a->head_dim > 128)
-    return fail(CP_ERR_UNSUPPORTED, "attention is built for head_dim <= 128 (got %lld)",
-                (long long)a->head_dim);
   if (mfma_path(a)) {
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
       return fail(CP_ERR_INVALID, "bf16 q, k, v must be 16-byte aligned");

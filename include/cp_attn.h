@@ -78,7 +78,9 @@ typedef struct {
  * sum of exp(scale * q.k) over visible keys.  bf16 inputs with D in {32, 64, 128}
  * are multiplied on the matrix cores (q, k, v, out 16-byte aligned); other D run on
  * row-per-wavefront kernels (element-aligned buffers).  Accumulation is float32;
- * a bf16 out is rounded to nearest even.  D > 128 gives CP_ERR_UNSUPPORTED.
+ * a bf16 out is rounded to nearest even.  CP_ERR_UNSUPPORTED for D > 128, for
+ * batch or heads_q above 65535, for one batch of q or of k/v of 2^31 bytes or more,
+ * and for batch * heads_q * max(Sq, Sk) >= 2^31 (grid indices are 32-bit).
  * out/lse must not overlap q, k or v (CP_ERR_ALIAS).
  */
 cp_status_t cp_attn_fwd(const cp_attn_args_t* args, const void* q, const void* k, const void* v,

@@ -65,6 +65,11 @@ def fwd(a, q=FAKE_A, k=FAKE_B, v=FAKE_C, out=1 << 44, lse=1 << 45):
     (dict(q_offset=-5), INVALID, "q_offset"),
     (dict(head_dim=256), UNSUPPORTED, "head_dim"),
     (dict(head_dim=256, dtype=1), UNSUPPORTED, "head_dim"),
+    # bounded before the byte-size test multiplies by it
+    (dict(head_dim=1 << 40), UNSUPPORTED, "head_dim"),
+    # 2^31 or more rows over batches and heads: the 32-bit grid indices would wrap
+    (dict(batch=65535, heads_q=65535, heads_kv=1, seqlen_q=1, seqlen_k=1, head_dim=16), UNSUPPORTED, "rows"),
+    (dict(batch=2, heads_q=1 << 15, heads_kv=1, seqlen_q=1, seqlen_k=1 << 15, head_dim=16), UNSUPPORTED, "rows"),
 ])
 def test_attn_fwd_rejects(kw, code, msg):
     st, err = fwd(args(**kw))
