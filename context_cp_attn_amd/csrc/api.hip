@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "cp_attn.h"
@@ -42,6 +43,16 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// True when the product of the (positive) sizes is below 2^62: a byte count that a
+// buffer can have.  Checked before any other arithmetic on caller sizes, so that
+// none of it can overflow int64.
+bool sizes_fit(std::initializer_list<int64_t> xs) {
+  int64_t p = 1;
+  for (const int64_t x : xs)
+    if (__builtin_mul_overflow(p, x, &p)) return false;
+  return p < (int64_t(1) << 62);
+}
 
 int64_t dtype_bytes(int32_t dt) { return dt == CP_DTYPE_BF16 ? 2 : 4; }
 
@@ -266,7 +277,8 @@ cp_status_t cp_attn_check_args(const cp_attn_args_t* a, int32_t* flags, hipStrea
 }
 
 size_t cp_attn_bwd_workspace_size(const cp_attn_args_t* a) {
-  if (!a || a->batch < 1 || a->heads_q < 1 || a->seqlen_q < 1) return 0;
+  if (!a || a->batch < 1 || a->heads_q < 1 || a->seqlen_q < 1 || !sizes_fit({a->batch, a->heads_q, a->seqlen_q, 8}))
+    return 0;
   // two row arrays: delta and the base-2 lse
   const int64_t rows = a->batch * a->heads_q * a->seqlen_q;
   return size_t(2 * cp::bwd_row_plane(rows)) * sizeof(float);
@@ -327,6 +339,8 @@ cp_status_t cp_lse_merge(int64_t batch, int64_t seqlen, int64_t heads, int64_t h
                          int32_t blk_dtype, hipStream_t stream) {
   if (batch < 1 || seqlen < 1 || heads < 1 || head_dim < 1)
     return fail(CP_ERR_INVALID, "sizes must be >= 1");
+  if (!sizes_fit({batch, seqlen, heads, head_dim, 4}))
+    return fail(CP_ERR_INVALID, "sizes describe 2^62 bytes or more");
   if (blk_dtype != CP_DTYPE_BF16 && blk_dtype != CP_DTYPE_F32)
     return fail(CP_ERR_INVALID, "unknown blk_dtype %d", (int)blk_dtype);
   if (head_dim % 4 || 64 % (head_dim / 4))
@@ -352,6 +366,8 @@ static cp_status_t relayout(const cp_relayout_args_t* a, const void* in, void* o
                 head_dim = a->head_dim, eb = a->elem_bytes, rep = a->rep;
   if (G < 1 || P < 1 || batch < 1 || seqlen < 1 || heads < 1 || head_dim < 1 || rep < 1)
     return fail(CP_ERR_INVALID, "sizes must be >= 1");
+  if (!sizes_fit({G, batch, seqlen, heads, head_dim, 4, rep}) || !sizes_fit({P, P, batch}))
+    return fail(CP_ERR_INVALID, "sizes describe 2^62 bytes or more");
   if (eb != 2 && eb != 4) return fail(CP_ERR_INVALID, "elem_bytes must be 2 or 4 (got %lld)", (long long)eb);
   if (a->inverse != 0 && a->inverse != 1) return fail(CP_ERR_INVALID, "inverse must be 0 or 1");
   if (seqlen % P)
@@ -404,6 +420,8 @@ cp_status_t cp_zigzag_reorder(const void* in, void* out, int64_t batch, int64_t 
                               int64_t row_bytes, int64_t P, int32_t strategy, int32_t inverse,
                               hipStream_t stream) {
   if (batch < 1 || seqlen < 1 || row_bytes < 1 || P < 1) return fail(CP_ERR_INVALID, "sizes must be >= 1");
+  if (!sizes_fit({batch, seqlen, row_bytes}) || !sizes_fit({batch, 2, P}))
+    return fail(CP_ERR_INVALID, "sizes describe 2^62 bytes or more");
   if (strategy != 0 && strategy != 1) return fail(CP_ERR_INVALID, "unknown reorder strategy %d", (int)strategy);
   if (inverse != 0 && inverse != 1) return fail(CP_ERR_INVALID, "inverse must be 0 or 1");
   if (strategy == 0 && seqlen % (2 * P))
@@ -429,6 +447,8 @@ cp_status_t cp_zigzag_reorder(const void* in, void* out, int64_t batch, int64_t 
 cp_status_t cp_pad_rows(const void* in, void* out, int64_t batch, int64_t seqlen, int64_t seqlen_out,
                         int64_t row_bytes, uint32_t fill, hipStream_t stream) {
   if (batch < 1 || seqlen < 1 || seqlen_out < 1 || row_bytes < 1) return fail(CP_ERR_INVALID, "sizes must be >= 1");
+  if (!sizes_fit({batch, seqlen, row_bytes}) || !sizes_fit({batch, seqlen_out, row_bytes}))
+    return fail(CP_ERR_INVALID, "sizes describe 2^62 bytes or more");
   if (fill != 0 && row_bytes % 4)
     return fail(CP_ERR_INVALID, "a non-zero fill word needs rows of whole 32-bit words (row_bytes %lld)",
                 (long long)row_bytes);

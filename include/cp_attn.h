@@ -31,7 +31,8 @@ typedef enum { CP_DTYPE_BF16 = 0, CP_DTYPE_F32 = 1 } cp_dtype_t;
 
 typedef enum {
   CP_OK = 0,
-  CP_ERR_INVALID = 1,      /* a size, shape relation or flag the operation does not admit */
+  CP_ERR_INVALID = 1,      /* a size, shape relation or flag the operation does not admit
+                              (also: sizes whose byte count would reach 2^62)            */
   CP_ERR_UNSUPPORTED = 2,  /* valid, but no kernel is compiled for it (head_dim, dtype)   */
   CP_ERR_ALIAS = 3,        /* an output buffer overlaps an input it must not overlap      */
   CP_ERR_HIP = 4           /* the HIP runtime reported an error at launch                 */

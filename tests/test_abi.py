@@ -157,6 +157,8 @@ def test_attn_bwd_workspace_and_alias():
     a = args()
     need = lib.cp_attn_bwd_workspace_size(ctypes.byref(a))
     assert need >= 4 * 4 * 64 and need % 256 == 0
+    # sizes whose row count overflows int64 ask for nothing (the call itself rejects them)
+    assert lib.cp_attn_bwd_workspace_size(ctypes.byref(args(batch=1 << 40, seqlen_q=1 << 40))) == 0
     base = [FAKE_A, FAKE_B, FAKE_C, 1 << 41, 1 << 42, 1 << 43, 1 << 44, 1 << 45, 1 << 46]
     st = lib.cp_attn_bwd(ctypes.byref(a), *base, 0, 1 << 47, need - 1, None)
     assert st == INVALID and "workspace" in lib.cp_last_error().decode()
@@ -188,6 +190,9 @@ def test_reorder_rejects():
     assert f(FAKE_A, FAKE_B, 1, 32, 4, 4, 5, 0, None) == INVALID     # unknown strategy
     assert f(FAKE_A, FAKE_B, 1, 32, 4, 4, 0, 3, None) == INVALID     # inverse flag
     assert f(FAKE_A, FAKE_A, 1, 32, 4, 4, 0, 0, None) == ALIAS
+    # sizes whose byte count overflows int64: rejected before any other arithmetic
+    assert f(FAKE_A, FAKE_B, 1 << 40, 1 << 40, 16, 4, 0, 0, None) == INVALID
+    assert "2^62" in lib.cp_last_error().decode()
 
 
 def test_merge_rejects():
@@ -199,6 +204,8 @@ def test_merge_rejects():
     # 32 GiB of accumulator and beyond: 32-bit vector indices would overflow
     assert f(1, 1 << 21, 32, 128, FAKE_A, FAKE_B, FAKE_C, 1 << 41, 1, None) == UNSUPPORTED
     assert "32 GiB" in lib.cp_last_error().decode()
+    assert f(1 << 30, 1 << 30, 1 << 20, 128, FAKE_A, FAKE_B, FAKE_C, 1 << 41, 1, None) == INVALID
+    assert "2^62" in lib.cp_last_error().decode()
 
 
 def test_relayout_ex_rejects():
@@ -219,6 +226,8 @@ def test_relayout_ex_rejects():
     assert call(elem_bytes=3)[0] == INVALID
     assert call(inverse=2)[0] == INVALID
     assert call(groups=70000)[0] == UNSUPPORTED
+    st, err = call(batch=1 << 40, seqlen=1 << 32, P=4)               # bytes overflow int64
+    assert st == INVALID and "2^62" in err
     # the head side is rep times the sequence side: an output just past the input's
     # end still overlaps when it is the larger side
     assert call(out=FAKE_A + 32 * 8 * 16 * 2 - 16)[0] == ALIAS
@@ -232,6 +241,7 @@ def test_pad_rows_rejects():
     assert f(FAKE_A, FAKE_B, 1, 8, 16, 6, 7, None) == INVALID          # fill word needs 4-byte rows
     assert f(FAKE_A, FAKE_A + 16, 1, 8, 16, 4, 0, None) == ALIAS
     assert f(0, FAKE_B, 1, 8, 16, 4, 0, None) == INVALID
+    assert f(FAKE_A, FAKE_B, 1 << 40, 8, 1 << 40, 4, 0, None) == INVALID   # bytes overflow int64
 
 
 def test_python_errors_are_valueerrors():
