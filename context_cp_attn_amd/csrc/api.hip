@@ -44,6 +44,9 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// a non-NULL, aligned stand-in for tensor pointers where only the sizes are checked
+const void* const kProbe = reinterpret_cast<const void*>(uintptr_t(1) << 12);
+
 // True when the product of the (positive) sizes is below 2^62: a byte count that a
 // buffer can have.  Checked before any other arithmetic on caller sizes, so that
 // none of it can overflow int64.
@@ -281,7 +284,14 @@ size_t cp_attn_bwd_workspace_size(const cp_attn_args_t* a) {
     return 0;
   // two row arrays: delta and the base-2 lse
   const int64_t rows = a->batch * a->heads_q * a->seqlen_q;
-  return size_t(2 * cp::bwd_row_plane(rows)) * sizeof(float);
+  int64_t floats = 2 * cp::bwd_row_plane(rows);
+  // then the dK / dV partials of a head-split backward (windowed or segmented
+  // problems with grouped heads on small grids), for arguments the call accepts
+  cp::AttnProblem p;
+  const std::string saved = g_last_error;
+  if (mfma_path(a) && check_attn(a, kProbe, kProbe, kProbe, &p) == CP_OK) floats += cp::bwd_head_split_floats(p);
+  g_last_error = saved;
+  return size_t(floats) * sizeof(float);
 }
 
 cp_status_t cp_attn_bwd(const cp_attn_args_t* a, const void* q, const void* k, const void* v,

@@ -127,20 +127,24 @@ struct QStage {
 
 // Shared skeleton of the dV and dK roles: a workgroup owns keys [j0, j0 + kRows) of
 // kv head g; wavefront w owns keys j0 + 32w + (0..31), one per lane column.
-// kDK selects the dK role (else dV); kLane enables the one-tile-per-lane
-// classification of windowed or segmented problems (a separate instance, so that
-// the dense kernel's register allocation does not carry it).
+// kDK selects the dK role (else dV).  kLane: the instance for windowed or segmented
+// problems, with the one-tile-per-lane classification and the query heads of the
+// group limited to [h_lo, h_end) (a separate instance, so that the dense kernel's
+// register allocation carries neither; the dense one walks every head of the group).
 template <class C, bool kDK, bool kLane>
 CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                         const float* __restrict__ lse2, const float* __restrict__ delta,
-                        float* __restrict__ grad, int accumulate, uint8_t* smem, int kt, int g, int b) {
+                        float* __restrict__ grad, int accumulate, uint8_t* smem, int kt, int g, int b,
+                        int h_lo_arg, int h_end_arg) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int G = p.Hq / p.Hkv;
+  const int h_lo = kLane ? h_lo_arg : 0;
+  const int h_end = kLane ? h_end_arg : G;
   const int j0 = kt * C::kRows;
   const int wj0 = j0 + wave * 32;
   const int64_t krs = int64_t(p.Hkv) * C::D;
@@ -186,8 +190,8 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
     int hh, it;
   };
   auto step = [&](Tq t) {
-    if (++t.hh == G) {
-      t.hh = 0;
+    if (++t.hh == h_end) {
+      t.hh = h_lo;
       --t.it;
     }
     return t;
@@ -237,15 +241,15 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
     wpart_m = __ballot(cw == kPartial);
   }
   auto next_tile = [&](Tq t) {
-    if (t.it >= it_hi) t = Tq{0, it_hi - 1};
+    if (t.it >= it_hi) t = Tq{h_lo, it_hi - 1};
     if (lane_cls) {
       if (t.it < it_lo) return Tq{t.hh, -1};
-      // live tiles at or below t.it; t.it itself keeps its head, a lower one starts at head 0
+      // live tiles at or below t.it; t.it itself keeps its head, a lower one starts at h_lo
       const int sh = t.it - it_lo;
       const uint64_t m = live_m & (sh == 63 ? ~uint64_t(0) : (uint64_t(2) << sh) - 1);
       if (!m) return Tq{t.hh, -1};
       const int it = it_lo + 63 - int(__builtin_clzll(m));
-      return it == t.it ? t : Tq{0, it};
+      return it == t.it ? t : Tq{h_lo, it};
     }
     while (!dense && t.it >= it_lo && tile_class(t, wg_k) == kEmpty) t = step(t);
     if (t.it < it_lo) t.it = -1;
@@ -303,7 +307,7 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
     __syncthreads();
   };
 
-  Tq cur = next_tile(Tq{0, n_it - 1});
+  Tq cur = next_tile(Tq{h_lo, n_it - 1});
   if (cur.it >= 0) {
     issue(cur, smem);
     publish(smem);
@@ -667,8 +671,13 @@ struct BwdArgs {
   float* dk;
   float* dv;
   int accumulate;
-  int n_kv;  // key-side items = 2 * B * Hkv * key blocks
+  int n_kv;  // key-side items = 2 * B * Hkv * key blocks * hsplit
   int n_q;   // query-side items = B * Hq * query blocks
+  // key-side items of windowed / segmented problems on small grids take half of the
+  // group's query heads each (hsplit = 2): the second half's dK / dV go to part
+  // ([2][B,Sk,Hkv,D] float32, dK then dV) and a second kernel adds them
+  int hsplit;
+  float* part;
 };
 
 template <class C, bool kLane>
@@ -683,19 +692,27 @@ __global__ __launch_bounds__(C::kThreads) void attn_bwd_kernel(BwdArgs a) {
   const int64_t u = blockIdx.x / 8;
   const int64_t width = N - 8 * u < 8 ? N - 8 * u : 8;
   const int64_t L = 8 * u + (blockIdx.x % 8 + u) % width;
-  const int64_t before = (L * a.n_kv) / N;  // key-side items placed before L
-  const bool kv_side = ((L + 1) * a.n_kv) / N > before;
+  // head-split grids list every key-side item first (they are the heavy ones);
+  // others interleave the two sides in proportion
+  const bool kv_first = kLane && a.hsplit > 1;
+  const int64_t before = kv_first ? (L < a.n_kv ? L : a.n_kv) : (L * a.n_kv) / N;  // key-side items before L
+  const bool kv_side = kv_first ? L < a.n_kv : ((L + 1) * a.n_kv) / N > before;
   if (kv_side) {
     const int i = int(before);
-    const int pair = i >> 1;
+    const int hs = kLane ? a.hsplit : 1;
+    const int pair = (i >> 1) / hs;  // the subsets of a key block are neighbours
+    const int sub = (i >> 1) % hs;
     const int bg = pair % (p.B * p.Hkv);
     const int kt = pair / (p.B * p.Hkv);
+    const int G = p.Hq / p.Hkv;
+    const int h_lo = sub * G / hs, h_end = (sub + 1) * G / hs;
+    const int64_t plane = int64_t(p.B) * p.Sk * p.Hkv * C::D;
     if ((i & 1) == 0)
-      key_role<C, true, kLane>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dk, a.accumulate, smem, kt, bg % p.Hkv,
-                        bg / p.Hkv);
+      key_role<C, true, kLane>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, sub ? a.part : a.dk,
+                               sub ? 0 : a.accumulate, smem, kt, bg % p.Hkv, bg / p.Hkv, h_lo, h_end);
     else
-      key_role<C, false, kLane>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dv, a.accumulate, smem, kt, bg % p.Hkv,
-                         bg / p.Hkv);
+      key_role<C, false, kLane>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, sub ? a.part + plane : a.dv,
+                                sub ? 0 : a.accumulate, smem, kt, bg % p.Hkv, bg / p.Hkv, h_lo, h_end);
   } else {
     const int i = int(L - before);
     const int bh = i % (p.B * p.Hq);
@@ -704,6 +721,30 @@ __global__ __launch_bounds__(C::kThreads) void attn_bwd_kernel(BwdArgs a) {
     dq_role<C, kLane>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dq, a.accumulate, smem, p.causal ? n_qt - 1 - r : r,
                bh % p.Hq, bh / p.Hq);
   }
+}
+
+// dK += part[0], dV += part[1] over [B,Sk,Hkv,D] float32 (n4 vectors of 4 each):
+// the second head subset's partial sums of the split key-side items.
+__global__ __launch_bounds__(256) void head_split_sum_kernel(int64_t n4, float* dk, float* dv,
+                                                             const float* part) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= 2 * n4) return;
+  const bool is_v = t >= n4;
+  f32x4* o = reinterpret_cast<f32x4*>(is_v ? dv : dk) + (is_v ? t - n4 : t);
+  *o += reinterpret_cast<const f32x4*>(part)[t];
+}
+
+// Key-side items per (kv head, key block) for this problem: 2 for windowed or
+// segmented problems with grouped heads whose grid is under two rounds of
+// workgroups (one per CU); each key-side item then walks half of the group's query
+// heads.  Without the split the key-side items, G times heavier than the query-side
+// ones, set the time of such small grids.
+int bwd_hsplit(const AttnProblem& p) {
+  if (!(p.window || p.q_seg) || p.Hq / p.Hkv < 2) return 1;
+  constexpr int kRows = 256;
+  const int64_t items = 2 * int64_t(p.B) * p.Hkv * ((p.Sk + kRows - 1) / kRows) +
+                        int64_t(p.B) * p.Hq * ((p.Sq + kRows - 1) / kRows);
+  return items < 2 * int64_t(device_cus()) ? 2 : 1;
 }
 
 template <int D>
@@ -720,21 +761,33 @@ hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const vo
                        p.Hq, static_cast<U>(out), static_cast<U>(dout), lse, delta, lse2);
   }
   using C = BwdCfg<D>;
+  static_assert(C::kRows == 256, "bwd_hsplit counts 256-row items");
+  const int hs = bwd_hsplit(p);
   BwdArgs a{p, static_cast<U>(q), static_cast<U>(k), static_cast<U>(v), static_cast<U>(dout), lse2, delta,
             dq, dk, dv, accumulate,
-            2 * p.B * p.Hkv * ((p.Sk + C::kRows - 1) / C::kRows),
-            p.B * p.Hq * ((p.Sq + C::kRows - 1) / C::kRows)};
+            2 * p.B * p.Hkv * ((p.Sk + C::kRows - 1) / C::kRows) * hs,
+            p.B * p.Hq * ((p.Sq + C::kRows - 1) / C::kRows), hs, delta + 2 * bwd_row_plane(rows)};
   {
     ProfScope ps(s, kProfBwdMfma);
     if (p.window || p.q_seg)
       hipLaunchKernelGGL((attn_bwd_kernel<C, true>), dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s, a);
     else
       hipLaunchKernelGGL((attn_bwd_kernel<C, false>), dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s, a);
+    if (hs > 1) {
+      const int64_t n4 = int64_t(p.B) * p.Sk * p.Hkv * (D / 4);
+      hipLaunchKernelGGL(head_split_sum_kernel, dim3(unsigned((2 * n4 + 255) / 256)), dim3(256), 0, s, n4, dk, dv,
+                         a.part);
+    }
   }
   return hipGetLastError();
 }
 
 }  // namespace
+
+int64_t bwd_head_split_floats(const AttnProblem& p) {
+  if (p.D != 32 && p.D != 64 && p.D != 128) return 0;
+  return bwd_hsplit(p) > 1 ? 2 * int64_t(p.B) * p.Sk * p.Hkv * p.D : 0;
+}
 
 hipError_t launch_attn_bwd_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
                                 const void* out, const float* lse, const void* dout, float* dq,

@@ -556,19 +556,8 @@ hipError_t launch_split(const AttnProblem& p, const void* q, const void* k, cons
   return hipGetLastError();
 }
 
-// Workgroup slots of the device at two workgroups per CU (cached per device).
-int wg_slots() {
-  static int slots[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-  if (!slots[dev]) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    slots[dev] = 2 * cus;
-  }
-  return slots[dev];
-}
+// Workgroup slots of the device at two workgroups per CU.
+int wg_slots() { return 2 * device_cus(); }
 
 // Fewer query tiles than two rounds of workgroup slots: split each tile's keys over
 // two wavefront groups, so the heaviest (causal) tiles no longer set the time.
@@ -593,6 +582,19 @@ hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const vo
 }
 
 }  // namespace
+
+int device_cus() {
+  static int cus_of[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus_of[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cus_of[dev] = cus;
+  }
+  return cus_of[dev];
+}
 
 // The combine pass moves 10 bytes per output element (two float32 partials in, bf16
 // out); with fewer than 8192 keys that is no longer small next to the attention of

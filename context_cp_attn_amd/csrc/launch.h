@@ -47,9 +47,15 @@ hipError_t launch_attn_bwd_rowwise_bf16(const AttnProblem& p, const void* q, con
                                         const void* out, const float* lse, const void* dout, float* dq,
                                         float* dk, float* dv, int accumulate, float* delta, hipStream_t s);
 
+// compute units of the current device (cached per device; 256 if it cannot be read)
+int device_cus();
+
 // backward workspace: delta [B,Hq,Sq] float32, then (bf16 matrix-core path) the
-// base-2 lse [B,Hq,Sq] float32 starting bwd_row_plane(rows) floats in
+// base-2 lse [B,Hq,Sq] float32 starting bwd_row_plane(rows) floats in, then, where
+// bwd_head_split_floats(p) > 0, that many floats of dK / dV partials starting
+// 2 * bwd_row_plane(rows) floats in
 inline int64_t bwd_row_plane(int64_t rows) { return (rows + 63) / 64 * 64; }
+int64_t bwd_head_split_floats(const AttnProblem& p);
 hipError_t launch_attn_bwd_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
                                 const void* out, const float* lse, const void* dout, float* dq,
                                 float* dk, float* dv, int accumulate, float* delta, hipStream_t s);
