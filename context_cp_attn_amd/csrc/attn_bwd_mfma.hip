@@ -734,17 +734,22 @@ __global__ __launch_bounds__(256) void head_split_sum_kernel(int64_t n4, float* 
   *o += reinterpret_cast<const f32x4*>(part)[t];
 }
 
-// Key-side items per (kv head, key block) for this problem: 2 for windowed or
-// segmented problems with grouped heads whose grid is under two rounds of
-// workgroups (one per CU); each key-side item then walks half of the group's query
-// heads.  Without the split the key-side items, G times heavier than the query-side
-// ones, set the time of such small grids.
+// Key-side items per (kv head, key block) for this problem: 2 for problems with
+// grouped heads whose grid is under 16 rounds of workgroups (one per CU); each
+// key-side item then walks half of the group's query heads.  Without the split the
+// key-side items, G times heavier than the query-side ones, set the time: on small
+// grids the largest of them outlasts the average load of a CU, and on larger ones
+// they leave the longer tail.  Measured (bf16, D=128, causal): 1.5-1.8x faster at
+// 2-8K tokens with 8 q / 2 kv or 32 q / 8 kv heads, -20% at 16K and -6% at 32K with
+// 8 / 2, -1.3% at 64K with 8 / 2 (12 rounds); never slower.  Beyond 16 rounds it is
+// left off (not measured there).
+constexpr int kHeadSplitRounds = 16;
 int bwd_hsplit(const AttnProblem& p) {
-  if (!(p.window || p.q_seg) || p.Hq / p.Hkv < 2) return 1;
+  if (p.Hq / p.Hkv < 2) return 1;
   constexpr int kRows = 256;
   const int64_t items = 2 * int64_t(p.B) * p.Hkv * ((p.Sk + kRows - 1) / kRows) +
                         int64_t(p.B) * p.Hq * ((p.Sq + kRows - 1) / kRows);
-  return items < 2 * int64_t(device_cus()) ? 2 : 1;
+  return items < kHeadSplitRounds * int64_t(device_cus()) ? 2 : 1;
 }
 
 template <int D>
@@ -769,7 +774,8 @@ hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const vo
             p.B * p.Hq * ((p.Sq + C::kRows - 1) / C::kRows), hs, delta + 2 * bwd_row_plane(rows)};
   {
     ProfScope ps(s, kProfBwdMfma);
-    if (p.window || p.q_seg)
+    // the general instance: windowed / segmented problems, and head-split grids
+    if (p.window || p.q_seg || hs > 1)
       hipLaunchKernelGGL((attn_bwd_kernel<C, true>), dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s, a);
     else
       hipLaunchKernelGGL((attn_bwd_kernel<C, false>), dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s, a);

@@ -125,10 +125,10 @@ cp_status_t cp_attn_fwd_merge(const cp_attn_args_t* args, const void* q, const v
 
 /* Workspace bytes cp_attn_bwd needs for args on the current device: two float32
    arrays of the rows [B,Hq,Sq], the per-row dO.O sums and the rows' lse in base 2;
-   for bf16 problems with a window or segment ids, grouped query heads and fewer
-   than two workgroups per compute unit, also float32 dK and dV partials
-   [2][B,Sk,Hkv,D] (the key side's work is then split over pairs of query heads and
-   the halves are added in a fixed order). */
+   for bf16 problems (D 32, 64, 128) with grouped query heads whose backward grid is
+   under 16 workgroups per compute unit, also float32 dK and dV partials
+   [2][B,Sk,Hkv,D] (the key side's work is then split over two halves of each
+   group's query heads and the halves are added in a fixed order). */
 size_t cp_attn_bwd_workspace_size(const cp_attn_args_t* args);
 
 /*

@@ -157,14 +157,14 @@ def test_attn_bwd_workspace_and_alias():
     a = args()
     need = lib.cp_attn_bwd_workspace_size(ctypes.byref(a))
     assert need >= 4 * 4 * 64 and need % 256 == 0
-    # a windowed problem with grouped heads on a small grid splits each key-side item
-    # over the group's heads: the workspace adds the float32 dK and dV partials
-    plain = need
-    masked = lib.cp_attn_bwd_workspace_size(ctypes.byref(args(window=100)))
-    assert masked == plain + 2 * 64 * 2 * 128 * 4
-    # not for one head per kv head, and not for arguments the call would reject
-    assert lib.cp_attn_bwd_workspace_size(ctypes.byref(args(window=100, heads_kv=4))) == plain
-    assert lib.cp_attn_bwd_workspace_size(ctypes.byref(args(window=100, heads_kv=3))) == plain
+    # grouped heads (4 q / 2 kv) on a grid of few workgroups: each key-side item is
+    # split over the group's heads and the workspace adds the float32 dK and dV
+    # partials [2][B,Sk,Hkv,D]; not for one q head per kv head, nor for arguments the
+    # call would reject
+    rows_only = lib.cp_attn_bwd_workspace_size(ctypes.byref(args(heads_kv=4)))
+    assert need == rows_only + 2 * 64 * 2 * 128 * 4
+    assert lib.cp_attn_bwd_workspace_size(ctypes.byref(args(window=100))) == need
+    assert lib.cp_attn_bwd_workspace_size(ctypes.byref(args(heads_kv=3))) == rows_only
     # sizes whose row count overflows int64 ask for nothing (the call itself rejects them)
     assert lib.cp_attn_bwd_workspace_size(ctypes.byref(args(batch=1 << 40, seqlen_q=1 << 40))) == 0
     base = [FAKE_A, FAKE_B, FAKE_C, 1 << 41, 1 << 42, 1 << 43, 1 << 44, 1 << 45, 1 << 46]
