@@ -260,6 +260,9 @@ CASES = {
     "window_1": (1, 150, 150, 2, 2, lambda Sq, Sk: dict(window=1)),
     # offsets and a window that leaves the first rows with no visible key
     "offset_window": (1, 140, 300, 2, 1, lambda Sq, Sk: dict(q_offset=20, k_offset=100, window=50)),
+    # three query heads per kv head: the backward splits the group's heads into
+    # uneven halves (1 + 2)
+    "gqa3": (1, 200, 330, 6, 2, lambda Sq, Sk: dict(q_offset=130)),
 }
 
 
@@ -335,7 +338,7 @@ def test_attn_fwd_merge(cp, name, dtype, D):
 
 
 @pytest.mark.parametrize("name", ["causal_square", "offsets", "zigzag_pos", "packed_window", "empty_rows",
-                                  "noncausal_window", "window_1", "offset_window"])
+                                  "noncausal_window", "window_1", "offset_window", "gqa3"])
 @pytest.mark.parametrize("dtype,D", [(torch.float32, 16), (torch.float32, 128), (torch.bfloat16, 64),
                                      (torch.bfloat16, 128), (torch.bfloat16, 16)])
 def test_attn_bwd(cp, name, dtype, D):
