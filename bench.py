@@ -19,7 +19,9 @@ before the timed region.  The relayout bandwidth is reported beside it.
 Legs timed in the same run (not part of value): the ring share of llama2-7b
 (2048 queries x 32 heads vs 16 zigzag KV blocks: the fused step with the merge in
 the attention epilogue, and the unfused fwd + merge pair), the 64K-token
-dual-chunk-swap reorder, and the packed + windowed 8K ring share (4 ranks x 4
+dual-chunk-swap reorder, the Ulysses rank share of llama3.1-8b at 64K with cp=4
+(q [1,65536,8,128] on k/v [1,65536,2,128], fwd + bwd), the packed + windowed 8K ring
+share (4 ranks x 4
 steps, fused fwd + merge, bwd; striped as chosen automatically for packed
 sequences, and dual-chunk-swap), and llama3.1-8b at 16K on 16 ranks beyond its 8 kv
 heads (Ulysses 8 x ring 2, and Ulysses 16 with kv heads replicated).  The CPU oracle
@@ -166,7 +168,8 @@ def packed_work(seg, P, layout, window, D):
 
 
 def legs(torch, cp, cp_inputs):
-    """Ring share (llama2-7b, cp=16), 64K reorder and the packed + windowed ring."""
+    """Ring share (llama2-7b, cp=16), 64K reorder, the llama3.1-8b 64K rank share (fwd + bwd),
+    the packed + windowed ring, and Ulysses beyond the kv head count."""
     out = {}
     # ring share of llama2-7b: rank 0, 16 zigzag steps of fwd + merge
     S, H, D, P = 32768, 32, 128, 16
@@ -206,6 +209,30 @@ def legs(torch, cp, cp_inputs):
     out["reorder_64k_4096_bf16_cp4"] = {"avg_ms": round(zms / zn, 5),
                                         "gbps": round(2 * x.numel() * 2 / (zms / zn) / 1e6, 1)}
     del x, y
+    # Ulysses rank share of llama3.1-8b at 64K (cp=4): q [1,65536,8,128], k/v [1,65536,2,128]
+    # (8 query heads on 2 kv heads), causal, one forward and one backward per pass
+    S, Hq, Hkv = 65536, 8, 2
+    q, k, v, do = (t.cuda() for t in cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D),
+                                                               (1, S, Hq, D)], seed=0))
+    o, l = cp.attn_fwd(q, k, v)
+    bws = cp.bwd_workspace(q, k)
+    gq, gk, gv = (torch.empty(t.shape, device="cuda") for t in (q, k, v))
+
+    def gqa_pass():
+        cp.attn_fwd(q, k, v, out=o, lse=l)
+        cp.attn_bwd(q, k, v, o, l, do, dq=gq, dk=gk, dv=gv, workspace=bws)
+
+    gqa_pass()
+    with cp._lib.KernelTrace() as tr:
+        ms = timed(torch, gqa_pass, 3)
+    ff = 4 * D * Hq * pairs_causal(S)
+    f_ms = tr.results["attn_fwd_mfma"][0] / tr.results["attn_fwd_mfma"][1]
+    b_ms = tr.results["attn_bwd_mfma"][0] / tr.results["attn_bwd_mfma"][1]
+    out["ulysses_llama31_8b_64k_cp4_rank_fwd_bwd"] = {
+        "ms_per_pass": round(ms, 3), "tflops": round(3 * ff / ms / 1e9, 2),
+        "fwd_avg_ms": round(f_ms, 4), "fwd_tflops": round(ff / f_ms / 1e9, 2),
+        "bwd_avg_ms": round(b_ms, 4), "bwd_tflops": round(2 * ff / b_ms / 1e9, 2)}
+    del q, k, v, do, o, l, bws, gq, gk, gv
     # packed + windowed ring share: 8K, 32 q / 8 kv heads, docs 256..4096, window 4096, cp=4,
     # with the automatic strategy (striped for packed sequences) and with dual-chunk-swap
     S, Hq, Hkv, P = 8192, 32, 8, 4
