@@ -1,6 +1,7 @@
 """Benchmark of the context-parallel attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-legs]
+    python bench.py --leg {ring,reorder,gqa64k,packed,usp}   (one leg alone, for profilers)
 
 Workload (one "step"): the Ulysses share of llama2-7b (MHA, 32 heads, D=128) at
 32K context with cp=16, every simulated rank on this one GPU:
@@ -56,6 +57,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-legs", action="store_true", help="skip the ring / reorder / packed legs")
+    ap.add_argument("--leg", choices=["ring", "reorder", "gqa64k", "packed", "usp"],
+                    help="run only this leg and print its JSON (for profilers; no step, no value)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-copy", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device copy (read 1 GiB + write 1 GiB) "
@@ -167,116 +170,123 @@ def packed_work(seg, P, layout, window, D):
     return pairs, empty / total
 
 
-def legs(torch, cp, cp_inputs):
+def legs(torch, cp, cp_inputs, only=None):
     """Ring share (llama2-7b, cp=16), 64K reorder, the llama3.1-8b 64K rank share (fwd + bwd),
-    the packed + windowed ring, and Ulysses beyond the kv head count."""
+    the packed + windowed ring, and Ulysses beyond the kv head count; ``only`` names
+    one of them (ring, reorder, gqa64k, packed, usp) to run that alone."""
     out = {}
-    # ring share of llama2-7b: rank 0, 16 zigzag steps of fwd + merge
-    S, H, D, P = 32768, 32, 128, 16
-    q, k, v = (t.cuda() for t in cp_inputs.normal_tensors([(1, S, H, D)] * 3, seed=0))
-    qz, kz, vz = (cp.zigzag_reorder(t, P) for t in (q, k, v))
-    del q, k, v
-    fl = 4 * D * H * (2 * P * (S // (2 * P)) ** 2 + S // (2 * P))
-    merge_bytes = (S // P) * H * D * (4 + 2 + 4) + 3 * (S // P) * H * 4
-    # unfused: attn_fwd writes (out bf16, lse), lse_merge folds them into (acc, lse_acc)
-    ring = cp.drivers.RingShare(qz, kz, vz, P, 0, fused=False)
-    ring.forward()
-    with cp._lib.KernelTrace() as tr:
-        ms = timed(torch, ring.forward, 5)
-    fwd_ms, n_fwd = tr.results.get("attn_fwd_mfma", (0.0, 1))
-    mg_ms, n_mg = tr.results.get("lse_merge", (0.0, 1))
-    # fused: the merge runs in the attention epilogue
-    ring_f = cp.drivers.RingShare(qz, kz, vz, P, 0, fused=True)
-    ring_f.forward()
-    with cp._lib.KernelTrace() as tr:
-        ms_f = timed(torch, ring_f.forward, 5)
-    fm_ms, n_fm = tr.results.get("attn_fwd_merge_mfma", (0.0, 1))
-    out["ring_llama2_7b_32k_cp16_rank0"] = {
-        "fused_ms_per_pass": round(ms_f, 4), "fused_tflops": round(fl / ms_f / 1e9, 2),
-        "attn_fwd_merge_mfma_avg_ms": round(fm_ms / n_fm, 5),
-        "unfused_ms_per_pass": round(ms, 4), "unfused_tflops": round(fl / ms / 1e9, 2),
-        "attn_fwd_mfma_avg_ms": round(fwd_ms / n_fwd, 5),
-        "lse_merge_avg_ms": round(mg_ms / n_mg, 5),
-        "lse_merge_gbps": round(merge_bytes / (mg_ms / n_mg) / 1e6, 1)}
-    del qz, kz, vz, ring, ring_f
-    # dual-chunk-swap reorder of 64K tokens into 8 chunks: [1,65536,4096] bf16 (512 MiB)
-    x = torch.randn(1, 65536, 4096, device="cuda").bfloat16()
-    y = torch.empty_like(x)
-    cp.zigzag_reorder(x, 4, out=y)
-    with cp._lib.KernelTrace() as tr:
-        timed(torch, lambda: cp.zigzag_reorder(x, 4, out=y), 10)
-    zms, zn = tr.results["zigzag_reorder"]
-    out["reorder_64k_4096_bf16_cp4"] = {"avg_ms": round(zms / zn, 5),
-                                        "gbps": round(2 * x.numel() * 2 / (zms / zn) / 1e6, 1)}
-    del x, y
-    # Ulysses rank share of llama3.1-8b at 64K (cp=4): q [1,65536,8,128], k/v [1,65536,2,128]
-    # (8 query heads on 2 kv heads), causal, one forward and one backward per pass
-    S, Hq, Hkv = 65536, 8, 2
-    q, k, v, do = (t.cuda() for t in cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D),
-                                                               (1, S, Hq, D)], seed=0))
-    o, l = cp.attn_fwd(q, k, v)
-    bws = cp.bwd_workspace(q, k)
-    gq, gk, gv = (torch.empty(t.shape, device="cuda") for t in (q, k, v))
+    D = 128
+    if only in (None, 'ring'):
+        # ring share of llama2-7b: rank 0, 16 zigzag steps of fwd + merge
+        S, H, D, P = 32768, 32, 128, 16
+        q, k, v = (t.cuda() for t in cp_inputs.normal_tensors([(1, S, H, D)] * 3, seed=0))
+        qz, kz, vz = (cp.zigzag_reorder(t, P) for t in (q, k, v))
+        del q, k, v
+        fl = 4 * D * H * (2 * P * (S // (2 * P)) ** 2 + S // (2 * P))
+        merge_bytes = (S // P) * H * D * (4 + 2 + 4) + 3 * (S // P) * H * 4
+        # unfused: attn_fwd writes (out bf16, lse), lse_merge folds them into (acc, lse_acc)
+        ring = cp.drivers.RingShare(qz, kz, vz, P, 0, fused=False)
+        ring.forward()
+        with cp._lib.KernelTrace() as tr:
+            ms = timed(torch, ring.forward, 5)
+        fwd_ms, n_fwd = tr.results.get("attn_fwd_mfma", (0.0, 1))
+        mg_ms, n_mg = tr.results.get("lse_merge", (0.0, 1))
+        # fused: the merge runs in the attention epilogue
+        ring_f = cp.drivers.RingShare(qz, kz, vz, P, 0, fused=True)
+        ring_f.forward()
+        with cp._lib.KernelTrace() as tr:
+            ms_f = timed(torch, ring_f.forward, 5)
+        fm_ms, n_fm = tr.results.get("attn_fwd_merge_mfma", (0.0, 1))
+        out["ring_llama2_7b_32k_cp16_rank0"] = {
+            "fused_ms_per_pass": round(ms_f, 4), "fused_tflops": round(fl / ms_f / 1e9, 2),
+            "attn_fwd_merge_mfma_avg_ms": round(fm_ms / n_fm, 5),
+            "unfused_ms_per_pass": round(ms, 4), "unfused_tflops": round(fl / ms / 1e9, 2),
+            "attn_fwd_mfma_avg_ms": round(fwd_ms / n_fwd, 5),
+            "lse_merge_avg_ms": round(mg_ms / n_mg, 5),
+            "lse_merge_gbps": round(merge_bytes / (mg_ms / n_mg) / 1e6, 1)}
+        del qz, kz, vz, ring, ring_f
+    if only in (None, 'reorder'):
+        # dual-chunk-swap reorder of 64K tokens into 8 chunks: [1,65536,4096] bf16 (512 MiB)
+        x = torch.randn(1, 65536, 4096, device="cuda").bfloat16()
+        y = torch.empty_like(x)
+        cp.zigzag_reorder(x, 4, out=y)
+        with cp._lib.KernelTrace() as tr:
+            timed(torch, lambda: cp.zigzag_reorder(x, 4, out=y), 10)
+        zms, zn = tr.results["zigzag_reorder"]
+        out["reorder_64k_4096_bf16_cp4"] = {"avg_ms": round(zms / zn, 5),
+                                            "gbps": round(2 * x.numel() * 2 / (zms / zn) / 1e6, 1)}
+        del x, y
+    if only in (None, 'gqa64k'):
+        # Ulysses rank share of llama3.1-8b at 64K (cp=4): q [1,65536,8,128], k/v [1,65536,2,128]
+        # (8 query heads on 2 kv heads), causal, one forward and one backward per pass
+        S, Hq, Hkv = 65536, 8, 2
+        q, k, v, do = (t.cuda() for t in cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D),
+                                                                   (1, S, Hq, D)], seed=0))
+        o, l = cp.attn_fwd(q, k, v)
+        bws = cp.bwd_workspace(q, k)
+        gq, gk, gv = (torch.empty(t.shape, device="cuda") for t in (q, k, v))
 
-    def gqa_pass():
-        cp.attn_fwd(q, k, v, out=o, lse=l)
-        cp.attn_bwd(q, k, v, o, l, do, dq=gq, dk=gk, dv=gv, workspace=bws)
+        def gqa_pass():
+            cp.attn_fwd(q, k, v, out=o, lse=l)
+            cp.attn_bwd(q, k, v, o, l, do, dq=gq, dk=gk, dv=gv, workspace=bws)
 
-    gqa_pass()
-    with cp._lib.KernelTrace() as tr:
-        ms = timed(torch, gqa_pass, 3)
-    ff = 4 * D * Hq * pairs_causal(S)
-    f_ms = tr.results["attn_fwd_mfma"][0] / tr.results["attn_fwd_mfma"][1]
-    b_ms = tr.results["attn_bwd_mfma"][0] / tr.results["attn_bwd_mfma"][1]
-    out["ulysses_llama31_8b_64k_cp4_rank_fwd_bwd"] = {
-        "ms_per_pass": round(ms, 3), "tflops": round(3 * ff / ms / 1e9, 2),
-        "fwd_avg_ms": round(f_ms, 4), "fwd_tflops": round(ff / f_ms / 1e9, 2),
-        "bwd_avg_ms": round(b_ms, 4), "bwd_tflops": round(2 * ff / b_ms / 1e9, 2)}
-    del q, k, v, do, o, l, bws, gq, gk, gv
-    # packed + windowed ring share: 8K, 32 q / 8 kv heads, docs 256..4096, window 4096, cp=4,
-    # with the automatic strategy (striped for packed sequences) and with dual-chunk-swap
-    S, Hq, Hkv, P = 8192, 32, 8, 4
-    q, k, v, do = (t.cuda() for t in cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D),
-                                                               (1, S, Hq, D)], seed=0))
-    seg = cp_inputs.segment_ids(cp_inputs.doc_lengths(S)).cuda()
-    C = S // P
-    for name, st in (("auto", cp.drivers.auto_strategy(packed=True)), ("dual_chunk_swap", 0)):
-        layout = cp.drivers.LAYOUT_OF_STRATEGY[st]
-        qz, kz, vz, dz, sz = (cp.zigzag_reorder(t, P, strategy=st) for t in (q, k, v, do, seg))
-        shares = [cp.drivers.RingShare(qz, kz, vz, P, r, layout=layout, seg=sz, window=4096) for r in range(P)]
+        gqa_pass()
+        with cp._lib.KernelTrace() as tr:
+            ms = timed(torch, gqa_pass, 3)
+        ff = 4 * D * Hq * pairs_causal(S)
+        f_ms = tr.results["attn_fwd_mfma"][0] / tr.results["attn_fwd_mfma"][1]
+        b_ms = tr.results["attn_bwd_mfma"][0] / tr.results["attn_bwd_mfma"][1]
+        out["ulysses_llama31_8b_64k_cp4_rank_fwd_bwd"] = {
+            "ms_per_pass": round(ms, 3), "tflops": round(3 * ff / ms / 1e9, 2),
+            "fwd_avg_ms": round(f_ms, 4), "fwd_tflops": round(ff / f_ms / 1e9, 2),
+            "bwd_avg_ms": round(b_ms, 4), "bwd_tflops": round(2 * ff / b_ms / 1e9, 2)}
+        del q, k, v, do, o, l, bws, gq, gk, gv
+    if only in (None, 'packed'):
+        # packed + windowed ring share: 8K, 32 q / 8 kv heads, docs 256..4096, window 4096, cp=4,
+        # with the automatic strategy (striped for packed sequences) and with dual-chunk-swap
+        S, Hq, Hkv, P = 8192, 32, 8, 4
+        q, k, v, do = (t.cuda() for t in cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D),
+                                                                   (1, S, Hq, D)], seed=0))
+        seg = cp_inputs.segment_ids(cp_inputs.doc_lengths(S)).cuda()
+        C = S // P
+        for name, st in (("auto", cp.drivers.auto_strategy(packed=True)), ("dual_chunk_swap", 0)):
+            layout = cp.drivers.LAYOUT_OF_STRATEGY[st]
+            qz, kz, vz, dz, sz = (cp.zigzag_reorder(t, P, strategy=st) for t in (q, k, v, do, seg))
+            shares = [cp.drivers.RingShare(qz, kz, vz, P, r, layout=layout, seg=sz, window=4096) for r in range(P)]
 
-        def packed_pass():
-            dk = torch.zeros(kz.shape, device="cuda")
-            dv = torch.zeros(vz.shape, device="cuda")
-            for r, sh in enumerate(shares):
-                o, l = sh.forward()
-                ob = o.bfloat16()
-                dq = torch.zeros(1, C, Hq, D, device="cuda")
-                sh.backward(ob, l, dz[:, r * C:(r + 1) * C], dq, dk, dv)
+            def packed_pass():
+                dk = torch.zeros(kz.shape, device="cuda")
+                dv = torch.zeros(vz.shape, device="cuda")
+                for r, sh in enumerate(shares):
+                    o, l = sh.forward()
+                    ob = o.bfloat16()
+                    dq = torch.zeros(1, C, Hq, D, device="cuda")
+                    sh.backward(ob, l, dz[:, r * C:(r + 1) * C], dq, dk, dv)
 
-        packed_pass()
-        ms = timed(torch, packed_pass, 3)
-        pairs, skipped = packed_work(seg[0].cpu().numpy(), P, layout, 4096, D)
-        fl = 12 * D * Hq * pairs  # forward 4*D + backward 8*D per visible pair and head
-        out[f"packed_window_8k_cp4_all_ranks_{name}"] = {
-            "strategy": layout, "ms_per_pass": round(ms, 3), "visible_pairs_per_head": pairs,
-            "tflops": round(fl / ms / 1e9, 2), "fwd_tiles_skipped_frac": round(skipped, 4)}
-    # beyond the kv head count, llama3.1-8b (32 q / 8 kv heads) at 16K tokens on 16 ranks:
-    # Ulysses 8 within groups x ring 2 across them (USP), and Ulysses 16 with kv heads
-    # replicated 2x; forward of all ranks, algorithmic causal FLOPs of the whole sequence
-    S, Hq, Hkv = 16384, 32, 8
-    q, k, v = (t.cuda() for t in cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D)], seed=0))
-    fl = 4 * D * Hq * S * (S + 1) / 2
-    usp = lambda: cp.drivers.usp_forward(q, k, v, 2, 8)
-    usp()
-    ms = timed(torch, usp, 3)
-    out["usp_llama31_8b_16k_ulysses8_ring2_fwd"] = {"ms_per_pass": round(ms, 3), "tflops": round(fl / ms / 1e9, 2)}
-    P = 16
-    st = lambda t: t.reshape(P, 1, S // P, t.shape[2], D)
-    uly = lambda: cp.drivers.ulysses_forward(st(q), st(k), st(v), P, kv_rep=2)
-    uly()
-    ms = timed(torch, uly, 3)
-    out["ulysses16_kv_rep2_llama31_8b_16k_fwd"] = {"ms_per_pass": round(ms, 3), "tflops": round(fl / ms / 1e9, 2)}
+            packed_pass()
+            ms = timed(torch, packed_pass, 3)
+            pairs, skipped = packed_work(seg[0].cpu().numpy(), P, layout, 4096, D)
+            fl = 12 * D * Hq * pairs  # forward 4*D + backward 8*D per visible pair and head
+            out[f"packed_window_8k_cp4_all_ranks_{name}"] = {
+                "strategy": layout, "ms_per_pass": round(ms, 3), "visible_pairs_per_head": pairs,
+                "tflops": round(fl / ms / 1e9, 2), "fwd_tiles_skipped_frac": round(skipped, 4)}
+    if only in (None, 'usp'):
+        # beyond the kv head count, llama3.1-8b (32 q / 8 kv heads) at 16K tokens on 16 ranks:
+        # Ulysses 8 within groups x ring 2 across them (USP), and Ulysses 16 with kv heads
+        # replicated 2x; forward of all ranks, algorithmic causal FLOPs of the whole sequence
+        S, Hq, Hkv = 16384, 32, 8
+        q, k, v = (t.cuda() for t in cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D)], seed=0))
+        fl = 4 * D * Hq * S * (S + 1) / 2
+        usp = lambda: cp.drivers.usp_forward(q, k, v, 2, 8)
+        usp()
+        ms = timed(torch, usp, 3)
+        out["usp_llama31_8b_16k_ulysses8_ring2_fwd"] = {"ms_per_pass": round(ms, 3), "tflops": round(fl / ms / 1e9, 2)}
+        P = 16
+        st = lambda t: t.reshape(P, 1, S // P, t.shape[2], D)
+        uly = lambda: cp.drivers.ulysses_forward(st(q), st(k), st(v), P, kv_rep=2)
+        uly()
+        ms = timed(torch, uly, 3)
+        out["ulysses16_kv_rep2_llama31_8b_16k_fwd"] = {"ms_per_pass": round(ms, 3), "tflops": round(fl / ms / 1e9, 2)}
     return out
 
 
@@ -334,6 +344,9 @@ def main():
     import context_cp_attn_amd as cp
     cp.load_library()
     torch.cuda.set_device(0)
+    if a.leg:
+        print(json.dumps({"leg": a.leg, "legs": legs(torch, cp, cp_inputs, only=a.leg)}), flush=True)
+        return
 
     step = UlyssesStep(torch, cp, cp_inputs)
     for _ in range(a.warmup):
