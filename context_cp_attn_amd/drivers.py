@@ -83,10 +83,13 @@ class RingShare:
     """
 
     def __init__(self, q, k, v, P: int, rank: int, layout="zigzag", seg=None, causal=True,
-                 window=0, scale=0.0, fused=True):
+                 window=0, scale=0.0, fused=None):
         self.q, self.k, self.v, self.seg = q, k, v, seg
         self.P, self.rank, self.layout = P, rank, layout
-        self.fused = fused  # merge inside the attention epilogue (else attn_fwd + lse_merge)
+        # True: the merge inside the attention epilogue; False: attn_fwd + lse_merge;
+        # None: the fused step unless the forward splits the block's keys over two
+        # workgroups (small grids of long blocks), which only the unfused pair can use
+        self.fused = fused
         self.S = q.shape[1]
         self.C = self.S // P
         self.mask = dict(causal=causal, window=window, scale=scale)
@@ -112,7 +115,11 @@ class RingShare:
         B, _, Hq, D = ql.shape
         acc = torch.zeros(B, C, Hq, D, device=ql.device, dtype=torch.float32)
         lse = torch.full((B, Hq, C), float("-inf"), device=ql.device, dtype=torch.float32)
-        if not self.fused:
+        fused, ws = self.fused, False
+        if fused is None:
+            ws = split_workspace(ql, _block(self.k, r, C), **self._mask(r))
+            fused = ws is False
+        if not fused:
             blk_o = torch.empty(B, C, Hq, D, device=ql.device, dtype=ql.dtype)
             blk_l = torch.empty(B, Hq, C, device=ql.device, dtype=torch.float32)
         for step in range(P):
@@ -120,10 +127,11 @@ class RingShare:
             if self._skip(src):
                 continue
             kb, vb = _block(self.k, src, C), _block(self.v, src, C)
-            if self.fused:
+            if fused:
                 ops.attn_fwd_merge(ql, kb, vb, acc, lse, **self._mask(src))
             else:
-                ops.attn_fwd(ql, kb, vb, out=blk_o, lse=blk_l, **self._mask(src))
+                ops.attn_fwd(ql, kb, vb, out=blk_o, lse=blk_l, workspace=None if ws is False else ws,
+                             **self._mask(src))
                 ops.lse_merge(acc, lse, blk_o, blk_l)
         return acc, lse
 
@@ -142,9 +150,17 @@ class RingShare:
         return dq, dk, dv
 
 
+def split_workspace(q, k, **mask):
+    """The forward's workspace when it splits each query tile's keys over two
+    workgroups for this block shape (the size does not depend on positions or
+    segment ids), else False."""
+    ws = ops.fwd_workspace(q, k, **mask)
+    return False if ws is None else ws
+
+
 def ring_forward_all(q, k, v, P, layout="zigzag", seg=None, **mask):
     """Every rank's ring forward; returns per-rank (out fp32, lse).  mask may hold
-    ``fused`` (default True)."""
+    ``fused`` (default None: the fused step unless the forward's key split applies)."""
     return [RingShare(q, k, v, P, r, layout, seg, **mask).forward() for r in range(P)]
 
 
@@ -199,7 +215,8 @@ def usp_forward(q, k, v, Pr, Pu, kv_rep=1, seg=None, causal=True, window=0, scal
     The sequence is zigzag-reordered for the Pr groups; group r's share is split
     contiguously over its Pu ranks and exchanged inside the group (heads slice u to
     rank (r, u)); rank (r, u) then runs the ring over the groups' blocks of its head
-    slice with the fused step.  Returns (out [1,S,Hq,D] float32 in sequence order,
+    slice with the fused step (or attn_fwd + lse_merge where the forward splits the
+    blocks' keys over two workgroups).  Returns (out [1,S,Hq,D] float32 in sequence order,
     lse [Pr][Pu][1][Hq/Pu][S/Pr] per rank).
     """
     if q.shape[0] != 1:
@@ -215,6 +232,13 @@ def usp_forward(q, k, v, Pr, Pu, kv_rep=1, seg=None, causal=True, window=0, scal
     Hl = ql.shape[4]
     acc = torch.zeros(ql.shape, device=q.device, dtype=torch.float32)
     lse = torch.full((Pr, Pu, 1, Hl, Sr), float("-inf"), device=q.device, dtype=torch.float32)
+    # the fused step, unless the forward splits the blocks' keys (as in RingShare)
+    ws = split_workspace(ql[0, 0], kl[0, 0], causal=causal, window=window, scale=scale, q_pos=pos[0],
+                         k_pos=pos[0], q_seg=None if sz is None else sz[:, :Sr].contiguous(),
+                         k_seg=None if sz is None else sz[:, :Sr].contiguous())
+    if ws is not False:
+        blk_o = torch.empty(ql.shape[2:], device=q.device, dtype=ql.dtype)
+        blk_l = torch.empty(1, Hl, Sr, device=q.device, dtype=torch.float32)
     for r in range(Pr):
         for u in range(Pu):
             for step in range(Pr):
@@ -222,7 +246,11 @@ def usp_forward(q, k, v, Pr, Pu, kv_rep=1, seg=None, causal=True, window=0, scal
                 m = dict(causal=causal, window=window, scale=scale, q_pos=pos[r], k_pos=pos[src])
                 if sz is not None:
                     m.update(q_seg=sz[:, r * Sr:(r + 1) * Sr].contiguous(), k_seg=sz[:, src * Sr:(src + 1) * Sr].contiguous())
-                ops.attn_fwd_merge(ql[r, u], kl[src, u], vl[src, u], acc[r, u], lse[r, u], **m)
+                if ws is False:
+                    ops.attn_fwd_merge(ql[r, u], kl[src, u], vl[src, u], acc[r, u], lse[r, u], **m)
+                else:
+                    ops.attn_fwd(ql[r, u], kl[src, u], vl[src, u], out=blk_o, lse=blk_l, workspace=ws, **m)
+                    ops.lse_merge(acc[r, u], lse[r, u], blk_o, blk_l)
     back = ops.ulysses_relayout_ex(acc, Pu, groups=Pr, inverse=True)   # [Pr][Pu][1][Sl][Hq][D]
     out = ops.zigzag_reorder(back.view(1, S, back.shape[4], back.shape[5]), Pr, inverse=True)
     return out, lse

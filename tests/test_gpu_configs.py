@@ -170,6 +170,33 @@ def test_ring_llama2_7b_32k_zigzag(cp):
         check_rows(f64(acc)[:, pick], f64(lse)[:, :, pick], ro, rl, 1e-2, 1e-3)
 
 
+def test_ring_and_usp_long_blocks(cp):
+    """Blocks of 8192 keys on a small grid: the drivers run attn_fwd with its
+    two-workgroup key split + lse_merge instead of the fused step (their default
+    choice there).  Ring ranks (automatic and forced fused) and a Ulysses-2 x ring-2
+    forward, sampled rows against the oracle's full attention, bf16, 16K tokens."""
+    S, Hq, Hkv, D = 16384, 4, 2, 128
+    q, k, v = cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D)], seed=5)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    qf, kf, vf = (f64(t) for t in (q, k, v))
+    P = 2
+    qz, kz, vz = (cp.zigzag_reorder(t, P) for t in (qd, kd, vd))
+    assert cp.drivers.split_workspace(qz[:, :S // P], kz[:, :S // P]) is not False
+    pick = np.r_[0, 1, 4095, 4096, 6000, 8191]
+    for r in range(P):
+        pos = oracle.rank_positions(r, P, S, "zigzag")
+        ro, rl = oracle.attn_fwd(qf[:, pos[pick]], kf, vf, q_pos=pos[pick])
+        for fused in (None, True):
+            say(f"ring long blocks: rank {r} fused={fused}")
+            acc, lse = cp.drivers.RingShare(qz, kz, vz, P, r, fused=fused).forward()
+            check_rows(f64(acc)[:, pick], f64(lse)[:, :, pick], ro, rl, 1e-2, 1e-3)
+    say("usp long blocks: Ulysses 2 x ring 2")
+    out, _ = cp.drivers.usp_forward(qd, kd, vd, 2, 2)
+    rows = np.r_[0, 2047, 4096, 8191, 12000, 16383]
+    ro, rl = oracle.attn_fwd(qf[:, rows], kf, vf, q_pos=rows)
+    assert max_err(f64(out)[:, rows], ro) <= 1e-2
+
+
 # ------------------------------------------------------------------ Ulysses llama3.1-8b GQA, 64K, cp=4
 
 def test_ulysses_llama31_8b_64k_gqa(cp):
