@@ -127,10 +127,12 @@ struct QStage {
 
 // Shared skeleton of the dV and dK roles: a workgroup owns keys [j0, j0 + kRows) of
 // kv head g; wavefront w owns keys j0 + 32w + (0..31), one per lane column.
-// kDK selects the dK role (else dV).  kLane: the instance for windowed or segmented
-// problems, with the one-tile-per-lane classification and the query heads of the
-// group limited to [h_lo, h_end) (a separate instance, so that the dense kernel's
-// register allocation carries neither; the dense one walks every head of the group).
+// kDK selects the dK role (else dV).  kLane: the general instance, launched for
+// windowed or segmented problems and for grids whose key-side items are split over
+// the group's query heads: one-tile-per-lane classification where it applies, and
+// the group's query heads limited to [h_lo, h_end).  The other instance (one query
+// head per kv head, no window or segment ids) carries neither, so its register
+// allocation is unaffected, and walks every head of the group.
 template <class C, bool kDK, bool kLane>
 CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
