@@ -48,6 +48,8 @@ SIGNATURES = {
     "cp_attn_check_args": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp]),
     "cp_attn_bwd": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                             c_vp, c_i32, c_vp, ctypes.c_size_t, c_vp]),
+    "cp_attn_bwd_rows_ready": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                            c_vp, c_i32, c_vp, ctypes.c_size_t, c_vp]),
     "cp_lse_merge": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp]),
     "cp_ulysses_relayout": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp]),
     "cp_ulysses_relayout_inv": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp]),

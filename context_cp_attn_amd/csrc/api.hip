@@ -294,10 +294,13 @@ size_t cp_attn_bwd_workspace_size(const cp_attn_args_t* a) {
   return size_t(floats) * sizeof(float);
 }
 
-cp_status_t cp_attn_bwd(const cp_attn_args_t* a, const void* q, const void* k, const void* v,
-                        const void* out, const float* lse, const void* dout, float* dq, float* dk,
-                        float* dv, int32_t accumulate, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+cp_status_t bwd_impl(const cp_attn_args_t* a, const void* q, const void* k, const void* v, const void* out,
+                     const float* lse, const void* dout, float* dq, float* dk, float* dv, int32_t accumulate,
+                     void* workspace, size_t workspace_bytes, bool rows_ready, hipStream_t stream) {
   cp::AttnProblem p;
   cp_status_t st = check_attn(a, q, k, v, &p);
   if (st != CP_OK) return st;
@@ -333,15 +336,34 @@ cp_status_t cp_attn_bwd(const cp_attn_args_t* a, const void* q, const void* k, c
   if (!aligned(lse, 4) || !aligned(dq, 4) || !aligned(dk, 4) || !aligned(dv, 4))
     return fail(CP_ERR_INVALID, "lse or a gradient buffer is misaligned");
   if (mfma_path(a)) {
-    e = cp::launch_attn_bwd_bf16(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, stream);
+    e = cp::launch_attn_bwd_bf16(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, rows_ready, stream);
   } else if (a->dtype == CP_DTYPE_BF16) {
-    e = cp::launch_attn_bwd_rowwise_bf16(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, stream);
+    e = cp::launch_attn_bwd_rowwise_bf16(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, rows_ready,
+                                         stream);
   } else {
     e = cp::launch_attn_bwd_f32(p, static_cast<const float*>(q), static_cast<const float*>(k),
                                 static_cast<const float*>(v), static_cast<const float*>(out), lse,
-                                static_cast<const float*>(dout), dq, dk, dv, accumulate, delta, stream);
+                                static_cast<const float*>(dout), dq, dk, dv, accumulate, delta, rows_ready, stream);
   }
   return hip_status(e, "cp_attn_bwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+cp_status_t cp_attn_bwd(const cp_attn_args_t* a, const void* q, const void* k, const void* v,
+                        const void* out, const float* lse, const void* dout, float* dq, float* dk,
+                        float* dv, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return bwd_impl(a, q, k, v, out, lse, dout, dq, dk, dv, accumulate, workspace, workspace_bytes, false, stream);
+}
+
+cp_status_t cp_attn_bwd_rows_ready(const cp_attn_args_t* a, const void* q, const void* k, const void* v,
+                                   const void* out, const float* lse, const void* dout, float* dq, float* dk,
+                                   float* dv, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  return bwd_impl(a, q, k, v, out, lse, dout, dq, dk, dv, accumulate, workspace, workspace_bytes, true, stream);
 }
 
 cp_status_t cp_lse_merge(int64_t batch, int64_t seqlen, int64_t heads, int64_t head_dim,

@@ -757,12 +757,12 @@ int bwd_hsplit(const AttnProblem& p) {
 template <int D>
 hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const void* v, const void* out,
                     const float* lse, const void* dout, float* dq, float* dk, float* dv, int accumulate,
-                    float* delta, hipStream_t s) {
+                    float* delta, bool rows_ready, hipStream_t s) {
   using U = const uint16_t*;
   const int64_t rows = int64_t(p.B) * p.Sq * p.Hq;
   const int64_t threads = rows * (D / 8);
   float* lse2 = delta + bwd_row_plane(rows);
-  {
+  if (!rows_ready) {
     ProfScope ps(s, kProfBwdDelta);
     hipLaunchKernelGGL(delta_kernel<D>, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, rows, p.Sq,
                        p.Hq, static_cast<U>(out), static_cast<U>(dout), lse, delta, lse2);
@@ -799,11 +799,12 @@ int64_t bwd_head_split_floats(const AttnProblem& p) {
 
 hipError_t launch_attn_bwd_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
                                 const void* out, const float* lse, const void* dout, float* dq,
-                                float* dk, float* dv, int accumulate, float* delta, hipStream_t s) {
+                                float* dk, float* dv, int accumulate, float* delta, bool rows_ready,
+                                hipStream_t s) {
   switch (p.D) {
-    case 128: return launch_d<128>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, s);
-    case 64: return launch_d<64>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, s);
-    case 32: return launch_d<32>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, s);
+    case 128: return launch_d<128>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, rows_ready, s);
+    case 64: return launch_d<64>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, rows_ready, s);
+    case 32: return launch_d<32>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, rows_ready, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -275,10 +275,11 @@ hipError_t fwd_nt(const AttnProblem& p, const T* q, const T* k, const T* v, OutT
 template <typename T, int NT>
 hipError_t bwd_nt(const AttnProblem& p, const T* q, const T* k, const T* v, const T* out,
                   const float* lse, const T* dout, float* dq, float* dk, float* dv, int accumulate,
-                  float* delta, hipStream_t s) {
+                  float* delta, bool rows_ready, hipStream_t s) {
   const int64_t rows = int64_t(p.B) * p.Sq * p.Hq;
   ProfScope ps(s, kProfBwdRowwise);
-  hipLaunchKernelGGL((delta_rowwise_kernel<T, NT>), dim3(unsigned((rows + kWaves - 1) / kWaves)),
+  if (!rows_ready)
+    hipLaunchKernelGGL((delta_rowwise_kernel<T, NT>), dim3(unsigned((rows + kWaves - 1) / kWaves)),
                      dim3(kThreads), 0, s, p.B, p.Sq, p.Hq, p.D, out, dout, delta);
   hipLaunchKernelGGL((dq_rowwise_kernel<T, NT>), dim3((p.Sq + kWaves - 1) / kWaves, p.Hq, p.B),
                      dim3(kThreads), 0, s, p, q, k, v, lse, dout, delta, dq, accumulate);
@@ -303,9 +304,10 @@ hipError_t launch_attn_fwd_merge_f32(const AttnProblem& p, const float* q, const
 
 hipError_t launch_attn_bwd_f32(const AttnProblem& p, const float* q, const float* k, const float* v,
                                const float* out, const float* lse, const float* dout, float* dq,
-                               float* dk, float* dv, int accumulate, float* delta, hipStream_t s) {
-  return p.D <= 64 ? bwd_nt<float, 1>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, s)
-                   : bwd_nt<float, 2>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, s);
+                               float* dk, float* dv, int accumulate, float* delta, bool rows_ready,
+                               hipStream_t s) {
+  return p.D <= 64 ? bwd_nt<float, 1>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, rows_ready, s)
+                   : bwd_nt<float, 2>(p, q, k, v, out, lse, dout, dq, dk, dv, accumulate, delta, rows_ready, s);
 }
 
 hipError_t launch_attn_fwd_rowwise_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
@@ -324,10 +326,11 @@ hipError_t launch_attn_fwd_merge_rowwise_bf16(const AttnProblem& p, const void* 
 
 hipError_t launch_attn_bwd_rowwise_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
                                         const void* out, const float* lse, const void* dout, float* dq,
-                                        float* dk, float* dv, int accumulate, float* delta, hipStream_t s) {
+                                        float* dk, float* dv, int accumulate, float* delta, bool rows_ready,
+                                        hipStream_t s) {
   using U = const uint16_t*;
-  return p.D <= 64 ? bwd_nt<uint16_t, 1>(p, U(q), U(k), U(v), U(out), lse, U(dout), dq, dk, dv, accumulate, delta, s)
-                   : bwd_nt<uint16_t, 2>(p, U(q), U(k), U(v), U(out), lse, U(dout), dq, dk, dv, accumulate, delta, s);
+  return p.D <= 64 ? bwd_nt<uint16_t, 1>(p, U(q), U(k), U(v), U(out), lse, U(dout), dq, dk, dv, accumulate, delta, rows_ready, s)
+                   : bwd_nt<uint16_t, 2>(p, U(q), U(k), U(v), U(out), lse, U(dout), dq, dk, dv, accumulate, delta, rows_ready, s);
 }
 
 }  // namespace cp

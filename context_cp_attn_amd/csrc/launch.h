@@ -45,7 +45,8 @@ hipError_t launch_attn_fwd_merge_rowwise_bf16(const AttnProblem& p, const void* 
                                               const void* v, float* acc, float* lse_acc, hipStream_t s);
 hipError_t launch_attn_bwd_rowwise_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
                                         const void* out, const float* lse, const void* dout, float* dq,
-                                        float* dk, float* dv, int accumulate, float* delta, hipStream_t s);
+                                        float* dk, float* dv, int accumulate, float* delta, bool rows_ready,
+                                        hipStream_t s);
 
 // compute units of the current device (cached per device; 256 if it cannot be read)
 int device_cus();
@@ -56,12 +57,16 @@ int device_cus();
 // 2 * bwd_row_plane(rows) floats in
 inline int64_t bwd_row_plane(int64_t rows) { return (rows + 63) / 64 * 64; }
 int64_t bwd_head_split_floats(const AttnProblem& p);
+// rows_ready: the workspace's row arrays already hold this problem's values (an
+// earlier call with the same out, lse and dout); the row pre-pass is skipped
 hipError_t launch_attn_bwd_bf16(const AttnProblem& p, const void* q, const void* k, const void* v,
                                 const void* out, const float* lse, const void* dout, float* dq,
-                                float* dk, float* dv, int accumulate, float* delta, hipStream_t s);
+                                float* dk, float* dv, int accumulate, float* delta, bool rows_ready,
+                                hipStream_t s);
 hipError_t launch_attn_bwd_f32(const AttnProblem& p, const float* q, const float* k, const float* v,
                                const float* out, const float* lse, const float* dout, float* dq,
-                               float* dk, float* dv, int accumulate, float* delta, hipStream_t s);
+                               float* dk, float* dv, int accumulate, float* delta, bool rows_ready,
+                               hipStream_t s);
 
 // precondition check of the position / segment arrays; writes a violation bit mask
 hipError_t launch_check_args(const int* q_pos, const int* k_pos, const int* q_seg, const int* k_seg, int64_t B,

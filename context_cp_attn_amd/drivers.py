@@ -140,13 +140,18 @@ class RingShare:
         partial dk/dv of every block into the whole-sequence dk/dv buffers."""
         r, C, P = self.rank, self.C, self.P
         ql = _block(self.q, r, C)
+        # every step uses the rows' same out, lse and dout: the first call derives the
+        # per-row values into the workspace, the later ones reuse them
+        ws = ops.bwd_workspace(ql, _block(self.k, r, C), **self._mask(r))
+        ready = False
         for step in range(P):
             src = (r - step) % P
             if self._skip(src):
                 continue
             ops.attn_bwd(ql, _block(self.k, src, C), _block(self.v, src, C), out, lse, dout,
                          dq=dq, dk=_block(dk, src, C), dv=_block(dv, src, C), accumulate=True,
-                         **self._mask(src))
+                         workspace=ws, rows_ready=ready, **self._mask(src))
+            ready = True
         return dq, dk, dv
 
 

@@ -163,8 +163,11 @@ def bwd_workspace(q, k, **mask) -> torch.Tensor:
 
 
 def attn_bwd(q, k, v, out, lse, dout, *, dq=None, dk=None, dv=None, accumulate=False, workspace=None,
-             **mask):
-    """(dq, dk, dv) float32 of one attention block given the rows' final (out, lse)."""
+             rows_ready=False, **mask):
+    """(dq, dk, dv) float32 of one attention block given the rows' final (out, lse).
+
+    rows_ready: ``workspace`` still holds the per-row values an earlier call with the
+    same out, lse and dout (and the same query shape) derived (cp_attn_bwd_rows_ready)."""
     _check_qkv(q, k, v)
     _dev(out, "out", q.dtype)
     _dev(dout, "dout", q.dtype)
@@ -179,9 +182,12 @@ def attn_bwd(q, k, v, out, lse, dout, *, dq=None, dk=None, dv=None, accumulate=F
     dv = torch.empty(v.shape, **f32) if dv is None else _dev(dv, "dv", torch.float32)
     lib = _lib.load()
     need = lib.cp_attn_bwd_workspace_size(ctypes.byref(a))
+    if rows_ready and workspace is None:
+        raise ValueError("rows_ready needs the workspace of an earlier call")
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
-    _lib.check(lib.cp_attn_bwd(ctypes.byref(a), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+    fn = lib.cp_attn_bwd_rows_ready if rows_ready else lib.cp_attn_bwd
+    _lib.check(fn(ctypes.byref(a), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
                                dk.data_ptr(), dv.data_ptr(), int(bool(accumulate)),
                                workspace.data_ptr(), workspace.numel(), _stream()))

@@ -147,6 +147,21 @@ cp_status_t cp_attn_bwd(const cp_attn_args_t* args, const void* q, const void* k
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * cp_attn_bwd for the later steps of a ring backward ([H] §"Ring Attention": every
+ * step's block gradient uses the rows' same final out and lse): the per-row values
+ * the backward derives from out, lse and dout (the dO.O sums and the base-2 lse) are
+ * taken from the workspace as an earlier cp_attn_bwd or cp_attn_bwd_rows_ready call
+ * left them, instead of being recomputed.  The caller guarantees that the workspace
+ * was last used by such a call, ordered before this one, with the same out, lse and
+ * dout (same contents) and the same batch, heads_q, seqlen_q and dtype / head_dim;
+ * the library cannot check this.  Arguments and errors as cp_attn_bwd.
+ */
+cp_status_t cp_attn_bwd_rows_ready(const cp_attn_args_t* args, const void* q, const void* k, const void* v,
+                                   const void* out, const float* lse, const void* dout,
+                                   float* dq, float* dk, float* dv, int32_t accumulate,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Debug check of the preconditions on args' arrays that the attention kernels rely
  * on but the host cannot see: q_pos / k_pos strictly increasing and >= 0 (the block
  * positions of [H] §"Ring Attention"), q_seg / k_seg non-decreasing along each of the

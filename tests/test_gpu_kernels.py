@@ -360,6 +360,27 @@ def test_attn_bwd(cp, name, dtype, D):
         torch.testing.assert_close(a, 2 * b, rtol=1e-6, atol=1e-6)
 
 
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 16)])
+def test_attn_bwd_rows_ready(cp, dtype, D):
+    """cp_attn_bwd_rows_ready: a second kv block's gradients with the per-row values
+    the first call left in the workspace equal a fresh call's, bit for bit."""
+    say(f"attn_bwd rows_ready D={D} {dtype}")
+    Sq, Sk, Hq, Hkv = 300, 260, 4, 2
+    q, k, v, k2, v2, do = (t.cuda() for t in cp_inputs.normal_tensors(
+        [(1, Sq, Hq, D), (1, Sk, Hkv, D), (1, Sk, Hkv, D), (1, Sk, Hkv, D), (1, Sk, Hkv, D), (1, Sq, Hq, D)],
+        seed=17, dtype=dtype))
+    m = dict(q_offset=Sk)
+    out, lse = cp.attn_fwd(q, k, v, **m)
+    ws = cp.bwd_workspace(q, k, **m)
+    cp.attn_bwd(q, k, v, out, lse, do, workspace=ws, **m)
+    got = cp.attn_bwd(q, k2, v2, out, lse, do, workspace=ws, rows_ready=True, **m)
+    ref = cp.attn_bwd(q, k2, v2, out, lse, do, **m)
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
+    with pytest.raises(ValueError):
+        cp.attn_bwd(q, k2, v2, out, lse, do, rows_ready=True, **m)
+
+
 @pytest.mark.parametrize("masks", ["long_docs", "long_window"])
 def test_attn_long_masked_ranges(cp, masks):
     """Segmented or windowed problems whose workgroups see more than 64 tiles: the
