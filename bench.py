@@ -80,28 +80,18 @@ def sha_of(*paths):
     return h.hexdigest()[:16]
 
 
-class UlyssesStep:
-    """All buffers of the step, allocated once; ``run`` launches one step."""
+class StepWorkload:
+    """The step's inputs, resident in HBM, and the drivers' preallocated Ulysses pass
+    (context_cp_attn_amd.drivers.UlyssesStep) over them."""
 
     P, S, H, D = 16, 32768, 32, 128
 
     def __init__(self, torch, cp, cp_inputs):
         P, S, H, D = self.P, self.S, self.H, self.D
-        self.torch, self.cp = torch, cp
-        dev = "cuda"
         q, k, v, do = cp_inputs.normal_tensors([(1, S, H, D)] * 4, seed=0)
         # the global [1,S,H,D] sequence split into P contiguous slices = [P][1][S/P][H][D]
-        self.stack = [t.reshape(P, 1, S // P, H, D).to(dev) for t in (q, k, v, do)]
-        bf, f32 = torch.bfloat16, torch.float32
-        sh = (P, 1, S, H // P, D)
-        self.ql, self.kl, self.vl, self.gl = (torch.empty(sh, device=dev, dtype=bf) for _ in range(4))
-        self.ol = torch.empty(sh, device=dev, dtype=bf)
-        self.lse = torch.empty(P, 1, H // P, S, device=dev, dtype=f32)
-        self.out = torch.empty(P, 1, S // P, H, D, device=dev, dtype=bf)
-        self.dql, self.dkl, self.dvl = (torch.empty(sh, device=dev, dtype=f32) for _ in range(3))
-        self.dq, self.dk, self.dv = (torch.empty(P, 1, S // P, H, D, device=dev, dtype=f32) for _ in range(3))
-        self.ws = cp.bwd_workspace(self.ql[0], self.kl[0])
-        self.fws = cp.fwd_workspace(self.ql[0], self.kl[0])   # None when the forward does not split
+        stack = [t.reshape(P, 1, S // P, H, D).to("cuda") for t in (q, k, v, do)]
+        self.step = cp.drivers.UlyssesStep(*stack, P)
         hp = H // P
         self.flops_fwd_rank = 4 * D * hp * pairs_causal(S)
         self.flops_bwd_rank = 8 * D * hp * pairs_causal(S)
@@ -111,21 +101,7 @@ class UlyssesStep:
         self.relayout_bytes = 5 * 2 * bf_bytes + 3 * 2 * 2 * bf_bytes
 
     def run(self):
-        cp, P = self.cp, self.P
-        qs, ks, vs, gs = self.stack
-        cp.ulysses_relayout(qs, P, out=self.ql)
-        cp.ulysses_relayout(ks, P, out=self.kl)
-        cp.ulysses_relayout(vs, P, out=self.vl)
-        for p in range(P):
-            cp.attn_fwd(self.ql[p], self.kl[p], self.vl[p], out=self.ol[p], lse=self.lse[p], workspace=self.fws)
-        cp.ulysses_relayout_inv(self.ol, P, out=self.out)
-        cp.ulysses_relayout(gs, P, out=self.gl)
-        for p in range(P):
-            cp.attn_bwd(self.ql[p], self.kl[p], self.vl[p], self.ol[p], self.lse[p], self.gl[p],
-                        dq=self.dql[p], dk=self.dkl[p], dv=self.dvl[p], workspace=self.ws)
-        cp.ulysses_relayout_inv(self.dql, P, out=self.dq)
-        cp.ulysses_relayout_inv(self.dkl, P, out=self.dk)
-        cp.ulysses_relayout_inv(self.dvl, P, out=self.dv)
+        self.step.run()
 
 
 def timed(torch, fn, reps):
@@ -348,7 +324,7 @@ def main():
         print(json.dumps({"leg": a.leg, "legs": legs(torch, cp, cp_inputs, only=a.leg)}), flush=True)
         return
 
-    step = UlyssesStep(torch, cp, cp_inputs)
+    step = StepWorkload(torch, cp, cp_inputs)
     for _ in range(a.warmup):
         step.run()
     torch.cuda.synchronize()

@@ -128,7 +128,9 @@ cp_status_t check_attn(const cp_attn_args_t* a, const void* q, const void* k, co
   p->Hq = int(a->heads_q);
   p->Hkv = int(a->heads_kv);
   p->D = int(a->head_dim);
-  p->causal = a->causal;
+  // the window bounds qpos - kpos on both sides (0 <= qpos - kpos < window), so a
+  // window carries the causal rule with it
+  p->causal = (a->causal || a->window) ? 1 : 0;
   p->q_offset = int(a->q_pos ? 0 : a->q_offset);
   p->k_offset = int(a->k_pos ? 0 : a->k_offset);
   p->q_pos = a->q_pos;
@@ -383,9 +385,13 @@ cp_status_t cp_lse_merge(int64_t batch, int64_t seqlen, int64_t heads, int64_t h
     return fail(CP_ERR_UNSUPPORTED, "merge of 2^31 - 512 or more 16-byte vectors (out_acc of 32 GiB or more)");
   if (!aligned(out_acc, 16) || !aligned(out_blk, blk_dtype == CP_DTYPE_BF16 ? 8 : 16))
     return fail(CP_ERR_INVALID, "out_acc must be 16-byte aligned, out_blk 8 (bf16) / 16 (f32)");
+  // the written buffers (out_acc, lse_acc) overlap neither each other nor a read-only
+  // one: a workgroup's in-place writes would race with other workgroups' reads
   const int64_t rows = batch * seqlen * heads;
-  if (overlaps(out_acc, rows * head_dim * 4, out_blk, rows * head_dim * dtype_bytes(blk_dtype)) ||
-      overlaps(lse_acc, rows * 4, lse_blk, rows * 4) || overlaps(out_acc, rows * head_dim * 4, lse_acc, rows * 4))
+  const int64_t acc_b = rows * head_dim * 4, blk_b = rows * head_dim * dtype_bytes(blk_dtype), lse_b = rows * 4;
+  if (overlaps(out_acc, acc_b, out_blk, blk_b) || overlaps(out_acc, acc_b, lse_blk, lse_b) ||
+      overlaps(lse_acc, lse_b, out_blk, blk_b) || overlaps(lse_acc, lse_b, lse_blk, lse_b) ||
+      overlaps(out_acc, acc_b, lse_acc, lse_b))
     return fail(CP_ERR_ALIAS, "merge buffers overlap");
   return hip_status(cp::launch_lse_merge(batch, seqlen, heads, head_dim, out_acc, lse_acc, out_blk,
                                          lse_blk, blk_dtype == CP_DTYPE_BF16, stream),

@@ -43,24 +43,20 @@ CP_DEVICE float wave_sum(float x) {
 // ---- visibility of a (query, key) pair -------------------------------------------
 // Positions are global token indices in [0, 2^31); segments int32 document ids.  The
 // key at kp is visible to the query at qp iff kp <= qp (causal), qp - kp < window
-// (when a window is given) and both carry the same segment id (when given).  With
-// d = qp - kp in (-2^31, 2^31) the two position rules are one unsigned range test,
-// (d - lo) mod 2^32 < span:
+// (when a window is given; the host turns the causal rule on with any window, so a
+// window means 0 <= qp - kp < window) and both carry the same segment id (when
+// given).  With d = qp - kp in (-2^31, 2^31) the position rules are one unsigned
+// range test, (d - lo) mod 2^32 < span:
 //   causal:     lo = 0,          span = window, or 2^31 without one (d >= 0);
-//   not causal: lo = 1 - 2^31,   span = window - lo (d < window), or 2^32 - 1 (any d).
+//   not causal: lo = 1 - 2^31,   span = 2^32 - 1 (any d).
 struct MaskSpec {
   uint32_t lo, span;
   int has_seg;
 };
 
 inline __host__ __device__ MaskSpec make_mask_spec(int causal, int window, int has_seg) {
-  const uint32_t lo = causal ? 0u : 1u - (1u << 31);
-  uint32_t span;
-  if (causal)
-    span = window ? uint32_t(window) : (1u << 31);
-  else
-    span = window ? uint32_t(window) - lo : 0xffffffffu;
-  return MaskSpec{lo, span, has_seg};
+  if (causal || window) return MaskSpec{0u, window ? uint32_t(window) : (1u << 31), has_seg};
+  return MaskSpec{1u - (1u << 31), 0xffffffffu, has_seg};
 }
 
 // Branch-free (bitwise) so that per-element masks compile to compares and selects.

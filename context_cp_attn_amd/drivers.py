@@ -26,8 +26,13 @@ LAYOUT_OF_STRATEGY = {ops.DUAL_CHUNK_SWAP: "zigzag", ops.STRIPED: "striped"}
 
 
 def auto_strategy(packed: bool) -> int:
-    """Reorder strategy chosen automatically from the packing configuration (the
-    MaxText packing PR's AUTO): striped for packed sequences, else dual-chunk-swap."""
+    """Reorder strategy chosen from the packing configuration.  The MaxText packing
+    PR ("Add Packing Support for Context Parallelism (Ring Attention)",
+    §Description) says only that the choice follows the packing configuration, not
+    which strategy each configuration gets; the reading here is striped for packed
+    sequences and dual-chunk-swap otherwise.  It is a policy, not a result: both
+    strategies give the same attention, and on the packed 8K workload of these
+    kernels dual-chunk-swap is the faster of the two."""
     return ops.STRIPED if packed else ops.DUAL_CHUNK_SWAP
 
 
@@ -43,10 +48,21 @@ def pad_sequence(x, multiple: int):
     return ops.pad_rows(x, padded_length(S, multiple)), S
 
 
-def pad_segments(seg, multiple: int, pad_id: int):
-    """Pad int32 segment ids [B][S] to a multiple, the pad tokens in segment
-    ``pad_id`` (an id no real token has), so that no real query sees a pad key
-    without a causal mask either."""
+def pad_segments(seg, multiple: int, pad_id: int | None = None):
+    """Pad int32 segment ids [B][S] to a multiple, the pad tokens in a segment of
+    their own, so that no real query sees a pad key without a causal mask either.
+
+    Segment ids must never decrease along a row (the attention kernels classify
+    whole tiles from their first and last ids), so the pad segment, which comes
+    last, needs an id above every real one: ``pad_id`` defaults to the largest id
+    + 1 (one device-to-host read), and a given ``pad_id`` that is not above every
+    real id raises ValueError."""
+    top = int(seg.max().item())
+    if pad_id is None:
+        pad_id = top + 1
+    elif pad_id <= top:
+        raise ValueError(f"pad_id {pad_id} must exceed every real segment id (largest {top}): "
+                         "segment ids may not decrease along the sequence")
     return ops.pad_rows(seg, padded_length(seg.shape[1], multiple), fill=pad_id)
 
 
@@ -211,6 +227,65 @@ def ulysses_backward(relayouted, lse, dout_stack, P, kv_rep=1, **mask):
         return dq, ops.ulysses_relayout_inv(dkl, P), ops.ulysses_relayout_inv(dvl, P)
     inv = lambda t: ops.ulysses_relayout_ex(t.unsqueeze(0), P, rep=kv_rep, inverse=True)[0]
     return dq, inv(dkl), inv(dvl)
+
+
+class UlyssesStep:
+    """One Ulysses forward + backward pass of all P ranks with every buffer
+    allocated once, so that repeated passes allocate nothing.
+
+    q_stack, k_stack, v_stack, dout_stack are [P][B][S/P][H][D] bf16 (rank s holds
+    sequence slice s, all heads; MHA, so q and k/v have the same head count).
+    ``run`` relayouts q, k, v to [P][B][S][H/P][D], runs rank p's attention forward
+    on its H/P heads over the whole sequence, returns the output to the sequence
+    layout (``out``), relayouts dout, runs every rank's backward and returns dq, dk,
+    dv (float32) to the sequence layout.  ``lse`` [P][B][H/P][S] keeps each rank's
+    row log-sum-exp.  The same sequence of calls as ``ulysses_forward`` +
+    ``ulysses_backward``, with the buffers reused.
+    """
+
+    def __init__(self, q_stack, k_stack, v_stack, dout_stack, P: int, **mask):
+        P_, B, Sl, H, D = q_stack.shape
+        if P_ != P or H % P:
+            raise ValueError(f"stack of {P_} ranks and {H} heads for degree {P}")
+        if tuple(k_stack.shape) != tuple(q_stack.shape):
+            raise ValueError("UlyssesStep takes MHA stacks (k/v shaped like q)")
+        self.P, self.mask = P, mask
+        self.stack = (q_stack, k_stack, v_stack, dout_stack)
+        dev, bf, f32 = q_stack.device, q_stack.dtype, torch.float32
+        S = Sl * P
+        sh = (P, B, S, H // P, D)
+        self.ql, self.kl, self.vl, self.gl, self.ol = (torch.empty(sh, device=dev, dtype=bf) for _ in range(5))
+        self.lse = torch.empty(P, B, H // P, S, device=dev, dtype=f32)
+        self.out = torch.empty(q_stack.shape, device=dev, dtype=bf)
+        self.dql, self.dkl, self.dvl = (torch.empty(sh, device=dev, dtype=f32) for _ in range(3))
+        self.dq, self.dk, self.dv = (torch.empty(q_stack.shape, device=dev, dtype=f32) for _ in range(3))
+        self.ws = ops.bwd_workspace(self.ql[0], self.kl[0], **mask)
+        self.fws = ops.fwd_workspace(self.ql[0], self.kl[0], **mask)   # None when the forward does not split
+
+    def forward(self):
+        P = self.P
+        qs, ks, vs, _ = self.stack
+        ops.ulysses_relayout(qs, P, out=self.ql)
+        ops.ulysses_relayout(ks, P, out=self.kl)
+        ops.ulysses_relayout(vs, P, out=self.vl)
+        for p in range(P):
+            ops.attn_fwd(self.ql[p], self.kl[p], self.vl[p], out=self.ol[p], lse=self.lse[p], workspace=self.fws,
+                         **self.mask)
+        ops.ulysses_relayout_inv(self.ol, P, out=self.out)
+
+    def backward(self):
+        P = self.P
+        ops.ulysses_relayout(self.stack[3], P, out=self.gl)
+        for p in range(P):
+            ops.attn_bwd(self.ql[p], self.kl[p], self.vl[p], self.ol[p], self.lse[p], self.gl[p],
+                         dq=self.dql[p], dk=self.dkl[p], dv=self.dvl[p], workspace=self.ws, **self.mask)
+        ops.ulysses_relayout_inv(self.dql, P, out=self.dq)
+        ops.ulysses_relayout_inv(self.dkl, P, out=self.dk)
+        ops.ulysses_relayout_inv(self.dvl, P, out=self.dv)
+
+    def run(self):
+        self.forward()
+        self.backward()
 
 
 def usp_forward(q, k, v, Pr, Pu, kv_rep=1, seg=None, causal=True, window=0, scale=0.0):

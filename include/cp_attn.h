@@ -50,8 +50,11 @@ typedef enum {
  * Key j is visible to query i iff all of:
  *   causal == 0  or  kpos[j] <= qpos[i]
  *   q_seg == NULL  or  q_seg[b,i] == k_seg[b,j]
- *   window == 0  or  qpos[i] - kpos[j] < window
- * where qpos[i] = q_pos ? q_pos[i] : q_offset + i (likewise kpos).
+ *   window == 0  or  0 <= qpos[i] - kpos[j] < window
+ * where qpos[i] = q_pos ? q_pos[i] : q_offset + i (likewise kpos).  The pages name
+ * the sliding window without defining it; it is read here as the window of the
+ * window most recent keys up to and including the query's own position, so a
+ * window implies the causal rule whatever causal says.
  * A query row with no visible key gets out = 0 and lse = -inf.
  */
 typedef struct {
@@ -69,7 +72,7 @@ typedef struct {
   const int32_t* k_pos;    /* NULL or device [Sk] strictly increasing global positions    */
   const int32_t* q_seg;    /* NULL or device [B, Sq] non-decreasing segment ids           */
   const int32_t* k_seg;    /* NULL or device [B, Sk]; non-NULL iff q_seg is non-NULL     */
-  int64_t window;          /* 0 = no window; > 0 = sliding window width                  */
+  int64_t window;          /* 0 = no window; > 0 = sliding window width (implies causal) */
   float softmax_scale;     /* 0 -> 1/sqrt(head_dim)                                      */
 } cp_attn_args_t;
 
@@ -123,7 +126,8 @@ cp_status_t cp_attn_fwd_ws(const cp_attn_args_t* args, const void* q, const void
 cp_status_t cp_attn_fwd_merge(const cp_attn_args_t* args, const void* q, const void* k, const void* v,
                               float* out_acc, float* lse_acc, hipStream_t stream);
 
-/* Workspace bytes cp_attn_bwd needs for args on the current device: two float32
+/* Workspace bytes cp_attn_bwd needs for args on the current device (the backward
+   of [HF] §Tests, stated with cp_attn_bwd below): two float32
    arrays of the rows [B,Hq,Sq], the per-row dO.O sums and the rows' lse in base 2;
    for bf16 problems (D 32, 64, 128) with grouped query heads whose backward grid is
    under 16 workgroups per compute unit, also float32 dK and dV partials
@@ -135,7 +139,12 @@ size_t cp_attn_bwd_workspace_size(const cp_attn_args_t* args);
  * Blockwise attention backward: the gradient of sum(dout * out) with respect to q,
  * k and v for this block, given the rows' FINAL out and lse (for a ring step these are
  * the merged values over all blocks, so the per-block gradients add up to the full
- * gradient).  dq [B,Sq,Hq,D], dk/dv [B,Sk,Hkv,D] float32; dk/dv are summed over the
+ * gradient).  The pages ask for the backward next to the forward ([HF] §Tests:
+ * forward and backward checked against plain attention) without stating it; this is
+ * the textbook gradient of softmax attention, P = exp(scale*q.k - lse) on visible
+ * pairs, Delta = rowsum(dout * out), dv = P^T dout, dS = P * (dout v^T - Delta),
+ * dq = scale dS k, dk = scale dS^T q, and applying it per block with the final out
+ * and lse is this library's reading of a ring backward.  dq [B,Sq,Hq,D], dk/dv [B,Sk,Hkv,D] float32; dk/dv are summed over the
  * query heads of each kv group.  accumulate = 1 adds into dq/dk/dv, 0 overwrites
  * them.  workspace: device memory of at least cp_attn_bwd_workspace_size(args)
  * bytes, 16-byte aligned, owned by the caller.  The result is deterministic (no
@@ -147,8 +156,9 @@ cp_status_t cp_attn_bwd(const cp_attn_args_t* args, const void* q, const void* k
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * cp_attn_bwd for the later steps of a ring backward ([H] §"Ring Attention": every
- * step's block gradient uses the rows' same final out and lse): the per-row values
+ * cp_attn_bwd for the later steps of a ring backward (in the blockwise reading of
+ * cp_attn_bwd, every step's block gradient uses the rows' same final out and lse;
+ * the pages do not state a ring backward): the per-row values
  * the backward derives from out, lse and dout (the dO.O sums and the base-2 lse) are
  * taken from the workspace as an earlier cp_attn_bwd or cp_attn_bwd_rows_ready call
  * left them, instead of being recomputed.  The caller guarantees that the workspace
@@ -179,7 +189,9 @@ cp_status_t cp_attn_check_args(const cp_attn_args_t* args, int32_t* flags, hipSt
  *   acc' = acc * e^(lse_acc - lse') + blk * e^(lse_blk - lse')
  * A part whose lse is -inf has weight 0 (both -inf gives acc' = 0, lse' = -inf).
  * out_acc [B,S,H,D] float32 (read and written), lse_acc [B,H,S] float32 (read and
- * written), out_blk [B,S,H,D] of blk_dtype, lse_blk [B,H,S] float32.
+ * written), out_blk [B,S,H,D] of blk_dtype, lse_blk [B,H,S] float32.  The two
+ * written buffers (out_acc, lse_acc) may overlap neither each other nor either
+ * read-only buffer (out_blk, lse_blk): CP_ERR_ALIAS.
  * CP_ERR_UNSUPPORTED when out_acc holds 32 GiB or more (B*S*H*D/4 >= 2^31 - 512
  * 16-byte vectors: the kernel indexes with 32-bit integers).
  */

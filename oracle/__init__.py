@@ -16,7 +16,7 @@ Everything is a plain, slow restatement of what the pages define, in float64:
   transpose / exchange steps of the handbook, for all ranks at once; kv-head
   replication beyond the kv head count and the Ulysses x ring hybrid (USP).
 * ``zigzag`` — the 2P-chunk zigzag (dual-chunk-swap) and the striped partitions,
-  their reorders, the automatic choice between them and the causal work counts.
+  their reorders and the causal work counts.
 * ``ring`` — ring attention per rank (forward and blockwise backward).
 * ``padding`` — padding a sequence at its end to a multiple of the CP degree.
 
@@ -31,6 +31,6 @@ from .ulysses import (seq_to_head, head_to_seq, ulysses_relayout, ulysses_relayo
                       ulysses_relayout_inv_sum, usp_relayout, usp_relayout_inv, usp_attn)
 from .zigzag import (chunk_order, reorder, reorder_inv, rank_positions, rank_chunks,  # noqa: F401
                      work, visible_pairs, striped_order, reorder_striped, reorder_striped_inv,
-                     auto_strategy, DUAL_CHUNK_SWAP, STRIPED)
+                     DUAL_CHUNK_SWAP, STRIPED)
 from .ring import ring_fwd, ring_bwd, ring_block_counts  # noqa: F401
 from .padding import padded_length, pad_rows, pad_segments  # noqa: F401

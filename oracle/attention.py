@@ -14,7 +14,10 @@ Extensions (readings where the pages are silent):
   (Ring Attention)", §Description and the ``segment_pos`` commit): a key is visible
   only to queries of the same document.
 * Sliding window (HF PR "[distributed] Context parallel module, with Ulysses",
-  §Tests): a key is visible iff qpos - kpos < window (window 0 = none).
+  §Tests names it without defining it): a key is visible iff
+  0 <= qpos - kpos < window, the window most recent positions up to the query's own
+  (window 0 = none).  The lower bound holds with or without the causal flag, so a
+  window implies the causal rule.
 * Grouped query heads (handbook §Ulysses, degree bounded by the KV head count):
   query head h uses kv head h // (Hq / Hkv).
 * A row with no visible key: out = 0 and lse = -inf (the handbook's code would give
@@ -59,7 +62,8 @@ def visible_mask(qpos, kpos, causal=True, qseg=None, kseg=None, window=0):
     if qseg is not None:
         vis &= np.asarray(qseg)[:, None] == np.asarray(kseg)[None, :]
     if window:
-        vis &= (qpos[:, None] - kpos[None, :]) < window
+        d = qpos[:, None] - kpos[None, :]
+        vis &= (d >= 0) & (d < window)
     return vis
 
 

@@ -1,10 +1,11 @@
 """Padding a sequence at its end to a multiple of the context-parallel degree.
 
 Definition followed: transformers PR "[distributed] Context parallel module, with
-Ulysses", "What this PR brings" (ModelContextParallel) and the later note on it: a
-sequence length the CP size does not divide is padded at its end to a multiple of
-it before the masks are built; embeddings and the attention mask get zeros, the
-position ids continue those of the last document, and only real tokens count.
+Ulysses", "What this PR brings" (ModelContextParallel) and the later note on it.
+In short: each sequence is padded at its end up to a multiple of the CP degree
+before any mask exists; the padded embedding and mask entries are zero, pad
+positions carry on from the last document, and pad tokens are excluded from what
+is counted.
 
 Here: ``pad_rows`` appends zero (or ``fill``) rows along the sequence axis, or
 truncates; pad tokens sit at positions S, S+1, ... (the sequence simply continues);

@@ -15,9 +15,9 @@ needs every earlier KV chunk in full and its own chunk (the diagonal) half.
 Striped (reorder strategy 1 of the same MaxText PR, left undefined there beyond its
 name; the handbook mentions a striped partition as the alternative): token t goes to
 rank t mod P, so rank r holds positions r, r+P, r+2P, ...; as for the zigzag the
-reordered sequence is the ranks' shares in rank order.  The PR picks the strategy
-automatically from the packing configuration; the reading taken here is striped for
-packed sequences and dual-chunk-swap otherwise (``auto_strategy``).
+reordered sequence is the ranks' shares in rank order.  (The PR's automatic choice
+between the two strategies is a host policy, not arithmetic of the method; it is
+not part of this oracle.)
 
 Pins (tests/test_oracle.py, tests/golden/): work = [2,6,10,14] in order and
 [8,8,8,8] zigzag at P = 4; the exact visible-pair count of every zigzag rank at every
@@ -96,11 +96,6 @@ def reorder_striped_inv(y, P, axis=1):
         src[axis] = row
         out[tuple(idx)] = y[tuple(src)]
     return out
-
-
-def auto_strategy(packed):
-    """Reorder strategy picked automatically: striped for packed sequences."""
-    return STRIPED if packed else DUAL_CHUNK_SWAP
 
 
 def rank_positions(rank, P, S, layout):

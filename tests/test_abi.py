@@ -208,7 +208,12 @@ def test_merge_rejects():
     f = lib.cp_lse_merge
     assert f(1, 8, 2, 128, FAKE_A, FAKE_B, FAKE_C, 1 << 41, 9, None) == INVALID
     assert f(1, 8, 2, 12, FAKE_A, FAKE_B, FAKE_C, 1 << 41, 1, None) == UNSUPPORTED
-    assert f(1, 8, 2, 128, FAKE_A, FAKE_B, FAKE_A, 1 << 41, 1, None) == ALIAS
+    assert f(1, 8, 2, 128, FAKE_A, FAKE_B, FAKE_A, 1 << 41, 1, None) == ALIAS        # out_acc / out_blk
+    # every pair of a written buffer (out_acc, lse_acc) with another buffer is refused
+    assert f(1, 8, 2, 128, FAKE_A, FAKE_B, FAKE_C, FAKE_A + 256, 1, None) == ALIAS  # out_acc / lse_blk
+    assert f(1, 8, 2, 128, FAKE_A, FAKE_C + 64, FAKE_C, 1 << 41, 1, None) == ALIAS   # lse_acc / out_blk
+    assert f(1, 8, 2, 128, FAKE_A, FAKE_B, FAKE_C, FAKE_B + 16, 1, None) == ALIAS   # lse_acc / lse_blk
+    assert f(1, 8, 2, 128, FAKE_A, FAKE_A + 4096, FAKE_C, 1 << 41, 1, None) == ALIAS  # out_acc / lse_acc
     # 32 GiB of accumulator and beyond: 32-bit vector indices would overflow
     assert f(1, 1 << 21, 32, 128, FAKE_A, FAKE_B, FAKE_C, 1 << 41, 1, None) == UNSUPPORTED
     assert "32 GiB" in lib.cp_last_error().decode()

@@ -52,6 +52,22 @@ def check_rows(out, lse, ref_o, ref_l, tol_o, tol_l):
     assert max_err(out, ref_o) <= tol_o
 
 
+def grad_tol(ref):
+    return 1e-2 * max(1.0, float(np.abs(ref).max()))
+
+
+def causal_band_grads(qs, ks, vs, gs, j0, j1):
+    """Oracle dK, dV of keys [j0, j1) of a causal problem: only the rows at or after
+    j0 see them, each through its full-row (out, lse), so the oracle runs those rows'
+    forward against every key and their backward against the band's keys (the
+    blockwise form of the gradient, the oracle's ring backward)."""
+    rows = np.arange(j0, qs.shape[1])
+    ro, rl = oracle.attn_fwd(qs[:, rows], ks, vs, q_pos=rows)
+    _, bk, bv = oracle.attn_bwd(qs[:, rows], ks[:, j0:j1], vs[:, j0:j1], ro, rl, gs[:, rows], q_pos=rows,
+                                k_offset=j0)
+    return bk, bv
+
+
 # ------------------------------------------------------------------ toy (fp32)
 
 def test_toy_full_ring_ulysses_reorder(cp):
@@ -110,6 +126,7 @@ def test_toy_ring_backward(cp, layout):
 
 # ------------------------------------------------------------------ Ulysses llama2-7b, 32K, cp=16
 
+@pytest.mark.timeout(600)
 def test_ulysses_llama2_7b_32k(cp):
     P, S, H, D = 16, 32768, 32, 128
     say("ulysses llama2-7b: inputs")
@@ -144,10 +161,51 @@ def test_ulysses_llama2_7b_32k(cp):
     _, tk, tv = oracle.attn_bwd(qs[:, tail], ks, vs, to, tl, gs[:, tail], q_pos=tail)
     assert max_err(f64(dk)[:, tail], tk[:, tail]) <= 1e-2 * max(1.0, np.abs(tk[:, tail]).max())
     assert max_err(f64(dv)[:, tail], tv[:, tail]) <= 1e-2 * max(1.0, np.abs(tv[:, tail]).max())
+    # an interior band of keys, seen by the second half of the rows
+    say("ulysses llama2-7b: dk/dv of keys [16384, 16512)")
+    bk, bv = causal_band_grads(qs, ks, vs, gs, 16384, 16512)
+    assert max_err(f64(dk)[:, 16384:16512], bk) <= grad_tol(bk)
+    assert max_err(f64(dv)[:, 16384:16512], bv) <= grad_tol(bv)
     # every row's P sums to one: sum_j dV_j = sum_i dO_i
     sdv = f64(dv).sum(axis=1)
     sdo = gs.sum(axis=1)
     assert max_err(sdv, sdo) <= 1e-2 * max(1.0, np.abs(sdo).max())
+
+
+@pytest.mark.timeout(600)
+def test_ulysses_step_all_ranks(cp):
+    """The benchmark's timed step (drivers.UlyssesStep, buffers reused): all 16 ranks'
+    outputs and gradients after the inverse relayouts, in the global sequence layout,
+    on sampled query rows (out, lse, dq, all 32 heads) and on the last 256 keys (dk,
+    dv, all heads), and sum_j dV_j = sum_i dO_i on every head."""
+    P, S, H, D = 16, 32768, 32, 128
+    say("ulysses step: inputs")
+    q, k, v, do = cp_inputs.normal_tensors([(1, S, H, D)] * 4, seed=0)
+    stack = [t.reshape(P, 1, S // P, H, D).cuda() for t in (q, k, v, do)]
+    step = cp.drivers.UlyssesStep(*stack, P)
+    step.run()
+    step.run()   # the second pass reuses every buffer of the first
+    torch.cuda.synchronize()
+    out = f64(step.out).reshape(1, S, H, D)
+    dq, dk, dv = (f64(t).reshape(1, S, H, D) for t in (step.dq, step.dk, step.dv))
+    lse = f64(step.lse)   # [P][1][H/P][S]: rank p holds heads [2p, 2p + 2)
+    lse = lse.transpose(1, 0, 2, 3).reshape(1, H, S)
+    qf, kf, vf, gf = (f64(t) for t in (q, k, v, do))
+    say("ulysses step: oracle on sampled rows, all heads")
+    rows = np.unique(np.r_[0, 1, 2047, 2048, 2049, 9000, 16383, 16384, 30000, np.arange(S - 8, S)])
+    ro, rl = oracle.attn_fwd(qf[:, rows], kf, vf, q_pos=rows)
+    check_rows(out[:, rows], lse[:, :, rows], ro, rl, 1e-2, 1e-3)
+    rq, _, _ = oracle.attn_bwd(qf[:, rows], kf, vf, ro, rl, gf[:, rows], q_pos=rows)
+    assert max_err(dq[:, rows], rq) <= grad_tol(rq)
+    say("ulysses step: dk/dv of the last 256 keys, all heads")
+    tail = np.arange(S - 256, S)
+    to, tl = oracle.attn_fwd(qf[:, tail], kf, vf, q_pos=tail)
+    _, tk, tv = oracle.attn_bwd(qf[:, tail], kf[:, tail], vf[:, tail], to, tl, gf[:, tail], q_pos=tail,
+                                k_offset=S - 256)
+    assert max_err(dk[:, tail], tk) <= grad_tol(tk)
+    assert max_err(dv[:, tail], tv) <= grad_tol(tv)
+    sdo = gf.sum(axis=1)
+    assert max_err(dv.sum(axis=1), sdo) <= grad_tol(sdo)
 
 
 # ------------------------------------------------------------------ ring llama2-7b, 32K, cp=16
@@ -199,6 +257,7 @@ def test_ring_and_usp_long_blocks(cp):
 
 # ------------------------------------------------------------------ Ulysses llama3.1-8b GQA, 64K, cp=4
 
+@pytest.mark.timeout(600)
 def test_ulysses_llama31_8b_64k_gqa(cp):
     P, S, Hq, Hkv, D = 4, 65536, 32, 8, 128
     say("ulysses llama3.1-8b: inputs")
@@ -229,13 +288,18 @@ def test_ulysses_llama31_8b_64k_gqa(cp):
     # group sums: sum_j dV[j, g] = sum over the group's 4 heads of sum_i dO
     sdo = gs.reshape(1, S, 2, 4, D).sum(axis=(1, 3))
     assert max_err(f64(dv).sum(axis=1), sdo) <= 1e-2 * max(1.0, np.abs(sdo).max())
+    # an interior band of keys of kv head 0 (its group: query heads 0-3)
+    say("ulysses llama3.1-8b: dk/dv of keys [57344, 57472), kv head 0")
+    bk, bv = causal_band_grads(qs[:, :, 0:4], ks[:, :, 0:1], vs[:, :, 0:1], gs[:, :, 0:4], 57344, 57472)
+    assert max_err(f64(dk)[:, 57344:57472, 0:1], bk) <= grad_tol(bk)
+    assert max_err(f64(dv)[:, 57344:57472, 0:1], bv) <= grad_tol(bv)
     say("ulysses llama3.1-8b: dual-chunk-swap reorder of 64K tokens")
     ids = torch.arange(S, dtype=torch.int32)[None].cuda()
     z = cp.zigzag_reorder(ids, P)
     np.testing.assert_array_equal(bits(z), oracle.reorder(bits(ids), P))
     x = torch.randn(1, S, 4096).bfloat16().cuda()
     y = cp.zigzag_reorder(x, P)
-    np.testing.assert_array_equal(bits(y[:, :, :64]), oracle.reorder(bits(x[:, :, :64]), P))
+    np.testing.assert_array_equal(bits(y), oracle.reorder(bits(x), P))   # all 512 MiB
     assert torch.equal(cp.zigzag_reorder(y, P, inverse=True), x)
 
 
@@ -279,24 +343,53 @@ def test_packed_window_small_all_elements(cp, strategy):
         assert max_err(f64(got), ref) <= 1e-2 * max(1.0, np.abs(ref).max())
 
 
+@pytest.mark.timeout(600)
 def test_packed_window_8k(cp):
+    """The packed + windowed workload at its full size, all 4 ranks: every output row
+    and every element of dq, dk and dv against the oracle.  Documents never see each
+    other, so the oracle runs per document (the oracle's packed = per-document
+    property)."""
     S, Hq, Hkv, D, P, W = 8192, 32, 8, 128, 4, 4096
     lens = cp_inputs.doc_lengths(S)
     say(f"packed+window 8K: docs {lens}")
     (q, k, v, do, seg), outs, lses, grads = _packed_ring(cp, S, Hq, Hkv, D, P, W, lens)
-    m = dict(window=W)
-    segn = seg.numpy()[0]
-    for r in range(P):
-        pos = oracle.rank_positions(r, P, S, "zigzag")
-        pick = np.r_[0, 1, 100, 1023, 1024, 1025, 2047]
-        qr = f64(q)[:, pos[pick]]
-        ro, rl = oracle.attn_fwd(qr, k, v, q_pos=pos[pick], q_seg=segn[pos[pick]][None], k_seg=segn[None], **m)
-        check_rows(f64(outs[r])[:, pick], f64(lses[r])[:, :, pick], ro, rl, 1e-2, 1e-3)
-    # per document and kv head: sum of dV over the document's keys = sum of dO over its queries
-    dv = f64(grads[2])
-    gs = f64(do).reshape(1, S, Hkv, Hq // Hkv, D).sum(axis=3)
+    qf, kf, vf, gf = (f64(t) for t in (q, k, v, do))
+    ro, rl = np.zeros(qf.shape), np.full((1, Hq, S), -np.inf)
+    rdq, rdk, rdv = np.zeros(qf.shape), np.zeros(kf.shape), np.zeros(vf.shape)
     s0 = 0
     for n in lens:
-        ref = gs[:, s0:s0 + n].sum(axis=1)
-        assert max_err(dv[:, s0:s0 + n].sum(axis=1), ref) <= 1e-2 * max(1.0, np.abs(ref).max())
+        d = slice(s0, s0 + n)
+        o, l = oracle.attn_fwd(qf[:, d], kf[:, d], vf[:, d], q_offset=s0, k_offset=s0, window=W)
+        ro[:, d], rl[:, :, d] = o, l
+        rdq[:, d], rdk[:, d], rdv[:, d] = oracle.attn_bwd(qf[:, d], kf[:, d], vf[:, d], o, l, gf[:, d],
+                                                           q_offset=s0, k_offset=s0, window=W)
         s0 += n
+    say("packed+window 8K: oracle done")
+    for r in range(P):
+        pos = oracle.rank_positions(r, P, S, "zigzag")
+        check_rows(f64(outs[r]), f64(lses[r]), ro[:, pos], rl[:, :, pos], 1e-2, 1e-3)
+    for got, ref in zip(grads, (rdq, rdk, rdv)):
+        assert max_err(f64(got), ref) <= grad_tol(ref)
+
+
+# ------------------------------------------------------------------ the step's kernels, every element
+
+@pytest.mark.timeout(600)
+def test_dense_causal_multiblock_all_elements(cp):
+    """The kernel instances of the Ulysses step (one query head per kv head, causal,
+    no window or segment ids; the forward's two-workgroup key split) on a smaller
+    sequence: 8192 tokens = 32 key blocks of the backward, 64 query tiles of the
+    forward per head; out, lse, dq, dk, dv compared on every element."""
+    S, H, D = 8192, 2, 128
+    q, k, v, do = cp_inputs.normal_tensors([(1, S, H, D)] * 4, seed=11)
+    qd, kd, vd, gd = (t.cuda() for t in (q, k, v, do))
+    assert cp.fwd_workspace(qd, kd) is not None    # the split forward runs here
+    o, l = cp.attn_fwd(qd, kd, vd)
+    dq, dk, dv = cp.attn_bwd(qd, kd, vd, o, l, gd)
+    torch.cuda.synchronize()
+    say("dense 8K: oracle")
+    ro, rl = oracle.attn_fwd(q, k, v)
+    check_rows(f64(o), f64(l), ro, rl, 1e-2, 1e-3)
+    refs = oracle.attn_bwd(q, k, v, ro, rl, do)
+    for got, ref in zip((dq, dk, dv), refs):
+        assert max_err(f64(got), ref) <= grad_tol(ref)

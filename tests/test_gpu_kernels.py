@@ -253,8 +253,8 @@ CASES = {
         q_pos=np.r_[np.arange(0, 128), np.arange(896, 1024)], k_pos=np.r_[np.arange(384, 512), np.arange(512, 640)])),
     "packed_window": (1, 520, 520, 4, 2, lambda Sq, Sk: dict(seg=[37, 150, 90, 243], window=64)),
     "empty_rows": (1, 130, 190, 2, 1, lambda Sq, Sk: dict(q_offset=0, k_offset=64)),
-    # a window without the causal mask: every later key is visible, earlier ones only
-    # within the window (qpos - kpos < 37)
+    # a window with the causal flag off: the window bounds qpos - kpos on both sides
+    # (0 <= qpos - kpos < 37), so later keys stay hidden
     "noncausal_window": (1, 210, 260, 2, 1, lambda Sq, Sk: dict(causal=False, window=37, q_offset=40)),
     # a window of 1: each row sees only the key at its own position
     "window_1": (1, 150, 150, 2, 2, lambda Sq, Sk: dict(window=1)),
