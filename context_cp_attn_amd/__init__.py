@@ -17,7 +17,7 @@ torch provides device memory and the stream; nothing here computes on the CPU.
 """
 
 from ._lib import CpError, load as load_library  # noqa: F401
-from .ops import (attn_fwd, attn_fwd_merge, attn_bwd, lse_merge, ulysses_relayout,  # noqa: F401
+from .ops import (attn_fwd, attn_fwd_merge, attn_bwd, attn_bwd_noalloc, lse_merge, ulysses_relayout,  # noqa: F401
                   ulysses_relayout_inv, ulysses_relayout_ex, zigzag_reorder, pad_rows, bwd_workspace,
                   check_attn_args, fwd_workspace)
 from . import drivers  # noqa: F401

@@ -13,6 +13,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcp_attn.
 
 CP_OK, CP_ERR_INVALID, CP_ERR_UNSUPPORTED, CP_ERR_ALIAS, CP_ERR_HIP = range(5)
 CP_DTYPE_BF16, CP_DTYPE_F32 = 0, 1
+# scratch bytes of cp_attn_bwd_noalloc per device (CP_ATTN_BWD_NOALLOC_MAX_BYTES)
+CP_ATTN_BWD_NOALLOC_MAX_BYTES = 32 << 20
 
 # (name, restype, argtypes) of every exported entry point
 c_i64, c_i32, c_vp, c_f = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
@@ -50,6 +52,8 @@ SIGNATURES = {
                             c_vp, c_i32, c_vp, ctypes.c_size_t, c_vp]),
     "cp_attn_bwd_rows_ready": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                             c_vp, c_i32, c_vp, ctypes.c_size_t, c_vp]),
+    "cp_attn_bwd_noalloc": (c_i32, [ctypes.POINTER(AttnArgs), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                    c_vp, c_i32, c_vp]),
     "cp_lse_merge": (c_i32, [c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp]),
     "cp_ulysses_relayout": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp]),
     "cp_ulysses_relayout_inv": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_vp]),

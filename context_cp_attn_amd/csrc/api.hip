@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "cp_attn.h"
@@ -366,6 +367,65 @@ cp_status_t cp_attn_bwd_rows_ready(const cp_attn_args_t* a, const void* q, const
                                    float* dv, int32_t accumulate, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream) {
   return bwd_impl(a, q, k, v, out, lse, dout, dq, dk, dv, accumulate, workspace, workspace_bytes, true, stream);
+}
+
+}  // extern "C"
+
+// ---- allocation-free backward ---------------------------------------------------
+// The scratch memory of cp_attn_bwd_noalloc: a file-scope device array, one copy per
+// device, alive until the process ends.  Host code never passes the array's name to
+// a kernel (on the host it names a stand-in, not device memory): the device address
+// of each device's copy is looked up once per device and kept.
+static __device__ __align__(256) uint8_t scratch[CP_ATTN_BWD_NOALLOC_MAX_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+// Device address of the current device's copy of scratch (looked up on the first
+// call on that device, with it current).
+cp_status_t scratch_of_current_device(void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CP_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p || !aligned(p, 256)) return fail(CP_ERR_HIP, "hipGetSymbolAddress(scratch) gave an unusable address");
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return CP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cp_status_t cp_attn_bwd_noalloc(const cp_attn_args_t* a, const void* q, const void* k, const void* v,
+                                const void* out, const float* lse, const void* dout, float* dq, float* dk,
+                                float* dv, int32_t accumulate, hipStream_t stream) {
+  cp::AttnProblem p;
+  cp_status_t st = check_attn(a, q, k, v, &p);
+  if (st != CP_OK) return st;
+  const size_t need = cp_attn_bwd_workspace_size(a);
+  if (need > size_t(CP_ATTN_BWD_NOALLOC_MAX_BYTES))
+    return fail(CP_ERR_UNSUPPORTED,
+                "this backward needs %zu bytes of scratch; the allocation-free entry point holds %zu "
+                "(use cp_attn_bwd with a caller-owned workspace)",
+                need, size_t(CP_ATTN_BWD_NOALLOC_MAX_BYTES));
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != CP_OK) return st;
+  // every kernel of the backward writes the scratch bytes it later reads (row
+  // arrays, head-split partials): nothing has to start at zero
+  return bwd_impl(a, q, k, v, out, lse, dout, dq, dk, dv, accumulate, ws, size_t(CP_ATTN_BWD_NOALLOC_MAX_BYTES),
+                  false, stream);
 }
 
 cp_status_t cp_lse_merge(int64_t batch, int64_t seqlen, int64_t heads, int64_t head_dim,

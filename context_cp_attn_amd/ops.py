@@ -180,6 +180,10 @@ def attn_bwd(q, k, v, out, lse, dout, *, dq=None, dk=None, dv=None, accumulate=F
     dq = torch.empty(q.shape, **f32) if dq is None else _dev(dq, "dq", torch.float32)
     dk = torch.empty(k.shape, **f32) if dk is None else _dev(dk, "dk", torch.float32)
     dv = torch.empty(v.shape, **f32) if dv is None else _dev(dv, "dv", torch.float32)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("dq, dk, dv must be shaped like q, k, v")
+    if out.shape != q.shape or dout.shape != q.shape or lse.shape != (q.shape[0], q.shape[2], q.shape[1]):
+        raise ValueError("out/dout must be shaped like q and lse [B,Hq,Sq]")
     lib = _lib.load()
     need = lib.cp_attn_bwd_workspace_size(ctypes.byref(a))
     if rows_ready and workspace is None:
@@ -191,6 +195,28 @@ def attn_bwd(q, k, v, out, lse, dout, *, dq=None, dk=None, dv=None, accumulate=F
                                out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
                                dk.data_ptr(), dv.data_ptr(), int(bool(accumulate)),
                                workspace.data_ptr(), workspace.numel(), _stream()))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, out, lse, dout, dq, dk, dv, *, accumulate=False, **mask):
+    """attn_bwd into the caller's dq, dk, dv with the library's own device scratch
+    (cp_attn_bwd_noalloc): no device memory is allocated, here or in the library.
+    Calls that may overlap on one device race on that scratch."""
+    _check_qkv(q, k, v)
+    _dev(out, "out", q.dtype)
+    _dev(dout, "dout", q.dtype)
+    _dev(lse, "lse", torch.float32)
+    for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _dev(t, n, torch.float32)
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} must be shaped like {n[1]} {tuple(ref.shape)}, got {tuple(t.shape)}")
+    if out.shape != q.shape or dout.shape != q.shape or lse.shape != (q.shape[0], q.shape[2], q.shape[1]):
+        raise ValueError("out/dout must be shaped like q and lse [B,Hq,Sq]")
+    a = make_args(q, k, **mask)
+    _debug_check(q, k, mask)
+    _lib.check(_lib.load().cp_attn_bwd_noalloc(ctypes.byref(a), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                               out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                               dk.data_ptr(), dv.data_ptr(), int(bool(accumulate)), _stream()))
     return dq, dk, dv
 
 

@@ -172,6 +172,24 @@ cp_status_t cp_attn_bwd_rows_ready(const cp_attn_args_t* args, const void* q, co
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Allocation-free cp_attn_bwd, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same backward and kernels, with the workspace taken from a
+ * scratch array that the library holds on every device it runs on until the
+ * process ends (CP_ATTN_BWD_NOALLOC_MAX_BYTES per device), so the caller passes
+ * inputs and outputs only.  Arguments, results and errors as cp_attn_bwd, plus
+ * CP_ERR_UNSUPPORTED when cp_attn_bwd_workspace_size(args) exceeds that size.
+ * Every call on a device shares that device's scratch, which keeps the last call's
+ * contents: calls that can overlap in time on one device (other streams, other
+ * host threads) race and must not be issued; calls ordered on one stream are safe.
+ * No part of the scratch has to start at zero.  Nothing is allocated or freed.
+ */
+#define CP_ATTN_BWD_NOALLOC_MAX_BYTES (32u << 20)
+cp_status_t cp_attn_bwd_noalloc(const cp_attn_args_t* args, const void* q, const void* k, const void* v,
+                                const void* out, const float* lse, const void* dout,
+                                float* dq, float* dk, float* dv, int32_t accumulate, hipStream_t stream);
+
+/*
  * Debug check of the preconditions on args' arrays that the attention kernels rely
  * on but the host cannot see: q_pos / k_pos strictly increasing and >= 0 (the block
  * positions of [H] §"Ring Attention"), q_seg / k_seg non-decreasing along each of the

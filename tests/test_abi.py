@@ -178,6 +178,20 @@ def test_attn_bwd_workspace_and_alias():
     assert st == ALIAS
 
 
+def test_attn_bwd_noalloc_rejects():
+    """Host-side checks of the allocation-free backward: argument errors as
+    cp_attn_bwd, and problems whose workspace exceeds the scratch the library holds
+    (the llama3.1-8b 64K share with its head-split partials) are refused before any
+    device work."""
+    lib = _lib.load()
+    base = [FAKE_A, FAKE_B, FAKE_C, 1 << 41, 1 << 42, 1 << 43, 1 << 44, 1 << 45, 1 << 46]
+    assert lib.cp_attn_bwd_noalloc(ctypes.byref(args(heads_kv=3)), *base, 0, None) == INVALID
+    big = args(seqlen_q=65536, seqlen_k=65536, heads_q=8, heads_kv=2, head_dim=128)
+    assert lib.cp_attn_bwd_workspace_size(ctypes.byref(big)) > _lib.CP_ATTN_BWD_NOALLOC_MAX_BYTES
+    assert lib.cp_attn_bwd_noalloc(ctypes.byref(big), *base, 0, None) == UNSUPPORTED
+    assert "scratch" in lib.cp_last_error().decode()
+
+
 def test_relayout_rejects():
     lib = _lib.load()
     f = lib.cp_ulysses_relayout
