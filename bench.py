@@ -60,6 +60,7 @@ def parse():
     ap.add_argument("--leg", choices=["ring", "reorder", "gqa64k", "packed", "usp"],
                     help="run only this leg and print its JSON (for profilers; no step, no value)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-relayout", action="store_true", help="skip the per-direction relayout timings")
     ap.add_argument("--profile-copy", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device copy (read 1 GiB + write 1 GiB) "
                          "that calibrates the FETCH_SIZE / WRITE_SIZE counters")
@@ -113,6 +114,58 @@ def timed(torch, fn, reps):
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / reps
+
+
+def frac(x, peak):
+    return round(x / peak, 4)
+
+
+def relayout_directions(torch, cp, step, cp_inputs, reps=20):
+    """Each relayout direction alone: one launch per rep, the 256 MB last-level cache
+    flushed before it by writing a 1 GiB buffer, HIP events around the launch on the
+    launch stream; median and min over the reps.  Bytes = one read + one write of
+    the tensor."""
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    us = step.step
+
+    def one(fn, nbytes):
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e))
+        ts.sort()
+        med, mn = ts[len(ts) // 2], ts[0]
+        gb_med, gb_max = nbytes / (med * 1e-3) / 1e9, nbytes / (mn * 1e-3) / 1e9
+        return {"bytes": nbytes, "median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                "gbps_median": round(gb_med, 1), "gbps_best": round(gb_max, 1),
+                "frac_median": frac(gb_med, PEAK_HBM_GBPS), "frac_best": frac(gb_max, PEAK_HBM_GBPS)}
+
+    P = step.P
+    qs = us.stack[0]
+    out = {
+        "seq_to_head_bf16_llama2_7b_cp16": one(lambda: cp.ulysses_relayout(qs, P, out=us.ql), 2 * qs.numel() * 2),
+        "head_to_seq_bf16_llama2_7b_cp16": one(lambda: cp.ulysses_relayout_inv(us.ol, P, out=us.out),
+                                               2 * us.ol.numel() * 2),
+        "head_to_seq_f32_llama2_7b_cp16": one(lambda: cp.ulysses_relayout_inv(us.dql, P, out=us.dq),
+                                              2 * us.dql.numel() * 4),
+    }
+    # the llama3.1-8b 64K Ulysses share (cp=4): q [4][1,16384,32,128] -> [4][1,65536,8,128],
+    # k [4][1,16384,8,128] -> [4][1,65536,2,128]
+    S, P4, D = 65536, 4, 128
+    for name, H in (("q", 32), ("kv", 8)):
+        (x,) = cp_inputs.normal_tensors([(P4, 1, S // P4, H, D)], seed=1)
+        x = x.cuda()
+        y = torch.empty(P4, 1, S, H // P4, D, device="cuda", dtype=x.dtype)
+        out[f"seq_to_head_bf16_llama31_8b_64k_cp4_{name}"] = one(lambda: cp.ulysses_relayout(x, P4, out=y),
+                                                                 2 * x.numel() * 2)
+        del x, y
+    del flush
+    return out
 
 
 def packed_work(seg, P, layout, window, D):
@@ -173,13 +226,20 @@ def legs(torch, cp, cp_inputs, only=None):
         with cp._lib.KernelTrace() as tr:
             ms_f = timed(torch, ring_f.forward, 5)
         fm_ms, n_fm = tr.results.get("attn_fwd_merge_mfma", (0.0, 1))
+        fm_tf = fl / P / (fm_ms / n_fm) / 1e9    # one step's pairs: the pass's over P steps
+        mg_gb = merge_bytes / (mg_ms / n_mg) / 1e6
         out["ring_llama2_7b_32k_cp16_rank0"] = {
             "fused_ms_per_pass": round(ms_f, 4), "fused_tflops": round(fl / ms_f / 1e9, 2),
+            "fused_frac": frac(fl / ms_f / 1e9, PEAK_BF16_TFLOPS),
             "attn_fwd_merge_mfma_avg_ms": round(fm_ms / n_fm, 5),
+            "attn_fwd_merge_mfma_tflops": round(fm_tf, 2), "attn_fwd_merge_mfma_frac": frac(fm_tf, PEAK_BF16_TFLOPS),
+            "kernel_time_frac_of_pass": round(fm_ms / 5 / ms_f, 4),
             "unfused_ms_per_pass": round(ms, 4), "unfused_tflops": round(fl / ms / 1e9, 2),
+            "unfused_frac": frac(fl / ms / 1e9, PEAK_BF16_TFLOPS),
             "attn_fwd_mfma_avg_ms": round(fwd_ms / n_fwd, 5),
             "lse_merge_avg_ms": round(mg_ms / n_mg, 5),
-            "lse_merge_gbps": round(merge_bytes / (mg_ms / n_mg) / 1e6, 1)}
+            "lse_merge_gbps": round(mg_gb, 1), "lse_merge_frac": frac(mg_gb, PEAK_HBM_GBPS),
+            "flop_per_pass": f"4*D*H*(2*P*c^2 + c), c = S/(2P): {fl:.4e}"}
         del qz, kz, vz, ring, ring_f
     if only in (None, 'reorder'):
         # dual-chunk-swap reorder of 64K tokens into 8 chunks: [1,65536,4096] bf16 (512 MiB)
@@ -189,8 +249,9 @@ def legs(torch, cp, cp_inputs, only=None):
         with cp._lib.KernelTrace() as tr:
             timed(torch, lambda: cp.zigzag_reorder(x, 4, out=y), 10)
         zms, zn = tr.results["zigzag_reorder"]
-        out["reorder_64k_4096_bf16_cp4"] = {"avg_ms": round(zms / zn, 5),
-                                            "gbps": round(2 * x.numel() * 2 / (zms / zn) / 1e6, 1)}
+        zgb = 2 * x.numel() * 2 / (zms / zn) / 1e6
+        out["reorder_64k_4096_bf16_cp4"] = {"avg_ms": round(zms / zn, 5), "gbps": round(zgb, 1),
+                                            "frac": frac(zgb, PEAK_HBM_GBPS)}
         del x, y
     if only in (None, 'gqa64k'):
         # Ulysses rank share of llama3.1-8b at 64K (cp=4): q [1,65536,8,128], k/v [1,65536,2,128]
@@ -214,8 +275,11 @@ def legs(torch, cp, cp_inputs, only=None):
         b_ms = tr.results["attn_bwd_mfma"][0] / tr.results["attn_bwd_mfma"][1]
         out["ulysses_llama31_8b_64k_cp4_rank_fwd_bwd"] = {
             "ms_per_pass": round(ms, 3), "tflops": round(3 * ff / ms / 1e9, 2),
+            "frac": frac(3 * ff / ms / 1e9, PEAK_BF16_TFLOPS),
             "fwd_avg_ms": round(f_ms, 4), "fwd_tflops": round(ff / f_ms / 1e9, 2),
-            "bwd_avg_ms": round(b_ms, 4), "bwd_tflops": round(2 * ff / b_ms / 1e9, 2)}
+            "fwd_frac": frac(ff / f_ms / 1e9, PEAK_BF16_TFLOPS),
+            "bwd_avg_ms": round(b_ms, 4), "bwd_tflops": round(2 * ff / b_ms / 1e9, 2),
+            "bwd_frac": frac(2 * ff / b_ms / 1e9, PEAK_BF16_TFLOPS)}
         del q, k, v, do, o, l, bws, gq, gk, gv
     if only in (None, 'packed'):
         # packed + windowed ring share: 8K, 32 q / 8 kv heads, docs 256..4096, window 4096, cp=4,
@@ -245,7 +309,8 @@ def legs(torch, cp, cp_inputs, only=None):
             fl = 12 * D * Hq * pairs  # forward 4*D + backward 8*D per visible pair and head
             out[f"packed_window_8k_cp4_all_ranks_{name}"] = {
                 "strategy": layout, "ms_per_pass": round(ms, 3), "visible_pairs_per_head": pairs,
-                "tflops": round(fl / ms / 1e9, 2), "fwd_tiles_skipped_frac": round(skipped, 4)}
+                "tflops": round(fl / ms / 1e9, 2), "frac": frac(fl / ms / 1e9, PEAK_BF16_TFLOPS),
+                "fwd_tiles_skipped_frac": round(skipped, 4)}
     if only in (None, 'usp'):
         # beyond the kv head count, llama3.1-8b (32 q / 8 kv heads) at 16K tokens on 16 ranks:
         # Ulysses 8 within groups x ring 2 across them (USP), and Ulysses 16 with kv heads
@@ -256,13 +321,15 @@ def legs(torch, cp, cp_inputs, only=None):
         usp = lambda: cp.drivers.usp_forward(q, k, v, 2, 8)
         usp()
         ms = timed(torch, usp, 3)
-        out["usp_llama31_8b_16k_ulysses8_ring2_fwd"] = {"ms_per_pass": round(ms, 3), "tflops": round(fl / ms / 1e9, 2)}
+        out["usp_llama31_8b_16k_ulysses8_ring2_fwd"] = {"ms_per_pass": round(ms, 3), "tflops": round(fl / ms / 1e9, 2),
+                                                         "frac": frac(fl / ms / 1e9, PEAK_BF16_TFLOPS)}
         P = 16
         st = lambda t: t.reshape(P, 1, S // P, t.shape[2], D)
         uly = lambda: cp.drivers.ulysses_forward(st(q), st(k), st(v), P, kv_rep=2)
         uly()
         ms = timed(torch, uly, 3)
-        out["ulysses16_kv_rep2_llama31_8b_16k_fwd"] = {"ms_per_pass": round(ms, 3), "tflops": round(fl / ms / 1e9, 2)}
+        out["ulysses16_kv_rep2_llama31_8b_16k_fwd"] = {"ms_per_pass": round(ms, 3), "tflops": round(fl / ms / 1e9, 2),
+                                                        "frac": frac(fl / ms / 1e9, PEAK_BF16_TFLOPS)}
     return out
 
 
@@ -374,6 +441,8 @@ def main():
         "bwd_tflops_fa_convention_10D": round(step.flops_bwd_rank * 10 / 8 / (bwd_ms * 1e-3) / 1e12, 2),
         "relayout_gbps": round(step.relayout_bytes / (rel_t * 1e-3) / 1e9, 1),
         "relayout_pct_hbm_peak": round(100 * step.relayout_bytes / (rel_t * 1e-3) / 1e9 / PEAK_HBM_GBPS, 1),
+        "fwd_frac": frac(step.flops_fwd_rank / (fwd_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS),
+        "bwd_frac": frac(step.flops_bwd_rank / (bwd_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS),
         "roofline": roof,
         "kernels": kern,
     }
@@ -384,6 +453,8 @@ def main():
         dst_buf.copy_(src_buf)
         torch.cuda.synchronize()
         del src_buf, dst_buf
+    if not a.no_relayout:
+        res["relayout_directions"] = relayout_directions(torch, cp, step, cp_inputs)
     if not a.no_legs:
         res["legs"] = legs(torch, cp, cp_inputs)
     res["cpu_baseline"] = None if a.no_cpu else cpu_baseline(torch, cp_inputs, a.cpu_seconds)

@@ -17,9 +17,11 @@ output to sequence order.
 
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
-from . import ops
+from . import _lib, ops
 
 
 LAYOUT_OF_STRATEGY = {ops.DUAL_CHUNK_SWAP: "zigzag", ops.STRIPED: "striped"}
@@ -111,6 +113,7 @@ class RingShare:
         self.mask = dict(causal=causal, window=window, scale=scale)
         self.pos = [rank_positions(r, P, self.S, layout, q.device) for r in range(P)]
         self.ws = None
+        self._steps = None   # per-step C-ABI arguments of the pass, built on first use
 
     def _skip(self, src):
         # A contiguous causal block later than the rank's own sees nothing; the
@@ -124,6 +127,24 @@ class RingShare:
             m.update(q_seg=_block(self.seg, r, C).contiguous(), k_seg=_block(self.seg, src, C).contiguous())
         return m
 
+    def _step_args(self, ql):
+        """Per step of the pass: the validated argument struct, the key / value block
+        pointers and the source block, built once (every array they point to is held
+        here), so that a forward or backward pass costs its P library calls and no
+        per-step host work."""
+        if self._steps is None:
+            steps = []
+            for step in range(self.P):
+                src = (self.rank - step) % self.P
+                if self._skip(src):
+                    continue
+                kb, vb = _block(self.k, src, self.C), _block(self.v, src, self.C)
+                m = self._mask(src)
+                ops._check_qkv(ql, kb, vb)
+                steps.append((ops.make_args(ql, kb, **m), kb.data_ptr(), vb.data_ptr(), src, m))
+            self._steps = steps
+        return self._steps
+
     def forward(self):
         """(out [B,S/P,Hq,D] float32, lse [B,Hq,S/P]) of this rank after P steps."""
         r, C, P = self.rank, self.C, self.P
@@ -135,6 +156,12 @@ class RingShare:
         if fused is None:
             ws = split_workspace(ql, _block(self.k, r, C), **self._mask(r))
             fused = ws is False
+        if fused and not ops.DEBUG:
+            lib, stream = _lib.load(), ops._stream()
+            qp, ap, lp = ql.data_ptr(), acc.data_ptr(), lse.data_ptr()
+            for a, kp, vp, _, _ in self._step_args(ql):
+                _lib.check(lib.cp_attn_fwd_merge(ctypes.byref(a), qp, kp, vp, ap, lp, stream))
+            return acc, lse
         if not fused:
             blk_o = torch.empty(B, C, Hq, D, device=ql.device, dtype=ql.dtype)
             blk_l = torch.empty(B, Hq, C, device=ql.device, dtype=torch.float32)
@@ -159,6 +186,24 @@ class RingShare:
         # every step uses the rows' same out, lse and dout: the first call derives the
         # per-row values into the workspace, the later ones reuse them
         ws = ops.bwd_workspace(ql, _block(self.k, r, C), **self._mask(r))
+        if not ops.DEBUG and ql.shape[0] == 1:
+            # the pass's cached arguments; the buffers are checked once per call
+            B, _, Hq, D = ql.shape
+            for t, n, dt in ((out, "out", ql.dtype), (dout, "dout", ql.dtype), (dq, "dq", torch.float32),
+                             (lse, "lse", torch.float32), (dk, "dk", torch.float32), (dv, "dv", torch.float32)):
+                ops._dev(t, n, dt)
+            if out.shape != ql.shape or dout.shape != ql.shape or dq.shape != ql.shape or \
+                    lse.shape != (B, Hq, C) or dk.shape != self.k.shape or dv.shape != self.v.shape:
+                raise ValueError("backward buffers do not match the rank's shapes")
+            lib, stream = _lib.load(), ops._stream()
+            blk = C * self.k.shape[2] * D * 4   # bytes of one rank's block of dk / dv
+            fn = lib.cp_attn_bwd
+            for a, kp, vp, src, _ in self._step_args(ql):
+                _lib.check(fn(ctypes.byref(a), ql.data_ptr(), kp, vp, out.data_ptr(), lse.data_ptr(),
+                              dout.data_ptr(), dq.data_ptr(), dk.data_ptr() + src * blk, dv.data_ptr() + src * blk,
+                              1, ws.data_ptr(), ws.numel(), stream))
+                fn = lib.cp_attn_bwd_rows_ready
+            return dq, dk, dv
         ready = False
         for step in range(P):
             src = (r - step) % P

@@ -1,10 +1,14 @@
 """Run one attention kernel a few times on synthetic bf16 inputs, for profilers.
 
-    python -m context_cp_attn_amd.profile_kernels {fwd|bwd} [S,Hq,Hkv,D] [--iters N]
+    python -m context_cp_attn_amd.profile_kernels {fwd|bwd|ring} [S,Hq,Hkv,D] [--iters N]
 
 Intended under ``rocprofv3 --pmc ...`` or ``--kernel-trace``: the inputs are made
 on the device, the chosen kernel runs ``iters`` times (default 2), and nothing
-else of the library is launched in between.
+else of the library is launched in between.  ``fwd`` / ``bwd``: causal attention of
+batch 1 at the given shape (the forward splits its keys over two workgroups where
+cp_attn_fwd_workspace_size asks for it).  ``ring``: rank 0's pass of the fused ring
+step over S tokens in zigzag order with P = 16 ranks (q [1,S/16,Hq,D] against the
+16 key blocks), one pass per iteration.
 """
 
 from __future__ import annotations
@@ -18,7 +22,7 @@ from . import ops
 
 def main() -> None:
     ap = argparse.ArgumentParser()
-    ap.add_argument("which", choices=["fwd", "bwd"])
+    ap.add_argument("which", choices=["fwd", "bwd", "ring"])
     ap.add_argument("shape", nargs="?", default="65536,8,2,128", help="S,Hq,Hkv,D (causal, batch 1)")
     ap.add_argument("--iters", type=int, default=2)
     a = ap.parse_args()
@@ -27,6 +31,16 @@ def main() -> None:
     q = torch.randn(1, S, Hq, D, device="cuda", generator=g).mul_(0.5).bfloat16()
     k = torch.randn(1, S, Hkv, D, device="cuda", generator=g).mul_(0.5).bfloat16()
     v = torch.randn(1, S, Hkv, D, device="cuda", generator=g).mul_(0.5).bfloat16()
+    if a.which == "ring":
+        from . import drivers
+        P = 16
+        qz, kz, vz = (ops.zigzag_reorder(t, P) for t in (q, k, v))
+        share = drivers.RingShare(qz, kz, vz, P, 0, fused=True)
+        for i in range(a.iters):
+            share.forward()
+            torch.cuda.synchronize()
+            print(f"ring {S},{Hq},{Hkv},{D} pass {i} done", flush=True)
+        return
     out, lse = ops.attn_fwd(q, k, v)
     if a.which == "bwd":
         do = torch.randn(q.shape, device="cuda", generator=g).mul_(0.5).bfloat16()
