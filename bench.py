@@ -90,9 +90,10 @@ class StepWorkload:
     def __init__(self, torch, cp, cp_inputs):
         P, S, H, D = self.P, self.S, self.H, self.D
         q, k, v, do = cp_inputs.normal_tensors([(1, S, H, D)] * 4, seed=0)
-        # the global [1,S,H,D] sequence split into P contiguous slices = [P][1][S/P][H][D]
-        stack = [t.reshape(P, 1, S // P, H, D).to("cuda") for t in (q, k, v, do)]
-        self.step = cp.drivers.UlyssesStep(*stack, P)
+        # the global [1,S,H,D] sequence split into P contiguous slices = [P][1][S/P][H][D];
+        # q, k, v held together in one [3][P][1][S/P][H][D] buffer (a fused QKV projection's output)
+        qkv = torch.stack([t.reshape(P, 1, S // P, H, D) for t in (q, k, v)]).to("cuda")
+        self.step = cp.drivers.UlyssesStep(qkv, do.reshape(P, 1, S // P, H, D).to("cuda"), P)
         hp = H // P
         self.flops_fwd_rank = 4 * D * hp * pairs_causal(S)
         self.flops_bwd_rank = 8 * D * hp * pairs_causal(S)
@@ -146,13 +147,21 @@ def relayout_directions(torch, cp, step, cp_inputs, reps=20):
                 "frac_median": frac(gb_med, PEAK_HBM_GBPS), "frac_best": frac(gb_max, PEAK_HBM_GBPS)}
 
     P = step.P
-    qs = us.stack[0]
+    qs = us.qkv[0]
     out = {
-        "seq_to_head_bf16_llama2_7b_cp16": one(lambda: cp.ulysses_relayout(qs, P, out=us.ql), 2 * qs.numel() * 2),
+        # one tensor [16][1,2048,32,128] -> [16][1,32768,2,128] per launch
+        "seq_to_head_bf16_llama2_7b_cp16": one(lambda: cp.ulysses_relayout(qs, P, out=us.qkvl[0]),
+                                               2 * qs.numel() * 2),
         "head_to_seq_bf16_llama2_7b_cp16": one(lambda: cp.ulysses_relayout_inv(us.ol, P, out=us.out),
                                                2 * us.ol.numel() * 2),
-        "head_to_seq_f32_llama2_7b_cp16": one(lambda: cp.ulysses_relayout_inv(us.dql, P, out=us.dq),
-                                              2 * us.dql.numel() * 4),
+        "head_to_seq_f32_llama2_7b_cp16": one(lambda: cp.ulysses_relayout_inv(us.dqkvl[0], P, out=us.dqkv[0]),
+                                              2 * us.dqkvl[0].numel() * 4),
+        # q, k and v in one launch, as the step runs them (three groups of the general relayout)
+        "seq_to_head_bf16_qkv_llama2_7b_cp16": one(
+            lambda: cp.ulysses_relayout_ex(us.qkv, P, groups=3, out=us.qkvl), 2 * us.qkv.numel() * 2),
+        "head_to_seq_f32_dqkv_llama2_7b_cp16": one(
+            lambda: cp.ulysses_relayout_ex(us.dqkvl, P, groups=3, inverse=True, out=us.dqkv),
+            2 * us.dqkvl.numel() * 4),
     }
     # the llama3.1-8b 64K Ulysses share (cp=4): q [4][1,16384,32,128] -> [4][1,65536,8,128],
     # k [4][1,16384,8,128] -> [4][1,65536,2,128]

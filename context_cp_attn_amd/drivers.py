@@ -278,62 +278,62 @@ class UlyssesStep:
     """One Ulysses forward + backward pass of all P ranks with every buffer
     allocated once, so that repeated passes allocate nothing.
 
-    q_stack, k_stack, v_stack, dout_stack are [P][B][S/P][H][D] bf16 (rank s holds
-    sequence slice s, all heads; MHA, so q and k/v have the same head count).
-    ``run`` relayouts q, k, v to [P][B][S][H/P][D], runs rank p's attention forward
-    on its H/P heads over the whole sequence, returns the output to the sequence
-    layout (``out``), relayouts dout, runs every rank's backward and returns dq, dk,
-    dv (float32) to the sequence layout.  ``lse`` [P][B][H/P][S] keeps each rank's
-    row log-sum-exp.  The same sequence of calls as ``ulysses_forward`` +
-    ``ulysses_backward``, with the buffers reused.
+    qkv_stack [3][P][B][S/P][H][D] bf16 holds q, k and v in one buffer (rank s holds
+    sequence slice s, all heads; MHA, so the three have the same shape), dout_stack
+    [P][B][S/P][H][D].  ``run`` relayouts q, k and v to [3][P][B][S][H/P][D] in one
+    launch (three groups of the general relayout), runs rank p's attention forward on
+    its H/P heads over the whole sequence, returns the output to the sequence layout
+    (``out``), relayouts dout, runs every rank's backward into one [3][P][B][S][H/P][D]
+    float32 buffer and returns dq, dk, dv to the sequence layout in one launch
+    (``dqkv`` [3][P][B][S/P][H][D]).  ``lse`` [P][B][H/P][S] keeps each rank's row
+    log-sum-exp.  The same sequence of calls as ``ulysses_forward`` +
+    ``ulysses_backward``, with the buffers reused and q / k / v exchanged together.
     """
 
-    def __init__(self, q_stack, k_stack, v_stack, dout_stack, P: int, **mask):
-        P_, B, Sl, H, D = q_stack.shape
+    def __init__(self, qkv_stack, dout_stack, P: int, **mask):
+        if qkv_stack.dim() != 6 or qkv_stack.shape[0] != 3:
+            raise ValueError("qkv_stack must be [3][P][B][S/P][H][D]")
+        _, P_, B, Sl, H, D = qkv_stack.shape
         if P_ != P or H % P:
             raise ValueError(f"stack of {P_} ranks and {H} heads for degree {P}")
-        if tuple(k_stack.shape) != tuple(q_stack.shape):
-            raise ValueError("UlyssesStep takes MHA stacks (k/v shaped like q)")
+        if tuple(dout_stack.shape) != tuple(qkv_stack.shape[1:]):
+            raise ValueError("dout_stack must be shaped like q")
         self.P, self.mask = P, mask
-        self.stack = (q_stack, k_stack, v_stack, dout_stack)
-        dev, bf, f32 = q_stack.device, q_stack.dtype, torch.float32
+        self.qkv, self.dout_stack = qkv_stack, dout_stack
+        dev, bf, f32 = qkv_stack.device, qkv_stack.dtype, torch.float32
         S = Sl * P
         sh = (P, B, S, H // P, D)
-        self.ql, self.kl, self.vl, self.gl, self.ol = (torch.empty(sh, device=dev, dtype=bf) for _ in range(5))
+        self.qkvl = torch.empty((3,) + sh, device=dev, dtype=bf)
+        self.gl, self.ol = (torch.empty(sh, device=dev, dtype=bf) for _ in range(2))
         self.lse = torch.empty(P, B, H // P, S, device=dev, dtype=f32)
-        self.out = torch.empty(q_stack.shape, device=dev, dtype=bf)
-        self.dql, self.dkl, self.dvl = (torch.empty(sh, device=dev, dtype=f32) for _ in range(3))
-        self.dq, self.dk, self.dv = (torch.empty(q_stack.shape, device=dev, dtype=f32) for _ in range(3))
-        self.ws = ops.bwd_workspace(self.ql[0], self.kl[0], **mask)
-        self.fws = ops.fwd_workspace(self.ql[0], self.kl[0], **mask)   # None when the forward does not split
+        self.out = torch.empty(dout_stack.shape, device=dev, dtype=bf)
+        self.dqkvl = torch.empty((3,) + sh, device=dev, dtype=f32)
+        self.dqkv = torch.empty(qkv_stack.shape, device=dev, dtype=f32)
+        ql, kl = self.qkvl[0, 0], self.qkvl[1, 0]
+        self.ws = ops.bwd_workspace(ql, kl, **mask)
+        self.fws = ops.fwd_workspace(ql, kl, **mask)   # None when the forward does not split
 
     def forward(self):
-        P = self.P
-        qs, ks, vs, _ = self.stack
-        ops.ulysses_relayout(qs, P, out=self.ql)
-        ops.ulysses_relayout(ks, P, out=self.kl)
-        ops.ulysses_relayout(vs, P, out=self.vl)
+        P, (ql, kl, vl) = self.P, self.qkvl
+        ops.ulysses_relayout_ex(self.qkv, P, groups=3, out=self.qkvl)
         for p in range(P):
-            ops.attn_fwd(self.ql[p], self.kl[p], self.vl[p], out=self.ol[p], lse=self.lse[p], workspace=self.fws,
-                         **self.mask)
+            ops.attn_fwd(ql[p], kl[p], vl[p], out=self.ol[p], lse=self.lse[p], workspace=self.fws, **self.mask)
         ops.ulysses_relayout_inv(self.ol, P, out=self.out)
 
     def backward(self):
-        P = self.P
-        ops.ulysses_relayout(self.stack[3], P, out=self.gl)
+        P, (ql, kl, vl), (dql, dkl, dvl) = self.P, self.qkvl, self.dqkvl
+        ops.ulysses_relayout(self.dout_stack, P, out=self.gl)
         for p in range(P):
-            ops.attn_bwd(self.ql[p], self.kl[p], self.vl[p], self.ol[p], self.lse[p], self.gl[p],
-                         dq=self.dql[p], dk=self.dkl[p], dv=self.dvl[p], workspace=self.ws, **self.mask)
-        ops.ulysses_relayout_inv(self.dql, P, out=self.dq)
-        ops.ulysses_relayout_inv(self.dkl, P, out=self.dk)
-        ops.ulysses_relayout_inv(self.dvl, P, out=self.dv)
+            ops.attn_bwd(ql[p], kl[p], vl[p], self.ol[p], self.lse[p], self.gl[p],
+                         dq=dql[p], dk=dkl[p], dv=dvl[p], workspace=self.ws, **self.mask)
+        ops.ulysses_relayout_ex(self.dqkvl, P, groups=3, inverse=True, out=self.dqkv)
 
     def run(self):
         self.forward()
         self.backward()
 
 
-def usp_forward(q, k, v, Pr, Pu, kv_rep=1, seg=None, causal=True, window=0, scale=0.0):
+def usp_forward(q, k, v, Pr, Pu, kv_rep=1, seg=None, causal=True, window=0, scale=0.0, keep=False):
     """Ulysses within groups of Pu ranks x ring attention across Pr groups, all
     Pr*Pu ranks on one GPU.  q [1,S,Hq,D], k/v [1,S,Hkv,D] in sequence order.
 
@@ -342,7 +342,8 @@ def usp_forward(q, k, v, Pr, Pu, kv_rep=1, seg=None, causal=True, window=0, scal
     rank (r, u)); rank (r, u) then runs the ring over the groups' blocks of its head
     slice with the fused step (or attn_fwd + lse_merge where the forward splits the
     blocks' keys over two workgroups).  Returns (out [1,S,Hq,D] float32 in sequence order,
-    lse [Pr][Pu][1][Hq/Pu][S/Pr] per rank).
+    lse [Pr][Pu][1][Hq/Pu][S/Pr] per rank), and with ``keep`` also the state
+    ``usp_backward`` needs (the exchanged q, k, v and every rank's final output).
     """
     if q.shape[0] != 1:
         raise ValueError("usp_forward takes batch 1")
@@ -378,4 +379,50 @@ def usp_forward(q, k, v, Pr, Pu, kv_rep=1, seg=None, causal=True, window=0, scal
                     ops.lse_merge(acc[r, u], lse[r, u], blk_o, blk_l)
     back = ops.ulysses_relayout_ex(acc, Pu, groups=Pr, inverse=True)   # [Pr][Pu][1][Sl][Hq][D]
     out = ops.zigzag_reorder(back.view(1, S, back.shape[4], back.shape[5]), Pr, inverse=True)
+    if keep:
+        mask = dict(causal=causal, window=window, scale=scale)
+        return out, lse, dict(ql=ql, kl=kl, vl=vl, acc=acc, pos=pos, sz=sz, Pr=Pr, Pu=Pu, kv_rep=kv_rep, mask=mask)
     return out, lse
+
+
+def usp_backward(state, lse, dout):
+    """Gradients through the Ulysses x ring hybrid of ``usp_forward(..., keep=True)``.
+
+    dout [1,S,Hq,D] in sequence order (the forward's input dtype).  dout takes the
+    forward's path (zigzag reorder for the Pr groups, Ulysses exchange inside each
+    group); rank (r, u) runs the ring backward over the groups' blocks with its final
+    output and lse (dq accumulated over the steps, the partial dk / dv of block src
+    added onto that block); dq, dk, dv then take the inverse path (the exchange back,
+    the copies of replicated kv heads summed, the inverse reorder).  Returns (dq, dk,
+    dv) float32 [1,S,H,D] in sequence order.
+    """
+    ql, kl, vl, acc, pos, sz = (state[n] for n in ("ql", "kl", "vl", "acc", "pos", "sz"))
+    Pr, Pu, rep, mask = state["Pr"], state["Pu"], state["kv_rep"], state["mask"]
+    S = dout.shape[1]
+    Sr, Sl = S // Pr, S // (Pr * Pu)
+    gl = ops.ulysses_relayout_ex(ops.zigzag_reorder(dout, Pr).view(Pr, Pu, 1, Sl, dout.shape[2], dout.shape[3]),
+                                 Pu, groups=Pr)
+    out_l = acc.to(ql.dtype)   # every rank's final output, in the dtype the backward takes
+    dql = torch.zeros(ql.shape, device=dout.device, dtype=torch.float32)
+    dkl = torch.zeros(kl.shape, device=dout.device, dtype=torch.float32)
+    dvl = torch.zeros(vl.shape, device=dout.device, dtype=torch.float32)
+    for r in range(Pr):
+        for u in range(Pu):
+            ws, ready = None, False
+            for step in range(Pr):
+                src = (r - step) % Pr
+                m = dict(mask, q_pos=pos[r], k_pos=pos[src])
+                if sz is not None:
+                    m.update(q_seg=sz[:, r * Sr:(r + 1) * Sr].contiguous(),
+                             k_seg=sz[:, src * Sr:(src + 1) * Sr].contiguous())
+                if ws is None:
+                    ws = ops.bwd_workspace(ql[r, u], kl[src, u], **m)
+                ops.attn_bwd(ql[r, u], kl[src, u], vl[src, u], out_l[r, u], lse[r, u], gl[r, u], dq=dql[r, u],
+                             dk=dkl[src, u], dv=dvl[src, u], accumulate=True, workspace=ws, rows_ready=ready, **m)
+                ready = True
+
+    def back(t, rep_):
+        y = ops.ulysses_relayout_ex(t, Pu, groups=Pr, rep=rep_, inverse=True)   # [Pr][Pu][1][Sl][H][D]
+        return ops.zigzag_reorder(y.view(1, S, y.shape[4], y.shape[5]), Pr, inverse=True)
+
+    return back(dql, 1), back(dkl, rep), back(dvl, rep)

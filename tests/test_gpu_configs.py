@@ -174,20 +174,23 @@ def test_ulysses_llama2_7b_32k(cp):
 
 @pytest.mark.timeout(600)
 def test_ulysses_step_all_ranks(cp):
-    """The benchmark's timed step (drivers.UlyssesStep, buffers reused): all 16 ranks'
-    outputs and gradients after the inverse relayouts, in the global sequence layout,
+    """The benchmark's timed step (drivers.UlyssesStep: q, k, v relayouted together,
+    buffers reused): all 16 ranks' outputs and gradients after the inverse relayouts,
+    in the global sequence layout,
     on sampled query rows (out, lse, dq, all 32 heads) and on the last 256 keys (dk,
     dv, all heads), and sum_j dV_j = sum_i dO_i on every head."""
     P, S, H, D = 16, 32768, 32, 128
     say("ulysses step: inputs")
     q, k, v, do = cp_inputs.normal_tensors([(1, S, H, D)] * 4, seed=0)
-    stack = [t.reshape(P, 1, S // P, H, D).cuda() for t in (q, k, v, do)]
-    step = cp.drivers.UlyssesStep(*stack, P)
+    qkv = torch.stack([t.reshape(P, 1, S // P, H, D) for t in (q, k, v)]).cuda()
+    step = cp.drivers.UlyssesStep(qkv, do.reshape(P, 1, S // P, H, D).cuda(), P)
     step.run()
     step.run()   # the second pass reuses every buffer of the first
     torch.cuda.synchronize()
+    # the grouped relayout of q, k, v is the three single ones, bit for bit
+    np.testing.assert_array_equal(bits(step.qkvl[1]), oracle.ulysses_relayout(bits(k.reshape(P, 1, S // P, H, D))))
     out = f64(step.out).reshape(1, S, H, D)
-    dq, dk, dv = (f64(t).reshape(1, S, H, D) for t in (step.dq, step.dk, step.dv))
+    dq, dk, dv = (f64(t).reshape(1, S, H, D) for t in step.dqkv)
     lse = f64(step.lse)   # [P][1][H/P][S]: rank p holds heads [2p, 2p + 2)
     lse = lse.transpose(1, 0, 2, 3).reshape(1, H, S)
     qf, kf, vf, gf = (f64(t) for t in (q, k, v, do))
