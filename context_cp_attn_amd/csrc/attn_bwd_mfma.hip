@@ -685,7 +685,7 @@ struct BwdArgs {
 template <class C, bool kLane>
 __global__ __launch_bounds__(C::kThreads) void attn_bwd_kernel(BwdArgs a) {
   __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
-  const AttnProblem& p = a.p;
+  const AttnProblem p = specialize<kLane>(a.p);
   const int64_t N = int64_t(a.n_kv) + a.n_q;
   // Workgroups go to the 8 XCDs round-robin by index.  Within each round of 8
   // consecutive workgroups the items are rotated by the round number, so that the

@@ -449,27 +449,30 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
 }
 
 template <class C, bool kLane>
-__global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_mfma_kernel(AttnProblem p, const uint16_t* q,
+__global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_mfma_kernel(AttnProblem pa, const uint16_t* q,
                                                                        const uint16_t* k, const uint16_t* v,
                                                                        uint16_t* out, float* lse) {
   __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
+  const AttnProblem p = specialize<kLane>(pa);
   fwd_body<C, false, kLane>(p, q, k, v, out, nullptr, lse, smem);
 }
 
 template <class C, bool kLane>
-__global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_merge_mfma_kernel(AttnProblem p, const uint16_t* q,
+__global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_merge_mfma_kernel(AttnProblem pa, const uint16_t* q,
                                                                              const uint16_t* k,
                                                                              const uint16_t* v, float* acc,
                                                                              float* lse_acc) {
   __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
+  const AttnProblem p = specialize<kLane>(pa);
   fwd_body<C, true, kLane>(p, q, k, v, nullptr, acc, lse_acc, smem);
 }
 
 template <class C, bool kLane>
-__global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_split_kernel(AttnProblem p, const uint16_t* q,
+__global__ __launch_bounds__(C::kThreads, 2) void attn_fwd_split_kernel(AttnProblem pa, const uint16_t* q,
                                                                         const uint16_t* k, const uint16_t* v,
                                                                         float* part_o, float* part_l) {
   __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
+  const AttnProblem p = specialize<kLane>(pa);
   fwd_body<C, false, kLane>(p, q, k, v, nullptr, nullptr, nullptr, smem, part_o, part_l);
 }
 

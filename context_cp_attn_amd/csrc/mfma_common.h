@@ -104,6 +104,22 @@ CP_DEVICE int first_true(int lo, int hi, Pred&& pred) {
   return lo;
 }
 
+// The kernel instances without the one-tile-per-lane classification (kLane = false)
+// are launched only for problems with no window and no segment ids.  Their copy of
+// the problem says so at compile time, so that the code paths of windowed and
+// segmented problems (per-tile classification from span loads, segment compares)
+// are not compiled into them and take no registers there.
+template <bool kLane>
+CP_DEVICE AttnProblem specialize(const AttnProblem& p) {
+  AttnProblem r = p;
+  if constexpr (!kLane) {
+    r.window = 0;
+    r.q_seg = nullptr;
+    r.k_seg = nullptr;
+  }
+  return r;
+}
+
 // ---- buffer resources ---------------------------------------------------------------
 // A raw buffer resource over nbytes from base: loads past the end read as zeros in
 // hardware, so ragged tiles need neither selects nor 64-bit address arithmetic.
