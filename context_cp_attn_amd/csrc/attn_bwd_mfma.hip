@@ -103,6 +103,20 @@ struct BwdCfg {
   static constexpr int kLdsBytes = 2 * kStageMax + kSpanTiles * 16;
   using TileM = DmaTile<BM, D, kThreads>;
   using TileN = DmaTile<BN, D, kThreads>;
+  // paired dK / dV role (problems with no window, segment ids or position arrays):
+  // a workgroup owns 128 keys and walks query tiles of BMP rows; its stages hold the
+  // Q and dO rows, lse2 and delta of a tile, spaced like the other roles' stages,
+  // followed by the P buffer ([QBLKP][4 key blocks][2 fragments][64 lanes] x 16 B)
+  static constexpr int kPairKeys = 128;
+  static constexpr int BMP = 96;
+  static constexpr int QBLKP = BMP / 32;
+  static constexpr int kTileMP = BMP * D;
+  static constexpr int kStageP = 2 * kTileMP * 2 + 2 * BMP * 4;
+  static constexpr int kPBytes = QBLKP * 4 * 2 * 64 * 16;
+  static constexpr int kLdsPair = 2 * kStageMax + kPBytes;
+  using TileMP = DmaTile<BMP, D, kThreads>;
+  static_assert(kStageP <= kStageMax, "pair stages fit the stage spacing");
+  static_assert(kLdsPair <= 160 * 1024, "LDS of one workgroup");
   static_assert(BM <= kThreads && BN <= kThreads, "one thread per row of the small arrays");
 };
 
@@ -417,9 +431,238 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
     }
 }
 
+// Paired dK / dV role of problems with no window, no segment ids and no position
+// arrays (positions are offset + index).  A workgroup owns keys [j0, j0 + 128) of kv
+// head g; wavefronts w and w + 4 (w < 4) own the same 32 keys j0 + 32w + (0..31),
+// one per lane column: wavefront w accumulates dK, wavefront w + 4 dV.  For every
+// query tile of BMP = 96 rows (three 32-query blocks) of every head of the group:
+//   phase A: P = exp(S - lse) of the three blocks, S = Q K^T computed once per block
+//     and pair -- block 0 by the dK wavefront, blocks 1 and 2 by the dV wavefront --
+//     and written to LDS as the bf16 B fragments of the next products;
+//   phase B: the dK wavefront forms dP = dO V^T, dS = P (dP - Delta) and
+//     dK^T += Q^T dS, the dV wavefront dV^T += dO^T P, both reading P from LDS.
+// Each P (and each exponential) is computed once: 7 products per block pair of keys
+// and queries with the dQ role, where the separate dV and dK roles take 8 (both
+// recompute S).  The phases are separated by a workgroup barrier; in phase B two
+// wavefronts per SIMD multiply.
+template <class C>
+CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                         const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                         const float* __restrict__ lse2, const float* __restrict__ delta, float* __restrict__ dk,
+                         float* __restrict__ dv, int accumulate, uint8_t* smem, int kt, int g, int b) {
+  constexpr int BM = C::BMP, QB = C::QBLKP;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int pr = __builtin_amdgcn_readfirstlane(wave & 3);  // key block of the pair
+  const bool is_dv = __builtin_amdgcn_readfirstlane(wave >> 2) != 0;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int G = p.Hq / p.Hkv;
+  const int j0 = kt * C::kPairKeys;
+  const int wj0 = j0 + pr * 32;
+  const int64_t krs = int64_t(p.Hkv) * C::D;
+  const int64_t qrs = int64_t(p.Hq) * C::D;
+
+  const Span wg_k = k_span(p, b, j0, min(j0 + C::kPairKeys, p.Sk) - 1);
+  const bool wave_live = wj0 < p.Sk;
+  const Span wv_k = k_span(p, b, min(wj0, p.Sk - 1), min(wj0 + 32, p.Sk) - 1);
+
+  // K rows (both wavefronts: S) and V rows (dK wavefront: dP) of this lane's key as
+  // B fragments (k-slots = head dims)
+  const int key = min(wj0 + l32, p.Sk - 1);
+  const bool key_ok = wj0 + l32 < p.Sk;
+  bf16x8 kf[C::KS], vf[C::KS];
+  {
+    const uint16_t* kr = k + (int64_t(b) * p.Sk + key) * krs + int64_t(g) * C::D;
+    const uint16_t* vr = v + (int64_t(b) * p.Sk + key) * krs + int64_t(g) * C::D;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(kr + s * 16 + hi * 8);
+      kf[s] = __builtin_bit_cast(bf16x8, key_ok ? x : u32x4{0, 0, 0, 0});
+      if (!is_dv) {
+        const u32x4 y = *reinterpret_cast<const u32x4*>(vr + s * 16 + hi * 8);
+        vf[s] = __builtin_bit_cast(bf16x8, key_ok ? y : u32x4{0, 0, 0, 0});
+      }
+    }
+  }
+  const int my_kpos = p.k_offset + key;
+
+  f32x16 acc[C::DB];  // dK^T (dK wavefront) or dV^T (dV wavefront)
+#pragma unroll
+  for (int d = 0; d < C::DB; ++d) acc[d] = f32x16{};
+
+  const float c2 = p.scale * kLog2e;
+  const int n_it = (p.Sq + BM - 1) / BM;
+  // tiles (query head hh of the group, query tile it), walked from the last query
+  // tile down with the group's heads innermost, as in the key roles
+  struct Tq {
+    int hh, it;
+  };
+  auto step = [&](Tq t) {
+    if (++t.hh == G) {
+      t.hh = 0;
+      --t.it;
+    }
+    return t;
+  };
+  auto qtile_span = [&](int it) { return q_span(p, b, it * BM, min(it * BM + BM, p.Sq) - 1); };
+  // every query tile of [it_lo, n_it) holds a visible pair (no window, no segment ids)
+  const int it_lo = first_true(0, n_it, [&](int it) { return !keys_after(p, qtile_span(it), wg_k); });
+  // this wavefront pair's class of a query tile, by range (empty ..., partial ..., full ...)
+  int it_wlo = 0, it_wfull = 0;
+  if (wave_live && p.causal) {
+    it_wlo = first_true(it_lo, n_it, [&](int it) { return !(wv_k.pos_lo > qtile_span(it).pos_hi); });
+    it_wfull = first_true(it_wlo, n_it, [&](int it) { return qtile_span(it).pos_lo >= wv_k.pos_hi; });
+  }
+  auto wave_class = [&](Tq t) {
+    if (!wave_live || t.it < it_wlo) return int(kEmpty);
+    return t.it >= it_wfull ? int(kFull) : int(kPartial);
+  };
+  typename C::TileMP tq, tg;
+  const uint32_t qrs_bytes = uint32_t(qrs) * 2u;
+  tq.init(qrs_bytes, tid);
+  tg.init(qrs_bytes, tid);
+  auto q_of = [&](uint8_t* base) { return reinterpret_cast<uint16_t*>(base); };
+  auto g_of = [&](uint8_t* base) { return q_of(base) + C::kTileMP; };
+  auto l_of = [&](uint8_t* base) { return reinterpret_cast<float*>(g_of(base) + C::kTileMP); };
+  auto d_of = [&](uint8_t* base) { return l_of(base) + BM; };
+  auto issue = [&](Tq t, uint8_t* base) {
+    const int h = g * G + t.hh;
+    const int i0 = t.it * BM;
+    tq.load(q + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq, q_of(base));
+    tg.load(dout + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq, g_of(base));
+    const int64_t li0 = (int64_t(b) * p.Hq + h) * p.Sq + i0;
+    if (wave == 0) dma_dwords<BM>(lse2, li0, p.Sq - i0, l_of(base), lane);
+    if (wave == 1) dma_dwords<BM>(delta, li0, p.Sq - i0, d_of(base), lane);
+  };
+  // P fragment j of query block qb of this pair, this lane
+  uint8_t* pbuf = smem + 2 * C::kStageMax;
+  auto p_at = [&](int qb, int j) {
+    return reinterpret_cast<bf16x8*>(pbuf + (((qb * 4 + pr) * 2 + j) * 64 + lane) * 16);
+  };
+  const MaskSpec ms = make_mask_spec(p.causal, 0, 0);
+
+  Tq cur = Tq{0, n_it - 1};
+  if (cur.it >= it_lo) {
+    issue(cur, smem);
+    wait_all();
+    __syncthreads();
+    int buf = 0;
+    while (true) {
+      Tq nxt = step(cur);
+      const bool has_next = nxt.it >= it_lo;
+      uint8_t* base = smem + buf * C::kStageMax;
+      if (has_next) issue(nxt, smem + (buf ^ 1) * C::kStageMax);
+      const int wcls = wave_class(cur);
+      const uint16_t* qs = q_of(base);
+      const uint16_t* gs = g_of(base);
+      const float* ls = l_of(base);
+      const float* ds = d_of(base);
+      const int qpos0 = p.q_offset + cur.it * BM;
+      // ---- phase A: P of query blocks 0 (dK wavefront) and 1, 2 (dV wavefront)
+      if (wcls != kEmpty) {
+        auto make_p = [&](int qb, auto masked) {
+          constexpr bool kMasked = decltype(masked)::value;
+          f32x16 s = f32x16{};
+          const int arow = qb * 32 + perm_row(l32);
+          pipelined_products<C::KS, C::kAhead>([&](int i) { return ld_row<C::D>(qs, arow, 2 * i + hi); },
+                                               [&](int i, bf16x8 f) { s = mma(f, kf[i], s); });
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int r0 = qb * 32 + key_of_reg(4 * jj, hi);
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + r0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 4 * jj + i;
+              float x = fmaf(s[r], c2, -l4[i]);
+              if constexpr (kMasked) x = pair_visible(ms, qpos0 + r0 + i, my_kpos, 0, 0) ? x : -INFINITY;
+              s[r] = __builtin_amdgcn_exp2f(x);
+            }
+          }
+          *p_at(qb, 0) = to_bf16x8(s, 0);
+          *p_at(qb, 1) = to_bf16x8(s, 8);
+        };
+        auto phase_a = [&](auto masked) {
+          if (!is_dv) {
+            make_p(0, masked);
+          } else {
+#pragma unroll
+            for (int qb = 1; qb < QB; ++qb) make_p(qb, masked);
+          }
+        };
+        if (wcls == kPartial)
+          phase_a(std::true_type{});
+        else
+          phase_a(std::false_type{});
+      }
+      __syncthreads();
+      // ---- phase B: dK^T += Q^T dS (dK wavefront), dV^T += dO^T P (dV wavefront):
+      // one product loop for both, reading Q^T or dO^T transposed from the stage
+      if (wcls != kEmpty) {
+        const uint16_t* at = is_dv ? gs : qs;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          bf16x8 bfrag[2] = {*p_at(qb, 0), *p_at(qb, 1)};
+          if (!is_dv) {
+            // dP = dO V^T, then dS = P (dP - Delta) in place of P
+            f32x16 dp = f32x16{};
+            const int arow = qb * 32 + perm_row(l32);
+            pipelined_products<C::KS, C::kAhead>([&](int i) { return ld_row<C::D>(gs, arow, 2 * i + hi); },
+                                                 [&](int i, bf16x8 f) { dp = mma(f, vf[i], dp); });
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int r0 = qb * 32 + key_of_reg(4 * jj, hi);
+              const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds + r0);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int r = 4 * jj + i;
+                // P of this key and row from its bf16 fragment (bf16 is the high half of a float)
+                const uint32_t w = __builtin_bit_cast(u32x4, bfrag[r >> 3])[(r & 7) >> 1];
+                const float pr_ = __uint_as_float((r & 1) ? (w & 0xffff0000u) : (w << 16));
+                dp[r] = pr_ * (dp[r] - d4[i]);
+              }
+            }
+            bfrag[0] = to_bf16x8(dp, 0);
+            bfrag[1] = to_bf16x8(dp, 8);
+          }
+          pipelined_products<2 * C::DB, C::kAhead>(
+              [&](int i) { return ld_tr<C::D>(at, (qb * 2 + i / C::DB) * 16, (i % C::DB) * 32); },
+              [&](int i, bf16x8 f) { acc[i % C::DB] = mma(f, bfrag[i / C::DB], acc[i % C::DB]); });
+        }
+      }
+      if (has_next) {
+        wait_all();
+        __syncthreads();
+      } else {
+        __syncthreads();
+        break;
+      }
+      cur = nxt;
+      buf ^= 1;
+    }
+  }
+
+  // epilogue: lane holds key column l32, dims d*32 + 8j + 4*hi + (0..3)
+  if (!key_ok) return;
+  const float sc = is_dv ? 1.0f : p.scale;
+  float* gr = (is_dv ? dv : dk) + ((int64_t(b) * p.Sk + wj0 + l32) * p.Hkv + g) * C::D;
+#pragma unroll
+  for (int d = 0; d < C::DB; ++d)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int off = d * 32 + 8 * j + 4 * hi;
+      f32x4 a{acc[d][4 * j] * sc, acc[d][4 * j + 1] * sc, acc[d][4 * j + 2] * sc, acc[d][4 * j + 3] * sc};
+      if (accumulate) a += *reinterpret_cast<const f32x4*>(gr + off);
+      *reinterpret_cast<f32x4*>(gr + off) = a;
+    }
+}
+
 // dQ role: a workgroup owns queries [q0, q0 + kRows) of head h; wavefront w owns
-// queries q0 + 32w + (0..31), one per lane column.
-template <class C, bool kLane>
+// queries q0 + 32w + (0..31), one per lane column.  kUse tells the kernels that call
+// it apart: each kernel instantiates its own copy (the host compilation pass accepts
+// one kernel's reference to a device-builtin function template specialization only).
+template <class C, bool kLane, int kUse = 0>
 CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                        const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                        const float* __restrict__ lse2, const float* __restrict__ delta, float* __restrict__ dq,
@@ -725,6 +968,33 @@ __global__ __launch_bounds__(C::kThreads) void attn_bwd_kernel(BwdArgs a) {
   }
 }
 
+// The grid of problems with no window, segment ids or position arrays: the paired
+// dK / dV items (128 keys each) and the dQ items, in the order and XCD rotation of
+// attn_bwd_kernel.
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void attn_bwd_pair_kernel(BwdArgs a) {
+  __shared__ __align__(16) uint8_t smem[C::kLdsPair];
+  const AttnProblem p = specialize<false>(a.p);
+  const int64_t N = int64_t(a.n_kv) + a.n_q;
+  const int64_t u = blockIdx.x / 8;
+  const int64_t width = N - 8 * u < 8 ? N - 8 * u : 8;
+  const int64_t L = 8 * u + (blockIdx.x % 8 + u) % width;
+  const int64_t before = (L * a.n_kv) / N;  // key-side items before L
+  if (((L + 1) * a.n_kv) / N > before) {
+    const int i = int(before);
+    const int bg = i % (p.B * p.Hkv);
+    pair_role<C>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dk, a.dv, a.accumulate, smem, i / (p.B * p.Hkv),
+                 bg % p.Hkv, bg / p.Hkv);
+  } else {
+    const int i = int(L - before);
+    const int bh = i % (p.B * p.Hq);
+    const int r = i / (p.B * p.Hq);
+    const int n_qt = (p.Sq + C::kRows - 1) / C::kRows;
+    dq_role<C, false, 1>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dq, a.accumulate, smem,
+                         p.causal ? n_qt - 1 - r : r, bh % p.Hq, bh / p.Hq);
+  }
+}
+
 // dK += part[0], dV += part[1] over [B,Sk,Hkv,D] float32 (n4 vectors of 4 each):
 // the second head subset's partial sums of the split key-side items.
 __global__ __launch_bounds__(256) void head_split_sum_kernel(int64_t n4, float* dk, float* dv,
@@ -770,15 +1040,21 @@ hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const vo
   using C = BwdCfg<D>;
   static_assert(C::kRows == 256, "bwd_hsplit counts 256-row items");
   const int hs = bwd_hsplit(p);
+  const bool general = p.window || p.q_seg || hs > 1;
+  // the paired dK / dV role where positions are offset + index
+  const bool pair = !general && !p.q_pos && !p.k_pos;
   BwdArgs a{p, static_cast<U>(q), static_cast<U>(k), static_cast<U>(v), static_cast<U>(dout), lse2, delta,
             dq, dk, dv, accumulate,
-            2 * p.B * p.Hkv * ((p.Sk + C::kRows - 1) / C::kRows) * hs,
+            pair ? p.B * p.Hkv * ((p.Sk + C::kPairKeys - 1) / C::kPairKeys)
+                 : 2 * p.B * p.Hkv * ((p.Sk + C::kRows - 1) / C::kRows) * hs,
             p.B * p.Hq * ((p.Sq + C::kRows - 1) / C::kRows), hs, delta + 2 * bwd_row_plane(rows)};
   {
     ProfScope ps(s, kProfBwdMfma);
     // the general instance: windowed / segmented problems, and head-split grids
-    if (p.window || p.q_seg || hs > 1)
+    if (general)
       hipLaunchKernelGGL((attn_bwd_kernel<C, true>), dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s, a);
+    else if (pair)
+      hipLaunchKernelGGL(attn_bwd_pair_kernel<C>, dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s, a);
     else
       hipLaunchKernelGGL((attn_bwd_kernel<C, false>), dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s, a);
     if (hs > 1) {

@@ -129,10 +129,11 @@ CP_DEVICE __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
 
 // N consecutive dwords of src from element first (valid of them exist; the rest
 // read as 0) into lds, copied by one wavefront with N / 64 LDS-DMA loads (lane i
-// writes dword i of each 64).
+// writes dword i of each 64) and, for N an odd multiple of 32, one more load by the
+// lower half of the wavefront (the upper half's lanes do not load).
 template <int N>
 CP_DEVICE void dma_dwords(const void* src, int64_t first, int valid, void* lds, int lane) {
-  static_assert(N % 64 == 0, "whole wavefronts");
+  static_assert(N % 32 == 0, "whole half-wavefronts");
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(reinterpret_cast<const uint8_t*>(src) + first * 4, uint32_t(valid > 0 ? valid : 0) * 4u);
   uint8_t* dst = static_cast<uint8_t*>(lds);
@@ -140,6 +141,12 @@ CP_DEVICE void dma_dwords(const void* src, int64_t first, int valid, void* lds, 
   for (int c = 0; c < N / 64; ++c)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 256 * c), 4,
                                             lane * 4 + 256 * c, 0, 0, 0);
+  if constexpr (N % 64 != 0) {
+    constexpr int c = N / 64;
+    if (lane < 32)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 256 * c), 4,
+                                              lane * 4 + 256 * c, 0, 0, 0);
+  }
 }
 
 // ---- row-major LDS tiles filled by LDS-DMA, read as rows or transposed ------------

@@ -293,6 +293,11 @@ CASES = {
     # three query heads per kv head: the backward splits the group's heads into
     # uneven halves (1 + 2)
     "gqa3": (1, 200, 330, 6, 2, lambda Sq, Sk: dict(q_offset=130)),
+    # one query head per kv head and positions from offsets: the backward's paired
+    # dK / dV role (96-row query tiles: ragged, offsets, rows that see no key, batch 2)
+    "mha_ragged": (2, 301, 301, 2, 2, lambda Sq, Sk: dict()),
+    "mha_offsets": (1, 170, 430, 3, 3, lambda Sq, Sk: dict(q_offset=260, k_offset=0)),
+    "mha_empty_rows": (1, 200, 290, 2, 2, lambda Sq, Sk: dict(q_offset=0, k_offset=97)),
 }
 
 
@@ -368,7 +373,8 @@ def test_attn_fwd_merge(cp, name, dtype, D):
 
 
 @pytest.mark.parametrize("name", ["causal_square", "offsets", "zigzag_pos", "packed_window", "empty_rows",
-                                  "noncausal_window", "window_1", "offset_window", "gqa3"])
+                                  "noncausal_window", "window_1", "offset_window", "gqa3", "noncausal",
+                                  "mha_ragged", "mha_offsets", "mha_empty_rows"])
 @pytest.mark.parametrize("dtype,D", [(torch.float32, 16), (torch.float32, 128), (torch.bfloat16, 64),
                                      (torch.bfloat16, 128), (torch.bfloat16, 16)])
 def test_attn_bwd(cp, name, dtype, D):
