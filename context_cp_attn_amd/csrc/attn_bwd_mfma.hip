@@ -433,18 +433,20 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
 
 // Paired dK / dV role of problems with no window, no segment ids and no position
 // arrays (positions are offset + index).  A workgroup owns keys [j0, j0 + 128) of kv
-// head g; wavefronts w and w + 4 (w < 4) own the same 32 keys j0 + 32w + (0..31),
-// one per lane column: wavefront w accumulates dK, wavefront w + 4 dV.  For every
-// query tile of BMP = 96 rows (three 32-query blocks) of every head of the group:
-//   phase A: P = exp(S - lse) of the three blocks, S = Q K^T computed once per block
-//     and pair -- block 0 by the dK wavefront, blocks 1 and 2 by the dV wavefront --
-//     and written to LDS as the bf16 B fragments of the next products;
-//   phase B: the dK wavefront forms dP = dO V^T, dS = P (dP - Delta) and
-//     dK^T += Q^T dS, the dV wavefront dV^T += dO^T P, both reading P from LDS.
+// head g; wavefronts w and w + 4 (w < 4, the two wavefronts of one SIMD) own the same
+// 32 keys j0 + 32w + (0..31), one per lane column: wavefront w accumulates dK and
+// holds the keys' V rows, wavefront w + 4 accumulates dV and holds their K rows.
+// For every query tile of BMP = 96 rows (three 32-query blocks) of every head of
+// the group:
+//   phase A: the dV wavefront forms S = Q K^T and P = exp(S - lse) of the three
+//     blocks and writes P to LDS as the bf16 B fragments of the next products; the
+//     dK wavefront meanwhile forms dP = dO V^T of the three blocks;
+//   phase B: the dK wavefront forms dS = P (dP - Delta) and dK^T += Q^T dS, the dV
+//     wavefront dV^T += dO^T P, both reading P from LDS.
 // Each P (and each exponential) is computed once: 7 products per block pair of keys
 // and queries with the dQ role, where the separate dV and dK roles take 8 (both
-// recompute S).  The phases are separated by a workgroup barrier; in phase B two
-// wavefronts per SIMD multiply.
+// recompute S).  The phases are separated by a workgroup barrier, and in each phase
+// both wavefronts of a SIMD run three products per block.
 template <class C>
 CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
@@ -468,22 +470,17 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
   const bool wave_live = wj0 < p.Sk;
   const Span wv_k = k_span(p, b, min(wj0, p.Sk - 1), min(wj0 + 32, p.Sk) - 1);
 
-  // K rows (both wavefronts: S) and V rows (dK wavefront: dP) of this lane's key as
-  // B fragments (k-slots = head dims)
+  // K rows (dV wavefront: S) or V rows (dK wavefront: dP) of this lane's key as B
+  // fragments (k-slots = head dims)
   const int key = min(wj0 + l32, p.Sk - 1);
   const bool key_ok = wj0 + l32 < p.Sk;
-  bf16x8 kf[C::KS], vf[C::KS];
+  bf16x8 kvf[C::KS];
   {
-    const uint16_t* kr = k + (int64_t(b) * p.Sk + key) * krs + int64_t(g) * C::D;
-    const uint16_t* vr = v + (int64_t(b) * p.Sk + key) * krs + int64_t(g) * C::D;
+    const uint16_t* kr = (is_dv ? k : v) + (int64_t(b) * p.Sk + key) * krs + int64_t(g) * C::D;
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       const u32x4 x = *reinterpret_cast<const u32x4*>(kr + s * 16 + hi * 8);
-      kf[s] = __builtin_bit_cast(bf16x8, key_ok ? x : u32x4{0, 0, 0, 0});
-      if (!is_dv) {
-        const u32x4 y = *reinterpret_cast<const u32x4*>(vr + s * 16 + hi * 8);
-        vf[s] = __builtin_bit_cast(bf16x8, key_ok ? y : u32x4{0, 0, 0, 0});
-      }
+      kvf[s] = __builtin_bit_cast(bf16x8, key_ok ? x : u32x4{0, 0, 0, 0});
     }
   }
   const int my_kpos = p.k_offset + key;
@@ -560,41 +557,42 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
       const float* ls = l_of(base);
       const float* ds = d_of(base);
       const int qpos0 = p.q_offset + cur.it * BM;
-      // ---- phase A: P of query blocks 0 (dK wavefront) and 1, 2 (dV wavefront)
+      // ---- phase A: S (dV wavefront) or dP (dK wavefront) of the three query blocks
+      f32x16 sp[QB];
       if (wcls != kEmpty) {
-        auto make_p = [&](int qb, auto masked) {
-          constexpr bool kMasked = decltype(masked)::value;
-          f32x16 s = f32x16{};
-          const int arow = qb * 32 + perm_row(l32);
-          pipelined_products<C::KS, C::kAhead>([&](int i) { return ld_row<C::D>(qs, arow, 2 * i + hi); },
-                                               [&](int i, bf16x8 f) { s = mma(f, kf[i], s); });
+        const uint16_t* as = is_dv ? qs : gs;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int r0 = qb * 32 + key_of_reg(4 * jj, hi);
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + r0);
+        for (int qb = 0; qb < QB; ++qb) sp[qb] = f32x16{};
+        pipelined_products<QB * C::KS, C::kAhead>(
+            [&](int i) { return ld_row<C::D>(as, (i / C::KS) * 32 + perm_row(l32), 2 * (i % C::KS) + hi); },
+            [&](int i, bf16x8 f) { sp[i / C::KS] = mma(f, kvf[i % C::KS], sp[i / C::KS]); });
+        if (is_dv) {
+          auto make_p = [&](auto masked) {
+            constexpr bool kMasked = decltype(masked)::value;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 4 * jj + i;
-              float x = fmaf(s[r], c2, -l4[i]);
-              if constexpr (kMasked) x = pair_visible(ms, qpos0 + r0 + i, my_kpos, 0, 0) ? x : -INFINITY;
-              s[r] = __builtin_amdgcn_exp2f(x);
+            for (int qb = 0; qb < QB; ++qb) {
+              f32x16 s = sp[qb];
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) {
+                const int r0 = qb * 32 + key_of_reg(4 * jj, hi);
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + r0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int r = 4 * jj + i;
+                  float x = fmaf(s[r], c2, -l4[i]);
+                  if constexpr (kMasked) x = pair_visible(ms, qpos0 + r0 + i, my_kpos, 0, 0) ? x : -INFINITY;
+                  s[r] = __builtin_amdgcn_exp2f(x);
+                }
+              }
+              *p_at(qb, 0) = to_bf16x8(s, 0);
+              *p_at(qb, 1) = to_bf16x8(s, 8);
             }
-          }
-          *p_at(qb, 0) = to_bf16x8(s, 0);
-          *p_at(qb, 1) = to_bf16x8(s, 8);
-        };
-        auto phase_a = [&](auto masked) {
-          if (!is_dv) {
-            make_p(0, masked);
-          } else {
-#pragma unroll
-            for (int qb = 1; qb < QB; ++qb) make_p(qb, masked);
-          }
-        };
-        if (wcls == kPartial)
-          phase_a(std::true_type{});
-        else
-          phase_a(std::false_type{});
+          };
+          if (wcls == kPartial)
+            make_p(std::true_type{});
+          else
+            make_p(std::false_type{});
+        }
       }
       __syncthreads();
       // ---- phase B: dK^T += Q^T dS (dK wavefront), dV^T += dO^T P (dV wavefront):
@@ -605,11 +603,8 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
         for (int qb = 0; qb < QB; ++qb) {
           bf16x8 bfrag[2] = {*p_at(qb, 0), *p_at(qb, 1)};
           if (!is_dv) {
-            // dP = dO V^T, then dS = P (dP - Delta) in place of P
-            f32x16 dp = f32x16{};
-            const int arow = qb * 32 + perm_row(l32);
-            pipelined_products<C::KS, C::kAhead>([&](int i) { return ld_row<C::D>(gs, arow, 2 * i + hi); },
-                                                 [&](int i, bf16x8 f) { dp = mma(f, vf[i], dp); });
+            // dS = P (dP - Delta), in place of P
+            f32x16 dp = sp[qb];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
               const int r0 = qb * 32 + key_of_reg(4 * jj, hi);
