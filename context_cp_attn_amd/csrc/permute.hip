@@ -19,8 +19,8 @@
 namespace cp {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kVPT = 4;  // vectors per thread per pass: loads issued before stores
+constexpr int kThreads = 128;
+constexpr int kVPT = 1;  // vectors per thread per pass: loads issued before stores
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -303,15 +303,19 @@ int pick_vec_bytes(int64_t run_bytes, const void* a, const void* b) {
   return 1;
 }
 
-// Blocks per span so that the whole grid has about 16384 blocks (64 per CU of 256;
-// a 256 MiB bf16 tensor then takes one pass of kThreads * kVPT 16-byte vectors per
-// block) while a span never gets more blocks than it has work.  Measured on the
-// llama2-7b relayout shapes and the 64K-token reorder against 2048 / 4096 / 8192
-// blocks: +2% (bf16 relayout) to +10% (float32 inverse), e.g. 5.5 -> 6.1 TB/s.
+// Blocks per span so that the whole grid has about 131072 small blocks (512 per CU
+// of 256; a 256 MiB bf16 tensor then takes one 2 KiB pass per block: one 16-byte
+// vector per thread) while a span never gets more blocks than it has work.  Many
+// short blocks keep more loads in flight per CU than fewer blocks that each issue
+// several loads before their stores.  Measured on the llama2-7b relayout shapes and
+// the 64K-token reorder: from 16384 blocks of 256 threads x 4 vectors to this, the
+// bf16 seq->head relayout 5.54 -> 6.25 TB/s, its inverse 5.59 -> 6.20, the 64K
+// reorder 6.24 -> 6.45; in between, 65536 blocks of 256 x 1 reached 6.07 / 6.17 /
+// 6.30 and 32768 of 256 x 2 5.71 / 5.79 / 6.25.
 int blocks_for(int64_t spans, int64_t vecs_per_span) {
   const int64_t per_block = int64_t(kThreads) * kVPT;
   int64_t need = (vecs_per_span + per_block - 1) / per_block;
-  int64_t want = (16384 + spans - 1) / spans;
+  int64_t want = (131072 + spans - 1) / spans;
   if (want < 1) want = 1;
   int64_t bps = need < want ? need : want;
   return int(bps < 1 ? 1 : bps);
