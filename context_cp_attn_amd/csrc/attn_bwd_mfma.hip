@@ -451,7 +451,8 @@ template <class C>
 CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                          const float* __restrict__ lse2, const float* __restrict__ delta, float* __restrict__ dk,
-                         float* __restrict__ dv, int accumulate, uint8_t* smem, int kt, int g, int b) {
+                         float* __restrict__ dv, int accumulate, uint8_t* smem, int kt, int g, int b, int h_lo,
+                         int h_end) {
   constexpr int BM = C::BMP, QB = C::QBLKP;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -491,14 +492,14 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
 
   const float c2 = p.scale * kLog2e;
   const int n_it = (p.Sq + BM - 1) / BM;
-  // tiles (query head hh of the group, query tile it), walked from the last query
-  // tile down with the group's heads innermost, as in the key roles
+  // tiles (query head hh of the group's heads [h_lo, h_end), query tile it), walked
+  // from the last query tile down with the heads innermost, as in the key roles
   struct Tq {
     int hh, it;
   };
   auto step = [&](Tq t) {
-    if (++t.hh == G) {
-      t.hh = 0;
+    if (++t.hh == h_end) {
+      t.hh = h_lo;
       --t.it;
     }
     return t;
@@ -540,7 +541,7 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
   };
   const MaskSpec ms = make_mask_spec(p.causal, 0, 0);
 
-  Tq cur = Tq{0, n_it - 1};
+  Tq cur = Tq{h_lo, n_it - 1};
   if (cur.it >= it_lo) {
     issue(cur, smem);
     wait_all();
@@ -911,10 +912,11 @@ struct BwdArgs {
   float* dk;
   float* dv;
   int accumulate;
-  int n_kv;  // key-side items = 2 * B * Hkv * key blocks * hsplit
+  int n_kv;  // key-side items = 2 * B * Hkv * 256-key blocks * hsplit (attn_bwd_kernel)
+             // or B * Hkv * 128-key blocks * hsplit (attn_bwd_pair_kernel)
   int n_q;   // query-side items = B * Hq * query blocks
-  // key-side items of windowed / segmented problems on small grids take half of the
-  // group's query heads each (hsplit = 2): the second half's dK / dV go to part
+  // key-side items of grouped-query problems on small grids take half of the group's
+  // query heads each (hsplit = 2): the second half's dK / dV go to part
   // ([2][B,Sk,Hkv,D] float32, dK then dV) and a second kernel adds them
   int hsplit;
   float* part;
@@ -964,8 +966,9 @@ __global__ __launch_bounds__(C::kThreads) void attn_bwd_kernel(BwdArgs a) {
 }
 
 // The grid of problems with no window, segment ids or position arrays: the paired
-// dK / dV items (128 keys each) and the dQ items, in the order and XCD rotation of
-// attn_bwd_kernel.
+// dK / dV items (128 keys each, split over two halves of the group's query heads on
+// small grids as in attn_bwd_kernel) and the dQ items, in the order and XCD rotation
+// of attn_bwd_kernel.
 template <class C>
 __global__ __launch_bounds__(C::kThreads) void attn_bwd_pair_kernel(BwdArgs a) {
   __shared__ __align__(16) uint8_t smem[C::kLdsPair];
@@ -974,12 +977,20 @@ __global__ __launch_bounds__(C::kThreads) void attn_bwd_pair_kernel(BwdArgs a) {
   const int64_t u = blockIdx.x / 8;
   const int64_t width = N - 8 * u < 8 ? N - 8 * u : 8;
   const int64_t L = 8 * u + (blockIdx.x % 8 + u) % width;
-  const int64_t before = (L * a.n_kv) / N;  // key-side items before L
-  if (((L + 1) * a.n_kv) / N > before) {
+  const bool kv_first = a.hsplit > 1;
+  const int64_t before = kv_first ? (L < a.n_kv ? L : a.n_kv) : (L * a.n_kv) / N;  // key-side items before L
+  const bool kv_side = kv_first ? L < a.n_kv : ((L + 1) * a.n_kv) / N > before;
+  if (kv_side) {
     const int i = int(before);
-    const int bg = i % (p.B * p.Hkv);
-    pair_role<C>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dk, a.dv, a.accumulate, smem, i / (p.B * p.Hkv),
-                 bg % p.Hkv, bg / p.Hkv);
+    const int hs = a.hsplit;
+    const int blk = i / hs;  // the head subsets of a key block are neighbours
+    const int sub = i % hs;
+    const int bg = blk % (p.B * p.Hkv);
+    const int G = p.Hq / p.Hkv;
+    const int64_t plane = int64_t(p.B) * p.Sk * p.Hkv * C::D;
+    pair_role<C>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, sub ? a.part : a.dk, sub ? a.part + plane : a.dv,
+                 sub ? 0 : a.accumulate, smem, blk / (p.B * p.Hkv), bg % p.Hkv, bg / p.Hkv, sub * G / hs,
+                 (sub + 1) * G / hs);
   } else {
     const int i = int(L - before);
     const int bh = i % (p.B * p.Hq);
@@ -1035,12 +1046,12 @@ hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const vo
   using C = BwdCfg<D>;
   static_assert(C::kRows == 256, "bwd_hsplit counts 256-row items");
   const int hs = bwd_hsplit(p);
-  const bool general = p.window || p.q_seg || hs > 1;
-  // the paired dK / dV role where positions are offset + index
-  const bool pair = !general && !p.q_pos && !p.k_pos;
+  // the paired dK / dV role: no window or segment ids, positions offset + index
+  const bool pair = !p.window && !p.q_seg && !p.q_pos && !p.k_pos;
+  const bool general = !pair && (p.window || p.q_seg || hs > 1);
   BwdArgs a{p, static_cast<U>(q), static_cast<U>(k), static_cast<U>(v), static_cast<U>(dout), lse2, delta,
             dq, dk, dv, accumulate,
-            pair ? p.B * p.Hkv * ((p.Sk + C::kPairKeys - 1) / C::kPairKeys)
+            pair ? p.B * p.Hkv * ((p.Sk + C::kPairKeys - 1) / C::kPairKeys) * hs
                  : 2 * p.B * p.Hkv * ((p.Sk + C::kRows - 1) / C::kRows) * hs,
             p.B * p.Hq * ((p.Sq + C::kRows - 1) / C::kRows), hs, delta + 2 * bwd_row_plane(rows)};
   {
