@@ -604,9 +604,15 @@ int device_cus() {
 // the row (a 2048-key causal block measured slower split than unsplit).
 constexpr int kSplitMinKeys = 8192;
 
+// With D = 128 the split pays only up to about 1.5 query tiles per CU: measured on
+// 256 CUs, 320 and 384 tiles ran 10% faster split, 448 and 512 tiles 4% and 7%
+// faster as two-group workgroups (the combine pass and the partials' traffic then
+// outweigh the finer granularity).  D = 64 still gained from the split at 512 tiles.
 bool fwd_split_applies(const AttnProblem& p) {
   const int64_t tiles = int64_t((p.Sq + 127) / 128) * p.Hq * p.B;
-  return p.Sk >= kSplitMinKeys && tiles < 2 * int64_t(wg_slots());
+  if (p.Sk < kSplitMinKeys) return false;
+  if (p.D == 128) return 2 * tiles <= 3 * int64_t(device_cus());
+  return tiles < 2 * int64_t(wg_slots());
 }
 
 size_t fwd_split_workspace_bytes(const AttnProblem& p) {
