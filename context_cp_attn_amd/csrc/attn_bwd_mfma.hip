@@ -551,48 +551,108 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
       Tq nxt = step(cur);
       const bool has_next = nxt.it >= it_lo;
       uint8_t* base = smem + buf * C::kStageMax;
-      if (has_next) issue(nxt, smem + (buf ^ 1) * C::kStageMax);
+      // The next tile's Q and dO rows are staged by 2 kIter LDS-DMA loads per thread.
+      // Issued together they hold a wavefront for hundreds of cycles (the loads of
+      // all eight wavefronts queue at the CU's address unit), so they are issued one
+      // every other product of phase A instead (dma_step); lse2 and delta go first.
+      uint8_t* nbase = smem + (buf ^ 1) * C::kStageMax;
+      const int nh = g * G + nxt.hh;
+      const int ni0 = max(nxt.it, 0) * BM;
+      const auto rq = C::TileMP::rows_rsrc(q + int64_t(b) * p.Sq * qrs + int64_t(nh) * C::D, qrs_bytes, ni0, p.Sq);
+      const auto rg =
+          C::TileMP::rows_rsrc(dout + int64_t(b) * p.Sq * qrs + int64_t(nh) * C::D, qrs_bytes, ni0, p.Sq);
+      if (has_next) {
+        const int64_t li0 = (int64_t(b) * p.Hq + nh) * p.Sq + ni0;
+        if (wave == 0) dma_dwords<BM>(lse2, li0, p.Sq - ni0, l_of(nbase), lane);
+        if (wave == 1) dma_dwords<BM>(delta, li0, p.Sq - ni0, d_of(nbase), lane);
+      }
+      constexpr int kIt = C::TileMP::kIter;
+      auto dma_step = [&](int j) {
+        if (j < 2 * kIt && has_next) {
+          if (j < kIt)
+            tq.load_iter(rq, j, q_of(nbase));
+          else
+            tg.load_iter(rg, j - kIt, g_of(nbase));
+        }
+      };
       const int wcls = wave_class(cur);
+      if (wcls == kEmpty) {
+#pragma unroll
+        for (int j = 0; j < 2 * kIt; ++j) dma_step(j);
+      }
       const uint16_t* qs = q_of(base);
       const uint16_t* gs = g_of(base);
       const float* ls = l_of(base);
       const float* ds = d_of(base);
       const int qpos0 = p.q_offset + cur.it * BM;
-      // ---- phase A: S (dV wavefront) or dP (dK wavefront) of the three query blocks
+      // ---- phase A: dP (dK wavefront) or S and P (dV wavefront) of the three query
+      // blocks.  The exponentials take as long as the products (the transcendental
+      // unit runs at a quarter of the vector rate), so the dV wavefront spreads those
+      // of each block over the products of the next one.
       f32x16 sp[QB];
       if (wcls != kEmpty) {
-        const uint16_t* as = is_dv ? qs : gs;
+        if (!is_dv) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sp[qb] = f32x16{};
-        pipelined_products<QB * C::KS, C::kAhead>(
-            [&](int i) { return ld_row<C::D>(as, (i / C::KS) * 32 + perm_row(l32), 2 * (i % C::KS) + hi); },
-            [&](int i, bf16x8 f) { sp[i / C::KS] = mma(f, kvf[i % C::KS], sp[i / C::KS]); });
-        if (is_dv) {
-          auto make_p = [&](auto masked) {
+          for (int qb = 0; qb < QB; ++qb) sp[qb] = f32x16{};
+          static_assert(QB * C::KS >= 4 * C::TileMP::kIter, "the DMA steps fit phase A's products");
+          pipelined_products<QB * C::KS, C::kAhead>(
+              [&](int i) { return ld_row<C::D>(gs, (i / C::KS) * 32 + perm_row(l32), 2 * (i % C::KS) + hi); },
+              [&](int i, bf16x8 f) {
+                sp[i / C::KS] = mma(f, kvf[i % C::KS], sp[i / C::KS]);
+                if ((i & 1) == 0) dma_step(i / 2);
+              });
+        } else {
+          // raised priority: the SIMD's matrix core serves this wavefront's S products
+          // first, so its exponentials start early and overlap the dK wavefront's dP
+          __builtin_amdgcn_s_setprio(1);
+          auto phase_a = [&](auto masked) {
             constexpr bool kMasked = decltype(masked)::value;
+            f32x4 l4[4];
+            auto load_lse = [&](int qb) {
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj)
+                l4[jj] = *reinterpret_cast<const f32x4*>(ls + qb * 32 + key_of_reg(4 * jj, hi));
+            };
+            // P = 2^(S c2 - lse2) of score r of block qb (masked on partial tiles)
+            auto exp_at = [&](int qb, int r) {
+              float x = fmaf(sp[qb][r], c2, -l4[r >> 2][r & 3]);
+              if constexpr (kMasked)
+                x = pair_visible(ms, qpos0 + qb * 32 + key_of_reg(r & ~3, hi) + (r & 3), my_kpos, 0, 0) ? x
+                                                                                                     : -INFINITY;
+              sp[qb][r] = __builtin_amdgcn_exp2f(x);
+            };
+            auto store_p = [&](int qb) {
+              *p_at(qb, 0) = to_bf16x8(sp[qb], 0);
+              *p_at(qb, 1) = to_bf16x8(sp[qb], 8);
+            };
+            constexpr int kPer = 16 / C::KS;  // scores per product
+            static_assert(kPer * C::KS == 16, "the products of a block cover the previous block's scores");
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-              f32x16 s = sp[qb];
+              if (qb > 0) load_lse(qb - 1);
+              sp[qb] = f32x16{};
+              pipelined_products<C::KS, C::kAhead>(
+                  [&](int i) { return ld_row<C::D>(qs, qb * 32 + perm_row(l32), 2 * i + hi); },
+                  [&](int i, bf16x8 f) {
+                    sp[qb] = mma(f, kvf[i], sp[qb]);
+                    if (((qb * C::KS + i) & 1) == 0) dma_step((qb * C::KS + i) / 2);
+                    if (qb > 0) {
 #pragma unroll
-              for (int jj = 0; jj < 4; ++jj) {
-                const int r0 = qb * 32 + key_of_reg(4 * jj, hi);
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + r0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int r = 4 * jj + i;
-                  float x = fmaf(s[r], c2, -l4[i]);
-                  if constexpr (kMasked) x = pair_visible(ms, qpos0 + r0 + i, my_kpos, 0, 0) ? x : -INFINITY;
-                  s[r] = __builtin_amdgcn_exp2f(x);
-                }
-              }
-              *p_at(qb, 0) = to_bf16x8(s, 0);
-              *p_at(qb, 1) = to_bf16x8(s, 8);
+                      for (int j = 0; j < kPer; ++j) exp_at(qb - 1, kPer * i + j);
+                    }
+                  });
+              if (qb > 0) store_p(qb - 1);
             }
+            load_lse(QB - 1);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) exp_at(QB - 1, r);
+            store_p(QB - 1);
           };
           if (wcls == kPartial)
-            make_p(std::true_type{});
+            phase_a(std::true_type{});
           else
-            make_p(std::false_type{});
+            phase_a(std::false_type{});
+          __builtin_amdgcn_s_setprio(0);
         }
       }
       __syncthreads();

@@ -215,17 +215,26 @@ struct DmaTile {
     }
   }
 
-  CP_DEVICE void load(const uint16_t* base, uint32_t row_stride_bytes, int row0, int nrows, uint16_t* lds_tile) const {
+  // buffer resource of rows [row0, nrows) (rows past nrows read as zeros)
+  CP_DEVICE static __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, uint32_t row_stride_bytes, int row0,
+                                                    int nrows) {
     const uint32_t skip = uint32_t(row0) * row_stride_bytes;
     const uint32_t valid = uint32_t(nrows - 1 - row0) * row_stride_bytes + uint32_t(D) * 2u;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const uint8_t*>(base) + skip, valid);
+    return make_rsrc(reinterpret_cast<const uint8_t*>(base) + skip, valid);
+  }
+
+  // one of the kIter loads of this thread (it < kIter)
+  CP_DEVICE void load_iter(const __amdgpu_buffer_rsrc_t& rs, int it, uint16_t* lds_tile) const {
+    const int s0 = it * NT + wbase;  // first chunk of this wavefront
+    if (kChunks % NT == 0 || s0 < kChunks)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds_tile + s0 * 8),
+                                               16, voff[it], 0, 0, 0);
+  }
+
+  CP_DEVICE void load(const uint16_t* base, uint32_t row_stride_bytes, int row0, int nrows, uint16_t* lds_tile) const {
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(base, row_stride_bytes, row0, nrows);
 #pragma unroll
-    for (int it = 0; it < kIter; ++it) {
-      const int s0 = it * NT + wbase;  // first chunk of this wavefront
-      if (kChunks % NT == 0 || s0 < kChunks)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(lds_tile + s0 * 8), 16, voff[it], 0, 0, 0);
-    }
+    for (int it = 0; it < kIter; ++it) load_iter(rs, it, lds_tile);
   }
 };
 
