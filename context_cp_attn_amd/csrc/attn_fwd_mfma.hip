@@ -327,7 +327,7 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, other_half(mx)) * c2;
+        mx = max_halves(mx) * c2;
         if (__any(mx > m + kRescaleLog2)) {
           const float mnew = fmaxf(m, mx);
           const float alpha = __builtin_amdgcn_exp2f(m - (mnew == -INFINITY ? 0.0f : mnew));
@@ -397,7 +397,7 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
   }
 
   // ---- epilogue: normalise; store out (bf16) and lse (natural log), or merge
-  const float lt = l + other_half(l);
+  const float lt = sum_halves(l);
   if (!row_ok) return;
   const bool any = lt > 0.0f;
   const float inv = any ? 1.0f / lt : 0.0f;

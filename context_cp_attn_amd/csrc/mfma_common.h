@@ -44,7 +44,17 @@ CP_DEVICE bf16x8 to_bf16x8(const f32x16& x, int base) {
 CP_DEVICE constexpr int perm_row(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
 CP_DEVICE constexpr int key_of_reg(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
 
-CP_DEVICE float other_half(float x) { return __shfl_xor(x, 32, 64); }
+// x of lane l combined with x of lane l ^ 32, in every lane.  v_permlane32_swap
+// (one VALU op) hands each lane both halves' values: r[0] = x[l mod 32], r[1] =
+// x[32 + l mod 32]; a cross-lane shuffle would be an LDS round trip.
+CP_DEVICE float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+CP_DEVICE float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // ---- tile classification -------------------------------------------------------
 enum : int { kEmpty = 0, kPartial = 1, kFull = 2 };
