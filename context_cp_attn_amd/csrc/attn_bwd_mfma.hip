@@ -655,7 +655,8 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
           __builtin_amdgcn_s_setprio(0);
         }
       }
-      __syncthreads();
+      // P is in LDS; the next tile's DMA stays in flight across this barrier
+      lds_barrier();
       // ---- phase B: dK^T += Q^T dS (dK wavefront), dV^T += dO^T P (dV wavefront):
       // one product loop for both, reading Q^T or dO^T transposed from the stage
       if (wcls != kEmpty) {

@@ -274,5 +274,20 @@ CP_DEVICE void pipelined_products(Load&& load, Mul&& mul) {
 // Wait for every outstanding memory operation of this wavefront (LDS-DMA included).
 CP_DEVICE void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Workgroup barrier after this wavefront's LDS operations only: its vector-memory
+// loads (the LDS-DMA of later tiles) stay in flight.  __syncthreads() would wait for
+// those too: its memory fence is lowered to s_waitcnt vmcnt(0) before s_barrier.
+// The signal fences and scheduling barriers keep the compiler from moving LDS
+// accesses across it (s_barrier alone is not a memory operation to the optimizer).
+CP_DEVICE void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  // s_waitcnt lgkmcnt(0), vmcnt and expcnt at their maxima (gfx9 encoding)
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 }  // namespace mfma
 }  // namespace cp
