@@ -119,8 +119,32 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
   const uint16_t* vbase = v + int64_t(b) * p.Sk * krs + int64_t(g) * C::D;
 
   const Span wg_q = q_span(p, b, q0, min(q0 + C::kRows, p.Sq) - 1);
+  if constexpr (kMerge) {
+    // A block none of whose keys these rows can see leaves the running result as it
+    // is: decided from the extreme positions / segment ids before any other load
+    // (half the query tiles of a zigzag ring step see no key of a later block).
+    const Span all_k = k_span(p, b, 0, p.Sk - 1);
+    if (keys_after(p, wg_q, all_k) || keys_before(p, wg_q, all_k)) return;
+  }
   const bool wave_live = wq0 < p.Sq;
   const Span wv_q = q_span(p, b, min(wq0, p.Sq - 1), min(wq0 + 32, p.Sq) - 1);
+  const int n_kt = (p.Sk + C::BN - 1) / C::BN;
+
+  // The K / V rows of the walk's first tile are requested now, before the key spans
+  // that fix it: it is tile 0 (key group 1 of a split pair: tile 1) whenever these
+  // rows see the first keys, as in every causal ring step.  Another first tile
+  // waits for this DMA to land before its own is issued.
+  typename C::Tile tk, tv;
+  const uint32_t krs_bytes = uint32_t(krs) * 2u;
+  tk.init(krs_bytes, gtid);
+  tv.init(krs_bytes, gtid);
+  const int spec_kt = C::NS > 1 ? grp : 0;
+  const bool spec = spec_kt < n_kt;
+  uint8_t* const stage0 = smem + ((C::SPLIT ? 0 : grp) * 2) * C::kStageBytes;
+  if (spec) {
+    tk.load(kbase, krs_bytes, spec_kt * C::BN, p.Sk, reinterpret_cast<uint16_t*>(stage0));
+    tv.load(vbase, krs_bytes, spec_kt * C::BN, p.Sk, reinterpret_cast<uint16_t*>(stage0) + C::kTileElems);
+  }
 
   // ---- Q fragments (B operand of S^T = K Q^T) and this lane's query position / segment
   const int row = min(wq0 + l32, p.Sq - 1);
@@ -143,7 +167,6 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
   float m = -INFINITY, l = 0.0f;
 
   const float c2 = p.scale * kLog2e;
-  const int n_kt = (p.Sk + C::BN - 1) / C::BN;
 
   // Spans of the key tiles.  With position or segment arrays each one is two
   // dependent global loads, which the walk and the per-wave classification would
@@ -174,7 +197,10 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
   if constexpr (kMerge) {
     // no key of this block is visible to these rows: merging a weight-0 block
     // leaves the running result as it is, so nothing is read or written
-    if (kt_lo >= kt_hi) return;
+    if (kt_lo >= kt_hi) {
+      wait_all();  // the first tile's DMA must land before the workgroup's LDS is freed
+      return;
+    }
   }
   // Without a window or segment ids every tile of [kt_lo, kt_hi) holds a visible
   // pair (its first key is visible to the run's last query, positions increasing),
@@ -234,18 +260,11 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     kt_wg_full = first_true(kt_lo, kt_hi, [&](int kt) {
       return kt * C::BN + C::BN > p.Sk || tile_span(kt).pos_hi > wg_q.pos_lo;
     });
-  typename C::Tile tk, tv;
-  const uint32_t krs_bytes = uint32_t(krs) * 2u;
-  tk.init(krs_bytes, gtid);
-  tv.init(krs_bytes, gtid);
   // stage layout: K tile, V tile (swizzled row-major), kpos, kseg
-  auto stage_load = [&](int kt, uint8_t* stage) {
-    uint16_t* ks = reinterpret_cast<uint16_t*>(stage);
-    uint16_t* vs = ks + C::kTileElems;
-    int* kpos = reinterpret_cast<int*>(vs + C::kTileElems);
+  // the tile's key positions and segment ids (stage_load adds its K / V rows)
+  auto stage_aux = [&](int kt, uint8_t* stage) {
+    int* kpos = reinterpret_cast<int*>(reinterpret_cast<uint16_t*>(stage) + 2 * C::kTileElems);
     int* kseg = kpos + C::BN;
-    tk.load(kbase, krs_bytes, kt * C::BN, p.Sk, ks);
-    tv.load(vbase, krs_bytes, kt * C::BN, p.Sk, vs);
     // key positions / segment ids: LDS-DMA from their arrays (one row wavefront of
     // the group each), or written as offset + index / 0; keys past the end are
     // masked by their index
@@ -262,6 +281,12 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
       for (int t = gtid; t < C::BN; t += C::kGroupThreads) kseg[t] = 0;
     }
   };
+  auto stage_load = [&](int kt, uint8_t* stage) {
+    uint16_t* ks = reinterpret_cast<uint16_t*>(stage);
+    tk.load(kbase, krs_bytes, kt * C::BN, p.Sk, ks);
+    tv.load(vbase, krs_bytes, kt * C::BN, p.Sk, ks + C::kTileElems);
+    stage_aux(kt, stage);
+  };
   auto stage_of = [&](int buf) { return smem + ((C::SPLIT ? 0 : grp) * 2 + buf) * C::kStageBytes; };
 
   // Live tiles are taken in pairs (t0, t1): key group 0 multiplies t0, group 1 t1
@@ -271,7 +296,14 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
   int t1 = (C::NS > 1 && t0 < n_kt) ? next_tile(t0 + 1) : n_kt;
   if (t0 < n_kt) {
     int cur = grp == 0 ? t0 : t1;
-    if (cur < n_kt) stage_load(cur, stage_of(0));
+    if (cur < n_kt) {
+      if (spec && cur == spec_kt) {
+        stage_aux(cur, stage_of(0));  // its K / V rows are already in flight
+      } else {
+        if (spec) wait_all();
+        stage_load(cur, stage_of(0));
+      }
+    }
     wait_all();
     __syncthreads();
     const MaskSpec ms = make_mask_spec(p.causal, p.window, p.q_seg != nullptr);
@@ -366,6 +398,10 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     };
     while (iter(std::integral_constant<int, 0>{}) && iter(std::integral_constant<int, 1>{})) {
     }
+  } else if (spec) {
+    // no live tile: the first tile's DMA lands before the stages are reused below
+    wait_all();
+    __syncthreads();
   }
 
   if constexpr (C::NS > 1 && !C::SPLIT) {
