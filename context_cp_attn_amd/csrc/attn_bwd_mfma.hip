@@ -10,21 +10,21 @@
 //
 // Two launches:
 //  1. delta: Delta = rowsum(dO * O) into the caller's workspace [B,Hq,Sq].
-//  2. one grid with three roles, each a workgroup of 8 wavefronts x 32 rows:
-//     dV role — owns 256 keys of a kv head (K as register B fragments) and streams
-//       query tiles of every head of the group: S = Q K^T, P, dV^T += dO^T P;
-//     dK role — same keys (K and V fragments): S, dP = dO V^T, dS, dK^T += Q^T dS;
+//  2. one grid with two roles, each a workgroup of 8 wavefronts:
+//     paired dK / dV role — owns 128 keys of a kv head; the two wavefronts of a SIMD
+//       share 32 keys (one holds their V rows and accumulates dK, the other their K
+//       rows and accumulates dV) and stream query tiles of the group's heads:
+//       S = Q K^T and P once per block pair (P passed through LDS), dP = dO V^T,
+//       dS, dK^T += Q^T dS, dV^T += dO^T P;
 //     dQ role — owns 256 queries of a head (Q and dO fragments) and streams key
 //       tiles: S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
-//     Splitting dV from dK recomputes S once more (8 instead of 7 products per
-//     block pair) but keeps every role under 256 registers, so two wavefronts run
-//     per SIMD and one's matrix products overlap the other's elementwise work.
-//     S and dP are computed query-major in the dV/dK roles so P and dS are directly
-//     the B operands of the next products.  Each LDS stage holds two row-major
-//     tiles (Q and dO, or K and V), XOR-swizzled and filled by LDS-DMA; the
-//     operands needed transposed (dO^T, Q^T, K^T) are read from the same tiles with
-//     the LDS transpose read.  The role lists, each heaviest first, are
-//     interleaved in one grid.
+//     7 products per block pair of keys and queries (4 would be counted).  S and dP
+//     are computed query-major in the pair role so P and dS are directly the B
+//     operands of the next products.  Each LDS stage holds two row-major tiles (Q
+//     and dO, or K and V), XOR-swizzled and filled by LDS-DMA; the operands needed
+//     transposed (dO^T, Q^T, K^T) are read from the same tiles with the LDS
+//     transpose read.  The role lists, each heaviest first, are interleaved in one
+//     grid.
 // Tiles are skipped / masked exactly as in the forward (empty / partial / full).
 #include <type_traits>
 
@@ -41,7 +41,7 @@ using namespace mfma;
 CP_DEVICE float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
 
 // ---- 1. Delta (and the base-2 lse) ----------------------------------------------
-// Both row arrays [B,Hq,Sq] go to the workspace, where the main kernel's key roles
+// Both row arrays [B,Hq,Sq] go to the workspace, where the main kernel's pair role
 // copy a query tile's values straight into LDS.
 template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(int64_t rows, int Sq, int Hq,
@@ -83,356 +83,44 @@ struct BwdCfg {
   static constexpr int D = D_;
   static constexpr int NW = 8;
   static constexpr int kThreads = 64 * NW;
-  static constexpr int kRows = 32 * NW;  // keys (dV/dK roles) or queries (dQ role) per workgroup
+  static constexpr int kRows = 32 * NW;  // queries per workgroup of the dQ role
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int BM = 128;         // query tile of the dV/dK roles
-  static constexpr int QBLK = BM / 32;
   static constexpr int BN = 128;         // key tile of the dQ role
   static constexpr int KB = BN / 32;
-  static constexpr int kTileM = BM * D, kTileN = BN * D;  // swizzled row-major tiles
-  // dV / dK stage: Q rows, dO rows, lse2, delta, qpos, qseg
-  static constexpr int kStageK = 2 * kTileM * 2 + 4 * BM * 4;
+  static constexpr int kTileN = BN * D;  // swizzled row-major tile
   // dQ stage: K rows, V rows, kpos, kseg
   static constexpr int kStageQ = 2 * kTileN * 2 + 2 * BN * 4;
-  static constexpr int kStageMax = kStageK > kStageQ ? kStageK : kStageQ;
   static constexpr int kAhead = 3;  // LDS operand reads issued this many products ahead
-  // spans of up to kSpanTiles query tiles (dV / dK roles) or key tiles (dQ role),
-  // cached when they come from position / segment arrays
+  // key-tile spans of the dQ role, cached (after its two stages) when they come from
+  // position / segment arrays
   static constexpr int kSpanTiles = 1024;
-  static constexpr int kLdsBytes = 2 * kStageMax + kSpanTiles * 16;
-  using TileM = DmaTile<BM, D, kThreads>;
   using TileN = DmaTile<BN, D, kThreads>;
-  // paired dK / dV role (problems with no window, segment ids or position arrays):
-  // a workgroup owns 128 keys and walks query tiles of BMP rows; its stages hold the
-  // Q and dO rows, lse2 and delta of a tile, spaced like the other roles' stages,
-  // followed by the P buffer ([QBLKP][4 key blocks][2 fragments][64 lanes] x 16 B)
+  // paired dK / dV role: a workgroup owns 128 keys and walks query tiles of BMP rows;
+  // its stages hold the Q and dO rows, lse2, delta, positions and segment ids of a
+  // tile, spaced like the dQ role's stages, followed by the P buffer
+  // ([QBLKP][4 key blocks][2 fragments][64 lanes] x 16 B)
   static constexpr int kPairKeys = 128;
   static constexpr int BMP = 96;
   static constexpr int QBLKP = BMP / 32;
   static constexpr int kTileMP = BMP * D;
-  static constexpr int kStageP = 2 * kTileMP * 2 + 2 * BMP * 4;
+  static constexpr int kStageP = 2 * kTileMP * 2 + 4 * BMP * 4;  // Q, dO, lse2, delta, qpos, qseg
+  static constexpr int kStageMax = kStageQ > kStageP ? kStageQ : kStageP;
   static constexpr int kPBytes = QBLKP * 4 * 2 * 64 * 16;
   static constexpr int kLdsPair = 2 * kStageMax + kPBytes;
   using TileMP = DmaTile<BMP, D, kThreads>;
-  static_assert(kStageP <= kStageMax, "pair stages fit the stage spacing");
-  static_assert(kLdsPair <= 160 * 1024, "LDS of one workgroup");
-  static_assert(BM <= kThreads && BN <= kThreads, "one thread per row of the small arrays");
+  // the general instance (windows, segment ids, position arrays) also caches the
+  // spans of up to kSpanTilesP query tiles after the P buffer
+  static constexpr int kSpanTilesP = 256;
+  static constexpr int kLdsPairL = kLdsPair + kSpanTilesP * 16;
+  static_assert(kLdsPairL <= 160 * 1024, "LDS of one workgroup");
+  static_assert(2 * kStageMax + kSpanTiles * 16 <= kLdsPair, "the dQ role's spans fit the pair kernel's LDS");
+  static_assert(BMP <= kThreads && BN <= kThreads, "one thread per row of the small arrays");
 };
 
-// Pointers into one LDS stage of the dV / dK roles.
-template <class C>
-struct QStage {
-  uint16_t* q;     // Q rows
-  uint16_t* g;     // dO rows
-  float* lse2;
-  float* delta;    // dK role
-  int* qpos;
-  int* qseg;
-  CP_DEVICE explicit QStage(uint8_t* base) {
-    q = reinterpret_cast<uint16_t*>(base);
-    g = q + C::kTileM;
-    lse2 = reinterpret_cast<float*>(g + C::kTileM);
-    delta = lse2 + C::BM;
-    qpos = reinterpret_cast<int*>(delta + C::BM);
-    qseg = qpos + C::BM;
-  }
-};
-
-// Shared skeleton of the dV and dK roles: a workgroup owns keys [j0, j0 + kRows) of
-// kv head g; wavefront w owns keys j0 + 32w + (0..31), one per lane column.
-// kDK selects the dK role (else dV).  kLane: the general instance, launched for
-// windowed or segmented problems and for grids whose key-side items are split over
-// the group's query heads: one-tile-per-lane classification where it applies, and
-// the group's query heads limited to [h_lo, h_end).  The other instance (one query
-// head per kv head, no window or segment ids) carries neither, so its register
-// allocation is unaffected, and walks every head of the group.
-template <class C, bool kDK, bool kLane>
-CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                        const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-                        const float* __restrict__ lse2, const float* __restrict__ delta,
-                        float* __restrict__ grad, int accumulate, uint8_t* smem, int kt, int g, int b,
-                        int h_lo_arg, int h_end_arg) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-  const int G = p.Hq / p.Hkv;
-  const int h_lo = kLane ? h_lo_arg : 0;
-  const int h_end = kLane ? h_end_arg : G;
-  const int j0 = kt * C::kRows;
-  const int wj0 = j0 + wave * 32;
-  const int64_t krs = int64_t(p.Hkv) * C::D;
-  const int64_t qrs = int64_t(p.Hq) * C::D;
-
-  const Span wg_k = k_span(p, b, j0, min(j0 + C::kRows, p.Sk) - 1);
-  const bool wave_live = wj0 < p.Sk;
-  const Span wv_k = k_span(p, b, min(wj0, p.Sk - 1), min(wj0 + 32, p.Sk) - 1);
-
-  // K (and V) rows of this lane's key as B fragments (k-slots = head dims)
-  const int key = min(wj0 + l32, p.Sk - 1);
-  const bool key_ok = wj0 + l32 < p.Sk;
-  bf16x8 kf[C::KS], vf[kDK ? C::KS : 1];
-  {
-    const uint16_t* kr = k + (int64_t(b) * p.Sk + key) * krs + int64_t(g) * C::D;
-    const uint16_t* vr = v + (int64_t(b) * p.Sk + key) * krs + int64_t(g) * C::D;
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(kr + s * 16 + hi * 8);
-      kf[s] = __builtin_bit_cast(bf16x8, key_ok ? x : u32x4{0, 0, 0, 0});
-      if constexpr (kDK) {
-        const u32x4 y = *reinterpret_cast<const u32x4*>(vr + s * 16 + hi * 8);
-        vf[s] = __builtin_bit_cast(bf16x8, key_ok ? y : u32x4{0, 0, 0, 0});
-      }
-    }
-  }
-  const int my_kpos = kpos_at(p, key);
-  const int my_kseg = kseg_at(p, b, key);
-
-  f32x16 acc[C::DB];
-#pragma unroll
-  for (int d = 0; d < C::DB; ++d) acc[d] = f32x16{};
-
-  const float c2 = p.scale * kLog2e;
-  const int n_it = (p.Sq + C::BM - 1) / C::BM;
-  // A tile is (query head of the group hh, query tile it).  Query tiles are walked
-  // from the last one down, the heads of the group innermost: every workgroup of
-  // this role starts at the end of the sequence and sweeps down at about the same
-  // pace, so the workgroups resident together read the same Q / dO tiles and the
-  // caches serve most of them (walked upward from their own diagonals they would
-  // spread over all of Q and dO at once).
-  struct Tq {
-    int hh, it;
-  };
-  auto step = [&](Tq t) {
-    if (++t.hh == h_end) {
-      t.hh = h_lo;
-      --t.it;
-    }
-    return t;
-  };
-  // Spans of the query tiles: with position or segment arrays each is two dependent
-  // global loads, so they are loaded once, in parallel, into LDS.
-  const bool span_cached = (p.q_pos != nullptr || p.q_seg != nullptr) && n_it <= C::kSpanTiles;
-  i32x4* span_l = reinterpret_cast<i32x4*>(smem + 2 * C::kStageMax);
-  if (span_cached) {
-    for (int t = tid; t < n_it; t += C::kThreads) {
-      const Span s = q_span(p, b, t * C::BM, min(t * C::BM + C::BM, p.Sq) - 1);
-      span_l[t] = i32x4{s.pos_lo, s.pos_hi, s.seg_lo, s.seg_hi};
-    }
-    __syncthreads();
-  }
-  auto qtile_span = [&](int it) {
-    if (span_cached) {
-      const i32x4 x = span_l[it];
-      return Span{x[0], x[1], x[2], x[3]};
-    }
-    return q_span(p, b, it * C::BM, min(it * C::BM + C::BM, p.Sq) - 1);
-  };
-  auto tile_class = [&](Tq t, const Span& ksp) { return classify(p, qtile_span(t.it), ksp, false); };
-  // the query tiles live for this key block lie in [it_lo, it_hi); the walk stays
-  // inside (queries wholly after the keys' window / segments are a suffix, those
-  // wholly before the keys a prefix)
-  const int it_hi = first_true(0, n_it, [&](int it) { return keys_before(p, qtile_span(it), wg_k); });
-  const int it_lo = first_true(0, it_hi, [&](int it) { return !keys_after(p, qtile_span(it), wg_k); });
-  // without a window or segment ids every query tile of [it_lo, it_hi) holds a
-  // visible pair (the keys' first position is visible to its last query)
-  const bool dense = !p.window && !p.q_seg;
-  // other problems with at most 64 query tiles in [it_lo, it_hi) classify them all
-  // at once, one tile per lane (the class does not depend on the head): bit masks
-  // over it - it_lo of the live tiles and of this wavefront's full / partial ones
-  const bool lane_cls = kLane && !dense && it_hi - it_lo <= 64;
-  uint64_t live_m = 0, wfull_m = 0, wpart_m = 0;
-  if (lane_cls) {
-    const int it = it_lo + lane;
-    int cg = kEmpty, cw = kEmpty;
-    if (it < it_hi) {
-      const Span qs = qtile_span(it);
-      cg = classify(p, qs, wg_k, false);
-      if (wave_live) cw = classify(p, qs, wv_k, false);
-    }
-    live_m = __ballot(cg != kEmpty);
-    wfull_m = __ballot(cw == kFull);
-    wpart_m = __ballot(cw == kPartial);
-  }
-  auto next_tile = [&](Tq t) {
-    if (t.it >= it_hi) t = Tq{h_lo, it_hi - 1};
-    if (lane_cls) {
-      if (t.it < it_lo) return Tq{t.hh, -1};
-      // live tiles at or below t.it; t.it itself keeps its head, a lower one starts at h_lo
-      const int sh = t.it - it_lo;
-      const uint64_t m = live_m & (sh == 63 ? ~uint64_t(0) : (uint64_t(2) << sh) - 1);
-      if (!m) return Tq{t.hh, -1};
-      const int it = it_lo + 63 - int(__builtin_clzll(m));
-      return it == t.it ? t : Tq{h_lo, it};
-    }
-    while (!dense && t.it >= it_lo && tile_class(t, wg_k) == kEmpty) t = step(t);
-    if (t.it < it_lo) t.it = -1;
-    return t;
-  };
-  // This wavefront's class of a query tile; dense problems by range (along the
-  // query tile index: empty ... empty, partial ..., full ... full; query rows past
-  // the end add nothing, so no tile is ragged here)
-  int it_wlo = 0, it_wfull = 0;
-  if (dense && wave_live && p.causal) {
-    it_wlo = first_true(it_lo, it_hi, [&](int it) { return !(wv_k.pos_lo > qtile_span(it).pos_hi); });
-    it_wfull = first_true(it_wlo, it_hi, [&](int it) { return qtile_span(it).pos_lo >= wv_k.pos_hi; });
-  }
-  auto wave_class = [&](Tq t) {
-    if (lane_cls) {
-      const uint64_t bit = uint64_t(1) << (t.it - it_lo);
-      return (wfull_m & bit) ? int(kFull) : (wpart_m & bit) ? int(kPartial) : int(kEmpty);
-    }
-    if (!dense) return tile_class(t, wv_k);
-    if (!wave_live || t.it < it_wlo) return int(kEmpty);
-    return t.it >= it_wfull ? int(kFull) : int(kPartial);
-  };
-  typename C::TileM tq, tg;
-  const uint32_t qrs_bytes = uint32_t(qrs) * 2u;
-  tq.init(qrs_bytes, tid);
-  tg.init(qrs_bytes, tid);
-  // The tile's per-query values go straight into the stage: lse2 and delta by
-  // LDS-DMA from the workspace, positions / segment ids by LDS-DMA from their
-  // arrays, or written as offset + row / 0 when there are none.  Rows past the end
-  // read as 0; their Q and dO rows are zero as well, so they add nothing.
-  static_assert(C::BM % 64 == 0, "whole wavefronts of rows");
-  auto issue = [&](Tq t, uint8_t* base) {
-    QStage<C> st(base);
-    const int h = g * G + t.hh;
-    const int i0 = t.it * C::BM;
-    tq.load(q + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq, st.q);
-    tg.load(dout + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq, st.g);
-    const int64_t li0 = (int64_t(b) * p.Hq + h) * p.Sq + i0;
-    const int wave = tid >> 6;
-    if (wave == 0) dma_dwords<C::BM>(lse2, li0, p.Sq - i0, st.lse2, lane);
-    if (kDK && wave == 1) dma_dwords<C::BM>(delta, li0, p.Sq - i0, st.delta, lane);
-    if (p.q_pos) {
-      if (wave == 2) dma_dwords<C::BM>(p.q_pos, i0, p.Sq - i0, st.qpos, lane);
-    } else if (tid < C::BM) {
-      st.qpos[tid] = p.q_offset + i0 + tid;
-    }
-    if (p.q_seg) {
-      if (wave == 3) dma_dwords<C::BM>(p.q_seg, int64_t(b) * p.Sq + i0, p.Sq - i0, st.qseg, lane);
-    } else if (tid < C::BM) {
-      st.qseg[tid] = 0;
-    }
-  };
-  auto publish = [&](uint8_t*) {
-    wait_all();
-    __syncthreads();
-  };
-
-  Tq cur = next_tile(Tq{h_lo, n_it - 1});
-  if (cur.it >= 0) {
-    issue(cur, smem);
-    publish(smem);
-    int buf = 0;
-    const MaskSpec ms = make_mask_spec(p.causal, p.window, p.q_seg != nullptr);
-    while (true) {
-      const Tq nxt = next_tile(step(cur));
-      const bool has_next = nxt.it >= 0;
-      uint8_t* nbase = smem + (buf ^ 1) * C::kStageMax;
-      if (has_next) issue(nxt, nbase);
-      const int wcls = wave_class(cur);
-      if (wcls != kEmpty) {
-        const QStage<C> st(smem + buf * C::kStageMax);
-        // One instantiation for masked tiles, one for full tiles, each branch-free
-        // (the mask goes into the exponent), so a tile's body is one basic block.
-        auto sdp = [&](int qb, f32x16& s, f32x16& dp) {
-          // S = Q K^T (and dP = dO V^T): lane column = this lane's key,
-          // register r = query row qb*32 + key_of_reg(r, hi)
-          s = f32x16{};
-          dp = f32x16{};
-          const int arow = qb * 32 + perm_row(l32);
-          // dK role: products alternate S (even) and dP (odd) over the k-steps
-          constexpr int kStep = kDK ? 2 : 1;
-          pipelined_products<kStep * C::KS, C::kAhead>(
-              [&](int i) { return ld_row<C::D>((i % kStep) ? st.g : st.q, arow, 2 * (i / kStep) + hi); },
-              [&](int i, bf16x8 f) {
-                if (i % kStep)
-                  dp = mma(f, vf[i / kStep], dp);
-                else
-                  s = mma(f, kf[i / kStep], s);
-              });
-        };
-        auto soft = [&](int qb, f32x16& s, const f32x16& dp, auto masked) {
-          constexpr bool kMasked = decltype(masked)::value;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int r0 = qb * 32 + key_of_reg(4 * jj, hi);
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(st.lse2 + r0);
-            f32x4 d4 = f32x4{0, 0, 0, 0};
-            if constexpr (kDK) d4 = *reinterpret_cast<const f32x4*>(st.delta + r0);
-            i32x4 qp4 = i32x4{0, 0, 0, 0}, qs4 = i32x4{0, 0, 0, 0};
-            if constexpr (kMasked) {
-              qp4 = *reinterpret_cast<const i32x4*>(st.qpos + r0);
-              qs4 = *reinterpret_cast<const i32x4*>(st.qseg + r0);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 4 * jj + i;
-              float x = fmaf(s[r], c2, -l4[i]);
-              // a hidden pair gets exponent -inf, so P = 0 exactly
-              if constexpr (kMasked) x = pair_visible(ms, qp4[i], my_kpos, qs4[i], my_kseg) ? x : -INFINITY;
-              const float pr = __builtin_amdgcn_exp2f(x);
-              if constexpr (kDK)
-                s[r] = pr * (dp[r] - d4[i]);  // dS
-              else
-                s[r] = pr;                    // P
-            }
-          }
-        };
-        // dV^T += dO^T P  or  dK^T += Q^T dS over the block's two 16-query k-steps;
-        // the A operand (dO^T or Q^T) is read transposed from the row-major tile
-        const uint16_t* at = kDK ? st.q : st.g;
-        auto grad = [&](int qb, const f32x16& s) {
-          const bf16x8 bfrag[2] = {to_bf16x8(s, 0), to_bf16x8(s, 8)};
-          pipelined_products<2 * C::DB, C::kAhead>(
-              [&](int i) { return ld_tr<C::D>(at, (qb * 2 + i / C::DB) * 16, (i % C::DB) * 32); },
-              [&](int i, bf16x8 f) { acc[i % C::DB] = mma(f, bfrag[i / C::DB], acc[i % C::DB]); });
-        };
-        auto body = [&](auto masked) {
-#pragma unroll
-          for (int qb = 0; qb < C::QBLK; ++qb) {
-            f32x16 s, dp;
-            sdp(qb, s, dp);
-            soft(qb, s, dp, masked);
-            grad(qb, s);
-          }
-        };
-        if (wcls == kPartial)
-          body(std::true_type{});
-        else
-          body(std::false_type{});
-      }
-      if (has_next)
-        publish(nbase);
-      else
-        __syncthreads();
-      if (!has_next) break;
-      cur = nxt;
-      buf ^= 1;
-    }
-  }
-
-  // epilogue: lane holds key column l32, dims d*32 + 8j + 4*hi + (0..3)
-  if (!key_ok) return;
-  const float sc = kDK ? p.scale : 1.0f;
-  float* gr = grad + ((int64_t(b) * p.Sk + wj0 + l32) * p.Hkv + g) * C::D;
-#pragma unroll
-  for (int d = 0; d < C::DB; ++d)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int off = d * 32 + 8 * j + 4 * hi;
-      f32x4 a{acc[d][4 * j] * sc, acc[d][4 * j + 1] * sc, acc[d][4 * j + 2] * sc, acc[d][4 * j + 3] * sc};
-      if (accumulate) a += *reinterpret_cast<const f32x4*>(gr + off);
-      *reinterpret_cast<f32x4*>(gr + off) = a;
-    }
-}
-
-// Paired dK / dV role of problems with no window, no segment ids and no position
-// arrays (positions are offset + index).  A workgroup owns keys [j0, j0 + 128) of kv
+// Paired dK / dV role.  kLane: the general instance (windows, segment ids, position
+// arrays); otherwise positions are offset + index and there is neither window nor
+// segment ids.  A workgroup owns keys [j0, j0 + 128) of kv
 // head g; wavefronts w and w + 4 (w < 4, the two wavefronts of one SIMD) own the same
 // 32 keys j0 + 32w + (0..31), one per lane column: wavefront w accumulates dK and
 // holds the keys' V rows, wavefront w + 4 accumulates dV and holds their K rows.
@@ -444,10 +132,10 @@ CP_DEVICE void key_role(const AttnProblem& p, const uint16_t* __restrict__ q, co
 //   phase B: the dK wavefront forms dS = P (dP - Delta) and dK^T += Q^T dS, the dV
 //     wavefront dV^T += dO^T P, both reading P from LDS.
 // Each P (and each exponential) is computed once: 7 products per block pair of keys
-// and queries with the dQ role, where the separate dV and dK roles take 8 (both
-// recompute S).  The phases are separated by a workgroup barrier, and in each phase
-// both wavefronts of a SIMD run three products per block.
-template <class C>
+// and queries with the dQ role, where separate dV and dK roles would take 8 (both
+// recomputing S).  The phases are separated by a workgroup barrier, and in each
+// phase both wavefronts of a SIMD run three products per block.
+template <class C, bool kLane>
 CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                          const float* __restrict__ lse2, const float* __restrict__ delta, float* __restrict__ dk,
@@ -484,7 +172,8 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
       kvf[s] = __builtin_bit_cast(bf16x8, key_ok ? x : u32x4{0, 0, 0, 0});
     }
   }
-  const int my_kpos = p.k_offset + key;
+  const int my_kpos = kLane ? kpos_at(p, key) : p.k_offset + key;
+  const int my_kseg = kLane ? kseg_at(p, b, key) : 0;
 
   f32x16 acc[C::DB];  // dK^T (dK wavefront) or dV^T (dV wavefront)
 #pragma unroll
@@ -493,7 +182,10 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
   const float c2 = p.scale * kLog2e;
   const int n_it = (p.Sq + BM - 1) / BM;
   // tiles (query head hh of the group's heads [h_lo, h_end), query tile it), walked
-  // from the last query tile down with the heads innermost, as in the key roles
+  // from the last query tile down with the heads innermost: every workgroup of this
+  // role starts at the end of the sequence and sweeps down at about the same pace, so
+  // the workgroups resident together read the same Q / dO tiles and the caches serve
+  // most of them
   struct Tq {
     int hh, it;
   };
@@ -504,16 +196,75 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
     }
     return t;
   };
-  auto qtile_span = [&](int it) { return q_span(p, b, it * BM, min(it * BM + BM, p.Sq) - 1); };
-  // every query tile of [it_lo, n_it) holds a visible pair (no window, no segment ids)
-  const int it_lo = first_true(0, n_it, [&](int it) { return !keys_after(p, qtile_span(it), wg_k); });
-  // this wavefront pair's class of a query tile, by range (empty ..., partial ..., full ...)
+  // Spans of the query tiles: with position or segment arrays (general instance) each
+  // is two dependent global loads, so up to kSpanTilesP of them are loaded once, in
+  // parallel, into LDS after the P buffer.
+  const bool span_cached = kLane && (p.q_pos != nullptr || p.q_seg != nullptr) && n_it <= C::kSpanTilesP;
+  i32x4* span_l = reinterpret_cast<i32x4*>(smem + C::kLdsPair);
+  if (span_cached) {
+    for (int t = tid; t < n_it; t += C::kThreads) {
+      const Span sp_ = q_span(p, b, t * BM, min(t * BM + BM, p.Sq) - 1);
+      span_l[t] = i32x4{sp_.pos_lo, sp_.pos_hi, sp_.seg_lo, sp_.seg_hi};
+    }
+    __syncthreads();
+  }
+  auto qtile_span = [&](int it) {
+    if (span_cached) {
+      const i32x4 x = span_l[it];
+      return Span{x[0], x[1], x[2], x[3]};
+    }
+    return q_span(p, b, it * BM, min(it * BM + BM, p.Sq) - 1);
+  };
+  // the query tiles live for this key block lie in [it_lo, it_hi) (queries wholly
+  // after the keys' window / segments are a suffix, those wholly before the keys a
+  // prefix)
+  const int it_hi =
+      kLane ? first_true(0, n_it, [&](int it) { return keys_before(p, qtile_span(it), wg_k); }) : n_it;
+  const int it_lo = first_true(0, it_hi, [&](int it) { return !keys_after(p, qtile_span(it), wg_k); });
+  // without a window or segment ids every query tile of [it_lo, it_hi) holds a visible
+  // pair and a wavefront pair's classes run by range (empty ..., partial ..., full ...);
+  // other problems classify up to 64 tiles at once, one per lane, else tile by tile
+  const bool dense = !kLane || (!p.window && !p.q_seg);
+  const bool lane_cls = kLane && !dense && it_hi - it_lo <= 64;
+  uint64_t live_m = 0, wfull_m = 0, wpart_m = 0;
+  if (lane_cls) {
+    const int it = it_lo + lane;
+    int cg = kEmpty, cw = kEmpty;
+    if (it < it_hi) {
+      const Span qs_ = qtile_span(it);
+      cg = classify(p, qs_, wg_k, false);
+      if (wave_live) cw = classify(p, qs_, wv_k, false);
+    }
+    live_m = __ballot(cg != kEmpty);
+    wfull_m = __ballot(cw == kFull);
+    wpart_m = __ballot(cw == kPartial);
+  }
+  // the live tile at or below t (heads innermost), or one with it = -1
+  auto next_tile = [&](Tq t) {
+    if (t.it >= it_hi) t = Tq{h_lo, it_hi - 1};
+    if (lane_cls) {
+      if (t.it < it_lo) return Tq{t.hh, -1};
+      const int sh = t.it - it_lo;
+      const uint64_t m = live_m & (sh == 63 ? ~uint64_t(0) : (uint64_t(2) << sh) - 1);
+      if (!m) return Tq{t.hh, -1};
+      const int it = it_lo + 63 - int(__builtin_clzll(m));
+      return it == t.it ? t : Tq{h_lo, it};
+    }
+    while (!dense && t.it >= it_lo && classify(p, qtile_span(t.it), wg_k, false) == kEmpty) t = step(t);
+    if (t.it < it_lo) t.it = -1;
+    return t;
+  };
   int it_wlo = 0, it_wfull = 0;
-  if (wave_live && p.causal) {
-    it_wlo = first_true(it_lo, n_it, [&](int it) { return !(wv_k.pos_lo > qtile_span(it).pos_hi); });
-    it_wfull = first_true(it_wlo, n_it, [&](int it) { return qtile_span(it).pos_lo >= wv_k.pos_hi; });
+  if (dense && wave_live && p.causal) {
+    it_wlo = first_true(it_lo, it_hi, [&](int it) { return !(wv_k.pos_lo > qtile_span(it).pos_hi); });
+    it_wfull = first_true(it_wlo, it_hi, [&](int it) { return qtile_span(it).pos_lo >= wv_k.pos_hi; });
   }
   auto wave_class = [&](Tq t) {
+    if (lane_cls) {
+      const uint64_t bit = uint64_t(1) << (t.it - it_lo);
+      return (wfull_m & bit) ? int(kFull) : (wpart_m & bit) ? int(kPartial) : int(kEmpty);
+    }
+    if (!dense) return wave_live ? classify(p, qtile_span(t.it), wv_k, false) : int(kEmpty);
     if (!wave_live || t.it < it_wlo) return int(kEmpty);
     return t.it >= it_wfull ? int(kFull) : int(kPartial);
   };
@@ -525,30 +276,50 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
   auto g_of = [&](uint8_t* base) { return q_of(base) + C::kTileMP; };
   auto l_of = [&](uint8_t* base) { return reinterpret_cast<float*>(g_of(base) + C::kTileMP); };
   auto d_of = [&](uint8_t* base) { return l_of(base) + BM; };
+  auto qp_of = [&](uint8_t* base) { return reinterpret_cast<int*>(d_of(base) + BM); };
+  auto qs_of = [&](uint8_t* base) { return qp_of(base) + BM; };
+  // per-row values of query tile i0 (rows past the end read as 0): lse2 and delta,
+  // and in the general instance the positions / segment ids (LDS-DMA from their
+  // arrays, or written as offset + row / 0)
+  auto issue_rows = [&](int h, int i0, uint8_t* base) {
+    const int64_t li0 = (int64_t(b) * p.Hq + h) * p.Sq + i0;
+    if (wave == 0) dma_dwords<BM>(lse2, li0, p.Sq - i0, l_of(base), lane);
+    if (wave == 1) dma_dwords<BM>(delta, li0, p.Sq - i0, d_of(base), lane);
+    if constexpr (kLane) {
+      if (p.q_pos) {
+        if (wave == 2) dma_dwords<BM>(p.q_pos, i0, p.Sq - i0, qp_of(base), lane);
+      } else if (tid < BM) {
+        qp_of(base)[tid] = p.q_offset + i0 + tid;
+      }
+      if (p.q_seg) {
+        if (wave == 3) dma_dwords<BM>(p.q_seg, int64_t(b) * p.Sq + i0, p.Sq - i0, qs_of(base), lane);
+      } else if (tid < BM) {
+        qs_of(base)[tid] = 0;
+      }
+    }
+  };
   auto issue = [&](Tq t, uint8_t* base) {
     const int h = g * G + t.hh;
     const int i0 = t.it * BM;
     tq.load(q + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq, q_of(base));
     tg.load(dout + int64_t(b) * p.Sq * qrs + int64_t(h) * C::D, qrs_bytes, i0, p.Sq, g_of(base));
-    const int64_t li0 = (int64_t(b) * p.Hq + h) * p.Sq + i0;
-    if (wave == 0) dma_dwords<BM>(lse2, li0, p.Sq - i0, l_of(base), lane);
-    if (wave == 1) dma_dwords<BM>(delta, li0, p.Sq - i0, d_of(base), lane);
+    issue_rows(h, i0, base);
   };
   // P fragment j of query block qb of this pair, this lane
   uint8_t* pbuf = smem + 2 * C::kStageMax;
   auto p_at = [&](int qb, int j) {
     return reinterpret_cast<bf16x8*>(pbuf + (((qb * 4 + pr) * 2 + j) * 64 + lane) * 16);
   };
-  const MaskSpec ms = make_mask_spec(p.causal, 0, 0);
+  const MaskSpec ms = make_mask_spec(p.causal, kLane ? p.window : 0, kLane && p.q_seg != nullptr);
 
-  Tq cur = Tq{h_lo, n_it - 1};
+  Tq cur = next_tile(Tq{h_lo, it_hi - 1});
   if (cur.it >= it_lo) {
     issue(cur, smem);
     wait_all();
     __syncthreads();
     int buf = 0;
     while (true) {
-      Tq nxt = step(cur);
+      Tq nxt = next_tile(step(cur));
       const bool has_next = nxt.it >= it_lo;
       uint8_t* base = smem + buf * C::kStageMax;
       // The next tile's Q and dO rows are staged by 2 kIter LDS-DMA loads per thread.
@@ -561,11 +332,7 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
       const auto rq = C::TileMP::rows_rsrc(q + int64_t(b) * p.Sq * qrs + int64_t(nh) * C::D, qrs_bytes, ni0, p.Sq);
       const auto rg =
           C::TileMP::rows_rsrc(dout + int64_t(b) * p.Sq * qrs + int64_t(nh) * C::D, qrs_bytes, ni0, p.Sq);
-      if (has_next) {
-        const int64_t li0 = (int64_t(b) * p.Hq + nh) * p.Sq + ni0;
-        if (wave == 0) dma_dwords<BM>(lse2, li0, p.Sq - ni0, l_of(nbase), lane);
-        if (wave == 1) dma_dwords<BM>(delta, li0, p.Sq - ni0, d_of(nbase), lane);
-      }
+      if (has_next) issue_rows(nh, ni0, nbase);
       constexpr int kIt = C::TileMP::kIter;
       auto dma_step = [&](int j) {
         if (j < 2 * kIt && has_next) {
@@ -585,6 +352,8 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
       const float* ls = l_of(base);
       const float* ds = d_of(base);
       const int qpos0 = p.q_offset + cur.it * BM;
+      const int* qps = qp_of(base);  // general instance: the tile's positions / segment ids
+      const int* qss = qs_of(base);
       // ---- phase A: dP (dK wavefront) or S and P (dV wavefront) of the three query
       // blocks.  The exponentials take as long as the products (the transcendental
       // unit runs at a quarter of the vector rate), so the dV wavefront spreads those
@@ -616,9 +385,13 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
             // P = 2^(S c2 - lse2) of score r of block qb (masked on partial tiles)
             auto exp_at = [&](int qb, int r) {
               float x = fmaf(sp[qb][r], c2, -l4[r >> 2][r & 3]);
-              if constexpr (kMasked)
-                x = pair_visible(ms, qpos0 + qb * 32 + key_of_reg(r & ~3, hi) + (r & 3), my_kpos, 0, 0) ? x
-                                                                                                     : -INFINITY;
+              if constexpr (kMasked) {
+                const int row = qb * 32 + key_of_reg(r & ~3, hi) + (r & 3);
+                if constexpr (kLane)
+                  x = pair_visible(ms, qps[row], my_kpos, qss[row], my_kseg) ? x : -INFINITY;
+                else
+                  x = pair_visible(ms, qpos0 + row, my_kpos, 0, 0) ? x : -INFINITY;
+              }
               sp[qb][r] = __builtin_amdgcn_exp2f(x);
             };
             auto store_p = [&](int qb) {
@@ -791,10 +564,10 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
   // the key tiles live for this query block lie in [kt_lo, kt_hi)
   const int kt_lo = first_true(0, n_kt, [&](int kt) { return !keys_before(p, wg_q, ktile_span(kt)); });
   const int kt_hi = first_true(kt_lo, n_kt, [&](int kt) { return keys_after(p, wg_q, ktile_span(kt)); });
-  // dense as in the key roles: no classification inside [kt_lo, kt_hi)
+  // without a window or segment ids: no classification inside [kt_lo, kt_hi)
   const bool dense = !p.window && !p.q_seg;
   // other problems with at most 64 key tiles in the range: all classified at once,
-  // one tile per lane, as in the key roles
+  // one tile per lane
   const bool lane_cls = kLane && !dense && kt_hi - kt_lo <= 64;
   uint64_t live_m = 0, wfull_m = 0, wpart_m = 0;
   if (lane_cls) {
@@ -843,8 +616,9 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
   auto ks_of = [&](uint8_t* base) { return reinterpret_cast<uint16_t*>(base); };
   auto vs_of = [&](uint8_t* base) { return ks_of(base) + C::kTileN; };
   auto kp_of = [&](uint8_t* base) { return reinterpret_cast<int*>(vs_of(base) + C::kTileN); };
-  // key positions / segment ids of the tile straight into the stage (as in the
-  // key roles); keys past the end are masked by their index
+  // key positions / segment ids of the tile straight into the stage (LDS-DMA from
+  // their arrays, or written as offset + index / 0); keys past the end are masked by
+  // their index
   static_assert(C::BN % 64 == 0, "whole wavefronts of keys");
   auto issue = [&](int kt, uint8_t* base) {
     tk.load(kbase, krs_bytes, kt * C::BN, p.Sk, ks_of(base));
@@ -957,10 +731,10 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
 }
 
 // ---- fused launch ------------------------------------------------------------------
-// Key-side items (dK then dV of each key block, key blocks lowest first = heaviest
-// under a causal mask) and query-side items (query blocks highest first) are merged
-// at the ratio of their counts, then rotated within each round of 8 workgroups so
-// that every XCD receives a fair share of each role.
+// Key-side items (key blocks lowest first = heaviest under a causal mask) and
+// query-side items (query blocks highest first) are merged at the ratio of their
+// counts, then rotated within each round of 8 workgroups so that every XCD receives
+// a fair share of each role.
 struct BwdArgs {
   AttnProblem p;
   const uint16_t* q;
@@ -973,8 +747,7 @@ struct BwdArgs {
   float* dk;
   float* dv;
   int accumulate;
-  int n_kv;  // key-side items = 2 * B * Hkv * 256-key blocks * hsplit (attn_bwd_kernel)
-             // or B * Hkv * 128-key blocks * hsplit (attn_bwd_pair_kernel)
+  int n_kv;  // key-side items = B * Hkv * 128-key blocks * hsplit
   int n_q;   // query-side items = B * Hq * query blocks
   // key-side items of grouped-query problems on small grids take half of the group's
   // query heads each (hsplit = 2): the second half's dK / dV go to part
@@ -983,61 +756,25 @@ struct BwdArgs {
   float* part;
 };
 
+// One grid of paired dK / dV items (128 keys each; on small grouped-query grids
+// split over two halves of the group's query heads) and dQ items.  kLane: the
+// general instance (windows, segment ids, position arrays: per-tile classification
+// of up to 64 tiles at once, masks from the staged positions / segment ids); the
+// other instance serves problems whose positions are offset + index and carries
+// none of that, so its register allocation is unaffected.
 template <class C, bool kLane>
-__global__ __launch_bounds__(C::kThreads) void attn_bwd_kernel(BwdArgs a) {
-  __shared__ __align__(16) uint8_t smem[C::kLdsBytes];
+__global__ __launch_bounds__(C::kThreads) void attn_bwd_pair_kernel(BwdArgs a) {
+  __shared__ __align__(16) uint8_t smem[kLane ? C::kLdsPairL : C::kLdsPair];
   const AttnProblem p = specialize<kLane>(a.p);
   const int64_t N = int64_t(a.n_kv) + a.n_q;
   // Workgroups go to the 8 XCDs round-robin by index.  Within each round of 8
   // consecutive workgroups the items are rotated by the round number, so that the
-  // periodic role pattern of the interleaved list cannot alias with the XCD index
-  // (at a 1:2 key/query ratio it would put every dK item on the even XCDs).
+  // periodic role pattern of the interleaved list cannot alias with the XCD index.
   const int64_t u = blockIdx.x / 8;
   const int64_t width = N - 8 * u < 8 ? N - 8 * u : 8;
   const int64_t L = 8 * u + (blockIdx.x % 8 + u) % width;
   // head-split grids list every key-side item first (they are the heavy ones);
   // others interleave the two sides in proportion
-  const bool kv_first = kLane && a.hsplit > 1;
-  const int64_t before = kv_first ? (L < a.n_kv ? L : a.n_kv) : (L * a.n_kv) / N;  // key-side items before L
-  const bool kv_side = kv_first ? L < a.n_kv : ((L + 1) * a.n_kv) / N > before;
-  if (kv_side) {
-    const int i = int(before);
-    const int hs = kLane ? a.hsplit : 1;
-    const int pair = (i >> 1) / hs;  // the subsets of a key block are neighbours
-    const int sub = (i >> 1) % hs;
-    const int bg = pair % (p.B * p.Hkv);
-    const int kt = pair / (p.B * p.Hkv);
-    const int G = p.Hq / p.Hkv;
-    const int h_lo = sub * G / hs, h_end = (sub + 1) * G / hs;
-    const int64_t plane = int64_t(p.B) * p.Sk * p.Hkv * C::D;
-    if ((i & 1) == 0)
-      key_role<C, true, kLane>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, sub ? a.part : a.dk,
-                               sub ? 0 : a.accumulate, smem, kt, bg % p.Hkv, bg / p.Hkv, h_lo, h_end);
-    else
-      key_role<C, false, kLane>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, sub ? a.part + plane : a.dv,
-                                sub ? 0 : a.accumulate, smem, kt, bg % p.Hkv, bg / p.Hkv, h_lo, h_end);
-  } else {
-    const int i = int(L - before);
-    const int bh = i % (p.B * p.Hq);
-    const int r = i / (p.B * p.Hq);
-    const int n_qt = (p.Sq + C::kRows - 1) / C::kRows;
-    dq_role<C, kLane>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dq, a.accumulate, smem, p.causal ? n_qt - 1 - r : r,
-               bh % p.Hq, bh / p.Hq);
-  }
-}
-
-// The grid of problems with no window, segment ids or position arrays: the paired
-// dK / dV items (128 keys each, split over two halves of the group's query heads on
-// small grids as in attn_bwd_kernel) and the dQ items, in the order and XCD rotation
-// of attn_bwd_kernel.
-template <class C>
-__global__ __launch_bounds__(C::kThreads) void attn_bwd_pair_kernel(BwdArgs a) {
-  __shared__ __align__(16) uint8_t smem[C::kLdsPair];
-  const AttnProblem p = specialize<false>(a.p);
-  const int64_t N = int64_t(a.n_kv) + a.n_q;
-  const int64_t u = blockIdx.x / 8;
-  const int64_t width = N - 8 * u < 8 ? N - 8 * u : 8;
-  const int64_t L = 8 * u + (blockIdx.x % 8 + u) % width;
   const bool kv_first = a.hsplit > 1;
   const int64_t before = kv_first ? (L < a.n_kv ? L : a.n_kv) : (L * a.n_kv) / N;  // key-side items before L
   const bool kv_side = kv_first ? L < a.n_kv : ((L + 1) * a.n_kv) / N > before;
@@ -1049,7 +786,7 @@ __global__ __launch_bounds__(C::kThreads) void attn_bwd_pair_kernel(BwdArgs a) {
     const int bg = blk % (p.B * p.Hkv);
     const int G = p.Hq / p.Hkv;
     const int64_t plane = int64_t(p.B) * p.Sk * p.Hkv * C::D;
-    pair_role<C>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, sub ? a.part : a.dk, sub ? a.part + plane : a.dv,
+    pair_role<C, kLane>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, sub ? a.part : a.dk, sub ? a.part + plane : a.dv,
                  sub ? 0 : a.accumulate, smem, blk / (p.B * p.Hkv), bg % p.Hkv, bg / p.Hkv, sub * G / hs,
                  (sub + 1) * G / hs);
   } else {
@@ -1057,7 +794,7 @@ __global__ __launch_bounds__(C::kThreads) void attn_bwd_pair_kernel(BwdArgs a) {
     const int bh = i % (p.B * p.Hq);
     const int r = i / (p.B * p.Hq);
     const int n_qt = (p.Sq + C::kRows - 1) / C::kRows;
-    dq_role<C, false, 1>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dq, a.accumulate, smem,
+    dq_role<C, kLane, kLane ? 2 : 1>(p, a.q, a.k, a.v, a.dout, a.lse2, a.delta, a.dq, a.accumulate, smem,
                          p.causal ? n_qt - 1 - r : r, bh % p.Hq, bh / p.Hq);
   }
 }
@@ -1075,7 +812,9 @@ __global__ __launch_bounds__(256) void head_split_sum_kernel(int64_t n4, float* 
 
 // Key-side items per (kv head, key block) for this problem: 2 for problems with
 // grouped heads whose grid is under 16 rounds of workgroups (one per CU); each
-// key-side item then walks half of the group's query heads.  Without the split the
+// key-side item then walks half of the group's query heads.  (Measured with the
+// separate dK and dV roles the kernel had before the paired role; the item count
+// below is the same: two per 256 keys then, one per 128 keys now.)  Without the split the
 // key-side items, G times heavier than the query-side ones, set the time: on small
 // grids the largest of them outlasts the average load of a CU, and on larger ones
 // they leave the longer tail.  Measured (bf16, D=128, causal): 1.5-1.8x faster at
@@ -1107,23 +846,19 @@ hipError_t launch_d(const AttnProblem& p, const void* q, const void* k, const vo
   using C = BwdCfg<D>;
   static_assert(C::kRows == 256, "bwd_hsplit counts 256-row items");
   const int hs = bwd_hsplit(p);
-  // the paired dK / dV role: no window or segment ids, positions offset + index
-  const bool pair = !p.window && !p.q_seg && !p.q_pos && !p.k_pos;
-  const bool general = !pair && (p.window || p.q_seg || hs > 1);
+  // the general instance takes windows, segment ids and position arrays
+  const bool general = p.window || p.q_seg || p.q_pos || p.k_pos;
   BwdArgs a{p, static_cast<U>(q), static_cast<U>(k), static_cast<U>(v), static_cast<U>(dout), lse2, delta,
-            dq, dk, dv, accumulate,
-            pair ? p.B * p.Hkv * ((p.Sk + C::kPairKeys - 1) / C::kPairKeys) * hs
-                 : 2 * p.B * p.Hkv * ((p.Sk + C::kRows - 1) / C::kRows) * hs,
+            dq, dk, dv, accumulate, p.B * p.Hkv * ((p.Sk + C::kPairKeys - 1) / C::kPairKeys) * hs,
             p.B * p.Hq * ((p.Sq + C::kRows - 1) / C::kRows), hs, delta + 2 * bwd_row_plane(rows)};
   {
     ProfScope ps(s, kProfBwdMfma);
-    // the general instance: windowed / segmented problems, and head-split grids
     if (general)
-      hipLaunchKernelGGL((attn_bwd_kernel<C, true>), dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s, a);
-    else if (pair)
-      hipLaunchKernelGGL(attn_bwd_pair_kernel<C>, dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s, a);
+      hipLaunchKernelGGL((attn_bwd_pair_kernel<C, true>), dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s,
+                         a);
     else
-      hipLaunchKernelGGL((attn_bwd_kernel<C, false>), dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s, a);
+      hipLaunchKernelGGL((attn_bwd_pair_kernel<C, false>), dim3(unsigned(a.n_kv + a.n_q)), dim3(C::kThreads), 0, s,
+                         a);
     if (hs > 1) {
       const int64_t n4 = int64_t(p.B) * p.Sk * p.Hkv * (D / 4);
       hipLaunchKernelGGL(head_split_sum_kernel, dim3(unsigned((2 * n4 + 255) / 256)), dim3(256), 0, s, n4, dk, dv,
