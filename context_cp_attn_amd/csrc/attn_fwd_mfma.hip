@@ -49,6 +49,24 @@ using namespace mfma;
 
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
+// LDS reads at explicit byte addresses.  The forward keeps the lane-dependent part of
+// every operand address in a few registers and adds the stage and product offsets as
+// instruction immediates, so one register set serves every stage of both key groups.
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+CP_DEVICE uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p));
+}
+CP_DEVICE bf16x8 lds_ld8(uint32_t a) { return *(const lds_bf16x8*)(uintptr_t(a)); }
+CP_DEVICE bf16x8 lds_tr8(uint32_t a0, uint32_t a1) {
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t(a0)));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t(a1)));
+  return __builtin_bit_cast(bf16x8, v8i16(__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7)));
+}
+// Keeps v in a register, redefined here as far as the optimizer knows: sums of it
+// and constants formed after this point are not hoisted out of the loop around it.
+CP_DEVICE void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
 // NW row wavefronts (32 query rows each) per key group; NS key groups (1 or 2) that
 // take alternate live key tiles of the same rows and combine their partial softmax
 // states at the end (for grids too small to fill the chip with whole tiles).
@@ -288,6 +306,27 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     stage_aux(kt, stage);
   };
   auto stage_of = [&](int buf) { return smem + ((C::SPLIT ? 0 : grp) * 2 + buf) * C::kStageBytes; };
+  // Lane-dependent byte offsets (within this group's stage 0, the group's stage base
+  // included) of the K row reads of S^T (one per k-step; the key block adds
+  // kb * 32 rows) and of the two halves of the V^T transposed reads of O^T (one per
+  // d block; the key step adds 16 rows).  The XOR swizzle of a row depends on the
+  // row modulo 16 only, so these are the same for every key block / key step.
+  uint32_t koff[C::KS], voff[2 * C::DB];
+  {
+    const uint32_t g0 = lds_addr(stage_of(0));
+    const int pr = perm_row(l32);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) koff[ks] = g0 + 2u * uint32_t(rm_elem<C::D>(pr, 2 * ks + hi));
+    const int gq = lane >> 4, iq = lane & 15;
+    const int r = 8 * (gq >> 1) + (iq >> 2);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int d = db * 32 + 16 * (gq & 1) + 4 * (iq & 3);
+      const uint32_t vt = g0 + 2u * C::kTileElems;
+      voff[2 * db] = vt + 2u * uint32_t(r * C::D + (((d >> 3) ^ chunk_xor<C::D>(r)) << 3) + (d & 7));
+      voff[2 * db + 1] = vt + 2u * uint32_t((r + 4) * C::D + (((d >> 3) ^ chunk_xor<C::D>(r + 4)) << 3) + (d & 7));
+    }
+  }
 
   // Live tiles are taken in pairs (t0, t1): key group 0 multiplies t0, group 1 t1
   // (with one group, t1 is unused).  Every wavefront walks the same pair sequence,
@@ -307,6 +346,86 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     wait_all();
     __syncthreads();
     const MaskSpec ms = make_mask_spec(p.causal, p.window, p.q_seg != nullptr);
+    f32x16 s[C::KB];    // S^T of a tile between its products and its softmax
+    bf16x8 pf[C::PT];   // P^T of a tile between its softmax and its V product
+    // product lists: S^T = K Q^T from stage B's K tile (kb = i % KB, k-step i / KB)
+    // and O^T += V^T P^T from stage B's V tile (d block i % DB, key step i / DB)
+    constexpr int kNS = C::KS * C::KB, kNV = C::PT * C::DB;
+    auto s_load = [&](auto bufc, int i) {
+      constexpr uint32_t sb = decltype(bufc)::value * C::kStageBytes;
+      return lds_ld8(koff[i / C::KB] + (sb + 2u * (i % C::KB) * 32 * C::D));
+    };
+    auto s_mul = [&](int i, bf16x8 f) { s[i % C::KB] = mma(f, qf[i / C::KB], s[i % C::KB]); };
+    auto v_load = [&](auto bufc, int i) {
+      const uint32_t rb = decltype(bufc)::value * C::kStageBytes + 2u * (i / C::DB) * 16 * C::D;
+      return lds_tr8(voff[2 * (i % C::DB)] + rb, voff[2 * (i % C::DB) + 1] + rb);
+    };
+    auto v_mul = [&](int i, bf16x8 f) { o[i % C::DB] = mma(f, pf[i / C::DB], o[i % C::DB]); };
+    auto pin_k = [&]() {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) pin(koff[ks]);
+    };
+    auto pin_v = [&]() {
+#pragma unroll
+      for (int j = 0; j < 2 * C::DB; ++j) pin(voff[j]);
+    };
+    // mask of tile kt (class wcls; key positions / segment ids from stage B) and
+    // its online softmax: s -> m, l (rescaling o) and pf
+    auto softmax = [&](auto bufc, int kt, int wcls) {
+      const uint16_t* ks_l = reinterpret_cast<const uint16_t*>(stage_of(decltype(bufc)::value));
+      const int* kpos_l = reinterpret_cast<const int*>(ks_l + 2 * C::kTileElems);
+      const int* kseg_l = kpos_l + C::BN;
+      if (wcls == kPartial) {
+        // keys of this lane's registers: key_of_reg(0, hi) plus a constant, so the
+        // bound test compares constants with one per-lane limit
+        const int lim = p.Sk - kt * C::BN - key_of_reg(0, hi);
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            // registers 4jj..4jj+3 hold 4 consecutive keys
+            const int rel = kb * 32 + key_of_reg(4 * jj, 0);  // key - key_of_reg(0, hi)
+            const int kk0 = kb * 32 + key_of_reg(4 * jj, hi);
+            const i32x4 kp4 = *reinterpret_cast<const i32x4*>(kpos_l + kk0);
+            const i32x4 kg4 = *reinterpret_cast<const i32x4*>(kseg_l + kk0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              // bitwise &: a short-circuit && here became one branch per element
+              const bool vis = (rel + i < lim) & pair_visible(ms, qp, kp4[i], qs, kg4[i]);
+              s[kb][4 * jj + i] = vis ? s[kb][4 * jj + i] : -INFINITY;
+            }
+          }
+      }
+
+      // online softmax (base 2) with lazy rescaling
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = max_halves(mx) * c2;
+      if (__any(mx > m + kRescaleLog2)) {
+        const float mnew = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - (mnew == -INFINITY ? 0.0f : mnew));
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
+      }
+      const float muse = m == -INFINITY ? 0.0f : m;
+      float rs = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -muse));
+          s[kb][r] = pv;
+          rs += pv;
+        }
+      l += rs;
+#pragma unroll
+      for (int t = 0; t < C::PT; ++t) pf[t] = to_bf16x8(s[t >> 1], 8 * (t & 1));
+    };
     // one tile per call, the stage index a compile-time constant (the loop below
     // alternates 0 and 1), so the swizzled LDS addresses of each stage are fixed
     auto iter = [&](auto bufc) -> bool {
@@ -317,78 +436,16 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
       const bool has_next = n0 < n_kt;
       // the DMA of the next tile runs while this one is multiplied
       if (nxt < n_kt) stage_load(nxt, stage_of(buf ^ 1));
-
       const int wcls = (wave_live && cur < n_kt) ? wave_class(cur) : kEmpty;
       if (wcls != kEmpty) {
-        const uint8_t* stage = stage_of(buf);
-        const uint16_t* ks_l = reinterpret_cast<const uint16_t*>(stage);
-        const uint16_t* vs_l = ks_l + C::kTileElems;
-        const int* kpos_l = reinterpret_cast<const int*>(vs_l + C::kTileElems);
-        const int* kseg_l = kpos_l + C::BN;
-
-        // S^T = K Q^T (K rows read ahead of their products)
-        f32x16 s[C::KB];
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
-        pipelined_products<C::KS * C::KB, C::kAhead>(
-            [&](int i) { return ld_row<C::D>(ks_l, (i % C::KB) * 32 + perm_row(l32), 2 * (i / C::KB) + hi); },
-            [&](int i, bf16x8 f) { s[i % C::KB] = mma(f, qf[i / C::KB], s[i % C::KB]); });
-
-        if (wcls == kPartial) {
-          const int nvalid = p.Sk - cur * C::BN;
-#pragma unroll
-          for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              // registers 4jj..4jj+3 hold 4 consecutive keys
-              const int kk0 = kb * 32 + key_of_reg(4 * jj, hi);
-              const i32x4 kp4 = *reinterpret_cast<const i32x4*>(kpos_l + kk0);
-              const i32x4 kg4 = *reinterpret_cast<const i32x4*>(kseg_l + kk0);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                // bitwise &: a short-circuit && here became one branch per element
-                const bool vis = (kk0 + i < nvalid) & pair_visible(ms, qp, kp4[i], qs, kg4[i]);
-                s[kb][4 * jj + i] = vis ? s[kb][4 * jj + i] : -INFINITY;
-              }
-            }
-        }
-
-        // online softmax (base 2) with lazy rescaling
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = max_halves(mx) * c2;
-        if (__any(mx > m + kRescaleLog2)) {
-          const float mnew = fmaxf(m, mx);
-          const float alpha = __builtin_amdgcn_exp2f(m - (mnew == -INFINITY ? 0.0f : mnew));
-          m = mnew;
-          l *= alpha;
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
-        }
-        const float muse = m == -INFINITY ? 0.0f : m;
-        float rs = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -muse));
-            s[kb][r] = pv;
-            rs += pv;
-          }
-        l += rs;
-
-        // O^T += V^T P^T (V^T fragments read ahead of their products)
-        bf16x8 pf[C::PT];
-#pragma unroll
-        for (int t = 0; t < C::PT; ++t) pf[t] = to_bf16x8(s[t >> 1], 8 * (t & 1));
-        pipelined_products<C::PT * C::DB, C::kAhead>(
-            [&](int i) { return ld_tr<C::D>(vs_l, (i / C::DB) * 16, (i % C::DB) * 32); },
-            [&](int i, bf16x8 f) { o[i % C::DB] = mma(f, pf[i / C::DB], o[i % C::DB]); });
+        pin_k();
+        pipelined_products<kNS, C::kAhead>([&](int i) { return s_load(bufc, i); }, s_mul);
+        softmax(bufc, cur, wcls);
+        pin_v();
+        pipelined_products<kNV, C::kAhead>([&](int i) { return v_load(bufc, i); }, v_mul);
       }
-
       wait_all();
       __syncthreads();
       t0 = n0;
