@@ -370,6 +370,16 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
                 sp[i / C::KS] = mma(f, kvf[i % C::KS], sp[i / C::KS]);
                 if ((i & 1) == 0) dma_step(i / 2);
               });
+          // dP - Delta now: this wavefront waits for the dV wavefront's exponentials
+          // at the barrier anyway, and phase B (where it forms dS) is its long one
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds + qb * 32 + key_of_reg(4 * jj, hi));
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sp[qb][4 * jj + i] -= d4[i];
+            }
         } else {
           // raised priority: the SIMD's matrix core serves this wavefront's S products
           // first, so its exponentials start early and overlap the dK wavefront's dP
@@ -438,20 +448,14 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
         for (int qb = 0; qb < QB; ++qb) {
           bf16x8 bfrag[2] = {*p_at(qb, 0), *p_at(qb, 1)};
           if (!is_dv) {
-            // dS = P (dP - Delta), in place of P
+            // dS = P (dP - Delta), in place of P (dP - Delta formed in phase A)
             f32x16 dp = sp[qb];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int r0 = qb * 32 + key_of_reg(4 * jj, hi);
-              const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds + r0);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int r = 4 * jj + i;
-                // P of this key and row from its bf16 fragment (bf16 is the high half of a float)
-                const uint32_t w = __builtin_bit_cast(u32x4, bfrag[r >> 3])[(r & 7) >> 1];
-                const float pr_ = __uint_as_float((r & 1) ? (w & 0xffff0000u) : (w << 16));
-                dp[r] = pr_ * (dp[r] - d4[i]);
-              }
+            for (int r = 0; r < 16; ++r) {
+              // P of this key and row from its bf16 fragment (bf16 is the high half of a float)
+              const uint32_t w = __builtin_bit_cast(u32x4, bfrag[r >> 3])[(r & 7) >> 1];
+              const float pr_ = __uint_as_float((r & 1) ? (w & 0xffff0000u) : (w << 16));
+              dp[r] = pr_ * dp[r];
             }
             bfrag[0] = to_bf16x8(dp, 0);
             bfrag[1] = to_bf16x8(dp, 8);
