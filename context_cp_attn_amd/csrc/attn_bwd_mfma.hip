@@ -155,9 +155,9 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
   const int64_t krs = int64_t(p.Hkv) * C::D;
   const int64_t qrs = int64_t(p.Hq) * C::D;
 
-  const Span wg_k = k_span(p, b, j0, min(j0 + C::kPairKeys, p.Sk) - 1);
+  const Span wg_k = uniform(k_span(p, b, j0, min(j0 + C::kPairKeys, p.Sk) - 1));
   const bool wave_live = wj0 < p.Sk;
-  const Span wv_k = k_span(p, b, min(wj0, p.Sk - 1), min(wj0 + 32, p.Sk) - 1);
+  const Span wv_k = uniform(k_span(p, b, min(wj0, p.Sk - 1), min(wj0 + 32, p.Sk) - 1));
 
   // K rows (dV wavefront: S) or V rows (dK wavefront: dP) of this lane's key as B
   // fragments (k-slots = head dims)
@@ -480,7 +480,9 @@ CP_DEVICE void pair_role(const AttnProblem& p, const uint16_t* __restrict__ q, c
   // epilogue: lane holds key column l32, dims d*32 + 8j + 4*hi + (0..3)
   if (!key_ok) return;
   const float sc = is_dv ? 1.0f : p.scale;
-  float* gr = (is_dv ? dv : dk) + ((int64_t(b) * p.Sk + wj0 + l32) * p.Hkv + g) * C::D;
+  int kcol = wj0 + l32;
+  pin(kcol);  // the row address is formed here, not kept live from the prologue
+  float* gr = (is_dv ? dv : dk) + ((int64_t(b) * p.Sk + kcol) * p.Hkv + g) * C::D;
 #pragma unroll
   for (int d = 0; d < C::DB; ++d)
 #pragma unroll
@@ -512,9 +514,9 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
   const int64_t krs = int64_t(p.Hkv) * C::D;
   const int64_t qrs = int64_t(p.Hq) * C::D;
 
-  const Span wg_q = q_span(p, b, q0, min(q0 + C::kRows, p.Sq) - 1);
+  const Span wg_q = uniform(q_span(p, b, q0, min(q0 + C::kRows, p.Sq) - 1));
   const bool wave_live = wq0 < p.Sq;
-  const Span wv_q = q_span(p, b, min(wq0, p.Sq - 1), min(wq0 + 32, p.Sq) - 1);
+  const Span wv_q = uniform(q_span(p, b, min(wq0, p.Sq - 1), min(wq0 + 32, p.Sq) - 1));
 
   const int row = min(wq0 + l32, p.Sq - 1);
   const bool row_ok = wq0 + l32 < p.Sq;
@@ -721,7 +723,9 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
   }
 
   if (!row_ok) return;
-  float* dqr = dq + (int64_t(b) * p.Sq + row) * qrs + int64_t(h) * C::D;
+  int qrow = row;
+  pin(qrow);  // the row address is formed here, not kept live from the prologue
+  float* dqr = dq + (int64_t(b) * p.Sq + qrow) * qrs + int64_t(h) * C::D;
 #pragma unroll
   for (int d = 0; d < C::DB; ++d)
 #pragma unroll

@@ -63,9 +63,6 @@ CP_DEVICE bf16x8 lds_tr8(uint32_t a0, uint32_t a1) {
   const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t(a1)));
   return __builtin_bit_cast(bf16x8, v8i16(__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7)));
 }
-// Keeps v in a register, redefined here as far as the optimizer knows: sums of it
-// and constants formed after this point are not hoisted out of the loop around it.
-CP_DEVICE void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
 // NW row wavefronts (32 query rows each) per key group; NS key groups (1 or 2) that
 // take alternate live key tiles of the same rows and combine their partial softmax

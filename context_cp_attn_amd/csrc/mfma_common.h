@@ -63,6 +63,20 @@ enum : int { kEmpty = 0, kPartial = 1, kFull = 2 };
 struct Span {
   int pos_lo, pos_hi, seg_lo, seg_hi;
 };
+// Keeps v in a vector register, redefined here as far as the optimizer knows: values
+// derived from it after this point are computed there, neither hoisted out of the
+// loop around it nor kept live from earlier uses.
+template <class T>
+CP_DEVICE void pin(T& v) {
+  asm volatile("" : "+v"(v));
+}
+
+// A span of wave-uniform rows, held in scalar registers (the compiler cannot always
+// prove the uniformity of values loaded or derived from the wavefront index).
+CP_DEVICE Span uniform(const Span& s) {
+  return Span{__builtin_amdgcn_readfirstlane(s.pos_lo), __builtin_amdgcn_readfirstlane(s.pos_hi),
+              __builtin_amdgcn_readfirstlane(s.seg_lo), __builtin_amdgcn_readfirstlane(s.seg_hi)};
+}
 
 CP_DEVICE int qpos_at(const AttnProblem& p, int i) { return p.q_pos ? p.q_pos[i] : p.q_offset + i; }
 CP_DEVICE int kpos_at(const AttnProblem& p, int j) { return p.k_pos ? p.k_pos[j] : p.k_offset + j; }
