@@ -658,8 +658,13 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
       const int nxt = next_tile(cur + 1);
       const bool has_next = nxt < n_kt;
       uint8_t* nbase = smem + (buf ^ 1) * C::kStageMax;
-      if (has_next) issue(nxt, nbase);
       const int wcls = wave_class(cur);
+      // The next stage's loads.  Issued by all eight wavefronts at once they queue at
+      // the CU's address unit, so in the dense instance wavefronts w and w + 4 issue
+      // theirs during key block w % 4 of this stage (the general instance, which also
+      // stages positions / segment ids, would spill registers doing so).
+      const int my_kb = kLane ? -1 : __builtin_amdgcn_readfirstlane(wave & 3);
+      if (has_next && (wcls == kEmpty || my_kb < 0 || my_kb >= C::KB)) issue(nxt, nbase);
       if (wcls != kEmpty) {
         uint8_t* base = smem + buf * C::kStageMax;
         const uint16_t* ks = ks_of(base);
@@ -671,6 +676,7 @@ CP_DEVICE void dq_role(const AttnProblem& p, const uint16_t* __restrict__ q, con
           constexpr bool kMasked = decltype(masked)::value;
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb) {
+            if (!kLane && has_next && kb == my_kb) issue(nxt, nbase);
             // S^T = K Q^T and dP^T = V dO^T for 32 keys: lane column = this lane's query
             f32x16 s = f32x16{}, dp = f32x16{};
             const int arow = kb * 32 + perm_row(l32);
