@@ -178,6 +178,26 @@ class RingShare:
                 ops.lse_merge(acc, lse, blk_o, blk_l)
         return acc, lse
 
+    def forward_graph(self):
+        """This rank's ring forward captured as one HIP graph, for passes whose steps
+        are short enough that launching them costs time: returns (replay, out, lse).
+        ``replay()`` enqueues the whole pass on the current stream and leaves its
+        result in ``out`` / ``lse``, buffers owned by the graph; it reads the share's
+        q, k, v tensors at replay time.  One eager pass on a side stream runs first
+        (it fills the share's cached launch arguments, which capture must not create).
+        Not with CP_ATTN_DEBUG, whose checks synchronise the stream."""
+        if ops.DEBUG:
+            raise RuntimeError("forward_graph: the CP_ATTN_DEBUG checks cannot run under graph capture")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.forward()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            out, lse = self.forward()
+        return graph.replay, out, lse
+
     def backward(self, out, lse, dout, dq, dk, dv):
         """Accumulate this rank's gradients: dq [B,S/P,..] of its queries, and the
         partial dk/dv of every block into the whole-sequence dk/dv buffers."""

@@ -396,3 +396,32 @@ def test_dense_causal_multiblock_all_elements(cp):
     refs = oracle.attn_bwd(q, k, v, ro, rl, do)
     for got, ref in zip((dq, dk, dv), refs):
         assert max_err(f64(got), ref) <= grad_tol(ref)
+
+
+# ------------------------------------------------------------------ ring pass as a HIP graph
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_ring_forward_graph_replays(cp, fused):
+    """A rank's ring forward captured as one HIP graph: every replay, with eager
+    passes and synchronisations between the replays, equals the eager pass bit for
+    bit, and the result matches the oracle on sampled rows."""
+    P, S, H, D, r = 8, 4096, 4, 128, 3
+    say(f"ring graph: P={P} S={S} H={H} rank {r} fused={fused}")
+    q, k, v = cp_inputs.normal_tensors([(1, S, H, D)] * 3, seed=11)
+    qz, kz, vz = (cp.zigzag_reorder(t.cuda(), P) for t in (q, k, v))
+    ring = cp.drivers.RingShare(qz, kz, vz, P, r, fused=fused)
+    ref_o, ref_l = (t.clone() for t in ring.forward())
+    replay, go, gl = ring.forward_graph()
+    for rep in range(4):
+        go.fill_(float("nan"))
+        replay()
+        torch.cuda.synchronize()
+        assert torch.equal(go, ref_o) and torch.equal(gl, ref_l), f"replay {rep}"
+        eo, el = ring.forward()
+        torch.cuda.synchronize()
+        assert torch.equal(eo, ref_o) and torch.equal(el, ref_l), f"eager pass after replay {rep}"
+    pos = oracle.rank_positions(r, P, S, "zigzag")
+    pick = np.r_[0, 1, 255, 256, 300, 511]
+    qf, kf, vf = (f64(t) for t in (q, k, v))
+    ro, rl = oracle.attn_fwd(qf[:, pos[pick]], kf, vf, q_pos=pos[pick])
+    check_rows(f64(go)[:, pick], f64(gl)[:, :, pick], ro, rl, 1e-2, 1e-3)
