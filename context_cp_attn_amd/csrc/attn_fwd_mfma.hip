@@ -48,6 +48,9 @@ namespace {
 using namespace mfma;
 
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
+// longest live key-tile range (64-key tiles) of a fused ring step whose two key
+// groups synchronise on their own (blocks of up to 4096 keys)
+constexpr int kGroupSyncMaxTiles = 64;
 
 // LDS reads at explicit byte addresses.  The forward keeps the lane-dependent part of
 // every operand address in a few registers and adds the stage and product offsets as
@@ -345,15 +348,16 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
     wait_all();
     __syncthreads();
     const MaskSpec ms = make_mask_spec(p.causal, p.window, p.q_seg != nullptr);
-    // In the fused ring step the two key groups synchronise each on its own after
-    // every tile (each has its own stages), so they drift apart instead of meeting at
-    // one workgroup barrier: every wavefront of the group finishes its loads and LDS
-    // accesses, adds one to the group's counter and waits until all NW have arrived
-    // at this tile.  Measured: the llama2-7b ring pass (16 tiles per group and step)
-    // 4% faster; the long forward (hundreds of tiles per group) 1.5% slower, so it
-    // keeps the workgroup barrier.  The wait gives up after 2^22 polls, a safety bound
-    // no correct run reaches.
+    // In the fused ring step over a short block the two key groups synchronise each
+    // on its own after every tile (each has its own stages), so they drift apart
+    // instead of meeting at one workgroup barrier: every wavefront of the group
+    // finishes its loads and LDS accesses, adds one to the group's counter and waits
+    // until all NW have arrived at this tile.  Measured: the llama2-7b ring pass (32
+    // live tiles per workgroup and step) 4% faster; long walks (hundreds of tiles)
+    // 1.5-4% slower, so they keep the workgroup barrier.  The wait gives up after
+    // 2^22 polls, a safety bound no correct run reaches.
     constexpr bool kGroupSync = kMerge && C::NS > 1 && !C::SPLIT;
+    const bool gsync = kGroupSync && kt_hi - kt_lo <= kGroupSyncMaxTiles;
     int arrived = 0;
     auto group_barrier = [&]() {
       wait_all();
@@ -470,7 +474,7 @@ CP_DEVICE void fwd_body(const AttnProblem& p, const uint16_t* __restrict__ q, co
         pin_v();
         pipelined_products<kNV, C::kAhead>([&](int i) { return v_load(bufc, i); }, v_mul);
       }
-      if constexpr (kGroupSync) {
+      if (gsync) {
         group_barrier();
       } else {
         wait_all();
