@@ -372,6 +372,32 @@ def test_attn_fwd_merge(cp, name, dtype, D):
     check_close(acc, f64(acc2), TOL[dtype]["out"], "fused vs unfused")
 
 
+
+@pytest.mark.parametrize("case", ["64_tiles", "64_tiles_and_1_key", "65_tiles", "causal_straddle"])
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 128)])
+def test_attn_fwd_merge_group_sync_boundary(cp, case, dtype, D):
+    """The fused ring step on a grid of few query tiles walks each tile's keys with two
+    key groups of one workgroup.  Each group waits only for its own waves after a key
+    tile when the workgroup's live keys span at most 64 tiles of 64 keys, and for the
+    whole workgroup otherwise.  Both sides of that limit against the oracle: 4096 keys
+    (64 tiles), 4097 (a 65th tile of one key), 4160 (65 full tiles), and a causal
+    problem whose first query tile sees exactly 64 tiles and whose second sees 66."""
+    Sq, Hq, Hkv = 256, 2, 1
+    Sk, m = {"64_tiles": (4096, dict(causal=False)), "64_tiles_and_1_key": (4097, dict(causal=False)),
+             "65_tiles": (4160, dict(causal=False)),
+             "causal_straddle": (4300, dict(q_offset=4096 - 128, k_offset=0))}[case]
+    say(f"attn_fwd_merge group-sync boundary {case} D={D} {dtype}")
+    q, k, v = cp_inputs.normal_tensors([(1, Sq, Hq, D), (1, Sk, Hkv, D), (1, Sk, Hkv, D)], seed=41, dtype=dtype)
+    g = torch.Generator().manual_seed(42)
+    acc0 = torch.randn(1, Sq, Hq, D, generator=g)
+    lse0 = torch.randn(1, Hq, Sq, generator=g) + 4
+    acc, lacc = acc0.cuda(), lse0.cuda()
+    cp.attn_fwd_merge(q.cuda(), k.cuda(), v.cuda(), acc, lacc, **to_dev(m))
+    blk_o, blk_l = oracle.attn_fwd(q, k, v, **oracle_mask(m))
+    ref_o, ref_l = oracle.lse_merge(f64(acc0), f64(lse0), blk_o, blk_l)
+    check_lse(lacc, ref_l, TOL[dtype]["lse"])
+    check_close(acc, ref_o, TOL[dtype]["out"], "merged out")
+
 @pytest.mark.parametrize("name", ["causal_square", "offsets", "zigzag_pos", "packed_window", "empty_rows",
                                   "noncausal_window", "window_1", "offset_window", "gqa3", "noncausal",
                                   "mha_ragged", "mha_offsets", "mha_empty_rows"])
