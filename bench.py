@@ -24,7 +24,8 @@ dual-chunk-swap reorder, the Ulysses rank share of llama3.1-8b at 64K with cp=4
 (q [1,65536,8,128] on k/v [1,65536,2,128], fwd + bwd), the packed + windowed 8K ring
 share (4 ranks x 4
 steps, fused fwd + merge, bwd; striped as chosen automatically for packed
-sequences, and dual-chunk-swap), and llama3.1-8b at 16K on 16 ranks beyond its 8 kv
+sequences, and dual-chunk-swap; the whole pass, and each rank's share alone, the
+slowest of which sets a 4-GPU step), and llama3.1-8b at 16K on 16 ranks beyond its 8 kv
 heads (Ulysses 8 x ring 2, and Ulysses 16 with kv heads replicated).  The CPU oracle
 is timed on a bounded sample of the step's attention rows (cpu_baseline).
 """
@@ -181,7 +182,8 @@ def packed_work(seg, P, layout, window, D):
     """Visible (query, key) pairs per head of a causal packed + windowed sequence
     (counted from the segment ids: a query sees the keys of its own document no
     further back than the window), and the fraction of the forward's query-tile x
-    key-tile blocks that hold no visible pair over all P ranks' P ring steps."""
+    key-tile blocks that hold no visible pair over all P ranks' P ring steps, and the
+    visible pairs per head of each rank's queries."""
     import numpy as np
     S = seg.shape[0]
     start = np.zeros(S, dtype=np.int64)
@@ -197,15 +199,19 @@ def packed_work(seg, P, layout, window, D):
         c = S // (2 * P)
         pos = [np.r_[np.arange(r * c, (r + 1) * c), np.arange((2 * P - 1 - r) * c, (2 * P - r) * c)] for r in range(P)]
     empty = total = 0
+    rank_pairs = []
     for r in range(P):
+        rank_pairs.append(0)
         for src in range(P):
             qp, kp = pos[r], pos[src]
             vis = (kp[None, :] <= qp[:, None]) & (seg[qp][:, None] == seg[kp][None, :]) & \
                   (qp[:, None] - kp[None, :] < window)
+            rank_pairs[-1] += int(vis.sum())
             blk = vis.reshape(C // 128, 128, C // 64, 64).any(axis=(1, 3))
             empty += int((~blk).sum())
             total += blk.size
-    return pairs, empty / total
+    assert sum(rank_pairs) == pairs
+    return pairs, empty / total, rank_pairs
 
 
 def legs(torch, cp, cp_inputs, only=None):
@@ -310,23 +316,37 @@ def legs(torch, cp, cp_inputs, only=None):
             qz, kz, vz, dz, sz = (cp.zigzag_reorder(t, P, strategy=st) for t in (q, k, v, do, seg))
             shares = [cp.drivers.RingShare(qz, kz, vz, P, r, layout=layout, seg=sz, window=4096) for r in range(P)]
 
+            dk = torch.zeros(kz.shape, device="cuda")
+            dv = torch.zeros(vz.shape, device="cuda")
+
+            def rank_pass(r):
+                o, l = shares[r].forward()
+                ob = o.bfloat16()
+                dq = torch.zeros(1, C, Hq, D, device="cuda")
+                shares[r].backward(ob, l, dz[:, r * C:(r + 1) * C], dq, dk, dv)
+
             def packed_pass():
-                dk = torch.zeros(kz.shape, device="cuda")
-                dv = torch.zeros(vz.shape, device="cuda")
-                for r, sh in enumerate(shares):
-                    o, l = sh.forward()
-                    ob = o.bfloat16()
-                    dq = torch.zeros(1, C, Hq, D, device="cuda")
-                    sh.backward(ob, l, dz[:, r * C:(r + 1) * C], dq, dk, dv)
+                dk.zero_()
+                dv.zero_()
+                for r in range(P):
+                    rank_pass(r)
 
             packed_pass()
             ms = timed(torch, packed_pass, 3)
-            pairs, skipped = packed_work(seg[0].cpu().numpy(), P, layout, 4096, D)
+            # each rank's share alone: on P GPUs the ranks run at once and the step
+            # lasts as long as the slowest of them
+            rank_ms = [timed(torch, lambda: rank_pass(r), 3) for r in range(P)]
+            pairs, skipped, rank_pairs = packed_work(seg[0].cpu().numpy(), P, layout, 4096, D)
             fl = 12 * D * Hq * pairs  # forward 4*D + backward 8*D per visible pair and head
+            slow = max(rank_ms)
             out[f"packed_window_8k_cp4_all_ranks_{name}"] = {
                 "strategy": layout, "ms_per_pass": round(ms, 3), "visible_pairs_per_head": pairs,
                 "tflops": round(fl / ms / 1e9, 2), "frac": frac(fl / ms / 1e9, PEAK_BF16_TFLOPS),
-                "fwd_tiles_skipped_frac": round(skipped, 4)}
+                "fwd_tiles_skipped_frac": round(skipped, 4),
+                "rank_ms": [round(x, 3) for x in rank_ms], "rank_visible_pairs_per_head": rank_pairs,
+                "slowest_rank_ms": round(slow, 3),
+                "per_gpu_tflops_at_slowest_rank": round(fl / P / slow / 1e9, 2),
+                "per_gpu_frac_at_slowest_rank": frac(fl / P / slow / 1e9, PEAK_BF16_TFLOPS)}
     if only in (None, 'usp'):
         # beyond the kv head count, llama3.1-8b (32 q / 8 kv heads) at 16K tokens on 16 ranks:
         # Ulysses 8 within groups x ring 2 across them (USP), and Ulysses 16 with kv heads

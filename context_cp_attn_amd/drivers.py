@@ -33,8 +33,11 @@ def auto_strategy(packed: bool) -> int:
     §Description) says only that the choice follows the packing configuration, not
     which strategy each configuration gets; the reading here is striped for packed
     sequences and dual-chunk-swap otherwise.  It is a policy, not a result: both
-    strategies give the same attention, and on the packed 8K workload of these
-    kernels dual-chunk-swap is the faster of the two."""
+    strategies give the same attention.  Under packing, dual-chunk-swap leaves the
+    ranks unequal (on the packed 8K workload of these kernels the heaviest rank holds
+    1.5x the mean of the visible pairs) while striped gives every rank the same
+    share; there the two tie on the slowest rank's time, which is what a step on P
+    GPUs takes, and dual-chunk-swap is faster only summed over the ranks."""
     return ops.STRIPED if packed else ops.DUAL_CHUNK_SWAP
 
 
