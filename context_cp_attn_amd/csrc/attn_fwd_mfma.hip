@@ -35,8 +35,10 @@
 //  * Causal grids run the heaviest query tiles of every head first.
 //  * Grids with fewer query tiles than two rounds of workgroup slots split each
 //    tile's live key tiles over two key groups: two wavefront groups of one
-//    workgroup combining through LDS, or (with a workspace and >= 8192 keys) two
-//    workgroups whose float32 partials a combine kernel merges.
+//    workgroup combining through LDS, or (with a workspace, >= 8192 keys and, at
+//    D = 128, at most 1.5 query tiles per CU) two workgroups whose float32
+//    partials a combine kernel merges.  In the fused ring step over a short block
+//    the two groups of a workgroup synchronise each on its own after every tile.
 #include <type_traits>
 
 #include "mfma_common.h"

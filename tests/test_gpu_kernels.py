@@ -374,7 +374,8 @@ def test_attn_fwd_merge(cp, name, dtype, D):
 
 
 @pytest.mark.parametrize("case", ["64_tiles", "64_tiles_and_1_key", "65_tiles", "causal_straddle"])
-@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 128)])
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.bfloat16, 32),
+                                     (torch.float32, 128)])
 def test_attn_fwd_merge_group_sync_boundary(cp, case, dtype, D):
     """The fused ring step on a grid of few query tiles walks each tile's keys with two
     key groups of one workgroup.  Each group waits only for its own waves after a key
