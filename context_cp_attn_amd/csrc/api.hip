@@ -112,9 +112,10 @@ cp_status_t check_attn(const cp_attn_args_t* a, const void* q, const void* k, co
         a->seqlen_k * a->heads_kv * a->head_dim * eb >= (int64_t(1) << 31))
       return fail(CP_ERR_UNSUPPORTED, "one batch of q or k/v exceeds 2^31 bytes");
   }
-  if (!a->q_pos && (a->q_offset < 0 || a->q_offset + a->seqlen_q > INT_MAX))
+  // (seqlen <= INT_MAX here, so the bounds are formed without overflow)
+  if (!a->q_pos && (a->q_offset < 0 || a->q_offset > INT_MAX - a->seqlen_q))
     return fail(CP_ERR_INVALID, "q_offset %lld: positions must lie in [0, 2^31)", (long long)a->q_offset);
-  if (!a->k_pos && (a->k_offset < 0 || a->k_offset + a->seqlen_k > INT_MAX))
+  if (!a->k_pos && (a->k_offset < 0 || a->k_offset > INT_MAX - a->seqlen_k))
     return fail(CP_ERR_INVALID, "k_offset %lld: positions must lie in [0, 2^31)", (long long)a->k_offset);
   if (mfma_path(a)) {
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
@@ -166,16 +167,14 @@ namespace {
 // problem is invalid, not on the matrix-core path, or large enough to fill the
 // current device with whole query tiles).
 size_t fwd_workspace_bytes(const cp_attn_args_t* a) {
-  if (!a || a->batch < 1 || a->seqlen_q < 1 || a->seqlen_k < 1 || a->heads_q < 1 || a->batch > 65535 ||
-      a->heads_q > 65535 || a->seqlen_q > INT_MAX || a->seqlen_k > INT_MAX || !mfma_path(a))
-    return 0;
-  cp::AttnProblem p{};
-  p.B = int(a->batch);
-  p.Sq = int(a->seqlen_q);
-  p.Sk = int(a->seqlen_k);
-  p.Hq = int(a->heads_q);
-  p.D = int(a->head_dim);
-  if (!cp::fwd_split_applies(p)) return 0;
+  if (!a || !mfma_path(a)) return 0;
+  // the call's own validation (on stand-in pointers), without touching the caller's
+  // last error
+  cp::AttnProblem p;
+  const std::string saved = g_last_error;
+  const bool valid = check_attn(a, kProbe, kProbe, kProbe, &p) == CP_OK;
+  g_last_error = saved;
+  if (!valid || !cp::fwd_split_applies(p)) return 0;
   return (cp::fwd_split_workspace_bytes(p) + 255) & ~size_t(255);
 }
 

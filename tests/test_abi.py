@@ -63,6 +63,10 @@ def fwd(a, q=FAKE_A, k=FAKE_B, v=FAKE_C, out=1 << 44, lse=1 << 45):
     (dict(q_seg=FAKE_A), INVALID, "both"),
     (dict(softmax_scale=-1.0), INVALID, "softmax_scale"),
     (dict(q_offset=-5), INVALID, "q_offset"),
+    # the last position would pass 2^31 (and q_offset + seqlen_q would pass 2^63)
+    (dict(q_offset=(1 << 31) - 64), INVALID, "q_offset"),
+    (dict(q_offset=(1 << 63) - 8), INVALID, "q_offset"),
+    (dict(k_offset=(1 << 63) - 8), INVALID, "k_offset"),
     (dict(head_dim=256), UNSUPPORTED, "head_dim"),
     (dict(head_dim=256, dtype=1), UNSUPPORTED, "head_dim"),
     # bounded before the byte-size test multiplies by it
@@ -101,6 +105,10 @@ def test_attn_fwd_workspace_rules():
     assert size(args(head_dim=16)) == 0              # bf16 without a matrix-core kernel
     assert size(args(seqlen_q=1 << 17, heads_q=16, heads_kv=2)) == 0   # fills the device
     assert size(args(batch=0)) == 0
+    # shapes the call itself refuses get no workspace size either
+    assert size(args(batch=65535, heads_q=65535, heads_kv=1, seqlen_q=1 << 30, seqlen_k=1 << 30)) == 0
+    assert size(args(seqlen_k=8192, q_offset=-1)) == 0
+    assert size(args(seqlen_k=8192, heads_q=6, heads_kv=4)) == 0
 
     def call(a, ws, nbytes):
         st = lib.cp_attn_fwd_ws(ctypes.byref(a), FAKE_A, FAKE_B, FAKE_C, 1 << 44, 1 << 45, ws, nbytes, None)
