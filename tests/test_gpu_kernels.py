@@ -6,6 +6,8 @@ attention float32 max-abs 1e-5 (out and lse); bf16 out 1e-2 and lse 1e-3; gradie
 1e-2 * max(1, max|ref|) (bf16) and 1e-5 * max(1, max|ref|) (float32).
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -659,3 +661,72 @@ def test_single_token_and_gqa_8(cp):
     ref_o, ref_l = oracle.attn_fwd(q, k, v)
     check_lse(lse, ref_l, 1e-3)
     check_close(out, ref_o, 1e-2, "out")
+
+
+def _random_problem(seed):
+    """A seeded random attention block: shapes, grouped heads, head dim and a mask
+    drawn from offsets, non-causal, windows, segment ids and position arrays (alone
+    and combined), as ring and packed shares produce them."""
+    rng = np.random.default_rng(1000 + seed)
+    D = int(rng.choice([32, 64, 128]))
+    B = int(rng.choice([1, 2]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    Hq = Hkv * int(rng.choice([1, 2, 3, 4]))
+    Sq, Sk = int(rng.integers(1, 401)), int(rng.integers(1, 521))
+    kind = ["offsets", "noncausal", "window", "segments", "positions", "positions_segments_window"][seed % 6]
+    m = {}
+    if kind in ("offsets", "window"):
+        m.update(q_offset=int(rng.integers(0, 400)), k_offset=int(rng.integers(0, 400)))
+    if kind == "noncausal":
+        m.update(causal=False)
+    if "window" in kind:
+        m.update(window=int(rng.integers(1, 300)))
+    if "positions" in kind:
+        # strictly increasing global positions, as a zigzag or striped share holds them
+        m.update(q_pos=np.sort(rng.choice(4 * max(Sq, Sk), Sq, replace=False)),
+                 k_pos=np.sort(rng.choice(4 * max(Sq, Sk), Sk, replace=False)))
+    if "segments" in kind:
+        # non-decreasing document ids of each batch row, over a shared range of ids
+        nd = int(rng.integers(1, 8))
+        m.update(q_seg=torch.from_numpy(np.sort(rng.integers(0, nd, (B, Sq)), axis=1).astype(np.int32)),
+                 k_seg=torch.from_numpy(np.sort(rng.integers(0, nd, (B, Sk)), axis=1).astype(np.int32)))
+    return (B, Sq, Sk, Hq, Hkv, D), kind, m
+
+
+# seeds of the random-block sweep (CP_RANDOM_BLOCKS widens it; 300 pass)
+RANDOM_BLOCKS = int(os.environ.get("CP_RANDOM_BLOCKS", "48"))
+
+
+@pytest.mark.parametrize("seed", range(RANDOM_BLOCKS))
+def test_attn_random_blocks(cp, seed):
+    """Seeded random blocks (bf16, matrix-core head dims): forward with and without a
+    workspace, the fused ring step from a running result, and the backward, each
+    against the oracle."""
+    (B, Sq, Sk, Hq, Hkv, D), kind, m = _random_problem(seed)
+    say(f"attn random seed={seed} B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hkv={Hkv} D={D} {kind}")
+    q, k, v, do = cp_inputs.normal_tensors([(B, Sq, Hq, D), (B, Sk, Hkv, D), (B, Sk, Hkv, D), (B, Sq, Hq, D)],
+                                           seed=50 + seed, dtype=torch.bfloat16)
+    dm = to_dev(m)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    out, lse = cp.attn_fwd(qd, kd, vd, **dm)
+    out1, lse1 = cp.attn_fwd(qd, kd, vd, workspace=False, **dm)
+    g = torch.Generator().manual_seed(seed)
+    acc0 = torch.randn(B, Sq, Hq, D, generator=g)
+    lse0 = torch.randn(B, Hq, Sq, generator=g) + 2
+    lse0[..., ::7] = -float("inf")
+    acc0[lse0.transpose(1, 2) == -float("inf")] = 0.0
+    acc, lacc = acc0.cuda(), lse0.cuda()
+    cp.attn_fwd_merge(qd, kd, vd, acc, lacc, **dm)
+    dq, dk, dv = cp.attn_bwd(qd, kd, vd, out, lse, dod, **dm)
+    om = oracle_mask(m)
+    ref_o, ref_l = oracle.attn_fwd(q, k, v, **om)
+    tol = TOL[torch.bfloat16]
+    for o_, l_, nm in ((out, lse, "ws"), (out1, lse1, "no ws")):
+        check_lse(l_, ref_l, tol["lse"])
+        check_close(o_, ref_o, tol["out"], f"out ({nm})")
+    mo, ml = oracle.lse_merge(f64(acc0), f64(lse0), ref_o, ref_l)
+    check_lse(lacc, ml, tol["lse"])
+    check_close(acc, mo, tol["out"], "merged out")
+    refs = oracle.attn_bwd(q, k, v, ref_o, ref_l, do, **om)
+    for got, ref, nm in zip((dq, dk, dv), refs, ("dq", "dk", "dv")):
+        check_close(got, ref, tol["grad"] * max(1.0, np.abs(ref).max()), nm)
