@@ -730,3 +730,59 @@ def test_attn_random_blocks(cp, seed):
     refs = oracle.attn_bwd(q, k, v, ref_o, ref_l, do, **om)
     for got, ref, nm in zip((dq, dk, dv), refs, ("dq", "dk", "dv")):
         check_close(got, ref, tol["grad"] * max(1.0, np.abs(ref).max()), nm)
+
+
+def _random_rows(rng, shape, dtype):
+    if dtype in (torch.int32, torch.uint8):
+        hi = 251 if dtype == torch.uint8 else 1 << 30
+        return torch.from_numpy(rng.integers(0, hi, shape).astype(np.int64)).to(dtype)
+    return torch.from_numpy(rng.standard_normal(shape)).to(dtype)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_permutations_random(cp, seed):
+    """Seeded random shapes for the data-movement kernels, bit for bit against the
+    oracle: the grouped / replicated Ulysses relayout and its inverse, both reorder
+    strategies and their inverses, and end padding / truncation.  Element sizes 1, 2
+    and 4 bytes, odd row sizes, degrees 1-8."""
+    rng = np.random.default_rng(2000 + seed)
+    dtype = [torch.bfloat16, torch.float32, torch.int32, torch.uint8][seed % 4]
+    say(f"permutations random seed={seed} {dtype}")
+    # relayout (element sizes 2 and 4)
+    if dtype != torch.uint8:
+        G, P, B = int(rng.integers(1, 4)), int(rng.integers(1, 9)), int(rng.integers(1, 3))
+        rep = int(rng.choice([1, 1, 2, 4]))
+        H = P * int(rng.integers(1, 4))
+        if rep > 1 and P % rep == 0 and rng.random() < 0.5:
+            H = (P // rep) * int(rng.integers(1, 3))   # fewer heads than the degree
+        D = int(rng.integers(1, 70))
+        S = P * int(rng.integers(1, 40))
+        x = _random_rows(rng, (G, P, B, S // P, H, D), dtype).cuda()
+        y = cp.ulysses_relayout_ex(x, P, groups=G, rep=rep)
+        ref = np.stack([oracle.ulysses_relayout_rep(bits(x[g]), rep) for g in range(G)])
+        np.testing.assert_array_equal(bits(y), ref)
+        if rep == 1:
+            z = cp.ulysses_relayout_ex(y, P, groups=G, inverse=True)
+            np.testing.assert_array_equal(bits(z), oracle.usp_relayout_inv(bits(y)))
+            assert torch.equal(z, x)
+    # reorders
+    P = int(rng.integers(1, 9))
+    B = int(rng.integers(1, 4))
+    tail = tuple(int(t) for t in rng.integers(1, 12, int(rng.integers(0, 3))))
+    for strategy, unit in ((0, 2 * P), (1, P)):
+        S = unit * int(rng.integers(1, 30))
+        x = _random_rows(rng, (B, S) + tail, dtype).cuda()
+        fwd, inv = ((oracle.reorder, oracle.reorder_inv) if strategy == 0
+                    else (oracle.reorder_striped, oracle.reorder_striped_inv))
+        y = cp.zigzag_reorder(x, P, strategy=strategy)
+        np.testing.assert_array_equal(bits(y), fwd(bits(x), P))
+        z = cp.zigzag_reorder(y, P, inverse=True, strategy=strategy)
+        np.testing.assert_array_equal(bits(z), inv(bits(y), P))
+    # padding and truncation
+    S = int(rng.integers(1, 300))
+    S_out = max(1, S + int(rng.integers(-S // 2, 40)))
+    x = _random_rows(rng, (B, S) + tail, dtype)
+    row_bytes = int(np.prod(tail, dtype=np.int64)) * x.element_size()
+    fill = int(rng.integers(1, 1000)) if dtype == torch.int32 and row_bytes % 4 == 0 and seed % 2 else 0
+    y = cp.pad_rows(x.cuda(), S_out, fill=fill)
+    np.testing.assert_array_equal(bits(y), oracle.pad_rows(bits(x), S_out, fill=fill))
