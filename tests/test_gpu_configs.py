@@ -425,3 +425,53 @@ def test_ring_forward_graph_replays(cp, fused):
     qf, kf, vf = (f64(t) for t in (q, k, v))
     ro, rl = oracle.attn_fwd(qf[:, pos[pick]], kf, vf, q_pos=pos[pick])
     check_rows(f64(go)[:, pick], f64(gl)[:, :, pick], ro, rl, 1e-2, 1e-3)
+
+
+# ------------------------------------------------------------------ random ring shares
+
+@pytest.mark.parametrize("seed", range(16))
+def test_ring_random_shares(cp, seed):
+    """Seeded random ring passes through the driver: degree 2-4, contiguous / zigzag /
+    striped partition, grouped heads, D 64 or 128, packed documents and a window
+    (alone or together), the fused or the unfused step; every rank's out and lse, and
+    dq, dk, dv of the whole sequence after all ranks' backward passes, against the
+    oracle's attention over the whole sequence."""
+    rng = np.random.default_rng(3000 + seed)
+    P = int(rng.integers(2, 5))
+    S = 2 * P * int(rng.integers(8, 97))
+    Hkv = int(rng.choice([1, 2]))
+    Hq = Hkv * int(rng.choice([1, 2, 4]))
+    D = int(rng.choice([64, 128]))
+    layout = ["zigzag", "striped", "contiguous"][seed % 3]
+    use_seg, window = bool(rng.integers(0, 2)), int(rng.choice([0, 0, int(rng.integers(1, S))]))
+    fused = [None, True, False][(seed // 3) % 3]
+    say(f"ring random seed={seed} P={P} S={S} Hq={Hq} Hkv={Hkv} D={D} {layout} seg={use_seg} "
+        f"window={window} fused={fused}")
+    q, k, v, do = cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D), (1, S, Hq, D)],
+                                           seed=70 + seed)
+    seg = cp_inputs.random_segment_ids(S, 1, max(2, S // 3), seed=seed) if use_seg else None
+    mask = dict(window=window)
+    if seg is not None:
+        mask.update(q_seg=seg.numpy(), k_seg=seg.numpy())
+    ro, rl = oracle.attn_fwd(q, k, v, **mask)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, ro, rl, do, **mask)
+    st = {"zigzag": 0, "striped": 1}.get(layout)
+    dev = [t.cuda() for t in (q, k, v, do)] + ([seg.cuda()] if seg is not None else [])
+    if st is not None:
+        dev = [cp.zigzag_reorder(t, P, strategy=st) for t in dev]
+    qd, kd, vd, dd = dev[:4]
+    sd = dev[4] if seg is not None else None
+    C = S // P
+    dk, dv = torch.zeros(kd.shape, device="cuda"), torch.zeros(vd.shape, device="cuda")
+    for r in range(P):
+        sh = cp.drivers.RingShare(qd, kd, vd, P, r, layout, seg=sd, window=window, fused=fused)
+        acc, lse = sh.forward()
+        pos = oracle.rank_positions(r, P, S, layout)
+        check_rows(f64(acc), f64(lse), ro[:, pos], rl[:, :, pos], 1e-2, 1e-3)
+        dq = torch.zeros(acc.shape, device="cuda")
+        sh.backward(acc.bfloat16(), lse, dd[:, r * C:(r + 1) * C], dq, dk, dv)
+        assert max_err(f64(dq), rq[:, pos]) <= grad_tol(rq), f"rank {r} dq"
+    if st is not None:
+        dk, dv = (cp.zigzag_reorder(t, P, inverse=True, strategy=st) for t in (dk, dv))
+    assert max_err(f64(dk), rk) <= grad_tol(rk), "dk"
+    assert max_err(f64(dv), rv) <= grad_tol(rv), "dv"
