@@ -6,6 +6,7 @@ attention float32 max-abs 1e-5 (out and lse); bf16 out 1e-2 and lse 1e-3; gradie
 1e-2 * max(1, max|ref|) (bf16) and 1e-5 * max(1, max|ref|) (float32).
 """
 
+import math
 import os
 
 import numpy as np
@@ -786,3 +787,44 @@ def test_permutations_random(cp, seed):
     fill = int(rng.integers(1, 1000)) if dtype == torch.int32 and row_bytes % 4 == 0 and seed % 2 else 0
     y = cp.pad_rows(x.cuda(), S_out, fill=fill)
     np.testing.assert_array_equal(bits(y), oracle.pad_rows(bits(x), S_out, fill=fill))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_ulysses_random(cp, seed):
+    """Seeded random Ulysses passes through the driver: degree 1-8 (kv heads
+    replicated where the degree exceeds them), grouped heads, D 64 or 128, causal or
+    not, windows and packed documents; out, lse, dq, dk, dv against the oracle's
+    attention over the whole sequence."""
+    rng = np.random.default_rng(4000 + seed)
+    P = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4]))
+    while (Hkv * G) % P:
+        G *= 2
+    Hq = Hkv * G
+    rep = P // math.gcd(P, Hkv)
+    D = int(rng.choice([64, 128]))
+    S = P * int(rng.integers(4, 80))
+    m = {}
+    kind = seed % 4
+    if kind == 1:
+        m["causal"] = False
+    elif kind == 2:
+        m["window"] = int(rng.integers(1, S))
+    elif kind == 3:
+        seg = cp_inputs.random_segment_ids(S, 1, max(2, S // 2), seed=seed)
+        m.update(q_seg=seg, k_seg=seg)
+    say(f"ulysses random seed={seed} P={P} Hq={Hq} Hkv={Hkv} rep={rep} D={D} S={S} {sorted(m)}")
+    q, k, v, do = cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D), (1, S, Hq, D)],
+                                           seed=90 + seed)
+    st = lambda t: t.reshape(P, 1, S // P, t.shape[2], D).cuda()
+    dm = to_dev(m)
+    out, lse, rel = cp.drivers.ulysses_forward(st(q), st(k), st(v), P, kv_rep=rep, **dm)
+    om = oracle_mask(m)
+    ro, rl = oracle.attn_fwd(q, k, v, **om)
+    check_close(out.reshape(1, S, Hq, D), ro, 1e-2, "out")
+    check_lse(torch.cat(list(lse), dim=1), rl, 1e-3)
+    dq, dk, dv = cp.drivers.ulysses_backward(rel, lse, st(do), P, kv_rep=rep, **dm)
+    refs = oracle.attn_bwd(q, k, v, ro, rl, do, **om)
+    for got, ref, nm in zip((dq, dk, dv), refs, ("dq", "dk", "dv")):
+        check_close(got.reshape(ref.shape), ref, 1e-2 * max(1.0, np.abs(ref).max()), nm)
