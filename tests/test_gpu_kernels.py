@@ -828,3 +828,35 @@ def test_ulysses_random(cp, seed):
     refs = oracle.attn_bwd(q, k, v, ro, rl, do, **om)
     for got, ref, nm in zip((dq, dk, dv), refs, ("dq", "dk", "dv")):
         check_close(got.reshape(ref.shape), ref, 1e-2 * max(1.0, np.abs(ref).max()), nm)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_usp_random(cp, seed):
+    """Seeded random Ulysses x ring (USP) passes: Pr ring groups of Pu Ulysses ranks
+    (kv heads replicated where Pu exceeds them), grouped heads, causal, windows and
+    packed documents; out, dq, dk, dv against the oracle's full attention."""
+    rng = np.random.default_rng(5000 + seed)
+    Pr, Pu = int(rng.choice([2, 3, 4])), int(rng.choice([1, 2, 4]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4]))
+    while (Hkv * G) % Pu:
+        G *= 2
+    Hq = Hkv * G
+    rep = Pu // math.gcd(Pu, Hkv)
+    D = int(rng.choice([64, 128]))
+    S = 2 * Pr * Pu * int(rng.integers(4, 40))
+    seg = cp_inputs.random_segment_ids(S, 1, max(2, S // 3), seed=seed) if seed % 2 else None
+    window = int(rng.integers(1, S)) if seed % 4 >= 2 else 0
+    say(f"usp random seed={seed} Pr={Pr} Pu={Pu} Hq={Hq} Hkv={Hkv} rep={rep} D={D} S={S} "
+        f"seg={seg is not None} window={window}")
+    q, k, v, do = cp_inputs.normal_tensors([(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D), (1, S, Hq, D)],
+                                           seed=110 + seed)
+    out, lse, state = cp.drivers.usp_forward(q.cuda(), k.cuda(), v.cuda(), Pr, Pu, kv_rep=rep,
+                                             seg=None if seg is None else seg.cuda(), window=window, keep=True)
+    dq, dk, dv = cp.drivers.usp_backward(state, lse, do.cuda())
+    sm = {} if seg is None else dict(q_seg=seg.numpy(), k_seg=seg.numpy())
+    ro, rl = oracle.attn_fwd(q, k, v, window=window, **sm)
+    check_close(out, ro, 1e-2, "usp out")
+    refs = oracle.attn_bwd(q, k, v, ro, rl, do, window=window, **sm)
+    for got, ref, nm in zip((dq, dk, dv), refs, ("dq", "dk", "dv")):
+        check_close(got, ref, 1e-2 * max(1.0, np.abs(ref).max()), f"usp {nm}")
