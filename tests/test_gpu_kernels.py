@@ -860,3 +860,44 @@ def test_usp_random(cp, seed):
     refs = oracle.attn_bwd(q, k, v, ro, rl, do, window=window, **sm)
     for got, ref, nm in zip((dq, dk, dv), refs, ("dq", "dk", "dv")):
         check_close(got, ref, 1e-2 * max(1.0, np.abs(ref).max()), f"usp {nm}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_attn_random_blocks_rowwise(cp, seed):
+    """The random blocks of test_attn_random_blocks on the row-per-wavefront kernels:
+    float32 (any D up to 128) and bf16 head dims without a matrix-core kernel; forward,
+    fused ring step and backward against the oracle at their own bars."""
+    (B, Sq, Sk, Hq, Hkv, _), kind, m = _random_problem(seed)
+    rng = np.random.default_rng(6000 + seed)
+    dtype = torch.float32 if seed % 2 == 0 else torch.bfloat16
+    D = int(rng.integers(1, 129)) if dtype == torch.float32 else int(rng.choice([8, 16, 24, 48, 80, 96, 112]))
+    Sq, Sk = min(Sq, 160), min(Sk, 200)    # one wavefront per row: kept small
+    if "q_pos" in m:
+        m["q_pos"], m["k_pos"] = m["q_pos"][:Sq], m["k_pos"][:Sk]
+    if "q_seg" in m:
+        m["q_seg"], m["k_seg"] = m["q_seg"][:, :Sq].contiguous(), m["k_seg"][:, :Sk].contiguous()
+    say(f"attn random rowwise seed={seed} B={B} Sq={Sq} Sk={Sk} Hq={Hq} Hkv={Hkv} D={D} {dtype} {kind}")
+    q, k, v, do = cp_inputs.normal_tensors([(B, Sq, Hq, D), (B, Sk, Hkv, D), (B, Sk, Hkv, D), (B, Sq, Hq, D)],
+                                           seed=150 + seed, dtype=dtype)
+    dm = to_dev(m)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    out, lse = cp.attn_fwd(qd, kd, vd, **dm)
+    g = torch.Generator().manual_seed(seed)
+    acc0 = torch.randn(B, Sq, Hq, D, generator=g)
+    lse0 = torch.randn(B, Hq, Sq, generator=g) + 2
+    acc, lacc = acc0.cuda(), lse0.cuda()
+    cp.attn_fwd_merge(qd, kd, vd, acc, lacc, **dm)
+    dq, dk, dv = cp.attn_bwd(qd, kd, vd, out, lse, dod, **dm)
+    om = oracle_mask(m)
+    ref_o, ref_l = oracle.attn_fwd(q, k, v, **om)
+    tol = TOL[dtype]
+    check_lse(lse, ref_l, tol["lse"])
+    check_close(out, ref_o, tol["out"], "out")
+    mo, ml = oracle.lse_merge(f64(acc0), f64(lse0), ref_o, ref_l)
+    check_lse(lacc, ml, tol["lse"])
+    check_close(acc, mo, tol["out"], "merged out")
+    # the backward's rows are the GPU forward's (bf16 out rounded): the oracle takes
+    # its own exact forward, within the gradient bar
+    refs = oracle.attn_bwd(q, k, v, ref_o, ref_l, do, **om)
+    for got, ref, nm in zip((dq, dk, dv), refs, ("dq", "dk", "dv")):
+        check_close(got, ref, tol["grad"] * max(1.0, np.abs(ref).max()), nm)
